@@ -1,0 +1,634 @@
+// C ABI of libbsa: argument validation, workspace layout and launch order.
+#include <math.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/bsa.h"
+#include "bsa_internal.h"
+
+#define BSA_API extern "C" __attribute__((visibility("default")))
+
+namespace bsa {
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+static thread_local std::string g_err;
+void set_error(const std::string& msg) { g_err = msg; }
+
+static bsa_status fail(bsa_status st, const std::string& msg) {
+  set_error(msg);
+  return st;
+}
+
+bool launch_ok(const char* name) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error(std::string("launch of ") + name + " failed: " + hipGetErrorString(e));
+    return false;
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// launch timer
+// ---------------------------------------------------------------------------
+struct TimerRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+static bool g_timer_on = false;
+static std::vector<TimerRec> g_timer;
+
+LaunchScope::LaunchScope(const char* n, hipStream_t s) : name(n), stream(s), slot(-1) {
+  if (!g_timer_on) return;
+  TimerRec r;
+  r.name = n;
+  if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
+  (void)hipEventRecord(r.a, s);
+  g_timer.push_back(r);
+  slot = (int)g_timer.size() - 1;
+}
+LaunchScope::~LaunchScope() {
+  if (slot >= 0) (void)hipEventRecord(g_timer[slot].b, stream);
+}
+
+static void timer_clear() {
+  for (auto& r : g_timer) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_timer.clear();
+}
+
+// ---------------------------------------------------------------------------
+// workspace carving
+// ---------------------------------------------------------------------------
+struct Carver {
+  size_t off = 0;
+  char* base = nullptr;
+  template <typename T>
+  T* take(int64_t n) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += (size_t)std::max<int64_t>(n, 0) * sizeof(T);
+    return p;
+  }
+};
+
+static void omega_table(double theta, int D, double* out) {
+  for (int i = 0; i < D / 2; ++i) out[i] = pow(theta, -2.0 * (double)i / (double)D);
+}
+
+static bool dim_ok(int D) { return D == 64 || D == 128; }
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+static bool strides_ok(const int64_t* s, int n, int D, int elt) {
+  for (int i = 0; i < n; ++i)
+    if (s[i] < 0 || ((s[i] * elt) & 15) != 0) return false;
+  (void)D;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// prefill plan
+// ---------------------------------------------------------------------------
+struct PrefillPlan {
+  int Nb, Hs, G, Dg, topk, kslot, sel_w, R, Gs, nbk;
+  bool bf16, per_group, use_index, rope_q, rope_k, have_pooled;
+  int nsplit, span, gate_qkind, ntiles, rows_per_bh;
+  int64_t nsel_rows, max_entries, max_items;
+  int attn_grid;
+  // workspace pointers
+  int32_t *pos_q, *pos_k, *chunk_q, *chunk_k;
+  uint16_t *q16, *k16;
+  float *q32, *k32;
+  uint16_t *p_hi, *p_lo;
+  float* pooled32;
+  uint64_t* part_keys;
+  int32_t* sel;
+  int32_t *counts, *cursor, *bucket_off, *tile_off, *scan_tmp;
+  uint32_t* entries;
+  int2* items;
+  uint16_t* part_o;
+  float* part_lse;
+  size_t bytes;
+};
+
+static int gate_waves_for(int rows_per_bh, int topk) {
+  const int v = (2 * topk + 64) <= 128 ? 2 : 4;
+  if (rows_per_bh <= 16) return 1;
+  return v == 2 ? 4 : 2;
+}
+
+static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* ws, bool gate_only) {
+  if (!a) return fail(BSA_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != BSA_DTYPE_F32 && a->dtype != BSA_DTYPE_BF16) return fail(BSA_ERR_INVALID_ARG, "dtype");
+  if (a->B < 1 || a->Lq < 1 || a->Lk < 1 || a->Hq < 1 || a->Hkv < 1) return fail(BSA_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (a->Hq % a->Hkv) return fail(BSA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+  if (!dim_ok(a->D)) return fail(BSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (a->block < 1) return fail(BSA_ERR_INVALID_ARG, "block must be >= 1");
+  if (a->topk < 0) return fail(BSA_ERR_INVALID_ARG, "topk must be >= 0");
+  if (a->causal != 0 && a->causal != 1) return fail(BSA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (a->causal && a->Lq > a->Lk) return fail(BSA_ERR_INVALID_ARG, "causal needs Lq <= Lk");
+  if (a->gate_mode != BSA_GATE_PER_HEAD && a->gate_mode != BSA_GATE_PER_GROUP) return fail(BSA_ERR_INVALID_ARG, "gate_mode");
+  if (!a->q || !a->k) return fail(BSA_ERR_INVALID_ARG, "q and k are required");
+  if (!gate_only && (!a->v || !a->o)) return fail(BSA_ERR_INVALID_ARG, "v and o are required");
+  if (gate_only && !a->sel_out) return fail(BSA_ERR_INVALID_ARG, "sel_out is required for bsa_select_blocks");
+  if ((a->index_q == nullptr) != (a->index_k == nullptr)) return fail(BSA_ERR_INVALID_ARG, "index_q and index_k go together");
+  const int elt = a->dtype == BSA_DTYPE_BF16 ? 2 : 4;
+  if (!aligned16(a->q) || !aligned16(a->k) || (a->v && !aligned16(a->v)) || (a->o && !aligned16(a->o)))
+    return fail(BSA_ERR_INVALID_ARG, "tensor base pointers must be 16-byte aligned");
+  if (!strides_ok(a->q_stride, 3, a->D, elt) || !strides_ok(a->k_stride, 3, a->D, elt) ||
+      (!gate_only && (!strides_ok(a->v_stride, 3, a->D, elt) || !strides_ok(a->o_stride, 3, a->D, elt))))
+    return fail(BSA_ERR_INVALID_ARG, "strides must be non-negative and keep rows 16-byte aligned");
+  P.bf16 = a->dtype == BSA_DTYPE_BF16;
+  P.per_group = a->gate_mode == BSA_GATE_PER_GROUP;
+  P.use_index = a->index_q != nullptr;
+  P.G = a->Hq / a->Hkv;
+  P.Nb = (int)(((int64_t)a->Lk + a->block - 1) / a->block);
+  P.Hs = P.per_group ? a->Hkv : a->Hq;
+  P.Dg = P.use_index ? a->Di : a->D;
+  if (P.use_index) {
+    if (!dim_ok(a->Di)) return fail(BSA_ERR_UNSUPPORTED, "index dim must be 64 or 128");
+    if (!aligned16(a->index_q) || !aligned16(a->index_k) || !strides_ok(a->iq_stride, 3, a->Di, elt) ||
+        !strides_ok(a->ik_stride, 3, a->Di, elt))
+      return fail(BSA_ERR_INVALID_ARG, "index tensor alignment/strides");
+  }
+  if (a->topk > BSA_MAX_TOPK) return fail(BSA_ERR_UNSUPPORTED, "topk above BSA_MAX_TOPK");
+  P.topk = std::min(a->topk, P.Nb);
+  P.kslot = std::max(P.topk, 1);
+  P.sel_w = a->topk + (a->causal ? 1 : 0);
+  P.R = P.per_group ? P.G : 1;
+  P.Gs = P.per_group ? 1 : P.G;
+  P.rope_q = a->doc_ids_q != nullptr;
+  P.rope_k = a->doc_ids_k != nullptr;
+  P.have_pooled = a->pooled != nullptr;
+  if (P.per_group && P.G > 8 && !P.bf16) {
+    // fp32 path sums in the gate kernel, no restriction; keep for symmetry
+  }
+  P.nsel_rows = (int64_t)a->B * P.Hs * a->Lq;
+  if (P.nsel_rows * P.sel_w >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "too many selection entries");
+  if ((int64_t)a->Lq * P.Gs * P.kslot >= ((int64_t)1 << 32)) return fail(BSA_ERR_UNSUPPORTED, "Lq * G * topk too large");
+  if ((int64_t)a->B * a->Hkv * P.Nb >= (int64_t)1 << 30) return fail(BSA_ERR_UNSUPPORTED, "too many KV blocks");
+  P.nbk = a->B * a->Hkv * P.Nb;
+  P.max_entries = P.nsel_rows * P.topk;
+  const int rows_item = 128;
+  P.max_items = (P.max_entries * P.R + rows_item - 1) / rows_item + std::min<int64_t>(P.nbk, P.max_entries);
+  // gate geometry
+  P.rows_per_bh = P.per_group ? a->Lq : a->Lq * P.G;
+  const int W = gate_waves_for(P.rows_per_bh, P.topk);
+  P.ntiles = (P.rows_per_bh + 16 * W - 1) / (16 * W);
+  const int64_t base_wg = (int64_t)a->B * a->Hkv * P.ntiles;
+  const int ncand_max = P.Nb;
+  P.nsplit = 1;
+  if (P.bf16 && P.topk > 0 && base_wg < 2048) {
+    const int want = (int)std::min<int64_t>((4096 + base_wg - 1) / base_wg, (ncand_max + 255) / 256);
+    P.nsplit = std::max(1, want);
+  }
+  P.span = (ncand_max + P.nsplit - 1) / P.nsplit;
+  P.span = (P.span + 63) / 64 * 64;
+  P.nsplit = (ncand_max + P.span - 1) / P.span;
+  if (P.nsplit < 1) P.nsplit = 1;
+  P.attn_grid = 256 * 8;  // persistent: 8 workgroups per CU
+
+  Carver c;
+  c.base = ws;
+  const int64_t B = a->B, Lq = a->Lq, Lk = a->Lk;
+  P.pos_q = P.rope_q ? c.take<int32_t>(B * Lq) : nullptr;
+  P.chunk_q = P.rope_q ? c.take<int32_t>(B * pos_chunks((int)Lq)) : nullptr;
+  P.pos_k = P.rope_k ? c.take<int32_t>(B * Lk) : nullptr;
+  P.chunk_k = P.rope_k ? c.take<int32_t>(B * pos_chunks((int)Lk)) : nullptr;
+  P.q16 = (P.rope_q && P.bf16) ? c.take<uint16_t>(B * Lq * a->Hq * a->D) : nullptr;
+  P.q32 = (P.rope_q && (!P.bf16 || !P.use_index)) ? c.take<float>(B * Lq * a->Hq * a->D) : nullptr;
+  P.k16 = (P.rope_k && P.bf16) ? c.take<uint16_t>(B * Lk * a->Hkv * a->D) : nullptr;
+  P.k32 = (P.rope_k && !P.bf16) ? c.take<float>(B * Lk * a->Hkv * a->D) : nullptr;
+  const int64_t npool = (int64_t)P.nbk * P.Dg;
+  if (P.bf16) {
+    P.p_hi = c.take<uint16_t>(npool);
+    P.p_lo = c.take<uint16_t>(npool);
+    P.pooled32 = nullptr;
+  } else {
+    P.p_hi = P.p_lo = nullptr;
+    P.pooled32 = P.have_pooled ? nullptr : c.take<float>(npool);
+  }
+  P.part_keys = (P.nsplit > 1) ? c.take<uint64_t>(P.nsel_rows * P.nsplit * P.topk) : nullptr;
+  P.sel = a->sel_out ? a->sel_out : c.take<int32_t>(P.nsel_rows * P.sel_w);
+  if (P.bf16 && !gate_only) {
+    P.counts = c.take<int32_t>(P.nbk);
+    P.cursor = c.take<int32_t>(P.nbk);
+    P.bucket_off = c.take<int32_t>(P.nbk + 1);
+    P.tile_off = c.take<int32_t>(P.nbk + 1);
+    P.scan_tmp = c.take<int32_t>(scan_tmp_len(P.nbk));
+    P.entries = c.take<uint32_t>(P.max_entries);
+    P.items = c.take<int2>(P.max_items);
+    P.part_o = c.take<uint16_t>(P.max_entries * P.R * a->D);
+    P.part_lse = c.take<float>(P.max_entries * P.R);
+  } else {
+    P.counts = P.cursor = P.bucket_off = P.tile_off = P.scan_tmp = nullptr;
+    P.entries = nullptr;
+    P.items = nullptr;
+    P.part_o = nullptr;
+    P.part_lse = nullptr;
+  }
+  P.bytes = c.off + 256;
+  return BSA_OK;
+}
+
+static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_bytes, void* stream, bool gate_only) {
+  PrefillPlan P;
+  bsa_status st = plan_prefill(a, P, nullptr, gate_only);
+  if (st != BSA_OK) return st;
+  if (!ws || ws_bytes < P.bytes) return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_prefill_workspace_bytes");
+  if (((uintptr_t)ws & 255) != 0) return fail(BSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  plan_prefill(a, P, reinterpret_cast<char*>(ws), gate_only);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const double theta = a->rope_theta > 0.f ? (double)a->rope_theta : 10000.0;
+  const int elt = P.bf16 ? 2 : 4;
+  (void)elt;
+
+  // 1. positions and RoPE
+  const void* q_att = a->q;
+  int64_t qa_s[3] = {a->q_stride[0], a->q_stride[1], a->q_stride[2]};
+  const void* k_att = a->k;
+  int64_t ka_s[3] = {a->k_stride[0], a->k_stride[1], a->k_stride[2]};
+  const int64_t qc_s[3] = {(int64_t)a->Lq * a->Hq * a->D, (int64_t)a->Hq * a->D, a->D};
+  const int64_t kc_s[3] = {(int64_t)a->Lk * a->Hkv * a->D, (int64_t)a->Hkv * a->D, a->D};
+  if (P.rope_q) {
+    if (!launch_doc_positions(a->doc_ids_q, a->B, a->Lq, P.chunk_q, P.pos_q, s)) return BSA_ERR_HIP;
+    RopeQParams rp;
+    rp.is_bf16 = P.bf16;
+    rp.B = a->B; rp.L = a->Lq; rp.H = a->Hq; rp.D = a->D;
+    rp.q = a->q; rp.qs_b = a->q_stride[0]; rp.qs_t = a->q_stride[1]; rp.qs_h = a->q_stride[2];
+    rp.pos = P.pos_q;
+    omega_table(theta, a->D, rp.omega);
+    rp.out16 = P.q16;
+    rp.out32 = P.q32;
+    if (!launch_rope_q(rp, s)) return BSA_ERR_HIP;
+    q_att = P.bf16 ? (const void*)P.q16 : (const void*)P.q32;
+    for (int i = 0; i < 3; ++i) qa_s[i] = qc_s[i];
+  }
+  const bool summarize = !P.have_pooled;
+  if (P.rope_k) {
+    if (!launch_doc_positions(a->doc_ids_k, a->B, a->Lk, P.chunk_k, P.pos_k, s)) return BSA_ERR_HIP;
+  }
+  // 2. block summaries (+ rotated keys)
+  {
+    SummaryParams sp;
+    sp.is_bf16 = P.bf16;
+    sp.B = a->B; sp.L = a->Lk; sp.H = a->Hkv; sp.block = a->block; sp.Nb = P.Nb;
+    sp.pooled_f32 = nullptr; sp.pooled_bf16 = nullptr; sp.plane_hi = nullptr; sp.plane_lo = nullptr; sp.k_rot = nullptr;
+    omega_table(theta, a->D, sp.omega);
+    if (P.use_index) {
+      // index keys drive the gate; keys for attention are rotated separately
+      if (summarize) {
+        sp.D = a->Di; sp.k = a->index_k;
+        sp.ks_b = a->ik_stride[0]; sp.ks_t = a->ik_stride[1]; sp.ks_h = a->ik_stride[2];
+        sp.pos = nullptr;
+        if (P.bf16) { sp.plane_hi = P.p_hi; sp.plane_lo = P.p_lo; } else sp.pooled_f32 = P.pooled32;
+        if (!launch_block_summary(sp, s)) return BSA_ERR_HIP;
+      }
+      if (P.rope_k && !gate_only) {
+        SummaryParams kr = sp;
+        kr.D = a->D; kr.k = a->k; kr.ks_b = a->k_stride[0]; kr.ks_t = a->k_stride[1]; kr.ks_h = a->k_stride[2];
+        kr.pos = P.pos_k; kr.plane_hi = kr.plane_lo = nullptr; kr.pooled_f32 = nullptr; kr.pooled_bf16 = nullptr;
+        kr.k_rot = P.bf16 ? (void*)P.k16 : (void*)P.k32;
+        if (!launch_block_summary(kr, s)) return BSA_ERR_HIP;
+      }
+    } else if (summarize || (P.rope_k && !gate_only)) {
+      sp.D = a->D; sp.k = a->k;
+      sp.ks_b = a->k_stride[0]; sp.ks_t = a->k_stride[1]; sp.ks_h = a->k_stride[2];
+      sp.pos = P.pos_k;
+      if (summarize) {
+        if (P.bf16) { sp.plane_hi = P.p_hi; sp.plane_lo = P.p_lo; } else sp.pooled_f32 = P.pooled32;
+      }
+      if (P.rope_k && !gate_only) sp.k_rot = P.bf16 ? (void*)P.k16 : (void*)P.k32;
+      if (!launch_block_summary(sp, s)) return BSA_ERR_HIP;
+    }
+    if (P.rope_k) {
+      k_att = P.bf16 ? (const void*)P.k16 : (const void*)P.k32;
+      for (int i = 0; i < 3; ++i) ka_s[i] = kc_s[i];
+    }
+    if (!summarize && P.bf16) {
+      const int64_t Nb = P.Nb, Hkv = a->Hkv, Dg = P.Dg;
+      if (!launch_pooled_to_planes(a->pooled, 0, Nb * Hkv * Dg, Hkv * Dg, Dg, a->B, P.Nb, a->Hkv, P.Dg, P.p_hi, P.p_lo, s))
+        return BSA_ERR_HIP;
+    }
+  }
+  // 3. gate + top-k
+  // gate query source: index q, else (rotated) q
+  const void* gq = P.use_index ? a->index_q : (P.rope_q ? (P.bf16 ? (const void*)P.q32 : (const void*)P.q32) : a->q);
+  int64_t gq_s[3];
+  if (P.use_index) { for (int i = 0; i < 3; ++i) gq_s[i] = a->iq_stride[i]; }
+  else if (P.rope_q) { for (int i = 0; i < 3; ++i) gq_s[i] = qc_s[i]; }
+  else { for (int i = 0; i < 3; ++i) gq_s[i] = a->q_stride[i]; }
+  const bool gq_f32 = !P.bf16 || (P.rope_q && !P.use_index);
+  if (P.bf16) {
+    GateParams g;
+    g.B = a->B; g.Lq = a->Lq; g.Lk = a->Lk; g.Hkv = a->Hkv; g.G = P.G; g.Hs = P.Hs; g.per_group = P.per_group;
+    g.rows_per_bh = P.rows_per_bh; g.ntiles = P.ntiles;
+    g.q = gq; g.qs_b = gq_s[0]; g.qs_t = gq_s[1]; g.qs_h = gq_s[2];
+    g.qkind = gq_f32 ? 1 : (P.per_group ? 2 : 0);
+    g.Dg = P.Dg;
+    g.p_hi = P.p_hi; g.p_lo = P.p_lo;
+    g.ps_h = (int64_t)P.Nb * P.Dg; g.ps_b = (int64_t)a->Hkv * g.ps_h; g.ps_j = P.Dg;
+    g.Nb = P.Nb; g.causal = a->causal; g.block = a->block; g.lens = nullptr;
+    g.topk = P.topk; g.nsplit = P.nsplit; g.span = P.span;
+    g.sel = P.sel; g.sel_w = P.sel_w; g.part = P.part_keys;
+    if (!launch_gate(g, s)) return BSA_ERR_HIP;
+    if (P.nsplit > 1 && !launch_gate_merge(g, s)) return BSA_ERR_HIP;
+  } else {
+    GateF32Params g;
+    g.B = a->B; g.Lq = a->Lq; g.Lk = a->Lk; g.Hkv = a->Hkv; g.G = P.G; g.Hs = P.Hs; g.per_group = P.per_group;
+    g.Dg = P.Dg;
+    g.q = reinterpret_cast<const float*>(gq); g.qs_b = gq_s[0]; g.qs_t = gq_s[1]; g.qs_h = gq_s[2];
+    g.pooled = P.have_pooled ? a->pooled : P.pooled32;
+    g.Nb = P.Nb; g.causal = a->causal; g.block = a->block; g.topk = P.topk;
+    g.sel = P.sel; g.sel_w = P.sel_w;
+    if (!launch_gate_f32(g, s)) return BSA_ERR_HIP;
+  }
+  if (gate_only) return BSA_OK;
+
+  // 4. attention
+  const float scale = a->scale != 0.f ? a->scale : (float)(1.0 / sqrt((double)a->D));
+  if (!P.bf16) {
+    AttnF32Params f;
+    f.B = a->B; f.Lq = a->Lq; f.Lk = a->Lk; f.Hq = a->Hq; f.Hkv = a->Hkv; f.G = P.G; f.D = a->D; f.block = a->block;
+    f.Hs = P.Hs; f.per_group = P.per_group; f.causal = a->causal;
+    f.q = reinterpret_cast<const float*>(q_att); f.qs_b = qa_s[0]; f.qs_t = qa_s[1]; f.qs_h = qa_s[2];
+    f.k = reinterpret_cast<const float*>(k_att); f.ks_b = ka_s[0]; f.ks_t = ka_s[1]; f.ks_h = ka_s[2];
+    f.v = reinterpret_cast<const float*>(a->v); f.vs_b = a->v_stride[0]; f.vs_t = a->v_stride[1]; f.vs_h = a->v_stride[2];
+    f.scale = scale;
+    f.sel = P.sel; f.sel_w = P.sel_w;
+    f.o = reinterpret_cast<float*>(a->o); f.os_b = a->o_stride[0]; f.os_t = a->o_stride[1]; f.os_h = a->o_stride[2];
+    f.lse_out = a->lse_out;
+    if (!launch_attn_rowwise_f32(f, s)) return BSA_ERR_HIP;
+    return BSA_OK;
+  }
+  AttnParams ap;
+  ap.B = a->B; ap.Lq = a->Lq; ap.Lk = a->Lk; ap.Hq = a->Hq; ap.Hkv = a->Hkv; ap.G = P.G; ap.D = a->D;
+  ap.block = a->block; ap.Nb = P.Nb; ap.Hs = P.Hs; ap.per_group = P.per_group; ap.Gs = P.Gs; ap.R = P.R;
+  ap.kslot = P.kslot; ap.causal = a->causal;
+  ap.q = reinterpret_cast<const uint16_t*>(q_att); ap.qs_b = qa_s[0]; ap.qs_t = qa_s[1]; ap.qs_h = qa_s[2];
+  ap.k = reinterpret_cast<const uint16_t*>(k_att); ap.ks_b = ka_s[0]; ap.ks_t = ka_s[1]; ap.ks_h = ka_s[2];
+  ap.v = reinterpret_cast<const uint16_t*>(a->v); ap.vs_b = a->v_stride[0]; ap.vs_t = a->v_stride[1]; ap.vs_h = a->v_stride[2];
+  ap.sl2 = (float)((double)scale * 1.4426950408889634074);
+  ap.entries = P.entries; ap.bucket_off = P.bucket_off; ap.tile_off = P.tile_off; ap.items = P.items;
+  ap.n_items = P.tile_off + P.nbk;
+  ap.grid = P.attn_grid;
+  ap.part_o = P.part_o; ap.part_lse = P.part_lse;
+  ap.sel = P.sel; ap.sel_w = P.sel_w;
+  ap.o = reinterpret_cast<uint16_t*>(a->o); ap.os_b = a->o_stride[0]; ap.os_t = a->o_stride[1]; ap.os_h = a->o_stride[2];
+  ap.lse_out = a->lse_out;
+  if (P.topk > 0) {
+    CsrParams cp;
+    cp.B = a->B; cp.Lq = a->Lq; cp.Lk = a->Lk; cp.Hkv = a->Hkv; cp.G = P.G; cp.Hs = P.Hs; cp.per_group = P.per_group;
+    cp.Nb = P.Nb; cp.block = a->block; cp.causal = a->causal;
+    cp.sel = P.sel; cp.sel_w = P.sel_w; cp.kslot = P.kslot; cp.R = P.R; cp.rows_item = 128;
+    cp.counts = P.counts; cp.cursor = P.cursor; cp.bucket_off = P.bucket_off; cp.tile_off = P.tile_off;
+    cp.scan_tmp = P.scan_tmp; cp.entries = P.entries; cp.items = P.items; cp.nbk = P.nbk;
+    if (!launch_csr(cp, s)) return BSA_ERR_HIP;
+    if (!launch_attn_gather(ap, s)) return BSA_ERR_HIP;
+  } else {
+    ap.kslot = 0;
+  }
+  if (!launch_attn_combine(ap, s)) return BSA_ERR_HIP;
+  return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// decode plan
+// ---------------------------------------------------------------------------
+struct DecodePlan {
+  int Nb, Hs, G, topk, umax, nsplit, span, sel_w, ntiles, rows_per_bh;
+  uint16_t *p_hi, *p_lo;
+  uint64_t* part_keys;
+  int32_t* sel;
+  int32_t *ulist, *ucount;
+  float *part_o, *part_lse;
+  size_t bytes;
+};
+
+static bsa_status plan_decode(const bsa_decode_args* a, DecodePlan& P, char* ws) {
+  if (!a) return fail(BSA_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != BSA_DTYPE_BF16) return fail(BSA_ERR_UNSUPPORTED, "decode supports bf16 q/k/v");
+  if (a->B < 1 || a->Lc < 1 || a->Hq < 1 || a->Hkv < 1) return fail(BSA_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (a->Hq % a->Hkv) return fail(BSA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+  if (!dim_ok(a->D)) return fail(BSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (a->block < 1) return fail(BSA_ERR_INVALID_ARG, "block must be >= 1");
+  if (a->topk < 0) return fail(BSA_ERR_INVALID_ARG, "topk must be >= 0");
+  if (a->topk > BSA_MAX_TOPK) return fail(BSA_ERR_UNSUPPORTED, "topk above BSA_MAX_TOPK");
+  if (a->gate_mode != BSA_GATE_PER_HEAD && a->gate_mode != BSA_GATE_PER_GROUP) return fail(BSA_ERR_INVALID_ARG, "gate_mode");
+  if (a->pooled_dtype != BSA_DTYPE_BF16 && a->pooled_dtype != BSA_DTYPE_F32) return fail(BSA_ERR_INVALID_ARG, "pooled_dtype");
+  if (!a->q || !a->kcache || !a->vcache || !a->pooled || !a->o) return fail(BSA_ERR_INVALID_ARG, "q, kcache, vcache, pooled and o are required");
+  P.G = a->Hq / a->Hkv;
+  if (P.G > 8) return fail(BSA_ERR_UNSUPPORTED, "decode supports at most 8 query heads per KV head");
+  if (a->block > (1 << 22)) return fail(BSA_ERR_UNSUPPORTED, "block too large");
+  P.Nb = (int)(((int64_t)a->Lc + a->block - 1) / a->block);
+  if (P.Nb >= (1 << 23)) return fail(BSA_ERR_UNSUPPORTED, "too many blocks for decode");
+  const bool per_group = a->gate_mode == BSA_GATE_PER_GROUP;
+  P.Hs = per_group ? a->Hkv : a->Hq;
+  P.topk = std::min(a->topk, P.Nb);
+  P.sel_w = a->topk + 1;
+  if ((per_group ? 1 : P.G) * P.sel_w > 512) return fail(BSA_ERR_UNSUPPORTED, "G * (topk + 1) above 512");
+  P.umax = (per_group ? 1 : P.G) * P.sel_w;
+  if (!aligned16(a->q) || !aligned16(a->kcache) || !aligned16(a->vcache) || !aligned16(a->pooled) || !aligned16(a->o))
+    return fail(BSA_ERR_INVALID_ARG, "tensor base pointers must be 16-byte aligned");
+  const int pe = a->pooled_dtype == BSA_DTYPE_BF16 ? 2 : 4;
+  if (!strides_ok(a->q_stride, 2, a->D, 2) || !strides_ok(a->k_stride, 3, a->D, 2) || !strides_ok(a->v_stride, 3, a->D, 2) ||
+      !strides_ok(a->o_stride, 2, a->D, 2) || !strides_ok(a->p_stride, 3, a->D, pe))
+    return fail(BSA_ERR_INVALID_ARG, "strides must be non-negative and keep rows 16-byte aligned");
+  P.rows_per_bh = per_group ? 1 : P.G;
+  P.ntiles = 1;
+  const int64_t base = (int64_t)a->B * a->Hkv;
+  const int ncand = P.Nb;
+  int want = (int)std::min<int64_t>((4096 + base - 1) / base, (ncand + 255) / 256);
+  want = std::max(want, 1);
+  P.span = ((ncand + want - 1) / want + 63) / 64 * 64;
+  P.nsplit = std::max(1, (ncand + P.span - 1) / P.span);
+  Carver c;
+  c.base = ws;
+  if (a->pooled_dtype == BSA_DTYPE_F32) {
+    const int64_t n = (int64_t)a->B * a->Hkv * P.Nb * a->D;
+    P.p_hi = c.take<uint16_t>(n);
+    P.p_lo = c.take<uint16_t>(n);
+  } else {
+    P.p_hi = P.p_lo = nullptr;
+  }
+  const int64_t nrows = (int64_t)a->B * P.Hs;
+  P.part_keys = P.nsplit > 1 ? c.take<uint64_t>(nrows * P.nsplit * std::max(P.topk, 1)) : nullptr;
+  P.sel = a->sel_out ? a->sel_out : c.take<int32_t>(nrows * P.sel_w);
+  P.ulist = c.take<int32_t>((int64_t)a->B * a->Hkv * P.umax);
+  P.ucount = c.take<int32_t>((int64_t)a->B * a->Hkv);
+  P.part_o = c.take<float>((int64_t)a->B * a->Hkv * P.umax * P.G * a->D);
+  P.part_lse = c.take<float>((int64_t)a->B * a->Hkv * P.umax * P.G);
+  P.bytes = c.off + 256;
+  return BSA_OK;
+}
+
+static bsa_status run_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes, void* stream) {
+  DecodePlan P;
+  bsa_status st = plan_decode(a, P, nullptr);
+  if (st != BSA_OK) return st;
+  if (!ws || ws_bytes < P.bytes) return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_decode_workspace_bytes");
+  if (((uintptr_t)ws & 255) != 0) return fail(BSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  plan_decode(a, P, reinterpret_cast<char*>(ws));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool per_group = a->gate_mode == BSA_GATE_PER_GROUP;
+  GateParams g;
+  g.B = a->B; g.Lq = 1; g.Lk = a->Lc; g.Hkv = a->Hkv; g.G = P.G; g.Hs = P.Hs; g.per_group = per_group;
+  g.rows_per_bh = P.rows_per_bh; g.ntiles = P.ntiles;
+  g.q = a->q; g.qs_b = a->q_stride[0]; g.qs_t = 0; g.qs_h = a->q_stride[1];
+  g.qkind = per_group ? 2 : 0;
+  g.Dg = a->D;
+  if (a->pooled_dtype == BSA_DTYPE_F32) {
+    if (!launch_pooled_to_planes(a->pooled, 0, a->p_stride[0], a->p_stride[1], a->p_stride[2], a->B, P.Nb, a->Hkv, a->D,
+                                 P.p_hi, P.p_lo, s))
+      return BSA_ERR_HIP;
+    g.p_hi = P.p_hi; g.p_lo = P.p_lo;
+    g.ps_h = (int64_t)P.Nb * a->D; g.ps_b = (int64_t)a->Hkv * g.ps_h; g.ps_j = a->D;
+  } else {
+    g.p_hi = reinterpret_cast<const uint16_t*>(a->pooled); g.p_lo = nullptr;
+    g.ps_b = a->p_stride[0]; g.ps_j = a->p_stride[1]; g.ps_h = a->p_stride[2];
+  }
+  g.Nb = P.Nb; g.causal = 1; g.block = a->block; g.lens = a->cache_lens;
+  g.topk = P.topk; g.nsplit = P.nsplit; g.span = P.span;
+  g.sel = P.sel; g.sel_w = P.sel_w; g.part = P.part_keys;
+  if (!launch_gate(g, s)) return BSA_ERR_HIP;
+  if (P.nsplit > 1 && !launch_gate_merge(g, s)) return BSA_ERR_HIP;
+  DecodeAttnParams d;
+  d.B = a->B; d.Lc = a->Lc; d.Hq = a->Hq; d.Hkv = a->Hkv; d.G = P.G; d.D = a->D; d.block = a->block; d.Hs = P.Hs;
+  d.per_group = per_group; d.topk = a->topk; d.umax = P.umax; d.lens = a->cache_lens;
+  d.q = reinterpret_cast<const uint16_t*>(a->q); d.qs_b = a->q_stride[0]; d.qs_h = a->q_stride[1];
+  d.k = reinterpret_cast<const uint16_t*>(a->kcache); d.ks_b = a->k_stride[0]; d.ks_t = a->k_stride[1]; d.ks_h = a->k_stride[2];
+  d.v = reinterpret_cast<const uint16_t*>(a->vcache); d.vs_b = a->v_stride[0]; d.vs_t = a->v_stride[1]; d.vs_h = a->v_stride[2];
+  const float scale = a->scale != 0.f ? a->scale : (float)(1.0 / sqrt((double)a->D));
+  d.sl2 = (float)((double)scale * 1.4426950408889634074);
+  d.sel = P.sel; d.ulist = P.ulist; d.ucount = P.ucount; d.part_o = P.part_o; d.part_lse = P.part_lse;
+  d.o = reinterpret_cast<uint16_t*>(a->o); d.os_b = a->o_stride[0]; d.os_h = a->o_stride[1];
+  d.lse_out = a->lse_out;
+  if (!launch_decode_union(d, s)) return BSA_ERR_HIP;
+  if (!launch_decode_attend(d, s)) return BSA_ERR_HIP;
+  if (!launch_decode_combine(d, s)) return BSA_ERR_HIP;
+  return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// summary
+// ---------------------------------------------------------------------------
+static bsa_status plan_summary(const bsa_summary_args* a, int32_t** chunk, int32_t** pos, char* ws, size_t* bytes) {
+  if (!a) return fail(BSA_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != BSA_DTYPE_F32 && a->dtype != BSA_DTYPE_BF16) return fail(BSA_ERR_INVALID_ARG, "dtype");
+  if (a->B < 1 || a->L < 1 || a->H < 1 || a->block < 1) return fail(BSA_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (!dim_ok(a->D)) return fail(BSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (!a->k || !a->pooled) return fail(BSA_ERR_INVALID_ARG, "k and pooled are required");
+  if (a->pooled_dtype != BSA_DTYPE_F32 && a->pooled_dtype != BSA_DTYPE_BF16) return fail(BSA_ERR_INVALID_ARG, "pooled_dtype");
+  if ((a->k_rot || a->pos_out) && !a->doc_ids) return fail(BSA_ERR_INVALID_ARG, "k_rot/pos_out need doc_ids");
+  const int elt = a->dtype == BSA_DTYPE_BF16 ? 2 : 4;
+  if (!aligned16(a->k) || !strides_ok(a->k_stride, 3, a->D, elt)) return fail(BSA_ERR_INVALID_ARG, "k alignment/strides");
+  if ((int64_t)a->B * ((a->L + a->block - 1) / a->block) >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "too many blocks");
+  Carver c;
+  c.base = ws;
+  *pos = nullptr;
+  *chunk = nullptr;
+  if (a->doc_ids) {
+    *chunk = c.take<int32_t>((int64_t)a->B * pos_chunks(a->L));
+    *pos = a->pos_out ? a->pos_out : c.take<int32_t>((int64_t)a->B * a->L);
+  }
+  *bytes = c.off + 256;
+  return BSA_OK;
+}
+
+static bsa_status run_summary(const bsa_summary_args* a, void* ws, size_t ws_bytes, void* stream) {
+  int32_t *chunk, *pos;
+  size_t need;
+  bsa_status st = plan_summary(a, &chunk, &pos, nullptr, &need);
+  if (st != BSA_OK) return st;
+  if (a->doc_ids) {
+    if (!ws || ws_bytes < need) return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_summary_workspace_bytes");
+    if (((uintptr_t)ws & 255) != 0) return fail(BSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    plan_summary(a, &chunk, &pos, reinterpret_cast<char*>(ws), &need);
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (a->doc_ids && !launch_doc_positions(a->doc_ids, a->B, a->L, chunk, pos, s)) return BSA_ERR_HIP;
+  SummaryParams sp;
+  sp.is_bf16 = a->dtype == BSA_DTYPE_BF16;
+  sp.B = a->B; sp.L = a->L; sp.H = a->H; sp.D = a->D; sp.block = a->block;
+  sp.Nb = (a->L + a->block - 1) / a->block;
+  sp.k = a->k; sp.ks_b = a->k_stride[0]; sp.ks_t = a->k_stride[1]; sp.ks_h = a->k_stride[2];
+  sp.pos = a->doc_ids ? pos : nullptr;
+  omega_table(a->rope_theta > 0.f ? (double)a->rope_theta : 10000.0, a->D, sp.omega);
+  sp.pooled_f32 = a->pooled_dtype == BSA_DTYPE_F32 ? reinterpret_cast<float*>(a->pooled) : nullptr;
+  sp.pooled_bf16 = a->pooled_dtype == BSA_DTYPE_BF16 ? reinterpret_cast<uint16_t*>(a->pooled) : nullptr;
+  sp.plane_hi = sp.plane_lo = nullptr;
+  sp.k_rot = a->k_rot;
+  return launch_block_summary(sp, s) ? BSA_OK : BSA_ERR_HIP;
+}
+
+}  // namespace bsa
+
+// ---------------------------------------------------------------------------
+// exported symbols
+// ---------------------------------------------------------------------------
+using namespace bsa;
+
+BSA_API size_t bsa_prefill_workspace_bytes(const bsa_prefill_args* a) {
+  PrefillPlan P;
+  return plan_prefill(a, P, nullptr, false) == BSA_OK ? P.bytes : 0;
+}
+
+BSA_API bsa_status bsa_sparse_attn_prefill(const bsa_prefill_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return run_prefill(a, ws, ws_bytes, stream, false);
+}
+
+BSA_API bsa_status bsa_select_blocks(const bsa_prefill_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return run_prefill(a, ws, ws_bytes, stream, true);
+}
+
+BSA_API size_t bsa_decode_workspace_bytes(const bsa_decode_args* a) {
+  DecodePlan P;
+  return plan_decode(a, P, nullptr) == BSA_OK ? P.bytes : 0;
+}
+
+BSA_API bsa_status bsa_sparse_attn_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return run_decode(a, ws, ws_bytes, stream);
+}
+
+BSA_API size_t bsa_summary_workspace_bytes(const bsa_summary_args* a) {
+  int32_t *c, *p;
+  size_t n = 0;
+  return plan_summary(a, &c, &p, nullptr, &n) == BSA_OK ? n : 0;
+}
+
+BSA_API bsa_status bsa_block_summary(const bsa_summary_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return run_summary(a, ws, ws_bytes, stream);
+}
+
+BSA_API const char* bsa_last_error(void) { return g_err.c_str(); }
+
+BSA_API int32_t bsa_version(void) { return 100; }  // 0.1.0
+
+BSA_API void bsa_timer_enable(int32_t on) { g_timer_on = on != 0; }
+
+BSA_API void bsa_timer_reset(void) { timer_clear(); }
+
+BSA_API bsa_status bsa_timer_report(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return fail(BSA_ERR_INVALID_ARG, "null argument");
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& r : g_timer) {
+    if (r.name != kernel) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(BSA_ERR_HIP, "event synchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(BSA_ERR_HIP, "event elapsed failed");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return BSA_OK;
+}

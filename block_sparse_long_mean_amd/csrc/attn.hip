@@ -1,0 +1,440 @@
+// Exact softmax attention over the selected blocks.
+//
+// "MiniMax released MSA ..." (news.hamidun.com), sections "How MSA Works" and
+// "Why Long Context is Hard to Scale": the main branch attends exactly, with
+// no approximation, over only the selected blocks.  One softmax spans all
+// selected keys of a query; it is evaluated block by block with running
+// (max, sum) statistics and merged with log-sum-exp weights, which is exact
+// up to rounding.
+//
+// Schedule (bf16):
+//  * attn_gather: KV-major.  A work item is one (b, kv head, block) bucket and
+//    a tile of up to 128 query rows that chose it.  The block's keys and
+//    values are staged in LDS (V transposed) in 64-key tiles; each wave holds
+//    32 gathered query rows.  S^T = K Q^T and O^T += V^T P^T run on
+//    v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the result is one
+//    normalised partial output (bf16) plus its log2-domain LSE per
+//    (row, slot).
+//  * attn_combine: query-major.  A workgroup takes 128 consecutive query
+//    tokens of one head, computes the causal attention inside each token's
+//    own block on MFMA, then folds in the row's partials by LSE weights and
+//    writes o (and lse).
+#include <math.h>
+
+#include "bsa_device.h"
+#include "bsa_internal.h"
+
+namespace bsa {
+
+constexpr int KT = 64;  // keys per LDS tile
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct AttnSmem {
+  uint16_t k[KT * (D + 8)];
+  uint16_t vt[D * (KT + 8)];
+};
+
+// Stage keys [key0, key0 + KT) of one kv head (zero past n_valid) into LDS:
+// K row-major, V transposed.
+template <int D>
+BSA_DEV void stage_kv(AttnSmem<D>& sm, const uint16_t* kb, int64_t ks_t, const uint16_t* vb, int64_t vs_t,
+                      int key0, int n_valid) {
+  const int tid = threadIdx.x;
+  constexpr int CH = D / 8;
+  for (int idx = tid; idx < KT * CH; idx += 256) {
+    const int kr = idx / CH, ch = idx % CH;
+    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (kr < n_valid) x = ld16(kb + (int64_t)(key0 + kr) * ks_t + ch * 8);
+    st16(&sm.k[kr * (D + 8) + ch * 8], x);
+  }
+  for (int idx = tid; idx < (KT / 4) * CH; idx += 256) {
+    const int kq = idx / CH, ch = idx % CH;
+    u16x8 r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kr = kq * 4 + i;
+      r[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (kr < n_valid) r[i] = ld16(vb + (int64_t)(key0 + kr) * vs_t + ch * 8);
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      u16x4 col = {r[0][d], r[1][d], r[2][d], r[3][d]};
+      *reinterpret_cast<u16x4*>(&sm.vt[(ch * 8 + d) * (KT + 8) + kq * 4]) = col;
+    }
+  }
+}
+
+// S^T (64 keys x 32 queries) for this wave: s0 keys 0..31, s1 keys 32..63.
+template <int D>
+BSA_DEV void qk_tile(const AttnSmem<D>& sm, const bf16x8 (&qf)[D / 16], f32x16& s0, f32x16& s1) {
+  const int lane = lane_id();
+  const int r = lane & 31, h = lane >> 5;
+  s0 = f32x16{};
+  s1 = f32x16{};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const bf16x8 a0 = as_bf(ld16(&sm.k[r * (D + 8) + 16 * s + 8 * h]));
+    const bf16x8 a1 = as_bf(ld16(&sm.k[(32 + r) * (D + 8) + 16 * s + 8 * h]));
+    s0 = mfma32(a0, qf[s], s0);
+    s1 = mfma32(a1, qf[s], s1);
+  }
+}
+
+// O^T (D x 32 queries) += V^T P^T for one 64-key tile; p0/p1 hold P^T in the
+// S^T result layout.
+template <int D>
+BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, f32x16 (&o)[D / 32]) {
+  const int lane = lane_id();
+  const int r = lane & 31, h = lane >> 5;
+  bf16x8 pb[4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pb[0][e] = (__bf16)p0[e];
+    pb[1][e] = (__bf16)p0[8 + e];
+    pb[2][e] = (__bf16)p1[e];
+    pb[3][e] = (__bf16)p1[8 + e];
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint16_t* vr = &sm.vt[(dt * 32 + r) * (KT + 8) + kk * 16 + 4 * h];
+      const u16x4 lo = *reinterpret_cast<const u16x4*>(vr);
+      const u16x4 hi = *reinterpret_cast<const u16x4*>(vr + 8);
+      const u16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      o[dt] = mfma32(as_bf(a), pb[kk], o[dt]);
+    }
+  }
+}
+
+// key index (within a 64-key tile) held by result register i of this lane
+BSA_DEV int krow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+// Online-softmax update of one lane's query column with a masked S^T tile
+// (masked entries already -inf).  Returns false when every entry is masked
+// for this query (state unchanged, p = 0).
+template <int D>
+BSA_DEV void softmax_update(f32x16& s0, f32x16& s1, float& m, float& l, f32x16 (&o)[D / 32]) {
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, fmaxf(s0[i], s1[i]));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  const float mnew = fmaxf(m, tmax);
+  if (mnew == -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = 0.f;
+      s1[i] = 0.f;
+    }
+    return;
+  }
+  const float corr = exp2f(m - mnew);
+  float rs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s0[i] = exp2f(s0[i] - mnew);
+    s1[i] = exp2f(s1[i] - mnew);
+    rs += s0[i] + s1[i];
+  }
+  rs += __shfl_xor(rs, 32, 64);
+  l = l * corr + rs;
+  m = mnew;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] *= corr;
+}
+
+template <int D>
+BSA_DEV void load_qf(const uint16_t* qrow, bool ok, bf16x8 (&qf)[D / 16]) {
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (ok) x = ld16(qrow + 16 * s + 8 * h);
+    qf[s] = as_bf(x);
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hq = lane >> 5;
+  const int nitems = *p.n_items;
+  const int g8 = gridDim.x >> 3;  // grid is a multiple of 8
+  const int x = blockIdx.x & 7, i0 = blockIdx.x >> 3;
+  const int per = nitems >> 3, rem = nitems & 7;
+  const int cnt_x = per + (x < rem ? 1 : 0);
+  const int off_x = x * per + (x < rem ? x : rem);
+
+  for (int it = i0; it < cnt_x; it += g8) {
+    const int2 item = p.items[off_x + it];
+    const int bucket = item.x, tile = item.y;
+    const int j = bucket % p.Nb;
+    const int hk = (bucket / p.Nb) % p.Hkv;
+    const int b = bucket / (p.Nb * p.Hkv);
+    const int e0 = p.bucket_off[bucket];
+    const int nrows = (p.bucket_off[bucket + 1] - e0) * p.R;
+    const int row0 = tile * 128;
+    const int lr = row0 + w * 32 + (lane & 31);
+    const bool valid = lr < nrows;
+    const bool wave_on = row0 + w * 32 < nrows;
+    int t = 0, slot = 0, hh = 0, rr = 0;
+    if (valid) {
+      const uint32_t ent = p.entries[e0 + lr / p.R];
+      rr = lr % p.R;
+      slot = (int)(ent % (uint32_t)p.kslot);
+      const uint32_t th = ent / (uint32_t)p.kslot;
+      hh = (int)(th % (uint32_t)p.Gs);
+      t = (int)(th / (uint32_t)p.Gs);
+    }
+    const int qh = p.per_group ? hk * p.G + rr : hk * p.G + hh;
+    const int hs = p.per_group ? hk : hk * p.G + hh;
+    bf16x8 qf[D / 16];
+    load_qf<D>(p.q + (int64_t)b * p.qs_b + (int64_t)t * p.qs_t + (int64_t)qh * p.qs_h, valid, qf);
+
+    float m = -INFINITY, l = 0.f;
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+    const int key0 = j * p.block;
+    const int n_keys = min(p.block, p.Lk - key0);
+    const uint16_t* kb = p.k + (int64_t)b * p.ks_b + (int64_t)hk * p.ks_h;
+    const uint16_t* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
+    for (int kt0 = 0; kt0 < n_keys; kt0 += KT) {
+      __syncthreads();
+      stage_kv<D>(sm, kb, p.ks_t, vb, p.vs_t, key0 + kt0, n_keys - kt0);
+      __syncthreads();
+      if (wave_on) {
+        f32x16 s0, s1;
+        qk_tile<D>(sm, qf, s0, s1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kr = kt0 + krow(i, hq);
+          s0[i] = kr < n_keys ? s0[i] * p.sl2 : -INFINITY;
+          s1[i] = kr + 32 < n_keys ? s1[i] * p.sl2 : -INFINITY;
+        }
+        softmax_update<D>(s0, s1, m, l, o);
+        pv_tile<D>(sm, s0, s1, o);
+      }
+    }
+    if (valid) {
+      const float inv = 1.0f / l;
+      const int64_t srow = ((int64_t)b * p.Hs + hs) * p.Lq + t;
+      const int64_t pidx = (srow * p.kslot + slot) * p.R + rr;
+      uint16_t* dst = p.part_o + pidx * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = dt * 32 + 8 * g + 4 * hq;
+          u16x4 v4 = {f2bf(o[dt][4 * g] * inv), f2bf(o[dt][4 * g + 1] * inv), f2bf(o[dt][4 * g + 2] * inv),
+                      f2bf(o[dt][4 * g + 3] * inv)};
+          *reinterpret_cast<u16x4*>(dst + d0) = v4;
+        }
+      }
+      if (hq == 0) p.part_lse[pidx] = m + log2f(l);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_combine_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hq = lane >> 5;
+  const int ntile = (p.Lq + 127) / 128;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int hh = lid % p.G;
+  int r = lid / p.G;
+  const int tile = r % ntile;
+  r /= ntile;
+  const int hk = r % p.Hkv;
+  const int b = r / p.Hkv;
+  const int h = hk * p.G + hh;
+  const int t = tile * 128 + w * 32 + (lane & 31);
+  const bool valid = t < p.Lq;
+  const int64_t off = (int64_t)p.Lk - p.Lq;
+  const int64_t qpos = off + t;
+
+  bf16x8 qf[D / 16];
+  load_qf<D>(p.q + (int64_t)b * p.qs_b + (int64_t)(valid ? t : 0) * p.qs_t + (int64_t)h * p.qs_h, valid, qf);
+  float m = -INFINITY, l = 0.f;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+
+  if (p.causal) {
+    const int tl = min(tile * 128 + 127, p.Lq - 1);
+    const int64_t kb0 = ((off + tile * 128) / p.block) * p.block;
+    const int64_t ke = off + tl + 1;
+    const int wt0 = tile * 128 + w * 32;
+    const bool wave_on = wt0 < p.Lq;
+    const int wt1 = min(wt0 + 31, p.Lq - 1);
+    const int64_t wkb = ((off + wt0) / p.block) * p.block;
+    const int64_t wke = off + wt1 + 1;
+    const int64_t my_kb = (qpos / p.block) * p.block;
+    const uint16_t* kb = p.k + (int64_t)b * p.ks_b + (int64_t)hk * p.ks_h;
+    const uint16_t* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
+    for (int64_t kt0 = kb0; kt0 < ke; kt0 += KT) {
+      __syncthreads();
+      stage_kv<D>(sm, kb, p.ks_t, vb, p.vs_t, (int)kt0, (int)min<int64_t>(KT, ke - kt0));
+      __syncthreads();
+      if (wave_on && kt0 < wke && kt0 + KT > wkb) {
+        f32x16 s0, s1;
+        qk_tile<D>(sm, qf, s0, s1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t k0 = kt0 + krow(i, hq);
+          const int64_t k1 = k0 + 32;
+          s0[i] = (valid && k0 >= my_kb && k0 <= qpos) ? s0[i] * p.sl2 : -INFINITY;
+          s1[i] = (valid && k1 >= my_kb && k1 <= qpos) ? s1[i] * p.sl2 : -INFINITY;
+        }
+        softmax_update<D>(s0, s1, m, l, o);
+        pv_tile<D>(sm, s0, s1, o);
+      }
+    }
+  }
+  if (!valid) return;  // no barrier below
+  // fold in the partials of the gate-chosen blocks
+  const int hs = p.per_group ? hk : h;
+  const int rr = p.per_group ? hh : 0;
+  const int64_t srow = ((int64_t)b * p.Hs + hs) * p.Lq + t;
+  const int64_t cur = p.causal ? qpos / p.block : -1;
+  const int32_t* srow_sel = p.sel + srow * p.sel_w;
+  for (int s = 0; s < p.kslot; ++s) {
+    const int jsel = srow_sel[s];
+    if (jsel < 0 || jsel == cur) break;
+    const int64_t pidx = (srow * p.kslot + s) * p.R + rr;
+    const float ls = p.part_lse[pidx];
+    const float mnew = fmaxf(m, ls);
+    const float c1 = exp2f(m - mnew), c2 = exp2f(ls - mnew);
+    const uint16_t* src = p.part_o + pidx * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * hq;
+        const u16x4 v4 = *reinterpret_cast<const u16x4*>(src + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[dt][4 * g + e] = o[dt][4 * g + e] * c1 + c2 * bf2f(v4[e]);
+      }
+    }
+    l = l * c1 + c2;
+    m = mnew;
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  uint16_t* dst = p.o + (int64_t)b * p.os_b + (int64_t)t * p.os_t + (int64_t)h * p.os_h;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = dt * 32 + 8 * g + 4 * hq;
+      u16x4 v4 = {f2bf(o[dt][4 * g] * inv), f2bf(o[dt][4 * g + 1] * inv), f2bf(o[dt][4 * g + 2] * inv),
+                  f2bf(o[dt][4 * g + 3] * inv)};
+      *reinterpret_cast<u16x4*>(dst + d0) = v4;
+    }
+  }
+  if (p.lse_out && hq == 0)
+    p.lse_out[((int64_t)b * p.Hq + h) * p.Lq + t] = l > 0.f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+}
+
+bool launch_attn_gather(const AttnParams& p, hipStream_t s) {
+  {
+    LaunchScope ls("attn_gather", s);
+    if (p.D == 128)
+      hipLaunchKernelGGL(attn_gather_kernel<128>, dim3(p.grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(attn_gather_kernel<64>, dim3(p.grid), dim3(256), 0, s, p);
+  }
+  return launch_ok("attn_gather");
+}
+
+bool launch_attn_combine(const AttnParams& p, hipStream_t s) {
+  const int ntile = (p.Lq + 127) / 128;
+  const int grid = p.B * p.Hq * ntile;
+  {
+    LaunchScope ls("attn_combine", s);
+    if (p.D == 128)
+      hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+  }
+  return launch_ok("attn_combine");
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: one wave per (b, t, h) query row, all its selected blocks, fp32
+// arithmetic throughout (keys on lanes for the scores, head dims on lanes for
+// the weighted sum).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void attn_rowwise_f32_kernel(AttnF32Params p) {
+  __shared__ float s_q[4][128];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nrows = (int64_t)p.B * p.Lq * p.Hq;
+  const int64_t row = (int64_t)blockIdx.x * 4 + w;
+  if (row >= nrows) return;  // wave-uniform; no workgroup barrier follows
+  const int h = (int)(row % p.Hq);
+  const int t = (int)((row / p.Hq) % p.Lq);
+  const int b = (int)(row / ((int64_t)p.Hq * p.Lq));
+  const int hk = h / p.G;
+  const int hs = p.per_group ? hk : h;
+  const float* qr = p.q + (int64_t)b * p.qs_b + (int64_t)t * p.qs_t + (int64_t)h * p.qs_h;
+  for (int d = lane; d < p.D; d += 64) s_q[w][d] = qr[d];
+  __builtin_amdgcn_wave_barrier();
+  const int64_t qpos = (int64_t)p.Lk - p.Lq + t;
+  const int64_t cur = qpos / p.block;
+  const int32_t* srow = p.sel + (((int64_t)b * p.Hs + hs) * p.Lq + t) * p.sel_w;
+  const float* kb = p.k + (int64_t)b * p.ks_b + (int64_t)hk * p.ks_h;
+  const float* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
+  float m = -INFINITY, l = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int s = 0; s < p.sel_w; ++s) {
+    const int j = srow[s];
+    if (j < 0) break;
+    const int64_t ka = (int64_t)j * p.block;
+    int64_t ke = min<int64_t>(ka + p.block, p.Lk);
+    if (p.causal && j == cur) ke = min<int64_t>(ke, qpos + 1);
+    for (int64_t k0 = ka; k0 < ke; k0 += 64) {
+      const int64_t key = k0 + lane;
+      float sc = -INFINITY;
+      if (key < ke) {
+        const float* kr = kb + key * p.ks_t;
+        float acc = 0.f;
+        for (int d = 0; d < p.D; ++d) acc = fmaf(s_q[w][d], kr[d], acc);
+        sc = acc * p.scale;
+      }
+      const float mnew = fmaxf(m, wave_max(sc));
+      const float corr = expf(m - mnew);
+      const float pk = key < ke ? expf(sc - mnew) : 0.f;
+      l = l * corr + wave_sum(pk);
+      a0 *= corr;
+      a1 *= corr;
+      const int nk = (int)min<int64_t>(64, ke - k0);
+      for (int kk = 0; kk < nk; ++kk) {
+        const float pv = __shfl(pk, kk, 64);
+        const float* vr = vb + (k0 + kk) * p.vs_t;
+        if (lane < p.D) a0 = fmaf(pv, vr[lane], a0);
+        if (lane + 64 < p.D) a1 = fmaf(pv, vr[lane + 64], a1);
+      }
+      m = mnew;
+    }
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  float* orow = p.o + (int64_t)b * p.os_b + (int64_t)t * p.os_t + (int64_t)h * p.os_h;
+  if (lane < p.D) orow[lane] = a0 * inv;
+  if (lane + 64 < p.D) orow[lane + 64] = a1 * inv;
+  if (p.lse_out && lane == 0) p.lse_out[((int64_t)b * p.Hq + h) * p.Lq + t] = l > 0.f ? m + logf(l) : -INFINITY;
+}
+
+bool launch_attn_rowwise_f32(const AttnF32Params& p, hipStream_t s) {
+  const int64_t nrows = (int64_t)p.B * p.Lq * p.Hq;
+  {
+    LaunchScope ls("attn_rowwise_f32", s);
+    hipLaunchKernelGGL(attn_rowwise_f32_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, p);
+  }
+  return launch_ok("attn_rowwise_f32");
+}
+
+}  // namespace bsa

@@ -1,0 +1,201 @@
+// Device-side helpers shared by the libbsa kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define BSA_WAVE 64
+#define BSA_DEV __device__ __forceinline__
+
+// ---------------------------------------------------------------------------
+// bfloat16 <-> float.  bf16 is stored as raw uint16 bits in memory.
+// ---------------------------------------------------------------------------
+BSA_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+// Round to nearest even (gfx950 converts in hardware).
+BSA_DEV uint16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+BSA_DEV __bf16 f2bfh(float f) { return (__bf16)f; }
+
+// 16 bytes = 8 bf16 from global/LDS
+BSA_DEV u16x8 ld16(const void* p) { return *reinterpret_cast<const u16x8*>(p); }
+BSA_DEV void st16(void* p, u16x8 v) { *reinterpret_cast<u16x8*>(p) = v; }
+BSA_DEV bf16x8 as_bf(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
+BSA_DEV u16x8 as_u16(bf16x8 v) { return __builtin_bit_cast(u16x8, v); }
+
+// Split a float into a bf16 head and a bf16 tail: x ~= hi + lo with
+// |x - hi - lo| <= 2^-16 |x|.  Three bf16 MFMA passes (hi.hi + hi.lo + lo.hi)
+// then give dot products close to fp32 accuracy.
+BSA_DEV void split_bf(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (layouts checked on the device):
+//  16x16x32: A lane l -> row l%16, k 8*(l/16)+e;  B lane l -> col l%16, same k;
+//            C lane l -> col l%16, rows 4*(l/16)+i.
+//  32x32x16: A lane l -> row l%32, k 8*(l/32)+e;  B lane l -> col l%32, same k;
+//            C lane l -> col l%32, row 8*(i/4) + 4*(l/32) + (i%4).
+// ---------------------------------------------------------------------------
+BSA_DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+BSA_DEV f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Wave primitives
+// ---------------------------------------------------------------------------
+BSA_DEV int lane_id() { return threadIdx.x & 63; }
+BSA_DEV uint64_t shfl_xor64(uint64_t v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = (uint32_t)__shfl_xor((int)lo, m, 64);
+  hi = (uint32_t)__shfl_xor((int)hi, m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+BSA_DEV uint64_t shfl64(uint64_t v, int src) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = (uint32_t)__shfl((int)lo, src, 64);
+  hi = (uint32_t)__shfl((int)hi, src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+BSA_DEV float wave_max(float v) {
+  for (int m = 32; m > 0; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+BSA_DEV float wave_sum(float v) {
+  for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Top-k keys.  A candidate is packed as a 64-bit key whose unsigned order is
+// (score ascending, block index descending): the larger key is the better
+// candidate, so equal scores prefer the lower block index.  Key 0 is below
+// every real key and marks an empty slot.
+// ---------------------------------------------------------------------------
+BSA_DEV uint32_t order_f32(float s) {
+  uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+BSA_DEV uint64_t make_key(float s, uint32_t j) {
+  return ((uint64_t)order_f32(s) << 32) | (uint64_t)(0xFFFFFFFFu - j);
+}
+BSA_DEV uint32_t key_index(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
+
+// Bitonic sort of 64*V keys held by one wave, element e = i*64 + lane in
+// register v[i]; result descending in e.
+template <int V>
+BSA_DEV void wave_sort_desc(uint64_t (&v)[V]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int size = 2; size <= 64 * V; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= 64) {
+        const int rs = stride >> 6;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const int j = i ^ rs;
+          if (j > i) {
+            const int e = i * 64 + lane;
+            const bool desc = (e & size) == 0;
+            const uint64_t a = v[i], b = v[j];
+            const bool sw = desc ? (a < b) : (a > b);
+            v[i] = sw ? b : a;
+            v[j] = sw ? a : b;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const uint64_t o = shfl_xor64(v[i], stride);
+          const int e = i * 64 + lane;
+          const bool lower = (lane & stride) == 0;
+          const bool desc = (e & size) == 0;
+          const bool keep_max = (lower == desc);
+          const uint64_t mx = v[i] > o ? v[i] : o;
+          const uint64_t mn = v[i] > o ? o : v[i];
+          v[i] = keep_max ? mx : mn;
+        }
+      }
+    }
+  }
+}
+
+// Ascending bitonic sort of 64 int32 values, one per lane.
+BSA_DEV int wave_sort_asc_i32(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int o = __shfl_xor(v, stride, 64);
+      const bool lower = (lane & stride) == 0;
+      const bool asc = (lane & size) == 0;
+      const bool keep_min = (lower == asc);
+      v = keep_min ? min(v, o) : max(v, o);
+    }
+  }
+  return v;
+}
+
+// Per-row candidate buffer in LDS: `cap` keys, a count and a threshold.
+// Appending is open to every lane; compaction is done by one whole wave and
+// keeps the best `topk` keys, sorted descending at the buffer's front.  Once
+// `topk` keys are held, the threshold is the k-th best key and only strictly
+// better candidates are appended.
+template <int V>  // cap = 64 * V
+BSA_DEV void row_compact(uint64_t* buf, int* cnt, uint64_t* thr, int topk) {
+  const int lane = lane_id();
+  const int c = *cnt;
+  uint64_t v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = i * 64 + lane;
+    v[i] = e < c ? buf[e] : 0ull;
+  }
+  wave_sort_desc<V>(v);
+  const int keep = c < topk ? c : topk;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = i * 64 + lane;
+    if (e < keep) buf[e] = v[i];
+  }
+  if (c >= topk && topk > 0) {
+    const int e = topk - 1;
+    uint64_t t = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (i == (e >> 6)) t = shfl64(v[i], e & 63);
+    if (lane == 0) *thr = t;
+  }
+  if (lane == 0) *cnt = keep;
+  __builtin_amdgcn_wave_barrier();
+}
+
+// XCD-aware remap: hardware hands workgroup w to XCD w % 8.  The logical id
+// returned makes each XCD work through one contiguous range of logical ids,
+// so that work items sharing data (consecutive logical ids) share an L2.
+BSA_DEV int xcd_remap(int w, int n) {
+  const int per = n >> 3, rem = n & 7, x = w & 7, i = w >> 3;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+// Angle reduction for RoPE: a = pos * omega formed in double, reduced to
+// [-pi, pi] in double, then sin/cos in float.
+BSA_DEV void rope_sincos(int pos, double omega, float& c, float& s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double a = (double)pos * omega;
+  a -= two_pi * rint(a * (1.0 / two_pi));
+  const float af = (float)a;
+  sincosf(af, &s, &c);
+}

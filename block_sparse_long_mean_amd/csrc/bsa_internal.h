@@ -1,0 +1,184 @@
+// Host-side interfaces between the C ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace bsa {
+
+// ---- launch bookkeeping (timer + error capture), defined in api.hip -------
+struct LaunchScope {
+  LaunchScope(const char* name, hipStream_t s);
+  ~LaunchScope();
+  const char* name;
+  hipStream_t stream;
+  int slot;
+};
+bool launch_ok(const char* name);  // checks hipGetLastError, records the message
+
+// ---- positions ----------------------------------------------------------
+constexpr int kPosChunk = 4096;
+inline int pos_chunks(int L) { return (L + kPosChunk - 1) / kPosChunk; }
+bool launch_doc_positions(const int32_t* doc, int B, int L, int32_t* chunk_last, int32_t* pos,
+                          hipStream_t s);
+
+// ---- block summary --------------------------------------------------------
+struct SummaryParams {
+  int is_bf16;
+  int B, L, H, D, block, Nb;
+  const void* k;
+  int64_t ks_b, ks_t, ks_h;
+  const int32_t* pos;  // per-document positions [B, L] or null (no RoPE)
+  double omega[64];    // RoPE frequencies theta^(-2i/D)
+  float* pooled_f32;   // public layout [B, Nb, H, D] or null
+  uint16_t* pooled_bf16;  // public layout or null
+  uint16_t* plane_hi;  // gate layout [B, H, Nb, D] hi/lo split, or null
+  uint16_t* plane_lo;
+  void* k_rot;         // [B, L, H, D] contiguous rotated keys or null
+};
+bool launch_block_summary(const SummaryParams& p, hipStream_t s);
+
+struct RopeQParams {
+  int is_bf16;
+  int B, L, H, D;
+  const void* q;
+  int64_t qs_b, qs_t, qs_h;
+  const int32_t* pos;
+  double omega[64];
+  uint16_t* out16;  // [B, L, H, D] bf16 or null
+  float* out32;     // [B, L, H, D] f32 or null
+};
+bool launch_rope_q(const RopeQParams& p, hipStream_t s);
+
+// fp32 or bf16 [B, Nb, H, D] (strided) -> hi/lo planes [B, H, Nb, D]
+bool launch_pooled_to_planes(const void* pooled, int is_bf16, int64_t ps_b, int64_t ps_j, int64_t ps_h,
+                             int B, int Nb, int H, int D, uint16_t* hi, uint16_t* lo, hipStream_t s);
+
+// ---- gate + top-k --------------------------------------------------------
+struct GateParams {
+  int B, Lq, Lk, Hkv, G, Hs, per_group;
+  int rows_per_bh;  // selection rows per (b, kv head)
+  int ntiles;       // row tiles per (b, kv head)
+  const void* q;    // gate query source
+  int64_t qs_b, qs_t, qs_h;
+  int qkind;        // 0 bf16 (exact), 1 f32 (split), 2 bf16 summed over the group (split)
+  int Dg;
+  const uint16_t* p_hi;
+  const uint16_t* p_lo;  // may be null (summaries exact in bf16)
+  int64_t ps_b, ps_h, ps_j;
+  int Nb;
+  int causal, block;
+  const int32_t* lens;  // decode: per-sequence cache lengths or null
+  int topk, nsplit, span;
+  int32_t* sel;
+  int sel_w;
+  uint64_t* part;  // [rows][nsplit][topk] when nsplit > 1
+};
+bool launch_gate(const GateParams& p, hipStream_t s);
+bool launch_gate_merge(const GateParams& p, hipStream_t s);
+
+// fp32 path: gate scored in fp32 against fp32 summaries [B, Nb, Hkv, Dg]
+struct GateF32Params {
+  int B, Lq, Lk, Hkv, G, Hs, per_group, Dg;
+  const float* q;
+  int64_t qs_b, qs_t, qs_h;
+  const float* pooled;  // [B, Nb, Hkv, Dg] contiguous
+  int Nb, causal, block, topk;
+  int32_t* sel;
+  int sel_w;
+};
+bool launch_gate_f32(const GateF32Params& p, hipStream_t s);
+
+// ---- selection inversion (CSR) --------------------------------------------
+struct CsrParams {
+  int B, Lq, Lk, Hkv, G, Hs, per_group, Nb, block, causal;
+  const int32_t* sel;
+  int sel_w;
+  int kslot;      // gate slots per selection row
+  int R;          // attention rows per entry (G per group, else 1)
+  int rows_item;  // attention rows per work item
+  int32_t* counts;      // [nbk]
+  int32_t* cursor;      // [nbk]
+  int32_t* bucket_off;  // [nbk + 1]
+  int32_t* tile_off;    // [nbk + 1]
+  int32_t* scan_tmp;    // [scan_tmp_len]
+  uint32_t* entries;
+  int2* items;
+  int nbk;
+};
+int64_t scan_tmp_len(int64_t n);
+bool launch_csr(const CsrParams& p, hipStream_t s);
+
+// ---- attention ------------------------------------------------------------
+struct AttnParams {
+  int B, Lq, Lk, Hq, Hkv, G, D, block, Nb, Hs, per_group, Gs, R, kslot, causal;
+  const uint16_t* q;
+  int64_t qs_b, qs_t, qs_h;
+  const uint16_t* k;
+  int64_t ks_b, ks_t, ks_h;
+  const uint16_t* v;
+  int64_t vs_b, vs_t, vs_h;
+  float sl2;  // softmax scale * log2(e)
+  const uint32_t* entries;
+  const int32_t* bucket_off;
+  const int32_t* tile_off;
+  const int2* items;
+  const int32_t* n_items;  // device scalar
+  int grid;                // persistent workgroups
+  uint16_t* part_o;        // [rows * kslot * R, D] bf16 (normalised)
+  float* part_lse;         // log2-domain lse
+  // combine
+  const int32_t* sel;
+  int sel_w;
+  uint16_t* o;
+  int64_t os_b, os_t, os_h;
+  float* lse_out;  // natural log, [B, Hq, Lq] or null
+};
+bool launch_attn_gather(const AttnParams& p, hipStream_t s);
+bool launch_attn_combine(const AttnParams& p, hipStream_t s);
+
+struct AttnF32Params {
+  int B, Lq, Lk, Hq, Hkv, G, D, block, Hs, per_group, causal;
+  const float* q;
+  int64_t qs_b, qs_t, qs_h;
+  const float* k;
+  int64_t ks_b, ks_t, ks_h;
+  const float* v;
+  int64_t vs_b, vs_t, vs_h;
+  float scale;
+  const int32_t* sel;
+  int sel_w;
+  float* o;
+  int64_t os_b, os_t, os_h;
+  float* lse_out;
+};
+bool launch_attn_rowwise_f32(const AttnF32Params& p, hipStream_t s);
+
+// ---- decode ---------------------------------------------------------------
+struct DecodeAttnParams {
+  int B, Lc, Hq, Hkv, G, D, block, Hs, per_group, topk, umax;
+  const int32_t* lens;
+  const uint16_t* q;
+  int64_t qs_b, qs_h;
+  const uint16_t* k;
+  int64_t ks_b, ks_t, ks_h;
+  const uint16_t* v;
+  int64_t vs_b, vs_t, vs_h;
+  float sl2;
+  const int32_t* sel;  // [B, Hs, topk + 1]
+  int32_t* ulist;      // [B * Hkv, umax] packed (j << 8 | head mask)
+  int32_t* ucount;     // [B * Hkv]
+  float* part_o;       // [B * Hkv * umax * G, D]
+  float* part_lse;
+  uint16_t* o;
+  int64_t os_b, os_h;
+  float* lse_out;
+};
+bool launch_decode_union(const DecodeAttnParams& p, hipStream_t s);
+bool launch_decode_attend(const DecodeAttnParams& p, hipStream_t s);
+bool launch_decode_combine(const DecodeAttnParams& p, hipStream_t s);
+
+void set_error(const std::string& msg);
+
+}  // namespace bsa

@@ -1,0 +1,415 @@
+// Gate: score every candidate block's summary with the gate query and keep
+// the top-k per selection row.
+//
+// MoBA repo card (ross.abutalabs.com/products/moba.json), card.what_it_is:
+// MoE-style top-k gating over KV blocks.  "MiniMax released MSA ..."
+// (news.hamidun.com), section "How MSA Works": a light index branch picks the
+// top-k blocks per query and per GQA group.  Readings where the pages are
+// silent: score = dot(gate query, block mean); per group the heads' scores are
+// summed, which equals scoring with the summed query; in causal mode only
+// blocks before the query's own block compete; ties go to the lower index.
+//
+// Scores run on bf16 MFMA (16x16x32).  Operands that are not exact in bf16
+// are split into hi + lo bf16 parts and the product is formed as
+// hi.hi + hi.lo + lo.hi, which is within a few fp32 ulps of the fp32 dot
+// product -- enough to reproduce a float64 ranking up to near-ties.
+#include "bsa_device.h"
+#include "bsa_internal.h"
+
+namespace bsa {
+
+struct RowInfo {
+  int t, hh;
+};
+
+BSA_DEV RowInfo row_to_th(int row, const GateParams& p) {
+  RowInfo r;
+  if (p.per_group) {
+    r.t = row;
+    r.hh = 0;
+  } else {
+    r.t = row / p.G;
+    r.hh = row % p.G;
+  }
+  return r;
+}
+
+// Absolute key position of query token t of sequence b.
+BSA_DEV int64_t qpos_of(const GateParams& p, int b, int t) {
+  int64_t Lk = p.Lk;
+  if (p.lens) {
+    int n = p.lens[b];
+    n = n < 1 ? 1 : (n > p.Lk ? p.Lk : n);
+    Lk = n;
+  }
+  return Lk - p.Lq + t;
+}
+
+// candidate blocks of query token t: [0, ncand)
+BSA_DEV int ncand_of(const GateParams& p, int b, int t) {
+  if (!p.causal) return p.Nb;
+  const int64_t cur = qpos_of(p, b, t) / p.block;
+  return (int)(cur < p.Nb ? cur : p.Nb);
+}
+
+// Load the 8 gate-query elements [d0, d0+8) of one row and split them.
+template <int QK>
+BSA_DEV void load_gate_q(const GateParams& p, int b, int hk, RowInfo ri, bool ok, int d0, bf16x8& hi, bf16x8& lo) {
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  if (ok) {
+    if constexpr (QK == 0 || QK == 2) {
+      const uint16_t* base = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.qs_b + (int64_t)ri.t * p.qs_t;
+      const int nh = (QK == 2) ? p.G : 1;
+      const int h0 = (QK == 2) ? hk * p.G : hk * p.G + ri.hh;
+      for (int g = 0; g < nh; ++g) {
+        u16x8 v = ld16(base + (int64_t)(h0 + g) * p.qs_h + d0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] += bf2f(v[e]);
+      }
+    } else {
+      const float* base = reinterpret_cast<const float*>(p.q) + (int64_t)b * p.qs_b + (int64_t)ri.t * p.qs_t;
+      const int h = p.per_group ? -1 : hk * p.G + ri.hh;
+      if (h >= 0) {
+        const f32x4* r = reinterpret_cast<const f32x4*>(base + (int64_t)h * p.qs_h + d0);
+        f32x4 a = r[0], c = r[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = a[e];
+          x[4 + e] = c[e];
+        }
+      } else {
+        for (int g = 0; g < p.G; ++g) {
+          const f32x4* r = reinterpret_cast<const f32x4*>(base + (int64_t)(hk * p.G + g) * p.qs_h + d0);
+          f32x4 a = r[0], c = r[1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] += a[e];
+            x[4 + e] += c[e];
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 h, l;
+    split_bf(x[e], h, l);
+    hi[e] = h;
+    lo[e] = l;
+  }
+}
+
+// Writes one finished row: top-k (desc keys in buf[0..cnt)) -> output.
+template <int V>
+BSA_DEV void emit_row(const GateParams& p, const uint64_t* buf, int cnt, int b, int hs, int t, int split) {
+  const int lane = lane_id();
+  const int64_t srow = ((int64_t)b * p.Hs + hs) * p.Lq + t;
+  if (p.nsplit == 1) {
+    int idx = lane < cnt ? (int)key_index(buf[lane]) : 0x7FFFFFFF;
+    idx = wave_sort_asc_i32(idx);
+    int32_t* out = p.sel + srow * p.sel_w;
+    const int cur = p.causal ? (int)(qpos_of(p, b, t) / p.block) : -1;
+    for (int e = lane; e < p.sel_w; e += 64) {
+      int val = -1;
+      if (e < cnt) val = idx;
+      else if (e == cnt && p.causal) val = cur;
+      out[e] = val;
+    }
+  } else {
+    uint64_t* out = p.part + (srow * p.nsplit + split) * p.topk;
+    for (int e = lane; e < p.topk; e += 64) out[e] = e < cnt ? buf[e] : 0ull;
+  }
+}
+
+template <int W, int DG, int V, int QK, bool LO>
+__global__ __launch_bounds__(64 * W) void gate_kernel(GateParams p) {
+  constexpr int ROWS = 16 * W;
+  constexpr int CAP = 64 * V;
+  constexpr int PADR = DG + 8;  // padded LDS row (bf16 elements)
+  constexpr int KS = DG / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t s_hi[64 * PADR];
+  __shared__ __attribute__((aligned(16))) uint16_t s_lo[LO ? 64 * PADR : 8];
+  __shared__ uint64_t s_buf[ROWS][CAP];
+  __shared__ int s_cnt[ROWS];
+  __shared__ uint64_t s_thr[ROWS];
+
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile_l = lid % p.ntiles;
+  const int rest = lid / p.ntiles;
+  const int split = rest % p.nsplit;
+  const int bh = rest / p.nsplit;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  // causal rows late in the sequence have the most candidates: start them first
+  const int tile = p.causal ? (p.ntiles - 1 - tile_l) : tile_l;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, kh = lane >> 4;
+  const int rbase = tile * ROWS + w * 16;
+
+  // gate-query fragments (A operand) of row rbase + r16
+  bf16x8 qh[KS], ql[KS];
+  {
+    const int row = rbase + r16;
+    const bool ok = row < p.rows_per_bh;
+    const RowInfo ri = row_to_th(ok ? row : 0, p);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) load_gate_q<QK>(p, b, hk, ri, ok, ks * 32 + kh * 8, qh[ks], ql[ks]);
+  }
+  // candidate counts of the 4 result rows this lane holds (rows 4*kh + i)
+  int ncand[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = rbase + 4 * kh + i;
+    ncand[i] = row < p.rows_per_bh ? ncand_of(p, b, row_to_th(row, p).t) : 0;
+  }
+  // the tile's last row has the most candidates
+  const int last_row = min(tile * ROWS + ROWS, p.rows_per_bh) - 1;
+  const int nc_max = ncand_of(p, b, row_to_th(last_row, p).t);
+  const int c_lo = split * p.span;
+  const int c_hi = min(c_lo + p.span, nc_max);
+
+  if (tid < ROWS) {
+    s_cnt[tid] = 0;
+    s_thr[tid] = 0ull;
+  }
+  const uint16_t* phi = p.p_hi + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h;
+  const uint16_t* plo = LO ? p.p_lo + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h : nullptr;
+
+  for (int c0 = c_lo; c0 < c_hi; c0 += 64) {
+    __syncthreads();
+    // stage 64 candidate summaries (hi and lo planes) into LDS
+    for (int idx = tid; idx < 64 * (DG / 8); idx += 64 * W) {
+      const int jr = idx / (DG / 8), ch = idx % (DG / 8);
+      const int j = c0 + jr;
+      u16x8 vh = {0, 0, 0, 0, 0, 0, 0, 0}, vl = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (j < c_hi) {
+        vh = ld16(phi + (int64_t)j * p.ps_j + ch * 8);
+        if constexpr (LO) vl = ld16(plo + (int64_t)j * p.ps_j + ch * 8);
+      }
+      st16(&s_hi[jr * PADR + ch * 8], vh);
+      if constexpr (LO) st16(&s_lo[jr * PADR + ch * 8], vl);
+    }
+    __syncthreads();
+    f32x4 acc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 bh16 = as_bf(ld16(&s_hi[(ct * 16 + r16) * PADR + ks * 32 + kh * 8]));
+        acc[ct] = mfma16(qh[ks], bh16, acc[ct]);
+        if constexpr (LO) {
+          const bf16x8 bl16 = as_bf(ld16(&s_lo[(ct * 16 + r16) * PADR + ks * 32 + kh * 8]));
+          acc[ct] = mfma16(qh[ks], bl16, acc[ct]);
+        }
+        if constexpr (QK != 0) acc[ct] = mfma16(ql[ks], bh16, acc[ct]);
+      }
+    }
+    // append candidates that beat their row's threshold
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = w * 16 + 4 * kh + i;
+      const uint64_t thr = s_thr[rl];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int j = c0 + ct * 16 + r16;
+        if (j < c_hi && j < ncand[i]) {
+          const uint64_t key = make_key(acc[ct][i], (uint32_t)j);
+          if (key > thr) {
+            const int slot = atomicAdd(&s_cnt[rl], 1);
+            s_buf[rl][slot] = key;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    for (int r = 0; r < 16; ++r) {
+      const int rl = w * 16 + r;
+      if (s_cnt[rl] > CAP - 64) row_compact<V>(s_buf[rl], &s_cnt[rl], &s_thr[rl], p.topk);
+    }
+  }
+  __syncthreads();
+  for (int r = 0; r < 16; ++r) {
+    const int row = rbase + r;
+    if (row >= p.rows_per_bh) break;
+    const int rl = w * 16 + r;
+    row_compact<V>(s_buf[rl], &s_cnt[rl], &s_thr[rl], p.topk);
+    const RowInfo ri = row_to_th(row, p);
+    const int hs = p.per_group ? hk : hk * p.G + ri.hh;
+    emit_row<V>(p, s_buf[rl], s_cnt[rl], b, hs, ri.t, split);
+  }
+}
+
+// Merge the per-split top-k lists of one selection row (one wave per row).
+template <int V>
+__global__ __launch_bounds__(256) void gate_merge_kernel(GateParams p) {
+  constexpr int CAP = 64 * V;
+  __shared__ uint64_t s_buf[4][CAP];
+  __shared__ int s_cnt[4];
+  __shared__ uint64_t s_thr[4];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nrows = (int64_t)p.B * p.Hs * p.Lq;
+  const int64_t srow = (int64_t)blockIdx.x * 4 + w;
+  if (srow >= nrows) return;  // wave-uniform; no workgroup barrier follows
+  const int t = (int)(srow % p.Lq);
+  const int hs = (int)((srow / p.Lq) % p.Hs);
+  const int b = (int)(srow / ((int64_t)p.Lq * p.Hs));
+  if (lane == 0) {
+    s_cnt[w] = 0;
+    s_thr[w] = 0ull;
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int sp = 0; sp < p.nsplit; ++sp) {
+    const uint64_t* src = p.part + (srow * p.nsplit + sp) * p.topk;
+    for (int e0 = 0; e0 < p.topk; e0 += 64) {
+      const uint64_t key = (e0 + lane < p.topk) ? src[e0 + lane] : 0ull;
+      const bool hit = key > s_thr[w];
+      const uint64_t m = __ballot(hit);
+      const int c = s_cnt[w];
+      const int pos = c + __popcll(m & ((1ull << lane) - 1ull));
+      if (hit) s_buf[w][pos] = key;
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 0) s_cnt[w] = c + __popcll(m);
+      __builtin_amdgcn_wave_barrier();
+      if (s_cnt[w] > CAP - 64) row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+    }
+  }
+  row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+  GateParams q = p;
+  q.nsplit = 1;
+  emit_row<V>(q, s_buf[w], s_cnt[w], b, hs, t, 0);
+}
+
+template <int W, int DG, int V>
+static void gate_dispatch_q(const GateParams& p, hipStream_t s, int grid) {
+  const bool lo = p.p_lo != nullptr;
+#define BSA_GATE_CASE(QK, LO)                                                               \
+  hipLaunchKernelGGL((gate_kernel<W, DG, V, QK, LO>), dim3(grid), dim3(64 * W), 0, s, p);
+  if (p.qkind == 0) {
+    if (lo) { BSA_GATE_CASE(0, true) } else { BSA_GATE_CASE(0, false) }
+  } else if (p.qkind == 1) {
+    if (lo) { BSA_GATE_CASE(1, true) } else { BSA_GATE_CASE(1, false) }
+  } else {
+    if (lo) { BSA_GATE_CASE(2, true) } else { BSA_GATE_CASE(2, false) }
+  }
+#undef BSA_GATE_CASE
+}
+
+int gate_cap_v(int topk) { return (2 * topk + 64) <= 128 ? 2 : 4; }
+int gate_waves(const GateParams& p) {
+  if (p.rows_per_bh <= 16) return 1;
+  return gate_cap_v(p.topk) == 2 ? 4 : 2;
+}
+
+bool launch_gate(const GateParams& p, hipStream_t s) {
+  const int W = gate_waves(p);
+  const int V = gate_cap_v(p.topk);
+  const int grid = p.B * p.Hkv * p.nsplit * p.ntiles;
+  {
+    LaunchScope ls("gate_topk", s);
+    if (p.Dg == 128) {
+      if (W == 4) gate_dispatch_q<4, 128, 2>(p, s, grid);
+      else if (W == 2) V == 2 ? gate_dispatch_q<2, 128, 2>(p, s, grid) : gate_dispatch_q<2, 128, 4>(p, s, grid);
+      else V == 2 ? gate_dispatch_q<1, 128, 2>(p, s, grid) : gate_dispatch_q<1, 128, 4>(p, s, grid);
+    } else {
+      if (W == 4) gate_dispatch_q<4, 64, 2>(p, s, grid);
+      else if (W == 2) V == 2 ? gate_dispatch_q<2, 64, 2>(p, s, grid) : gate_dispatch_q<2, 64, 4>(p, s, grid);
+      else V == 2 ? gate_dispatch_q<1, 64, 2>(p, s, grid) : gate_dispatch_q<1, 64, 4>(p, s, grid);
+    }
+  }
+  return launch_ok("gate_topk");
+}
+
+bool launch_gate_merge(const GateParams& p, hipStream_t s) {
+  const int64_t nrows = (int64_t)p.B * p.Hs * p.Lq;
+  const int grid = (int)((nrows + 3) / 4);
+  {
+    LaunchScope ls("gate_merge", s);
+    if (gate_cap_v(p.topk) == 2)
+      hipLaunchKernelGGL(gate_merge_kernel<2>, dim3(grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(gate_merge_kernel<4>, dim3(grid), dim3(256), 0, s, p);
+  }
+  return launch_ok("gate_merge");
+}
+
+// ---------------------------------------------------------------------------
+// fp32 gate: one wave per selection row, scores in plain fp32 FMA against the
+// fp32 summaries, same buffer/compaction top-k.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gate_f32_kernel(GateF32Params p) {
+  constexpr int V = 2, CAP = 128;
+  __shared__ uint64_t s_buf[4][CAP];
+  __shared__ int s_cnt[4];
+  __shared__ uint64_t s_thr[4];
+  __shared__ float s_q[4][128];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nrows = (int64_t)p.B * p.Hs * p.Lq;
+  const int64_t srow = (int64_t)blockIdx.x * 4 + w;
+  if (srow >= nrows) return;  // wave-uniform
+  const int t = (int)(srow % p.Lq);
+  const int hs = (int)((srow / p.Lq) % p.Hs);
+  const int b = (int)(srow / ((int64_t)p.Lq * p.Hs));
+  const int hk = p.per_group ? hs : hs / p.G;
+  for (int d = lane; d < p.Dg; d += 64) {
+    float x = 0.f;
+    if (p.per_group) {
+      for (int g = 0; g < p.G; ++g) x += p.q[(int64_t)b * p.qs_b + (int64_t)t * p.qs_t + (int64_t)(hk * p.G + g) * p.qs_h + d];
+    } else {
+      x = p.q[(int64_t)b * p.qs_b + (int64_t)t * p.qs_t + (int64_t)hs * p.qs_h + d];
+    }
+    s_q[w][d] = x;
+  }
+  if (lane == 0) {
+    s_cnt[w] = 0;
+    s_thr[w] = 0ull;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int64_t qpos = (int64_t)p.Lk - p.Lq + t;
+  const int cur = (int)(qpos / p.block);
+  const int ncand = p.causal ? min(cur, p.Nb) : p.Nb;
+  for (int c0 = 0; c0 < ncand; c0 += 64) {
+    const int j = c0 + lane;
+    uint64_t key = 0ull;
+    if (j < ncand) {
+      const float* pr = p.pooled + (((int64_t)b * p.Nb + j) * p.Hkv + hk) * p.Dg;
+      float s = 0.f;
+      for (int d = 0; d < p.Dg; ++d) s = fmaf(s_q[w][d], pr[d], s);
+      key = make_key(s, (uint32_t)j);
+    }
+    const bool hit = key > s_thr[w];
+    const uint64_t m = __ballot(hit);
+    const int c = s_cnt[w];
+    const int pos = c + __popcll(m & ((1ull << lane) - 1ull));
+    if (hit) s_buf[w][pos] = key;
+    __builtin_amdgcn_wave_barrier();
+    if (lane == 0) s_cnt[w] = c + __popcll(m);
+    __builtin_amdgcn_wave_barrier();
+    if (s_cnt[w] > CAP - 64) row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+  }
+  row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+  const int cnt = s_cnt[w];
+  int idx = lane < cnt ? (int)key_index(s_buf[w][lane]) : 0x7FFFFFFF;
+  idx = wave_sort_asc_i32(idx);
+  int32_t* out = p.sel + srow * p.sel_w;
+  for (int e = lane; e < p.sel_w; e += 64) {
+    int val = -1;
+    if (e < cnt) val = idx;
+    else if (e == cnt && p.causal) val = cur;
+    out[e] = val;
+  }
+}
+
+bool launch_gate_f32(const GateF32Params& p, hipStream_t s) {
+  const int64_t nrows = (int64_t)p.B * p.Hs * p.Lq;
+  const int grid = (int)((nrows + 3) / 4);
+  {
+    LaunchScope ls("gate_f32", s);
+    hipLaunchKernelGGL(gate_f32_kernel, dim3(grid), dim3(256), 0, s, p);
+  }
+  return launch_ok("gate_f32");
+}
+
+}  // namespace bsa

@@ -1,0 +1,199 @@
+/*
+ * bsa.h -- C ABI of libbsa, block-sparse attention for AMD MI355X (gfx950).
+ *
+ * The method (what the calls compute):
+ *   - Every query (per query head), or every GQA group, scores per-block key
+ *     summaries and keeps the top-k KV blocks; exact softmax attention then
+ *     runs over only the kept blocks.  MoBA repo card
+ *     (ross.abutalabs.com/products/moba.json), card.what_it_is: MoE-style
+ *     top-k gating over KV blocks, switchable to full attention; "MiniMax
+ *     released MSA ..." (news.hamidun.com), section "How MSA Works": an index
+ *     branch picks the top-k blocks per query and GQA group, a main branch
+ *     attends exactly over them.
+ *   - Block summaries are routing keys kept in GPU memory ("100 Millionen
+ *     Token: Gedaechtnis oder Trugbild?", aitalk.it, section "Das Gehirn mit
+ *     zwei Geschwindigkeiten"); this library forms them as the mean of the
+ *     block's keys.  The same section gives document-wise RoPE: positions
+ *     restart at 0 at each document start.
+ *   Readings where the pages are silent (causal masking, the forced own
+ *   block, the tie rule, the RoPE form) are stated at each call below.
+ *
+ * Conventions for every call:
+ *   - Every pointer in an args struct is DEVICE memory unless marked HOST.
+ *     The caller owns all buffers, including the workspace; the library never
+ *     allocates or frees device memory and keeps no state across calls other
+ *     than the last error message and the optional launch timer.
+ *   - Tensors are addressed by element strides for their outer dimensions;
+ *     the innermost (head) dimension is contiguous and each row starts on a
+ *     16-byte boundary.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Inputs must stay valid until the stream reaches the
+ *     call's end.  No host synchronisation happens inside a call.
+ *   - Arguments are validated before anything is enqueued: a call that
+ *     returns an error has enqueued nothing (BSA_ERR_HIP excepted, which
+ *     reports a failed launch).  No C++ exception crosses the ABI.
+ *   - Results are bitwise deterministic for identical inputs and shapes.
+ *   - NaN or Inf inputs give undefined results.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t bsa_status;
+#define BSA_OK 0
+#define BSA_ERR_INVALID_ARG 1 /* a null required pointer, a bad size or stride */
+#define BSA_ERR_UNSUPPORTED 2 /* a valid request outside what the kernels handle */
+#define BSA_ERR_WORKSPACE 3   /* workspace missing, too small or misaligned */
+#define BSA_ERR_HIP 4         /* the HIP runtime rejected a launch */
+
+#define BSA_DTYPE_F32 0
+#define BSA_DTYPE_BF16 1
+
+#define BSA_GATE_PER_HEAD 0  /* one selection per query head (MoBA card) */
+#define BSA_GATE_PER_GROUP 1 /* one per GQA group, head scores summed (MiniMax page) */
+
+#define BSA_MAX_TOPK 64
+
+/*
+ * Prefill.  q [B, Lq, Hq, D], k and v [B, Lk, Hkv, D], Hq a multiple of Hkv
+ * (G = Hq / Hkv query heads share a KV head); D is 64 or 128.
+ *
+ * Block j holds key tokens [j*block, min((j+1)*block, Lk)); Nb = ceil(Lk/block).
+ * Causal mode: query i sits at key position p = Lk - Lq + i; its own block
+ * cur = p / block is always attended with keys <= p and is not counted in
+ * topk; only blocks j < cur compete.  Non-causal: every block competes and
+ * nothing is forced.  The gate keeps min(topk, #candidates) blocks by score,
+ * breaking ties toward the lower block index; topk >= #candidates attends
+ * every candidate (full attention).
+ *
+ * Gate score of block j: (gate query) . (summary of block j), where the
+ * summary is the mean of block j's keys (index_k's when given, else k's,
+ * after RoPE when doc_ids_k is given) and the gate query is the query head's
+ * vector (index_q's when given, else q's after RoPE), or for
+ * BSA_GATE_PER_GROUP the sum of the group's G head vectors.
+ *
+ * Output o[b, i, h] = sum_u softmax_u(scale * q.k_u) v_u over the union of
+ * the selected blocks' keys (one softmax over all of them); an empty key set
+ * gives o = 0 and lse = -inf.
+ */
+typedef struct bsa_prefill_args {
+    int32_t dtype;                 /* BSA_DTYPE_*: element type of q, k, v, o, index_q, index_k */
+    int32_t B, Lq, Lk, Hq, Hkv, D; /* Lq <= Lk when causal */
+    const void* q;  int64_t q_stride[3];   /* (b, t, h) element strides */
+    const void* k;  int64_t k_stride[3];
+    const void* v;  int64_t v_stride[3];
+    void* o;        int64_t o_stride[3];   /* output, same element type as q */
+    int32_t block;                 /* tokens per KV block, >= 1 */
+    int32_t topk;                  /* 0 <= topk <= BSA_MAX_TOPK (clamped to Nb) */
+    int32_t causal;                /* 0 or 1 */
+    int32_t gate_mode;             /* BSA_GATE_* */
+    const void* index_q; int64_t iq_stride[3]; /* optional [B, Lq, Hq, Di]; both or neither with index_k */
+    const void* index_k; int64_t ik_stride[3]; /* optional [B, Lk, Hkv, Di] */
+    int32_t Di;                    /* index dimension (64 or 128) when index tensors are given */
+    const int32_t* doc_ids_q;      /* optional [B, Lq] contiguous: rotate q by document-wise RoPE */
+    const int32_t* doc_ids_k;      /* optional [B, Lk] contiguous: rotate k by document-wise RoPE */
+    float rope_theta;              /* RoPE base; <= 0 means 10000 (pairs (i, i+D/2)) */
+    float scale;                   /* softmax scale; 0 means 1/sqrt(D) */
+    const float* pooled;           /* optional precomputed summaries [B, Nb, Hkv, Dg] fp32
+                                      contiguous; when given the summary step is skipped */
+    int32_t* sel_out;              /* optional [B, Hs, Lq, topk + causal] int32, Hs = Hq (per head)
+                                      or Hkv (per group): chosen blocks ascending, the forced
+                                      block last when causal, -1 padded */
+    float* lse_out;                /* optional [B, Hq, Lq] natural-log softmax normaliser */
+} bsa_prefill_args;
+
+/* Workspace bytes bsa_sparse_attn_prefill needs for `a` (0 if `a` is invalid;
+ * bsa_last_error() then says why).  The workspace must be 256-byte aligned. */
+size_t bsa_prefill_workspace_bytes(const bsa_prefill_args* a);
+
+/* Runs the whole prefill: [positions + RoPE] -> block summaries -> gate and
+ * top-k -> selection inversion -> gathered attention -> combine.
+ * Errors: BSA_ERR_INVALID_ARG / BSA_ERR_UNSUPPORTED for bad or unsupported
+ * arguments, BSA_ERR_WORKSPACE if ws_bytes is below the query's answer,
+ * BSA_ERR_HIP if a launch fails. */
+bsa_status bsa_sparse_attn_prefill(const bsa_prefill_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/* Gate and top-k only (writes a->sel_out, which is then required; o and v
+ * are not touched and may be NULL).  Same workspace query as prefill. */
+bsa_status bsa_select_blocks(const bsa_prefill_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Decode: one new token per sequence.  q [B, Hq, D]; kcache, vcache
+ * [B, Lc, Hkv, D]; pooled [B, Nb, Hkv, D] block summaries of the cache
+ * (Nb = ceil(Lc / block)), as produced by bsa_block_summary or any other
+ * source: routing keys kept in GPU memory ("100 Millionen Token ...",
+ * section "Das Gehirn mit zwei Geschwindigkeiten").  Sequence b holds
+ * n_b = cache_lens[b] tokens (Lc when cache_lens is NULL; values are clamped
+ * to [1, Lc]); the new token is already cached at position n_b - 1, so its
+ * block cur = (n_b - 1) / block is forced (keys up to n_b - 1) and blocks
+ * 0..cur-1 compete for topk slots, ties to the lower index.
+ */
+typedef struct bsa_decode_args {
+    int32_t dtype;                 /* BSA_DTYPE_BF16 (q, caches, o) */
+    int32_t B, Lc, Hq, Hkv, D;
+    const void* q;      int64_t q_stride[2];   /* (b, h) */
+    const void* kcache; int64_t k_stride[3];   /* (b, t, h) */
+    const void* vcache; int64_t v_stride[3];
+    const void* pooled; int64_t p_stride[3];   /* (b, j, h) */
+    int32_t pooled_dtype;          /* BSA_DTYPE_BF16 or BSA_DTYPE_F32 */
+    const int32_t* cache_lens;     /* optional [B] */
+    int32_t block, topk, gate_mode;
+    float scale;                   /* 0 means 1/sqrt(D) */
+    void* o;            int64_t o_stride[2];   /* [B, Hq, D] output */
+    int32_t* sel_out;              /* optional [B, Hs, topk + 1]: chosen ascending, forced last, -1 padded */
+    float* lse_out;                /* optional [B, Hq] */
+} bsa_decode_args;
+
+size_t bsa_decode_workspace_bytes(const bsa_decode_args* a);
+bsa_status bsa_sparse_attn_decode(const bsa_decode_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Block summaries (the offline encoding of a memory): pooled[b, j, h, :] =
+ * mean of the keys of block j (a short last block averages the tokens it
+ * has), after document-wise RoPE when doc_ids is given.  Positions restart
+ * at 0 at every change of doc id ("100 Millionen Token ...", section "Das
+ * Gehirn mit zwei Geschwindigkeiten"); the rotation pairs (i, i + D/2) with
+ * angle pos * theta^(-2i/D), formed in double precision.  Sums are fp32.
+ */
+typedef struct bsa_summary_args {
+    int32_t dtype;                 /* element type of k (and k_rot) */
+    int32_t B, L, H, D, block;
+    const void* k; int64_t k_stride[3];        /* (b, t, h) */
+    const int32_t* doc_ids;        /* optional [B, L] contiguous */
+    float rope_theta;              /* <= 0 means 10000 */
+    void* pooled;                  /* [B, Nb, H, D] contiguous output */
+    int32_t pooled_dtype;          /* BSA_DTYPE_F32 or BSA_DTYPE_BF16 (round to nearest even) */
+    void* k_rot;                   /* optional [B, L, H, D] contiguous rotated keys (k's dtype);
+                                      needs doc_ids */
+    int32_t* pos_out;              /* optional [B, L] per-document positions; needs doc_ids */
+} bsa_summary_args;
+
+size_t bsa_summary_workspace_bytes(const bsa_summary_args* a);
+bsa_status bsa_block_summary(const bsa_summary_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* bsa_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t bsa_version(void);
+
+/*
+ * Optional launch timer (off by default; host-side state, not thread-safe).
+ * While enabled, every kernel launch is bracketed by HIP events recorded on
+ * the launch stream.  bsa_timer_report synchronises on those events and
+ * returns, for the kernel named `kernel` (HOST string), the summed duration in
+ * milliseconds and the launch count since the last reset.
+ */
+void bsa_timer_enable(int32_t on);
+void bsa_timer_reset(void);
+bsa_status bsa_timer_report(const char* kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H */

@@ -255,6 +255,7 @@ def prefill(
     pooled=None,
     tokens=None,
     return_scores: bool = False,
+    force_sel=None,
 ):
     """Block-sparse attention prefill, evaluated row by row.
 
@@ -271,6 +272,10 @@ def prefill(
       own block are masked.
     pooled: optional precomputed block summaries [B, Nb, Hkv, Dg].
     tokens: optional list of query indices to evaluate (all by default).
+    force_sel: optional [B, Hs, T, w] block lists (-1 padded) that replace
+      the gate's choice for the evaluated tokens -- used to evaluate the exact
+      attention on another implementation's selection when two selections
+      differ only by near-tied gate scores.
 
     Returns a dict with
       o    [B, T, Hq, D]       outputs for the evaluated tokens,
@@ -337,6 +342,8 @@ def prefill(
                     scores_out[b, hs, ti, :n_cand] = s
                 ch = select_topk(s, n_cand, topk)
                 row = ch + ([cur] if causal else [])
+                if force_sel is not None:
+                    row = [int(x) for x in np.asarray(force_sel)[b, hs, ti] if x >= 0]
                 sel[b, hs, ti, : len(row)] = row
                 chosen_by_head[hs] = row
             for h in range(Hq):
@@ -378,6 +385,7 @@ def decode(
     scale: float | None = None,
     pairs=None,
     return_scores: bool = False,
+    force_sel=None,
 ):
     """One decode step per sequence over a cached KV sequence.
 
@@ -388,7 +396,8 @@ def decode(
     is already in the cache at position n-1, so its block cur = (n-1)//block
     is forced, candidates are blocks 0..cur-1, and keys 0..n-1 of the forced
     block are attended.  pairs: optional list of (b, h) query rows to
-    evaluate (default all).  kcache/vcache only need to support slicing
+    evaluate (default all).  force_sel [B, Hs, w] (optional) replaces the
+    gate's choice, as in prefill.  kcache/vcache only need to support slicing
     [b, a:e, hk] -- a caller may pass an object that fetches slices lazily.
 
     Returns dict: o [B, Hq, D] (rows not evaluated stay 0), lse [B, Hq],
@@ -421,6 +430,8 @@ def decode(
             s = pk @ gvec if cur > 0 else np.zeros(0)
             ch = select_topk(s, cur, topk)
             row = ch + [cur]
+            if force_sel is not None:
+                row = [int(x) for x in np.asarray(force_sel)[b, hs] if x >= 0]
             sel[b, hs, : len(row)] = row
             done_sel[(b, hs)] = row
             if return_scores:

@@ -1,0 +1,100 @@
+"""Helpers for comparing the HIP library with the float64 oracle.
+
+Selection rule: the chosen block set must equal the oracle's, except where the
+k-th and (k+1)-th best gate scores lie within a relative 1e-4 of each other.
+Then the GPU set passes if it has the oracle's size, holds the forced block,
+holds every block scoring above tau + delta, and no block scoring below
+tau - delta (tau = the oracle's k-th best score, delta = 1e-4 * max(|s_k|,
+|s_k+1|)); that row's output is compared with the oracle's exact attention on
+the GPU's own set.
+
+Output rule: max-abs error <= 1e-2 for bf16 inputs and <= 1e-5 for fp32
+inputs.  A bf16 output is itself rounded to 8 significant bits, which alone
+moves a value by up to 2^-8 |o| (more than 1e-2 once |o| >= 2.56); for bf16
+outputs the bound is therefore 1e-2 on top of that storage rounding:
+|got - ref| <= 1e-2 + 2^-8 |ref|.  The plain max-abs error, the relative
+error (max-abs / max |o_ref|) and the RMS error are printed for every case.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TIE_REL = 1e-4
+
+
+def valid_set(row):
+    return sorted(int(x) for x in row if x >= 0)
+
+
+def check_selection(gpu_sel, ora_sel, ora_scores, topk, causal, cur_of=None, rel=TIE_REL):
+    """Compare [B, Hs, T, W] selections. Returns list of (b, hs, ti) rows that
+    differ within the tie window (callers re-evaluate those rows)."""
+    gpu_sel = np.asarray(gpu_sel)
+    ora_sel = np.asarray(ora_sel)
+    assert gpu_sel.shape == ora_sel.shape, (gpu_sel.shape, ora_sel.shape)
+    diff_rows = []
+    B, Hs, T, W = gpu_sel.shape
+    neq = np.any(gpu_sel != ora_sel, axis=-1)
+    for b, hs, ti in zip(*np.nonzero(neq)):
+        g = valid_set(gpu_sel[b, hs, ti])
+        o = valid_set(ora_sel[b, hs, ti])
+        if g == o:
+            # same set, different order/padding: the layout is part of the contract
+            raise AssertionError(f"row {(b, hs, ti)}: same set, different layout {gpu_sel[b, hs, ti]} vs {ora_sel[b, hs, ti]}")
+        cur = None
+        if causal:
+            cur = o[-1]
+            assert g and g[-1] == cur, f"row {(b, hs, ti)}: forced block missing {g} vs {o}"
+        gg = [j for j in g if j != cur]
+        og = [j for j in o if j != cur]
+        assert len(gg) == len(og), f"row {(b, hs, ti)}: sizes differ {g} vs {o}"
+        s = np.asarray(ora_scores[b, hs, ti], dtype=np.float64)
+        cand = np.nonzero(~np.isnan(s))[0]
+        order = sorted(cand, key=lambda j: (-s[j], j))
+        k = len(og)
+        tau = s[order[k - 1]]
+        nxt = s[order[k]] if k < len(order) else tau
+        delta = rel * max(abs(tau), abs(nxt))
+        must = {int(j) for j in cand if s[j] > tau + delta}
+        forbid = {int(j) for j in cand if s[j] < tau - delta}
+        assert all(not np.isnan(s[j]) for j in gg), f"row {(b, hs, ti)}: non-candidate chosen {gg}"
+        assert must <= set(gg), f"row {(b, hs, ti)}: missing clear winners {sorted(must - set(gg))}; gpu {g} oracle {o}"
+        assert not (forbid & set(gg)), f"row {(b, hs, ti)}: chose clear losers {sorted(forbid & set(gg))}; gpu {g} oracle {o}"
+        diff_rows.append((int(b), int(hs), int(ti)))
+    return diff_rows
+
+
+def err_stats(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    e = np.abs(got - ref)
+    mx = float(e.max()) if e.size else 0.0
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    rms = float(np.sqrt((e ** 2).mean())) if e.size else 0.0
+    return {"max_abs": mx, "rel": mx / scale if scale > 0 else mx, "rms": rms, "ref_max": scale}
+
+
+def assert_close(got, ref, atol, rel=None, what="o", bf16_storage=False):
+    st = err_stats(got, ref)
+    msg = f"{what}: max_abs={st['max_abs']:.3e} rel={st['rel']:.3e} rms={st['rms']:.3e} |ref|max={st['ref_max']:.3e}"
+    print(msg)
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    bound = atol + (2.0 ** -8) * np.abs(r) if bf16_storage else atol
+    worst = float(np.max(np.abs(g - r) - bound)) if g.size else -1.0
+    assert worst <= 0.0, msg + f" (exceeds bound by {worst:.3e})"
+    if rel is not None:
+        assert st["rel"] <= rel, msg
+    return st
+
+
+def to_np(t):
+    import torch
+
+    return t.detach().to("cpu", torch.float64).numpy() if t.dtype.is_floating_point else t.detach().cpu().numpy()
+
+
+def ln2():
+    return math.log(2.0)

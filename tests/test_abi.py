@@ -1,0 +1,114 @@
+"""The C-ABI library: it loads, exports every symbol include/bsa.h declares,
+and rejects bad arguments with the documented status codes before anything
+is enqueued (host-only checks; no kernel runs here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import block_sparse_long_mean_amd as m
+
+    if not os.path.exists(m.LIB_PATH):
+        from block_sparse_long_mean_amd import build
+
+        build.build()
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(m):
+    names = declared_functions()
+    assert len(names) >= 12, names
+    out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (bsa_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(m.lib(), n)
+    # nothing but the C ABI is exported under the bsa_ prefix
+    assert exported == set(names), exported - set(names)
+
+
+def test_version(m):
+    assert m.version() >= 100
+
+
+def _args(m, **kw):
+    a = m.PrefillArgs()
+    a.dtype = m.BSA_DTYPE_BF16
+    a.B, a.Lq, a.Lk, a.Hq, a.Hkv, a.D = 1, 256, 256, 4, 2, 128
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 255) & ~255
+    a.q = a.k = a.v = a.o = base
+    a.q_stride = m.I64x3(256 * 4 * 128, 4 * 128, 128)
+    a.k_stride = a.v_stride = m.I64x3(256 * 2 * 128, 2 * 128, 128)
+    a.o_stride = a.q_stride
+    a.block, a.topk, a.causal, a.gate_mode = 64, 2, 1, 0
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a, buf
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", 0, 1), ("Hq", 3, 1), ("D", 96, 2), ("block", 0, 1), ("topk", -1, 1), ("topk", 65, 2),
+    ("causal", 2, 1), ("gate_mode", 7, 1), ("dtype", 5, 1),
+])
+def test_prefill_rejects_bad_arguments(m, field, value, status):
+    a, _buf = _args(m, **{field: value})
+    assert m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a)) == 0
+    st = m.lib().bsa_sparse_attn_prefill(ctypes.byref(a), None, 0, None)
+    assert st == status, (st, m.lib().bsa_last_error())
+    assert m.lib().bsa_last_error()
+
+
+def test_prefill_short_workspace(m):
+    a, _buf = _args(m)
+    need = m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a))
+    assert need > 0
+    assert m.lib().bsa_sparse_attn_prefill(ctypes.byref(a), None, 0, None) == m.BSA_ERR_WORKSPACE
+    assert m.lib().bsa_sparse_attn_prefill(ctypes.byref(a), ctypes.c_void_p(256), need - 1, None) == m.BSA_ERR_WORKSPACE
+    # misaligned workspace
+    assert m.lib().bsa_sparse_attn_prefill(ctypes.byref(a), ctypes.c_void_p(257), need + 512, None) == m.BSA_ERR_WORKSPACE
+
+
+def test_prefill_misaligned_and_null(m):
+    a, _buf = _args(m)
+    a.q = a.q + 2
+    assert m.lib().bsa_sparse_attn_prefill(ctypes.byref(a), None, 0, None) == m.BSA_ERR_INVALID_ARG
+    a, _buf = _args(m)
+    a.v = None
+    assert m.lib().bsa_sparse_attn_prefill(ctypes.byref(a), None, 0, None) == m.BSA_ERR_INVALID_ARG
+    a, _buf = _args(m, Lq=300)  # causal needs Lq <= Lk
+    assert m.lib().bsa_sparse_attn_prefill(ctypes.byref(a), None, 0, None) == m.BSA_ERR_INVALID_ARG
+    assert m.lib().bsa_select_blocks(ctypes.byref(_args(m)[0]), None, 0, None) == m.BSA_ERR_INVALID_ARG  # no sel_out
+
+
+def test_decode_and_summary_validation(m):
+    d = m.DecodeArgs()
+    d.dtype = m.BSA_DTYPE_F32
+    d.B, d.Lc, d.Hq, d.Hkv, d.D = 1, 1024, 4, 2, 128
+    assert m.lib().bsa_sparse_attn_decode(ctypes.byref(d), None, 0, None) == m.BSA_ERR_UNSUPPORTED
+    d.dtype = m.BSA_DTYPE_BF16
+    assert m.lib().bsa_sparse_attn_decode(ctypes.byref(d), None, 0, None) == m.BSA_ERR_INVALID_ARG  # null tensors
+    s = m.SummaryArgs()
+    s.dtype, s.B, s.L, s.H, s.D, s.block = m.BSA_DTYPE_BF16, 1, 100, 2, 128, 0
+    assert m.lib().bsa_block_summary(ctypes.byref(s), None, 0, None) == m.BSA_ERR_INVALID_ARG
+
+
+def test_timer_report_unknown_kernel_is_empty(m):
+    m.timer_reset()
+    assert m.timer_report("no_such_kernel") == (0.0, 0)

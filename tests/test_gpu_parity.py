@@ -1,0 +1,212 @@
+"""Parity of the HIP library (through its C ABI) against the float64 oracle.
+
+Every case is seeded and synthetic; sizes span several tiles and a ragged
+tail.  Selections must match exactly except inside the 1e-4 tie window;
+outputs within max-abs 1e-2 (bf16) or 1e-5 (fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from bsa_testutil import assert_close, check_selection, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bsa():
+    import block_sparse_long_mean_amd as m
+
+    m.lib()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _ref_with_gpu_sel(ref, diff_rows, gpu_sel, run_oracle):
+    """Recompute oracle outputs of the tokens whose selection legitimately
+    differs (near-ties), on the GPU's selection."""
+    if not diff_rows:
+        return ref
+    toks = sorted({t for (_, _, t) in diff_rows})
+    fs = np.asarray(gpu_sel)[:, :, toks]
+    r2 = run_oracle(tokens=toks, force_sel=fs)
+    o = ref["o"].copy()
+    lse = ref["lse"].copy()
+    for i, t in enumerate(toks):
+        o[:, t] = r2["o"][:, i]
+        lse[:, :, t] = r2["lse"][:, :, i]
+    return {"o": o, "lse": lse}
+
+
+def run_prefill_case(bsa, *, dtype, B, Lq, Lk, Hq, Hkv, D, block, topk, causal, gate="head", sigma=1.0, seed=0,
+                     Di=None, doc_mean=None, atol, rel, lse_atol):
+    name = f"prefill dtype={dtype} B{B} Lq{Lq} Lk{Lk} H{Hq}/{Hkv} D{D} block{block} topk{topk} causal{causal} gate={gate} Di={Di} doc={doc_mean} seed{seed}"
+    _say("case " + name)
+    q = synth.host_tensor((B, Lq, Hq, D), sigma, seed, synth.TID["q"], dtype)
+    k = synth.host_tensor((B, Lk, Hkv, D), sigma, seed, synth.TID["k"], dtype)
+    v = synth.host_tensor((B, Lk, Hkv, D), sigma, seed, synth.TID["v"], dtype)
+    iq = ik = None
+    if Di:
+        iq = synth.host_tensor((B, Lq, Hq, Di), sigma, seed, synth.TID["index_q"], dtype)
+        ik = synth.host_tensor((B, Lk, Hkv, Di), sigma, seed, synth.TID["index_k"], dtype)
+    dq = dk = None
+    if doc_mean:
+        dk = np.stack([synth.random_doc_ids(Lk, doc_mean, seed + b) for b in range(B)])
+        dq = np.zeros((B, Lq), dtype=np.int32)  # the query chunk is one document
+    dev = lambda x: None if x is None else x.cuda()
+    o, sel, lse = bsa.sparse_attn_prefill(
+        dev(q), dev(k), dev(v), block, topk, causal, gate=gate, index_q=dev(iq), index_k=dev(ik),
+        doc_ids_q=None if dq is None else torch.from_numpy(dq).cuda(),
+        doc_ids_k=None if dk is None else torch.from_numpy(dk).cuda(),
+        return_sel=True, return_lse=True)
+    torch.cuda.synchronize()
+    _say("  gpu done")
+
+    def run_oracle(tokens=None, force_sel=None, scores=False):
+        return oracle.prefill(q, k, v, block=block, topk=topk, causal=causal, gate=gate, index_q=iq, index_k=ik,
+                              doc_ids_q=dq, doc_ids_k=dk, tokens=tokens, force_sel=force_sel,
+                              return_scores=scores)
+
+    ref = run_oracle(scores=True)
+    gsel = sel.cpu().numpy()
+    diff = check_selection(gsel, ref["sel"], ref["scores"], topk, causal)
+    _say(f"  selection rows {gsel.shape[0] * gsel.shape[1] * gsel.shape[2]}, near-tie differences {len(diff)}")
+    ref = _ref_with_gpu_sel(ref, diff, gsel, run_oracle)
+    st = assert_close(to_np(o), ref["o"], atol, rel, bf16_storage=(dtype == "bf16"))
+    assert_close(to_np(lse), ref["lse"], lse_atol, None, what="lse")
+    return st
+
+
+def test_tiny_fp32_causal(bsa):
+    """1 head, L2048, D64, block 128, top-3 + own block, fp32 N(0,1), seed 0."""
+    run_prefill_case(bsa, dtype="f32", B=1, Lq=2048, Lk=2048, Hq=1, Hkv=1, D=64, block=128, topk=3, causal=True,
+                     seed=0, atol=1e-5, rel=None, lse_atol=1e-5)
+
+
+def test_fp32_group_ragged(bsa):
+    run_prefill_case(bsa, dtype="f32", B=2, Lq=333, Lk=333, Hq=4, Hkv=2, D=128, block=48, topk=2, causal=True,
+                     gate="group", seed=1, atol=1e-5, rel=None, lse_atol=1e-5)
+
+
+def test_bf16_per_head_moba_like(bsa):
+    """GQA 8/2, D128, block 256, top-3 + own block, N(0,1)/sqrt(128), ragged length."""
+    run_prefill_case(bsa, dtype="bf16", B=1, Lq=3000, Lk=3000, Hq=8, Hkv=2, D=128, block=256, topk=3, causal=True,
+                     sigma=128 ** -0.5, seed=2, atol=1e-2, rel=1e-2, lse_atol=5e-3)
+
+
+def test_bf16_index_branch_group(bsa):
+    """Index q/k of dim 64 per head, scores summed over the group, block 64, top-16 + own."""
+    run_prefill_case(bsa, dtype="bf16", B=1, Lq=2085, Lk=2085, Hq=16, Hkv=2, D=128, block=64, topk=16, causal=True,
+                     gate="group", Di=64, seed=3, atol=1e-2, rel=1e-2, lse_atol=5e-3)
+
+
+def test_bf16_d64_batch_offset_queries(bsa):
+    """B=2, Lq < Lk (queries at the end), D64, block 32."""
+    run_prefill_case(bsa, dtype="bf16", B=2, Lq=200, Lk=1500, Hq=4, Hkv=4, D=64, block=32, topk=5, causal=True,
+                     seed=4, atol=1e-2, rel=1e-2, lse_atol=5e-3)
+
+
+def test_bf16_memory_doc_rope_noncausal(bsa):
+    """MSA-style: a memory of short documents with document-wise RoPE, one query chunk, non-causal top-16."""
+    run_prefill_case(bsa, dtype="bf16", B=1, Lq=128, Lk=20000, Hq=8, Hkv=2, D=128, block=64, topk=16, causal=False,
+                     seed=5, doc_mean=400.0, atol=1e-2, rel=1e-2, lse_atol=5e-3)
+
+
+def test_bf16_topk_zero_and_full(bsa):
+    run_prefill_case(bsa, dtype="bf16", B=1, Lq=700, Lk=700, Hq=2, Hkv=1, D=128, block=64, topk=0, causal=True,
+                     seed=6, atol=1e-2, rel=1e-2, lse_atol=5e-3)
+    run_prefill_case(bsa, dtype="bf16", B=1, Lq=700, Lk=700, Hq=2, Hkv=1, D=128, block=64, topk=11, causal=True,
+                     seed=7, atol=1e-2, rel=1e-2, lse_atol=5e-3)
+
+
+def test_dense_switch_matches_torch_sdpa(bsa):
+    """top-k covering every block is full causal attention (MoBA's full/sparse switch)."""
+    B, L, H, D = 1, 1024, 4, 128
+    q = synth.host_tensor((B, L, H, D), 1.0, 8, 0, "bf16").cuda()
+    k = synth.host_tensor((B, L, H, D), 1.0, 8, 1, "bf16").cuda()
+    v = synth.host_tensor((B, L, H, D), 1.0, 8, 2, "bf16").cuda()
+    _say("case dense switch L1024 block64 topk16")
+    o = bsa.sparse_attn_prefill(q, k, v, 64, 16, True)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.float().transpose(1, 2), k.float().transpose(1, 2), v.float().transpose(1, 2), is_causal=True).transpose(1, 2)
+    assert_close(o.float().cpu().numpy(), ref.cpu().numpy(), 1e-2, 1e-2, bf16_storage=True)
+
+
+def test_block_summary_with_doc_rope(bsa):
+    B, L, H, D, block = 2, 3000, 2, 128, 64
+    _say("case block_summary doc-rope B2 L3000 H2 D128 block64")
+    k = synth.host_tensor((B, L, H, D), 1.0, 9, 1, "bf16")
+    ids = np.stack([synth.random_doc_ids(L, 300.0, 9 + b) for b in range(B)])
+    pooled, k_rot, pos = bsa.block_summary(k.cuda(), block, doc_ids=torch.from_numpy(ids).cuda(),
+                                           return_k_rot=True, return_pos=True)
+    torch.cuda.synchronize()
+    pos_ref = oracle.doc_positions(ids)
+    assert np.array_equal(pos.cpu().numpy(), pos_ref)
+    rot_ref = oracle.rope_rotate_half(k, pos_ref)
+    got = k_rot.float().cpu().numpy().astype(np.float64)
+    # bf16 storage: within half an ulp of the float64 value (plus fp32 rotation error)
+    assert np.all(np.abs(got - rot_ref) <= np.abs(rot_ref) * 2.0 ** -8 + 1e-6)
+    pool_ref = oracle.block_pool(k, block, pos=pos_ref)
+    assert_close(pooled.cpu().numpy(), pool_ref, 2e-6, None, what="pooled")
+    # plain summary, bf16 output: nearest-even rounding of the fp32 mean
+    p16 = bsa.block_summary(k.cuda(), block, out_dtype=torch.bfloat16)
+    ref = oracle.block_pool(k, block)
+    got = p16.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-7)
+
+
+@pytest.mark.parametrize("gate", ["head", "group"])
+def test_decode_ragged_lengths(bsa, gate):
+    B, Hq, Hkv, Lc, D, block, topk = 3, 8, 2, 5000, 128, 128, 8
+    _say(f"case decode gate={gate} B3 H8/2 Lc5000 block128 topk8")
+    q = synth.host_tensor((B, Hq, D), 1.0, 10, 0, "bf16")
+    k = synth.host_tensor((B, Lc, Hkv, D), 1.0, 10, 1, "bf16")
+    v = synth.host_tensor((B, Lc, Hkv, D), 1.0, 10, 2, "bf16")
+    lens = np.array([5000, 3333, 129], dtype=np.int32)
+    pooled = torch.from_numpy(oracle.block_pool(k, block)).to(torch.bfloat16)  # caller's routing keys
+    o, sel, lse = bsa.sparse_attn_decode(q.cuda(), k.cuda(), v.cuda(), pooled.cuda(), topk, block, gate=gate,
+                                         cache_lens=torch.from_numpy(lens).cuda(), return_sel=True, return_lse=True)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q, k, v, pooled, block=block, topk=topk, gate=gate, cache_lens=lens, return_scores=True)
+    Hs = Hkv if gate == "group" else Hq
+    nb = pooled.shape[1]
+    scores = np.full((B, Hs, 1, nb), np.nan)
+    for (b, hs), s in ref["scores"].items():
+        scores[b, hs, 0, : len(s)] = s
+    gsel = sel.cpu().numpy()[:, :, None]
+    diff = check_selection(gsel, ref["sel"][:, :, None], scores, topk, True)
+    if diff:
+        ref = oracle.decode(q, k, v, pooled, block=block, topk=topk, gate=gate, cache_lens=lens, force_sel=gsel[:, :, 0])
+    assert_close(to_np(o), ref["o"], 1e-2, 1e-2, bf16_storage=True)
+    assert_close(to_np(lse), ref["lse"], 5e-3, None, what="lse")
+
+
+def test_deterministic_bitwise(bsa):
+    B, L, Hq, Hkv, D = 1, 4096, 8, 2, 128
+    _say("case determinism L4096 H8/2 block128 topk4")
+    q = synth.host_tensor((B, L, Hq, D), 1.0, 11, 0, "bf16").cuda()
+    k = synth.host_tensor((B, L, Hkv, D), 1.0, 11, 1, "bf16").cuda()
+    v = synth.host_tensor((B, L, Hkv, D), 1.0, 11, 2, "bf16").cuda()
+    a, sa = bsa.sparse_attn_prefill(q, k, v, 128, 4, True, return_sel=True)
+    b, sb = bsa.sparse_attn_prefill(q, k, v, 128, 4, True, return_sel=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sa, sb)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_select_blocks_matches_prefill_selection(bsa):
+    B, L, Hq, Hkv, D = 1, 2048, 4, 2, 128
+    _say("case select_blocks vs prefill")
+    q = synth.host_tensor((B, L, Hq, D), 1.0, 12, 0, "bf16").cuda()
+    k = synth.host_tensor((B, L, Hkv, D), 1.0, 12, 1, "bf16").cuda()
+    v = synth.host_tensor((B, L, Hkv, D), 1.0, 12, 2, "bf16").cuda()
+    _, s1 = bsa.sparse_attn_prefill(q, k, v, 64, 8, True, return_sel=True)
+    s2 = bsa.select_blocks(q, k, 64, 8, True)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)

@@ -1,0 +1,310 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+  * prefill at 128K -- MiniMax-style index/main branch: batch 1, 131072
+    tokens, 64 query heads / 8 KV heads, head dim 128, block 64, index q/k of
+    dim 64, gate scores summed over each group's 8 heads, top-16 blocks per
+    group plus the own block, causal, bf16 N(0,1);
+  * decode -- 16 sequences x 1 new token over 1,048,576-token caches,
+    32/8 heads, head dim 128, block 128, bf16 routing keys (8192 blocks)
+    precomputed once by the library's block summary, top-32 per query head
+    plus the own block, bf16 N(0,1).
+Inputs are generated on the device and resident in HBM before timing.
+
+Prints one JSON line.  `value` is whole-step token throughput (prefill
+tokens + decode tokens per second); `breakdown` splits prefill and decode;
+`roofline` covers the dominant kernel; `cpu_baseline` times the float64
+oracle on a bounded sample of the prefill.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+PREFILL = dict(B=1, L=131072, Hq=64, Hkv=8, D=128, block=64, Di=64, topk=16, causal=True, gate="group", sigma=1.0)
+DECODE = dict(B=16, Lc=1048576, Hq=32, Hkv=8, D=128, block=128, topk=32, gate="head", sigma=1.0)
+SEED = 0
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_prefill_inputs():
+    import synth
+
+    c = PREFILL
+    t = synth.TID
+    q = synth.device_tensor((c["B"], c["L"], c["Hq"], c["D"]), c["sigma"], SEED, t["q"], "bf16")
+    k = synth.device_tensor((c["B"], c["L"], c["Hkv"], c["D"]), c["sigma"], SEED, t["k"], "bf16")
+    v = synth.device_tensor((c["B"], c["L"], c["Hkv"], c["D"]), c["sigma"], SEED, t["v"], "bf16")
+    iq = synth.device_tensor((c["B"], c["L"], c["Hq"], c["Di"]), c["sigma"], SEED, t["index_q"], "bf16")
+    ik = synth.device_tensor((c["B"], c["L"], c["Hkv"], c["Di"]), c["sigma"], SEED, t["index_k"], "bf16")
+    return q, k, v, iq, ik
+
+
+def make_decode_inputs(m):
+    import synth
+
+    c = DECODE
+    t = synth.TID
+    # distinct seed stream from the prefill inputs
+    q = synth.device_tensor((c["B"], c["Hq"], c["D"]), c["sigma"], SEED + 1, t["q"], "bf16")
+    kc = synth.device_tensor((c["B"], c["Lc"], c["Hkv"], c["D"]), c["sigma"], SEED + 1, t["k"], "bf16")
+    vc = synth.device_tensor((c["B"], c["Lc"], c["Hkv"], c["D"]), c["sigma"], SEED + 1, t["v"], "bf16")
+    import torch
+
+    pooled = m.block_summary(kc, c["block"], out_dtype=torch.bfloat16)  # routing keys, computed once
+    return q, kc, vc, pooled
+
+
+def prefill_pairs():
+    """Exact attended (query, key) pair counts of the prefill workload:
+    (pairs in gate-chosen blocks, pairs in own blocks)."""
+    c = PREFILL
+    L, bs, k = c["L"], c["block"], c["topk"]
+    gate = 0
+    diag = 0
+    for t in range(L):
+        cur = t // bs
+        gate += min(k, cur) * bs  # earlier blocks are always full
+        diag += t - cur * bs + 1
+    return gate * c["Hq"] * c["B"], diag * c["Hq"] * c["B"]
+
+
+def decode_bytes(sel):
+    """Algorithmic HBM bytes of one decode step: routing keys streamed once,
+    every distinct chosen block's keys and values once per KV head, q and o."""
+    import numpy as np
+
+    c = DECODE
+    nb = -(-c["Lc"] // c["block"])
+    G = c["Hq"] // c["Hkv"]
+    s = sel.cpu().numpy()  # [B, Hq, topk+1]
+    distinct = 0
+    for b in range(c["B"]):
+        for hk in range(c["Hkv"]):
+            blk = s[b, hk * G:(hk + 1) * G].reshape(-1)
+            distinct += len(set(int(x) for x in blk if x >= 0))
+    pooled = c["B"] * (nb - 1) * c["Hkv"] * c["D"] * 2  # blocks before the own block are scored
+    kv = distinct * c["block"] * c["D"] * 2 * 2
+    qo = 2 * c["B"] * c["Hq"] * c["D"] * 2
+    return pooled + kv + qo, distinct
+
+
+def cpu_baseline(q, k, v, iq, ik, budget_s=20.0):
+    """Time the float64 oracle on a seeded sample of prefill tokens."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    c = PREFILL
+    rng = np.random.default_rng(1234)
+    toks_all = np.sort(rng.choice(c["L"], size=4096, replace=False))
+    kh, vh, ikh = k.cpu(), v.cpu(), ik.cpu()
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        t0 = time.perf_counter()
+        pooled = oracle.block_pool(ikh, c["block"])
+        t_pool = time.perf_counter() - t0
+        done = 0
+        t1 = time.perf_counter()
+        step = 16
+        while done < len(toks_all) and time.perf_counter() - t1 < budget_s:
+            toks = toks_all[done:done + step].tolist()
+            qh = q[:, toks].cpu()
+            iqh = iq[:, toks].cpu()
+            # the oracle sees the sampled queries as rows Lq-Lk..: give it the
+            # full-length index positions by evaluating tokens in place
+            oracle.prefill(_RowView(qh, toks, c["L"]), kh, vh, block=c["block"], topk=c["topk"], causal=True,
+                           gate="group", index_q=_RowView(iqh, toks, c["L"]), index_k=ikh, pooled=pooled,
+                           tokens=toks)
+            done += len(toks)
+        t_rows = time.perf_counter() - t1
+    # throughput for the whole sequence: the pooling is paid once per sequence
+    per_token = t_rows / done
+    total = t_pool + per_token * c["L"]
+    return {
+        "value": round(c["L"] / total, 3),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {c['L']} prefill tokens (seeded, all 64 heads) in {t_rows:.1f} s plus one full "
+                  f"index-key pooling pass in {t_pool:.1f} s; whole-sequence time extrapolated linearly "
+                  f"({total:.0f} s); float64 NumPy, 1 thread",
+    }
+
+
+class _RowView:
+    """Presents sampled query rows at their true positions to the oracle."""
+
+    def __init__(self, rows, toks, L):
+        self.rows = rows
+        self.index = {t: i for i, t in enumerate(toks)}
+        self.shape = (rows.shape[0], L) + tuple(rows.shape[2:])
+
+    def __getitem__(self, key):
+        b, t = key
+        return self.rows[b, self.index[t]]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the path shards by KV head or "
+              f"sequence with no exchange, see the design notes", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_long_mean_amd as m
+
+    m.lib()
+    torch.cuda.set_device(0)
+    _log("generating prefill inputs")
+    q, k, v, iq, ik = make_prefill_inputs()
+    _log("generating decode inputs (68.7 GB of KV cache)")
+    dq, kc, vc, pooled = make_decode_inputs(m)
+    torch.cuda.synchronize()
+    c, d = PREFILL, DECODE
+    o = torch.empty_like(q)
+    do = torch.empty_like(dq)
+    pws = torch.empty(m.prefill_workspace_bytes(q, k, block=c["block"], topk=c["topk"], causal=True, gate="group",
+                                                index_q=iq, index_k=ik), dtype=torch.uint8, device="cuda")
+    dws = torch.empty(m.decode_workspace_bytes(dq, kc, vc, pooled, block=d["block"], topk=d["topk"]),
+                      dtype=torch.uint8, device="cuda")
+    dsel = torch.empty((d["B"], d["Hq"], d["topk"] + 1), dtype=torch.int32, device="cuda")
+    _log(f"workspaces: prefill {pws.numel() / 1e9:.2f} GB, decode {dws.numel() / 1e6:.1f} MB")
+
+    def prefill():
+        m.sparse_attn_prefill(q, k, v, c["block"], c["topk"], True, gate="group", index_q=iq, index_k=ik, out=o,
+                              workspace=pws)
+
+    def decode():
+        r = m.sparse_attn_decode(dq, kc, vc, pooled, d["topk"], d["block"], out=do, workspace=dws,
+                                 return_sel=True)
+        return r
+
+    for i in range(args.warmup):
+        prefill()
+        decode()
+        torch.cuda.synchronize()
+        _log(f"warmup {i + 1}/{args.warmup} done")
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    m.timer_reset()
+    m.timer_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    last_sel = None
+    for i in range(args.steps):
+        ev[i][0].record(st)
+        prefill()
+        ev[i][1].record(st)
+        _, last_sel = decode()
+        ev[i][2].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    m.timer_enable(False)
+    pre_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    dec_ms = sum(b.elapsed_time(c2) for _, b, c2 in ev) / args.steps
+    step_ms = sum(a.elapsed_time(c2) for a, _, c2 in ev) / args.steps
+    _log(f"timed {args.steps} steps: prefill {pre_ms:.3f} ms, decode {dec_ms:.3f} ms, step {step_ms:.3f} ms "
+         f"(host wall {wall * 1e3 / args.steps:.3f} ms/step)")
+
+    kernels = ["doc_chunk_last", "doc_positions", "rope_q", "block_summary", "pooled_to_planes", "gate_topk",
+               "gate_merge", "decode_gate", "decode_gate_merge", "csr_fill", "csr_count", "csr_scan", "csr_scatter", "attn_gather", "attn_combine",
+               "decode_union", "decode_attend", "decode_combine"]
+    per_kernel = {}
+    for name in kernels:
+        ms, n = m.timer_report(name)
+        if n:
+            per_kernel[name] = {"ms_total": round(ms, 4), "launches": n, "ms_avg": round(ms / n, 4)}
+    m.timer_reset()
+    for name, r in sorted(per_kernel.items(), key=lambda x: -x[1]["ms_total"]):
+        _log(f"  {name:18s} avg {r['ms_avg']:.4f} ms x{r['launches']}")
+
+    gate_pairs, diag_pairs = prefill_pairs()
+    flops_total = 4.0 * c["D"] * (gate_pairs + diag_pairs)
+    flops_gather = 4.0 * c["D"] * gate_pairs
+    dbytes, distinct = decode_bytes(last_sel)
+    pre_tflops = flops_total / (pre_ms * 1e-3) / 1e12
+    dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
+    tokens = c["B"] * c["L"] + d["B"]
+    value = tokens / (step_ms * 1e-3)
+
+    dom = max(per_kernel.items(), key=lambda x: x[1]["ms_total"])[0]
+    if dom == "attn_gather":
+        achieved = flops_gather / (per_kernel[dom]["ms_avg"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "kernel_ms": per_kernel[dom]["ms_avg"]}
+    else:
+        roof = {"bound": "unknown", "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None,
+                "kernel": dom, "kernel_ms": per_kernel[dom]["ms_avg"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("timing the float64 oracle on a sample of the prefill (CPU)")
+        cpu = cpu_baseline(q, k, v, iq, ik, args.cpu_budget)
+
+    out = {
+        "metric": "block-sparse attn prefill tokens/s + MFMA TFLOP/s at 128K; decode HBM GB/s",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "128K MiniMax-style prefill (B1 L131072 H64/8 D128 block64 index-dim64 group-summed "
+                        "top16+own causal) + decode (B16 x 1 token, 1,048,576-token caches, H32/8 D128 block128 "
+                        "top32+own)",
+            "global_batch": c["B"],
+            "seq_len": c["L"],
+            "parallelism": "single GPU",
+        },
+        "breakdown": {
+            "prefill_ms": round(pre_ms, 4),
+            "prefill_tokens_per_s": round(c["B"] * c["L"] / (pre_ms * 1e-3), 1),
+            "prefill_attended_tflops": round(pre_tflops, 2),
+            "prefill_attended_tflop": round(flops_total / 1e12, 4),
+            "decode_ms": round(dec_ms, 4),
+            "decode_tokens_per_s": round(d["B"] / (dec_ms * 1e-3), 1),
+            "decode_hbm_gbs": round(dec_gbs, 1),
+            "decode_algorithmic_gb": round(dbytes / 1e9, 4),
+            "decode_distinct_blocks": distinct,
+            "kernels_ms_avg": {k2: v2["ms_avg"] for k2, v2 in per_kernel.items()},
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -338,7 +338,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
     g.ps_h = (int64_t)P.Nb * P.Dg; g.ps_b = (int64_t)a->Hkv * g.ps_h; g.ps_j = P.Dg;
     g.Nb = P.Nb; g.causal = a->causal; g.block = a->block; g.lens = nullptr;
     g.topk = P.topk; g.nsplit = P.nsplit; g.span = P.span;
-    g.sel = P.sel; g.sel_w = P.sel_w; g.part = P.part_keys;
+    g.sel = P.sel; g.sel_w = P.sel_w; g.part = P.part_keys; g.tag = "gate";
     if (!launch_gate(g, s)) return BSA_ERR_HIP;
     if (P.nsplit > 1 && !launch_gate_merge(g, s)) return BSA_ERR_HIP;
   } else {
@@ -497,7 +497,7 @@ static bsa_status run_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes
   }
   g.Nb = P.Nb; g.causal = 1; g.block = a->block; g.lens = a->cache_lens;
   g.topk = P.topk; g.nsplit = P.nsplit; g.span = P.span;
-  g.sel = P.sel; g.sel_w = P.sel_w; g.part = P.part_keys;
+  g.sel = P.sel; g.sel_w = P.sel_w; g.part = P.part_keys; g.tag = "decode_gate";
   if (!launch_gate(g, s)) return BSA_ERR_HIP;
   if (P.nsplit > 1 && !launch_gate_merge(g, s)) return BSA_ERR_HIP;
   DecodeAttnParams d;

@@ -74,6 +74,7 @@ struct GateParams {
   int32_t* sel;
   int sel_w;
   uint64_t* part;  // [rows][nsplit][topk] when nsplit > 1
+  const char* tag;  // launch name prefix for the timer ("gate" or "decode_gate")
 };
 bool launch_gate(const GateParams& p, hipStream_t s);
 bool launch_gate_merge(const GateParams& p, hipStream_t s);

@@ -308,7 +308,7 @@ bool launch_gate(const GateParams& p, hipStream_t s) {
   const int V = gate_cap_v(p.topk);
   const int grid = p.B * p.Hkv * p.nsplit * p.ntiles;
   {
-    LaunchScope ls("gate_topk", s);
+    LaunchScope ls(p.tag && p.tag[0] == 'd' ? "decode_gate" : "gate_topk", s);
     if (p.Dg == 128) {
       if (W == 4) gate_dispatch_q<4, 128, 2>(p, s, grid);
       else if (W == 2) V == 2 ? gate_dispatch_q<2, 128, 2>(p, s, grid) : gate_dispatch_q<2, 128, 4>(p, s, grid);
@@ -319,20 +319,20 @@ bool launch_gate(const GateParams& p, hipStream_t s) {
       else V == 2 ? gate_dispatch_q<1, 64, 2>(p, s, grid) : gate_dispatch_q<1, 64, 4>(p, s, grid);
     }
   }
-  return launch_ok("gate_topk");
+  return launch_ok(p.tag && p.tag[0] == 'd' ? "decode_gate" : "gate_topk");
 }
 
 bool launch_gate_merge(const GateParams& p, hipStream_t s) {
   const int64_t nrows = (int64_t)p.B * p.Hs * p.Lq;
   const int grid = (int)((nrows + 3) / 4);
   {
-    LaunchScope ls("gate_merge", s);
+    LaunchScope ls(p.tag && p.tag[0] == 'd' ? "decode_gate_merge" : "gate_merge", s);
     if (gate_cap_v(p.topk) == 2)
       hipLaunchKernelGGL(gate_merge_kernel<2>, dim3(grid), dim3(256), 0, s, p);
     else
       hipLaunchKernelGGL(gate_merge_kernel<4>, dim3(grid), dim3(256), 0, s, p);
   }
-  return launch_ok("gate_merge");
+  return launch_ok(p.tag && p.tag[0] == 'd' ? "decode_gate_merge" : "gate_merge");
 }
 
 // ---------------------------------------------------------------------------

@@ -120,9 +120,8 @@ struct PrefillPlan {
 };
 
 static int gate_waves_for(int rows_per_bh, int topk) {
-  const int v = (2 * topk + 64) <= 128 ? 2 : 4;
-  if (rows_per_bh <= 16) return 1;
-  return v == 2 ? 4 : 2;
+  (void)topk;
+  return rows_per_bh <= 16 ? 1 : 4;
 }
 
 static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* ws, bool gate_only) {

@@ -123,17 +123,65 @@ BSA_DEV void emit_row(const GateParams& p, const uint64_t* buf, int cnt, int b, 
   }
 }
 
-template <int W, int DG, int V, int QK, bool LO>
+// ---------------------------------------------------------------------------
+// Running top-k held in registers.  In the 16x16 MFMA result layout the 16
+// lanes of lane group g = lane/16 hold rows 4g..4g+3, each row's candidates
+// spread over those 16 lanes.  Each row keeps its best k keys in the same 16
+// lanes: element e = 16*m + (lane % 16) lives in register m, sorted
+// descending; unused elements are 0.  Inserting a candidate is a 16-lane
+// ballot (how many held keys beat it), a one-place shift and a write; all four
+// lane groups insert into their own rows at once.
+// ---------------------------------------------------------------------------
+template <int KR>
+BSA_DEV void list_insert(uint64_t (&L)[KR], uint64_t c, bool active, int lane, int topk) {
+  const int g = lane >> 4, li = lane & 15;
+  int pos = 0;
+#pragma unroll
+  for (int m = 0; m < KR; ++m) {
+    const uint64_t bal = __ballot(L[m] > c);
+    pos += __popc((uint32_t)(bal >> (16 * g)) & 0xFFFFu);
+  }
+  active = active && pos < topk;
+  uint64_t prev[KR];
+#pragma unroll
+  for (int m = 0; m < KR; ++m) {
+    const uint64_t up = shfl64(L[m], (lane + 63) & 63);
+    const uint64_t carry = m > 0 ? shfl64(L[m > 0 ? m - 1 : 0], (lane + 15) & 63) : 0ull;
+    prev[m] = li > 0 ? up : carry;
+  }
+#pragma unroll
+  for (int m = 0; m < KR; ++m) {
+    const int e = m * 16 + li;
+    uint64_t nv = e < pos ? L[m] : (e == pos ? c : prev[m]);
+    if (e >= topk) nv = 0ull;
+    if (active) L[m] = nv;
+  }
+}
+
+// k-th best key of the row held by this lane's group (0 while fewer than k).
+template <int KR>
+BSA_DEV uint64_t list_kth(const uint64_t (&L)[KR], int lane, int topk) {
+  const int e = topk - 1;
+  uint64_t v = 0ull;
+#pragma unroll
+  for (int m = 0; m < KR; ++m)
+    if (m == (e >> 4)) v = L[m];
+  return shfl64(v, (lane & 48) + (e & 15));
+}
+
+template <int W, int DG, int KR, int QK, bool LO>
 __global__ __launch_bounds__(64 * W) void gate_kernel(GateParams p) {
   constexpr int ROWS = 16 * W;
-  constexpr int CAP = 64 * V;
   constexpr int PADR = DG + 8;  // padded LDS row (bf16 elements)
   constexpr int KS = DG / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t s_hi[64 * PADR];
-  __shared__ __attribute__((aligned(16))) uint16_t s_lo[LO ? 64 * PADR : 8];
-  __shared__ uint64_t s_buf[ROWS][CAP];
-  __shared__ int s_cnt[ROWS];
-  __shared__ uint64_t s_thr[ROWS];
+  constexpr int CPR = DG / 8;                       // 16-byte chunks per summary row
+  constexpr int NPF = (64 * CPR + 64 * W - 1) / (64 * W);  // chunks per thread per plane
+  constexpr int STAGE_BYTES = (LO ? 2 : 1) * 64 * PADR * 2;
+  constexpr int EMIT_BYTES = W * 16 * 64 * 8;
+  constexpr int SMEM = STAGE_BYTES > EMIT_BYTES ? STAGE_BYTES : EMIT_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  uint16_t* s_hi = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* s_lo = s_hi + 64 * PADR;
 
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int tile_l = lid % p.ntiles;
@@ -168,30 +216,51 @@ __global__ __launch_bounds__(64 * W) void gate_kernel(GateParams p) {
   const int last_row = min(tile * ROWS + ROWS, p.rows_per_bh) - 1;
   const int nc_max = ncand_of(p, b, row_to_th(last_row, p).t);
   const int c_lo = split * p.span;
-  const int c_hi = min(c_lo + p.span, nc_max);
+  const int c_hi = p.topk > 0 ? min(c_lo + p.span, nc_max) : c_lo;
 
-  if (tid < ROWS) {
-    s_cnt[tid] = 0;
-    s_thr[tid] = 0ull;
-  }
   const uint16_t* phi = p.p_hi + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h;
   const uint16_t* plo = LO ? p.p_lo + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h : nullptr;
 
+  uint64_t L[4][KR];
+  uint64_t thr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    thr[i] = 0ull;
+#pragma unroll
+    for (int m = 0; m < KR; ++m) L[i][m] = 0ull;
+  }
+
+  // register prefetch of one chunk of summaries (hi and lo planes)
+  u16x8 pf_h[NPF], pf_l[LO ? NPF : 1];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int n = 0; n < NPF; ++n) {
+      const int idx = tid + n * 64 * W;
+      const int jr = idx / CPR, ch = idx % CPR;
+      const int j = c0 + jr;
+      pf_h[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if constexpr (LO) pf_l[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (idx < 64 * CPR && j < c_hi) {
+        pf_h[n] = ld16(phi + (int64_t)j * p.ps_j + ch * 8);
+        if constexpr (LO) pf_l[n] = ld16(plo + (int64_t)j * p.ps_j + ch * 8);
+      }
+    }
+  };
+  if (c_lo < c_hi) fetch(c_lo);
+
   for (int c0 = c_lo; c0 < c_hi; c0 += 64) {
     __syncthreads();
-    // stage 64 candidate summaries (hi and lo planes) into LDS
-    for (int idx = tid; idx < 64 * (DG / 8); idx += 64 * W) {
-      const int jr = idx / (DG / 8), ch = idx % (DG / 8);
-      const int j = c0 + jr;
-      u16x8 vh = {0, 0, 0, 0, 0, 0, 0, 0}, vl = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (j < c_hi) {
-        vh = ld16(phi + (int64_t)j * p.ps_j + ch * 8);
-        if constexpr (LO) vl = ld16(plo + (int64_t)j * p.ps_j + ch * 8);
+#pragma unroll
+    for (int n = 0; n < NPF; ++n) {
+      const int idx = tid + n * 64 * W;
+      if (idx < 64 * CPR) {
+        const int jr = idx / CPR, ch = idx % CPR;
+        st16(&s_hi[jr * PADR + ch * 8], pf_h[n]);
+        if constexpr (LO) st16(&s_lo[jr * PADR + ch * 8], pf_l[n]);
       }
-      st16(&s_hi[jr * PADR + ch * 8], vh);
-      if constexpr (LO) st16(&s_lo[jr * PADR + ch * 8], vl);
     }
     __syncthreads();
+    if (c0 + 64 < c_hi) fetch(c0 + 64);
     f32x4 acc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -207,38 +276,54 @@ __global__ __launch_bounds__(64 * W) void gate_kernel(GateParams p) {
         if constexpr (QK != 0) acc[ct] = mfma16(ql[ks], bh16, acc[ct]);
       }
     }
-    // append candidates that beat their row's threshold
+    // merge this chunk into the running lists, one candidate per lane group
+    // per step, until no lane holds a candidate that beats its row's k-th key
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rl = w * 16 + 4 * kh + i;
-      const uint64_t thr = s_thr[rl];
+      uint64_t key[4];
+      int pend = 0;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int j = c0 + ct * 16 + r16;
-        if (j < c_hi && j < ncand[i]) {
-          const uint64_t key = make_key(acc[ct][i], (uint32_t)j);
-          if (key > thr) {
-            const int slot = atomicAdd(&s_cnt[rl], 1);
-            s_buf[rl][slot] = key;
-          }
-        }
+        const bool ok = j < c_hi && j < ncand[i];
+        key[ct] = ok ? make_key(acc[ct][i], (uint32_t)j) : 0ull;
+        if (key[ct] > thr[i]) pend |= 1 << ct;
+      }
+      while (true) {
+        const uint64_t bal = __ballot(pend != 0);
+        if (bal == 0ull) break;
+        const uint32_t gm = (uint32_t)(bal >> (16 * kh)) & 0xFFFFu;
+        const int src = gm ? 16 * kh + __ffs((int)gm) - 1 : lane;
+        const int ct0 = pend ? __ffs(pend) - 1 : 0;
+        const uint64_t mine = ct0 == 0 ? key[0] : ct0 == 1 ? key[1] : ct0 == 2 ? key[2] : key[3];
+        const uint64_t cnd = shfl64(pend ? mine : 0ull, src);
+        const uint64_t c = gm ? cnd : 0ull;
+        if (gm && lane == src) pend &= pend - 1;
+        list_insert<KR>(L[i], c, c > thr[i], lane, p.topk);
+        thr[i] = list_kth<KR>(L[i], lane, p.topk);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          if (key[ct] <= thr[i]) pend &= ~(1 << ct);
       }
     }
-    __syncthreads();
-    for (int r = 0; r < 16; ++r) {
-      const int rl = w * 16 + r;
-      if (s_cnt[rl] > CAP - 64) row_compact<V>(s_buf[rl], &s_cnt[rl], &s_thr[rl], p.topk);
-    }
   }
+  // emit: each wave writes its 16 rows' lists to LDS, then finishes them row by row
+  __syncthreads();
+  uint64_t* s_emit = reinterpret_cast<uint64_t*>(smem) + w * 16 * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 0; m < KR; ++m) s_emit[(4 * kh + i) * 64 + m * 16 + r16] = L[i][m];
   __syncthreads();
   for (int r = 0; r < 16; ++r) {
     const int row = rbase + r;
     if (row >= p.rows_per_bh) break;
-    const int rl = w * 16 + r;
-    row_compact<V>(s_buf[rl], &s_cnt[rl], &s_thr[rl], p.topk);
+    const uint64_t* buf = s_emit + r * 64;
+    const bool has = lane < p.topk && lane < KR * 16 && buf[lane] != 0ull;
+    const int cnt = __popcll(__ballot(has));
     const RowInfo ri = row_to_th(row, p);
     const int hs = p.per_group ? hk : hk * p.G + ri.hh;
-    emit_row<V>(p, s_buf[rl], s_cnt[rl], b, hs, ri.t, split);
+    emit_row<1>(p, buf, cnt, b, hs, ri.t, split);
   }
 }
 
@@ -282,11 +367,11 @@ __global__ __launch_bounds__(256) void gate_merge_kernel(GateParams p) {
   emit_row<V>(q, s_buf[w], s_cnt[w], b, hs, t, 0);
 }
 
-template <int W, int DG, int V>
+template <int W, int DG, int KR>
 static void gate_dispatch_q(const GateParams& p, hipStream_t s, int grid) {
   const bool lo = p.p_lo != nullptr;
 #define BSA_GATE_CASE(QK, LO)                                                               \
-  hipLaunchKernelGGL((gate_kernel<W, DG, V, QK, LO>), dim3(grid), dim3(64 * W), 0, s, p);
+  hipLaunchKernelGGL((gate_kernel<W, DG, KR, QK, LO>), dim3(grid), dim3(64 * W), 0, s, p);
   if (p.qkind == 0) {
     if (lo) { BSA_GATE_CASE(0, true) } else { BSA_GATE_CASE(0, false) }
   } else if (p.qkind == 1) {
@@ -297,26 +382,29 @@ static void gate_dispatch_q(const GateParams& p, hipStream_t s, int grid) {
 #undef BSA_GATE_CASE
 }
 
-int gate_cap_v(int topk) { return (2 * topk + 64) <= 128 ? 2 : 4; }
-int gate_waves(const GateParams& p) {
-  if (p.rows_per_bh <= 16) return 1;
-  return gate_cap_v(p.topk) == 2 ? 4 : 2;
+template <int W, int DG>
+static void gate_dispatch_k(const GateParams& p, hipStream_t s, int grid) {
+  const int kr = p.topk <= 16 ? 1 : p.topk <= 32 ? 2 : p.topk <= 48 ? 3 : 4;
+  if (kr == 1) gate_dispatch_q<W, DG, 1>(p, s, grid);
+  else if (kr == 2) gate_dispatch_q<W, DG, 2>(p, s, grid);
+  else if (kr == 3) gate_dispatch_q<W, DG, 3>(p, s, grid);
+  else gate_dispatch_q<W, DG, 4>(p, s, grid);
 }
+
+int gate_cap_v(int topk) { return (2 * topk + 64) <= 128 ? 2 : 4; }
+int gate_waves(const GateParams& p) { return p.rows_per_bh <= 16 ? 1 : 4; }
 
 bool launch_gate(const GateParams& p, hipStream_t s) {
   const int W = gate_waves(p);
-  const int V = gate_cap_v(p.topk);
   const int grid = p.B * p.Hkv * p.nsplit * p.ntiles;
   {
     LaunchScope ls(p.tag && p.tag[0] == 'd' ? "decode_gate" : "gate_topk", s);
     if (p.Dg == 128) {
-      if (W == 4) gate_dispatch_q<4, 128, 2>(p, s, grid);
-      else if (W == 2) V == 2 ? gate_dispatch_q<2, 128, 2>(p, s, grid) : gate_dispatch_q<2, 128, 4>(p, s, grid);
-      else V == 2 ? gate_dispatch_q<1, 128, 2>(p, s, grid) : gate_dispatch_q<1, 128, 4>(p, s, grid);
+      if (W == 4) gate_dispatch_k<4, 128>(p, s, grid);
+      else gate_dispatch_k<1, 128>(p, s, grid);
     } else {
-      if (W == 4) gate_dispatch_q<4, 64, 2>(p, s, grid);
-      else if (W == 2) V == 2 ? gate_dispatch_q<2, 64, 2>(p, s, grid) : gate_dispatch_q<2, 64, 4>(p, s, grid);
-      else V == 2 ? gate_dispatch_q<1, 64, 2>(p, s, grid) : gate_dispatch_q<1, 64, 4>(p, s, grid);
+      if (W == 4) gate_dispatch_k<4, 64>(p, s, grid);
+      else gate_dispatch_k<1, 64>(p, s, grid);
     }
   }
   return launch_ok(p.tag && p.tag[0] == 'd' ? "decode_gate" : "gate_topk");

@@ -113,7 +113,7 @@ struct PrefillPlan {
   int32_t* sel;
   int32_t *counts, *cursor, *bucket_off, *tile_off, *scan_tmp;
   uint32_t* entries;
-  int2* items;
+  int4* items;
   uint16_t* part_o;
   float* part_lse;
   size_t bytes;
@@ -160,8 +160,8 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
   }
   if (a->topk > BSA_MAX_TOPK) return fail(BSA_ERR_UNSUPPORTED, "topk above BSA_MAX_TOPK");
   P.topk = std::min(a->topk, P.Nb);
-  P.kslot = std::max(P.topk, 1);
   P.sel_w = a->topk + (a->causal ? 1 : 0);
+  P.kslot = std::max(P.sel_w, 1);  // one partial slot per selection entry (own block included)
   P.R = P.per_group ? P.G : 1;
   P.Gs = P.per_group ? 1 : P.G;
   P.rope_q = a->doc_ids_q != nullptr;
@@ -175,7 +175,8 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
   if ((int64_t)a->Lq * P.Gs * P.kslot >= ((int64_t)1 << 32)) return fail(BSA_ERR_UNSUPPORTED, "Lq * G * topk too large");
   if ((int64_t)a->B * a->Hkv * P.Nb >= (int64_t)1 << 30) return fail(BSA_ERR_UNSUPPORTED, "too many KV blocks");
   P.nbk = a->B * a->Hkv * P.Nb;
-  P.max_entries = P.nsel_rows * P.topk;
+  P.max_entries = P.nsel_rows * (P.topk + (a->causal ? 1 : 0));
+  if (P.per_group && (128 % P.G) != 0) return fail(BSA_ERR_UNSUPPORTED, "per-group gating needs G dividing 128");
   const int rows_item = 128;
   P.max_items = (P.max_entries * P.R + rows_item - 1) / rows_item + std::min<int64_t>(P.nbk, P.max_entries);
   // gate geometry
@@ -224,7 +225,7 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
     P.tile_off = c.take<int32_t>(P.nbk + 1);
     P.scan_tmp = c.take<int32_t>(scan_tmp_len(P.nbk));
     P.entries = c.take<uint32_t>(P.max_entries);
-    P.items = c.take<int2>(P.max_items);
+    P.items = c.take<int4>(P.max_items);
     P.part_o = c.take<uint16_t>(P.max_entries * P.R * a->D);
     P.part_lse = c.take<float>(P.max_entries * P.R);
   } else {
@@ -383,7 +384,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
   ap.sel = P.sel; ap.sel_w = P.sel_w;
   ap.o = reinterpret_cast<uint16_t*>(a->o); ap.os_b = a->o_stride[0]; ap.os_t = a->o_stride[1]; ap.os_h = a->o_stride[2];
   ap.lse_out = a->lse_out;
-  if (P.topk > 0) {
+  if (P.max_entries > 0) {
     CsrParams cp;
     cp.B = a->B; cp.Lq = a->Lq; cp.Lk = a->Lk; cp.Hkv = a->Hkv; cp.G = P.G; cp.Hs = P.Hs; cp.per_group = P.per_group;
     cp.Nb = P.Nb; cp.block = a->block; cp.causal = a->causal;
@@ -392,8 +393,6 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
     cp.scan_tmp = P.scan_tmp; cp.entries = P.entries; cp.items = P.items; cp.nbk = P.nbk;
     if (!launch_csr(cp, s)) return BSA_ERR_HIP;
     if (!launch_attn_gather(ap, s)) return BSA_ERR_HIP;
-  } else {
-    ap.kslot = 0;
   }
   if (!launch_attn_combine(ap, s)) return BSA_ERR_HIP;
   return BSA_OK;

@@ -9,16 +9,19 @@
 //
 // Schedule (bf16):
 //  * attn_gather: KV-major.  A work item is one (b, kv head, block) bucket and
-//    a tile of up to 128 query rows that chose it.  The block's keys and
-//    values are staged in LDS (V transposed) in 64-key tiles; each wave holds
-//    32 gathered query rows.  S^T = K Q^T and O^T += V^T P^T run on
+//    a tile of up to 128 query rows that chose it (the causal own block is one
+//    of the chosen blocks, attended with the per-key causal mask).  The
+//    block's keys and values are staged in LDS (V transposed) in 64-key tiles
+//    and kept there across consecutive items of the same bucket; each wave
+//    holds 32 gathered query rows.  S^T = K Q^T and O^T += V^T P^T run on
 //    v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the result is one
 //    normalised partial output (bf16) plus its log2-domain LSE per
-//    (row, slot).
-//  * attn_combine: query-major.  A workgroup takes 128 consecutive query
-//    tokens of one head, computes the causal attention inside each token's
-//    own block on MFMA, then folds in the row's partials by LSE weights and
-//    writes o (and lse).
+//    (row, slot).  Persistent workgroups walk contiguous item ranges and
+//    prefetch the next item's row metadata and queries during the current
+//    item's MFMAs.
+//  * attn_merge: streaming.  Sixteen lanes per output row read the row's
+//    partials (8 head dims each), merge them with LSE weights and write o (and
+//    lse).
 #include <math.h>
 
 #include "bsa_device.h"
@@ -34,6 +37,38 @@ struct AttnSmem {
   uint16_t k[KT * (D + 8)];
   uint16_t vt[D * (KT + 8)];
 };
+
+// Per-wave staging of the next work item's query rows: for each 16-column
+// chunk s, lane l's 16 bytes land at qs[w][s][l] (global_load_lds_dwordx4
+// writes lane l's data at the wave's LDS base + 16*l).
+template <int D>
+struct QStage {
+  uint16_t qs[4][D / 16][64][8];
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int D>
+BSA_DEV void prefetch_q_lds(QStage<D>& st, const uint16_t* qrow, bool ok) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane_id() >> 5;
+  if (ok) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      __builtin_amdgcn_global_load_lds((const void*)(qrow + 16 * s + 8 * h), (lds_ptr_t)(&st.qs[w][s][0][0]), 16, 0,
+                                       0);
+  }
+}
+
+template <int D>
+BSA_DEV void read_q_lds(const QStage<D>& st, bool ok, bf16x8 (&qf)[D / 16]) {
+  const int w = threadIdx.x >> 6, l = lane_id();
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const u16x8 x = *reinterpret_cast<const u16x8*>(&st.qs[w][s][l][0]);
+    qf[s] = as_bf(ok ? x : u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+  }
+}
 
 // Stage keys [key0, key0 + KT) of one kv head (zero past n_valid) into LDS:
 // K row-major, V transposed.
@@ -156,44 +191,75 @@ BSA_DEV void load_qf(const uint16_t* qrow, bool ok, bf16x8 (&qf)[D / 16]) {
 }
 
 // ---------------------------------------------------------------------------
+// Row metadata of one lane's query row in a work item; lr is the row's index
+// inside the item (the item record holds the tile's first entry and its row
+// count).
+struct GRow {
+  int t, slot, qh, hs, rr;
+  bool valid;
+};
+
+BSA_DEV GRow grow_of(const AttnParams& p, int4 rec, int hk, int lr) {
+  GRow g;
+  g.valid = lr < rec.z;
+  g.t = 0;
+  g.slot = 0;
+  g.rr = 0;
+  int hh = 0;
+  if (g.valid) {
+    const uint32_t ent = p.entries[rec.y + lr / p.R];
+    g.rr = lr % p.R;
+    g.slot = (int)(ent % (uint32_t)p.kslot);
+    const uint32_t th = ent / (uint32_t)p.kslot;
+    hh = (int)(th % (uint32_t)p.Gs);
+    g.t = (int)(th / (uint32_t)p.Gs);
+  }
+  g.qh = p.per_group ? hk * p.G + g.rr : hk * p.G + hh;
+  g.hs = p.per_group ? hk : hk * p.G + hh;
+  return g;
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) QStage<D> qst;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hq = lane >> 5;
   const int nitems = *p.n_items;
-  const int g8 = gridDim.x >> 3;  // grid is a multiple of 8
-  const int x = blockIdx.x & 7, i0 = blockIdx.x >> 3;
+  // XCD x owns items [off_x, off_x + cnt_x); its workgroups split that range
+  // into contiguous runs so that consecutive items mostly share a bucket.
+  const int x = blockIdx.x & 7, wi = blockIdx.x >> 3, nw = gridDim.x >> 3;
   const int per = nitems >> 3, rem = nitems & 7;
   const int cnt_x = per + (x < rem ? 1 : 0);
   const int off_x = x * per + (x < rem ? x : rem);
+  const int it_begin = off_x + (int)(((int64_t)cnt_x * wi) / nw);
+  const int it_end = off_x + (int)(((int64_t)cnt_x * (wi + 1)) / nw);
+  if (it_begin >= it_end) return;  // uniform for the workgroup
 
-  for (int it = i0; it < cnt_x; it += g8) {
-    const int2 item = p.items[off_x + it];
-    const int bucket = item.x, tile = item.y;
+  const int lrow = w * 32 + (lane & 31);
+  int staged = -1;  // bucket whose single key tile sits in LDS
+
+  int4 rec = p.items[it_begin];
+  GRow g = grow_of(p, rec, (rec.x / p.Nb) % p.Hkv, lrow);
+  bf16x8 qf[D / 16];
+  {
+    const int b = rec.x / (p.Nb * p.Hkv);
+    load_qf<D>(p.q + (int64_t)b * p.qs_b + (int64_t)g.t * p.qs_t + (int64_t)g.qh * p.qs_h, g.valid, qf);
+  }
+
+  for (int it = it_begin; it < it_end; ++it) {
+    const int bucket = rec.x;
     const int j = bucket % p.Nb;
     const int hk = (bucket / p.Nb) % p.Hkv;
     const int b = bucket / (p.Nb * p.Hkv);
-    const int e0 = p.bucket_off[bucket];
-    const int nrows = (p.bucket_off[bucket + 1] - e0) * p.R;
-    const int row0 = tile * 128;
-    const int lr = row0 + w * 32 + (lane & 31);
-    const bool valid = lr < nrows;
-    const bool wave_on = row0 + w * 32 < nrows;
-    int t = 0, slot = 0, hh = 0, rr = 0;
-    if (valid) {
-      const uint32_t ent = p.entries[e0 + lr / p.R];
-      rr = lr % p.R;
-      slot = (int)(ent % (uint32_t)p.kslot);
-      const uint32_t th = ent / (uint32_t)p.kslot;
-      hh = (int)(th % (uint32_t)p.Gs);
-      t = (int)(th / (uint32_t)p.Gs);
-    }
-    const int qh = p.per_group ? hk * p.G + rr : hk * p.G + hh;
-    const int hs = p.per_group ? hk : hk * p.G + hh;
-    bf16x8 qf[D / 16];
-    load_qf<D>(p.q + (int64_t)b * p.qs_b + (int64_t)t * p.qs_t + (int64_t)qh * p.qs_h, valid, qf);
+    const bool wave_on = w * 32 < rec.z;
+    // next item: its record now, its rows after staging, its queries (into
+    // LDS) after the first score tile
+    const bool has_next = it + 1 < it_end;
+    const int4 rec_n = has_next ? p.items[it + 1] : rec;
+    GRow g_n = g;
 
+    const int64_t qpos = (int64_t)p.Lk - p.Lq + g.t;
     float m = -INFINITY, l = 0.f;
     f32x16 o[D / 32];
 #pragma unroll
@@ -203,142 +269,139 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
     const uint16_t* kb = p.k + (int64_t)b * p.ks_b + (int64_t)hk * p.ks_h;
     const uint16_t* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
     for (int kt0 = 0; kt0 < n_keys; kt0 += KT) {
-      __syncthreads();
-      stage_kv<D>(sm, kb, p.ks_t, vb, p.vs_t, key0 + kt0, n_keys - kt0);
-      __syncthreads();
+      const bool single = n_keys <= KT;
+      if (!(single && staged == bucket)) {
+        __syncthreads();
+        stage_kv<D>(sm, kb, p.ks_t, vb, p.vs_t, key0 + kt0, n_keys - kt0);
+        __syncthreads();
+        staged = single ? bucket : -1;
+      }
+      const bool first = kt0 == 0;
+      if (first && has_next) g_n = grow_of(p, rec_n, (rec_n.x / p.Nb) % p.Hkv, lrow);
+      f32x16 s0, s1;
+      if (wave_on) qk_tile<D>(sm, qf, s0, s1);
+      if (first && has_next) {
+        const int b_n = rec_n.x / (p.Nb * p.Hkv);
+        prefetch_q_lds<D>(qst, p.q + (int64_t)b_n * p.qs_b + (int64_t)g_n.t * p.qs_t + (int64_t)g_n.qh * p.qs_h,
+                          g_n.valid);
+      }
       if (wave_on) {
-        f32x16 s0, s1;
-        qk_tile<D>(sm, qf, s0, s1);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kr = kt0 + krow(i, hq);
-          s0[i] = kr < n_keys ? s0[i] * p.sl2 : -INFINITY;
-          s1[i] = kr + 32 < n_keys ? s1[i] * p.sl2 : -INFINITY;
+          const int64_t ka = key0 + kr;
+          const bool ok0 = kr < n_keys && (!p.causal || ka <= qpos);
+          const bool ok1 = kr + 32 < n_keys && (!p.causal || ka + 32 <= qpos);
+          s0[i] = ok0 ? s0[i] * p.sl2 : -INFINITY;
+          s1[i] = ok1 ? s1[i] * p.sl2 : -INFINITY;
         }
         softmax_update<D>(s0, s1, m, l, o);
         pv_tile<D>(sm, s0, s1, o);
       }
     }
-    if (valid) {
+    // the next item's queries: wait for the LDS-bound loads, then read back
+    if (has_next) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+      read_q_lds<D>(qst, g_n.valid, qf);
+    }
+    if (g.valid) {
       const float inv = 1.0f / l;
-      const int64_t srow = ((int64_t)b * p.Hs + hs) * p.Lq + t;
-      const int64_t pidx = (srow * p.kslot + slot) * p.R + rr;
+      const int64_t srow = ((int64_t)b * p.Hs + g.hs) * p.Lq + g.t;
+      const int64_t pidx = (srow * p.kslot + g.slot) * p.R + g.rr;
       uint16_t* dst = p.part_o + pidx * D;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = dt * 32 + 8 * g + 4 * hq;
-          u16x4 v4 = {f2bf(o[dt][4 * g] * inv), f2bf(o[dt][4 * g + 1] * inv), f2bf(o[dt][4 * g + 2] * inv),
-                      f2bf(o[dt][4 * g + 3] * inv)};
+        for (int gg = 0; gg < 4; ++gg) {
+          const int d0 = dt * 32 + 8 * gg + 4 * hq;
+          u16x4 v4 = {f2bf(o[dt][4 * gg] * inv), f2bf(o[dt][4 * gg + 1] * inv), f2bf(o[dt][4 * gg + 2] * inv),
+                      f2bf(o[dt][4 * gg + 3] * inv)};
           *reinterpret_cast<u16x4*>(dst + d0) = v4;
         }
       }
       if (hq == 0) p.part_lse[pidx] = m + log2f(l);
     }
+    rec = rec_n;
+    g = g_n;
   }
 }
 
 // ---------------------------------------------------------------------------
+// Merge: output row (b, t, h) <- LSE-weighted sum of its selection row's
+// partials (the slots of its sel row, own block included).  D/8 lanes per
+// row, 8 head dims per lane; slots are read eight at a time so their loads
+// are in flight together.
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_combine_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int hq = lane >> 5;
-  const int ntile = (p.Lq + 127) / 128;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int hh = lid % p.G;
-  int r = lid / p.G;
-  const int tile = r % ntile;
-  r /= ntile;
-  const int hk = r % p.Hkv;
-  const int b = r / p.Hkv;
-  const int h = hk * p.G + hh;
-  const int t = tile * 128 + w * 32 + (lane & 31);
-  const bool valid = t < p.Lq;
-  const int64_t off = (int64_t)p.Lk - p.Lq;
-  const int64_t qpos = off + t;
-
-  bf16x8 qf[D / 16];
-  load_qf<D>(p.q + (int64_t)b * p.qs_b + (int64_t)(valid ? t : 0) * p.qs_t + (int64_t)h * p.qs_h, valid, qf);
-  float m = -INFINITY, l = 0.f;
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
-
-  if (p.causal) {
-    const int tl = min(tile * 128 + 127, p.Lq - 1);
-    const int64_t kb0 = ((off + tile * 128) / p.block) * p.block;
-    const int64_t ke = off + tl + 1;
-    const int wt0 = tile * 128 + w * 32;
-    const bool wave_on = wt0 < p.Lq;
-    const int wt1 = min(wt0 + 31, p.Lq - 1);
-    const int64_t wkb = ((off + wt0) / p.block) * p.block;
-    const int64_t wke = off + wt1 + 1;
-    const int64_t my_kb = (qpos / p.block) * p.block;
-    const uint16_t* kb = p.k + (int64_t)b * p.ks_b + (int64_t)hk * p.ks_h;
-    const uint16_t* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
-    for (int64_t kt0 = kb0; kt0 < ke; kt0 += KT) {
-      __syncthreads();
-      stage_kv<D>(sm, kb, p.ks_t, vb, p.vs_t, (int)kt0, (int)min<int64_t>(KT, ke - kt0));
-      __syncthreads();
-      if (wave_on && kt0 < wke && kt0 + KT > wkb) {
-        f32x16 s0, s1;
-        qk_tile<D>(sm, qf, s0, s1);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t k0 = kt0 + krow(i, hq);
-          const int64_t k1 = k0 + 32;
-          s0[i] = (valid && k0 >= my_kb && k0 <= qpos) ? s0[i] * p.sl2 : -INFINITY;
-          s1[i] = (valid && k1 >= my_kb && k1 <= qpos) ? s1[i] * p.sl2 : -INFINITY;
-        }
-        softmax_update<D>(s0, s1, m, l, o);
-        pv_tile<D>(sm, s0, s1, o);
-      }
-    }
-  }
-  if (!valid) return;  // no barrier below
-  // fold in the partials of the gate-chosen blocks
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RPW = 64 / LPR;       // rows per wave
+  constexpr int SB = 8;               // slots per batch
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int li = lane % LPR;
+  const int64_t nrows = (int64_t)p.B * p.Lq * p.Hq;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + w) * RPW + lane / LPR;
+  const bool ok = row < nrows;
+  const int64_t rr_ = ok ? row : 0;
+  const int h = (int)(rr_ % p.Hq);
+  const int t = (int)((rr_ / p.Hq) % p.Lq);
+  const int b = (int)(rr_ / ((int64_t)p.Hq * p.Lq));
+  const int hk = h / p.G;
   const int hs = p.per_group ? hk : h;
-  const int rr = p.per_group ? hh : 0;
+  const int rr = p.per_group ? h % p.G : 0;
   const int64_t srow = ((int64_t)b * p.Hs + hs) * p.Lq + t;
-  const int64_t cur = p.causal ? qpos / p.block : -1;
-  const int32_t* srow_sel = p.sel + srow * p.sel_w;
-  for (int s = 0; s < p.kslot; ++s) {
-    const int jsel = srow_sel[s];
-    if (jsel < 0 || jsel == cur) break;
-    const int64_t pidx = (srow * p.kslot + s) * p.R + rr;
-    const float ls = p.part_lse[pidx];
-    const float mnew = fmaxf(m, ls);
-    const float c1 = exp2f(m - mnew), c2 = exp2f(ls - mnew);
-    const uint16_t* src = p.part_o + pidx * D;
+  const int32_t* sr = p.sel + srow * p.sel_w;
+  // number of valid slots (valid entries come first, -1 after): the row's
+  // lanes count a strided share each, then sum across the row's lanes
+  int n = 0;
+  if (ok) {
+    for (int s = li; s < p.sel_w; s += LPR) n += sr[s] >= 0 ? 1 : 0;
+  }
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+  for (int m2 = 1; m2 < LPR; m2 <<= 1) n += __shfl_xor(n, m2, 64);
+  float M = -INFINITY, W = 0.f;
+  float acc[8];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = dt * 32 + 8 * g + 4 * hq;
-        const u16x4 v4 = *reinterpret_cast<const u16x4*>(src + d0);
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < n; s0 += SB) {
+    float ls[SB];
+    u16x8 ov[SB];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[dt][4 * g + e] = o[dt][4 * g + e] * c1 + c2 * bf2f(v4[e]);
+    for (int u = 0; u < SB; ++u) {
+      const int s = s0 + u;
+      ls[u] = -INFINITY;
+      ov[u] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (s < n) {
+        const int64_t pidx = (srow * p.kslot + s) * p.R + rr;
+        ls[u] = p.part_lse[pidx];
+        ov[u] = ld16(p.part_o + pidx * D + li * 8);
       }
     }
-    l = l * c1 + c2;
-    m = mnew;
-  }
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  uint16_t* dst = p.o + (int64_t)b * p.os_b + (int64_t)t * p.os_t + (int64_t)h * p.os_h;
+    float mb = M;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
+    for (int u = 0; u < SB; ++u) mb = fmaxf(mb, ls[u]);
+    const float c = exp2f(M - mb);
+    W *= c;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = dt * 32 + 8 * g + 4 * hq;
-      u16x4 v4 = {f2bf(o[dt][4 * g] * inv), f2bf(o[dt][4 * g + 1] * inv), f2bf(o[dt][4 * g + 2] * inv),
-                  f2bf(o[dt][4 * g + 3] * inv)};
-      *reinterpret_cast<u16x4*>(dst + d0) = v4;
+    for (int e = 0; e < 8; ++e) acc[e] *= c;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const float wu = exp2f(ls[u] - mb);  // 0 for unused slots
+      W += wu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wu, bf2f(ov[u][e]), acc[e]);
     }
+    M = mb;
   }
-  if (p.lse_out && hq == 0)
-    p.lse_out[((int64_t)b * p.Hq + h) * p.Lq + t] = l > 0.f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+  if (!ok) return;
+  const float inv = W > 0.f ? 1.0f / W : 0.f;
+  u16x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = f2bf(acc[e] * inv);
+  st16(p.o + (int64_t)b * p.os_b + (int64_t)t * p.os_t + (int64_t)h * p.os_h + li * 8, out);
+  if (p.lse_out && li == 0)
+    p.lse_out[((int64_t)b * p.Hq + h) * p.Lq + t] = W > 0.f ? (M + log2f(W)) * 0.69314718055994530942f : -INFINITY;
 }
 
 bool launch_attn_gather(const AttnParams& p, hipStream_t s) {
@@ -353,16 +416,17 @@ bool launch_attn_gather(const AttnParams& p, hipStream_t s) {
 }
 
 bool launch_attn_combine(const AttnParams& p, hipStream_t s) {
-  const int ntile = (p.Lq + 127) / 128;
-  const int grid = p.B * p.Hq * ntile;
+  const int64_t nrows = (int64_t)p.B * p.Lq * p.Hq;
+  const int rpw = 64 / (p.D / 8);
+  const int64_t grid = (nrows + 4 * rpw - 1) / (4 * rpw);
   {
-    LaunchScope ls("attn_combine", s);
+    LaunchScope ls("attn_merge", s);
     if (p.D == 128)
-      hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(attn_merge_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(attn_merge_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, p);
   }
-  return launch_ok("attn_combine");
+  return launch_ok("attn_merge");
 }
 
 // ---------------------------------------------------------------------------

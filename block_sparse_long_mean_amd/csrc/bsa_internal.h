@@ -105,7 +105,7 @@ struct CsrParams {
   int32_t* tile_off;    // [nbk + 1]
   int32_t* scan_tmp;    // [scan_tmp_len]
   uint32_t* entries;
-  int2* items;
+  int4* items;
   int nbk;
 };
 int64_t scan_tmp_len(int64_t n);
@@ -124,7 +124,7 @@ struct AttnParams {
   const uint32_t* entries;
   const int32_t* bucket_off;
   const int32_t* tile_off;
-  const int2* items;
+  const int4* items;  // {bucket, first entry, rows, tile}
   const int32_t* n_items;  // device scalar
   int grid;                // persistent workgroups
   uint16_t* part_o;        // [rows * kslot * R, D] bf16 (normalised)

@@ -22,8 +22,8 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n, in
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
-// Gate-chosen entries of a selection row are the first ones, ascending; the
-// forced own block (causal) follows them.  slot = position in the row.
+// Every valid entry of a selection row (the gate's blocks, then the forced own
+// block when causal) becomes one bucket entry; slot = position in the row.
 struct SelEntry {
   bool valid;
   int bucket;
@@ -43,10 +43,6 @@ BSA_DEV SelEntry decode_sel(const CsrParams& p, int64_t idx) {
   const int t = (int)(srow % p.Lq);
   const int hs = (int)((srow / p.Lq) % p.Hs);
   const int b = (int)(srow / ((int64_t)p.Lq * p.Hs));
-  if (p.causal) {
-    const int64_t cur = ((int64_t)p.Lk - p.Lq + t) / p.block;
-    if (j == cur) return r;
-  }
   const int hk = p.per_group ? hs : hs / p.G;
   const int hh = p.per_group ? 0 : hs % p.G;
   const int Gs = p.per_group ? 1 : p.G;
@@ -191,11 +187,17 @@ __global__ __launch_bounds__(256) void scan_apply_kernel(CsrParams p) {
   }
 }
 
-// one thread per bucket: write its work items
+// one thread per bucket: write its work items {bucket, first entry, rows, tile}
 __global__ __launch_bounds__(256) void expand_items_kernel(CsrParams p) {
+  const int ept = p.rows_item / p.R;  // entries per tile
   for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < p.nbk; g += (int64_t)gridDim.x * 256) {
     const int t0 = p.tile_off[g], t1 = p.tile_off[g + 1];
-    for (int t = t0; t < t1; ++t) p.items[t] = make_int2((int)g, t - t0);
+    const int e0 = p.bucket_off[g];
+    const int rows = (p.bucket_off[g + 1] - e0) * p.R;
+    for (int t = t0; t < t1; ++t) {
+      const int k = t - t0;
+      p.items[t] = make_int4((int)g, e0 + k * ept, min(p.rows_item, rows - k * p.rows_item), k);
+    }
   }
 }
 

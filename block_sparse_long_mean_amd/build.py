@@ -15,6 +15,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libbsa.so")
 SOURCES = ["api.hip", "summary.hip", "gate.hip", "csr.hip", "attn.hip", "decode.hip"]
 ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
@@ -39,7 +40,7 @@ def _filter(text: str) -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-I" + INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{_filter(r.stdout + r.stderr)}")

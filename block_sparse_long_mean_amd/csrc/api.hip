@@ -6,7 +6,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/bsa.h"
+#include "bsa.h"
 #include "bsa_internal.h"
 
 #define BSA_API extern "C" __attribute__((visibility("default")))
@@ -115,9 +115,16 @@ struct PrefillPlan {
   uint32_t* entries;
   int4* items;
   uint16_t* part_o;
-  float* part_lse;
+  float2* part_ml;
+  int sh_h, sh_t, lgR;
   size_t bytes;
 };
+
+static int ceil_log2(int x) {
+  int b = 0;
+  while ((1 << b) < x) ++b;
+  return b;
+}
 
 static int gate_waves_for(int rows_per_bh, int topk) {
   (void)topk;
@@ -172,7 +179,11 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
   }
   P.nsel_rows = (int64_t)a->B * P.Hs * a->Lq;
   if (P.nsel_rows * P.sel_w >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "too many selection entries");
-  if ((int64_t)a->Lq * P.Gs * P.kslot >= ((int64_t)1 << 32)) return fail(BSA_ERR_UNSUPPORTED, "Lq * G * topk too large");
+  P.sh_h = ceil_log2(P.kslot);
+  P.sh_t = P.sh_h + ceil_log2(P.Gs);
+  P.lgR = ceil_log2(P.R);
+  if (P.sh_t >= 31 || (int64_t)(a->Lq - 1) >= ((int64_t)1 << (32 - P.sh_t)))
+    return fail(BSA_ERR_UNSUPPORTED, "Lq too large for the packed selection entries");
   if ((int64_t)a->B * a->Hkv * P.Nb >= (int64_t)1 << 30) return fail(BSA_ERR_UNSUPPORTED, "too many KV blocks");
   P.nbk = a->B * a->Hkv * P.Nb;
   P.max_entries = P.nsel_rows * (P.topk + (a->causal ? 1 : 0));
@@ -224,16 +235,16 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
     P.bucket_off = c.take<int32_t>(P.nbk + 1);
     P.tile_off = c.take<int32_t>(P.nbk + 1);
     P.scan_tmp = c.take<int32_t>(scan_tmp_len(P.nbk));
-    P.entries = c.take<uint32_t>(P.max_entries);
+    P.entries = c.take<uint32_t>(P.max_entries + 256);  // speculative reads past the end stay inside
     P.items = c.take<int4>(P.max_items);
     P.part_o = c.take<uint16_t>(P.max_entries * P.R * a->D);
-    P.part_lse = c.take<float>(P.max_entries * P.R);
+    P.part_ml = c.take<float2>(P.max_entries * P.R);
   } else {
     P.counts = P.cursor = P.bucket_off = P.tile_off = P.scan_tmp = nullptr;
     P.entries = nullptr;
     P.items = nullptr;
     P.part_o = nullptr;
-    P.part_lse = nullptr;
+    P.part_ml = nullptr;
   }
   P.bytes = c.off + 256;
   return BSA_OK;
@@ -373,6 +384,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
   ap.B = a->B; ap.Lq = a->Lq; ap.Lk = a->Lk; ap.Hq = a->Hq; ap.Hkv = a->Hkv; ap.G = P.G; ap.D = a->D;
   ap.block = a->block; ap.Nb = P.Nb; ap.Hs = P.Hs; ap.per_group = P.per_group; ap.Gs = P.Gs; ap.R = P.R;
   ap.kslot = P.kslot; ap.causal = a->causal;
+  ap.sh_h = P.sh_h; ap.sh_t = P.sh_t; ap.lgR = P.lgR;
   ap.q = reinterpret_cast<const uint16_t*>(q_att); ap.qs_b = qa_s[0]; ap.qs_t = qa_s[1]; ap.qs_h = qa_s[2];
   ap.k = reinterpret_cast<const uint16_t*>(k_att); ap.ks_b = ka_s[0]; ap.ks_t = ka_s[1]; ap.ks_h = ka_s[2];
   ap.v = reinterpret_cast<const uint16_t*>(a->v); ap.vs_b = a->v_stride[0]; ap.vs_t = a->v_stride[1]; ap.vs_h = a->v_stride[2];
@@ -380,7 +392,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
   ap.entries = P.entries; ap.bucket_off = P.bucket_off; ap.tile_off = P.tile_off; ap.items = P.items;
   ap.n_items = P.tile_off + P.nbk;
   ap.grid = P.attn_grid;
-  ap.part_o = P.part_o; ap.part_lse = P.part_lse;
+  ap.part_o = P.part_o; ap.part_ml = P.part_ml;
   ap.sel = P.sel; ap.sel_w = P.sel_w;
   ap.o = reinterpret_cast<uint16_t*>(a->o); ap.os_b = a->o_stride[0]; ap.os_t = a->o_stride[1]; ap.os_h = a->o_stride[2];
   ap.lse_out = a->lse_out;
@@ -389,6 +401,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
     cp.B = a->B; cp.Lq = a->Lq; cp.Lk = a->Lk; cp.Hkv = a->Hkv; cp.G = P.G; cp.Hs = P.Hs; cp.per_group = P.per_group;
     cp.Nb = P.Nb; cp.block = a->block; cp.causal = a->causal;
     cp.sel = P.sel; cp.sel_w = P.sel_w; cp.kslot = P.kslot; cp.R = P.R; cp.rows_item = 128;
+    cp.sh_h = P.sh_h; cp.sh_t = P.sh_t;
     cp.counts = P.counts; cp.cursor = P.cursor; cp.bucket_off = P.bucket_off; cp.tile_off = P.tile_off;
     cp.scan_tmp = P.scan_tmp; cp.entries = P.entries; cp.items = P.items; cp.nbk = P.nbk;
     if (!launch_csr(cp, s)) return BSA_ERR_HIP;

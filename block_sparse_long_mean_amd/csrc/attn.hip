@@ -32,18 +32,27 @@ namespace bsa {
 constexpr int KT = 64;  // keys per LDS tile
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
+constexpr int VTS = KT + 4;  // V^T row stride: 136 bytes keeps 16 lanes' 8-byte reads on distinct banks
+
 template <int D>
 struct AttnSmem {
   uint16_t k[KT * (D + 8)];
-  uint16_t vt[D * (KT + 8)];
+  uint16_t vt[D * VTS];
 };
 
-// Per-wave staging of the next work item's query rows: for each 16-column
-// chunk s, lane l's 16 bytes land at qs[w][s][l] (global_load_lds_dwordx4
-// writes lane l's data at the wave's LDS base + 16*l).
+// Per-wave LDS staging area, used twice per work item:
+//  * the next item's query rows: for each 16-column chunk s, lane l's 16
+//    bytes land at elements [(s*64 + l)*8, +8) (global_load_lds_dwordx4
+//    writes lane l's data at the wave's LDS base + 16*l);
+//  * the finished partial outputs, row-major with rows padded by 8 bytes, so
+//    that every global store instruction writes whole 256-byte rows.
 template <int D>
 struct QStage {
-  uint16_t qs[4][D / 16][64][8];
+  static constexpr int QELEMS = (D / 16) * 64 * 8;
+  static constexpr int RS = D + 4;  // padded output row (bf16 elements)
+  static constexpr int OELEMS = 32 * RS;
+  static constexpr int ELEMS = QELEMS > OELEMS ? QELEMS : OELEMS;
+  uint16_t buf[4][ELEMS];
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -55,8 +64,8 @@ BSA_DEV void prefetch_q_lds(QStage<D>& st, const uint16_t* qrow, bool ok) {
   if (ok) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
-      __builtin_amdgcn_global_load_lds((const void*)(qrow + 16 * s + 8 * h), (lds_ptr_t)(&st.qs[w][s][0][0]), 16, 0,
-                                       0);
+      __builtin_amdgcn_global_load_lds((const void*)(qrow + 16 * s + 8 * h), (lds_ptr_t)(&st.buf[w][s * 64 * 8]), 16,
+                                       0, 0);
   }
 }
 
@@ -65,8 +74,50 @@ BSA_DEV void read_q_lds(const QStage<D>& st, bool ok, bf16x8 (&qf)[D / 16]) {
   const int w = threadIdx.x >> 6, l = lane_id();
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    const u16x8 x = *reinterpret_cast<const u16x8*>(&st.qs[w][s][l][0]);
+    const u16x8 x = *reinterpret_cast<const u16x8*>(&st.buf[w][(s * 64 + l) * 8]);
     qf[s] = as_bf(ok ? x : u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+  }
+}
+
+// O^T tile of the wave's 32 rows -> bf16 rows in LDS -> global:
+// D/8 lanes write one row's D elements (16 bytes each), 64*8/D rows per
+// store instruction.  Rows [nvalid, 32) of the wave are not written; row r's
+// destination element offset is held by lane r.
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+BSA_DEV void pack_partials(const f32x16 (&o)[D / 32], u16x4_t (&pk)[D / 8]) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg)
+      pk[dt * 4 + gg] = u16x4_t{f2bf(o[dt][4 * gg]), f2bf(o[dt][4 * gg + 1]), f2bf(o[dt][4 * gg + 2]),
+                                f2bf(o[dt][4 * gg + 3])};
+}
+
+template <int D>
+BSA_DEV void store_partials(QStage<D>& st, const u16x4_t (&pk)[D / 8], int64_t dst_mine, int nvalid,
+                            uint16_t* part_o) {
+  const int w = threadIdx.x >> 6, lane = lane_id(), r = lane & 31, h = lane >> 5;
+  constexpr int RS = QStage<D>::RS;
+  uint16_t* sb = st.buf[w];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) *reinterpret_cast<u16x4_t*>(sb + r * RS + dt * 32 + 8 * gg + 4 * h) = pk[dt * 4 + gg];
+  __builtin_amdgcn_wave_barrier();
+  constexpr int CPR = D / 8, RPI = 64 / CPR;
+  const int c = lane % CPR;
+#pragma unroll
+  for (int n = 0; n < 32 / RPI; ++n) {
+    const int rr = n * RPI + lane / CPR;
+    const int64_t dst = (int64_t)shfl64((uint64_t)dst_mine, rr);
+    if (rr < nvalid) {
+      const u16x4_t a = *reinterpret_cast<const u16x4_t*>(sb + rr * RS + c * 8);
+      const u16x4_t b = *reinterpret_cast<const u16x4_t*>(sb + rr * RS + c * 8 + 4);
+      const u16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      st16(part_o + dst + c * 8, v);
+    }
   }
 }
 
@@ -83,8 +134,11 @@ BSA_DEV void stage_kv(AttnSmem<D>& sm, const uint16_t* kb, int64_t ks_t, const u
     if (kr < n_valid) x = ld16(kb + (int64_t)(key0 + kr) * ks_t + ch * 8);
     st16(&sm.k[kr * (D + 8) + ch * 8], x);
   }
+  // V: a thread takes 4 consecutive keys x 8 head dims and writes them
+  // transposed; consecutive lanes take consecutive key quads so that their
+  // LDS writes of one V^T row are contiguous
   for (int idx = tid; idx < (KT / 4) * CH; idx += 256) {
-    const int kq = idx / CH, ch = idx % CH;
+    const int kq = idx % (KT / 4), ch = idx / (KT / 4);
     u16x8 r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -95,7 +149,7 @@ BSA_DEV void stage_kv(AttnSmem<D>& sm, const uint16_t* kb, int64_t ks_t, const u
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       u16x4 col = {r[0][d], r[1][d], r[2][d], r[3][d]};
-      *reinterpret_cast<u16x4*>(&sm.vt[(ch * 8 + d) * (KT + 8) + kq * 4]) = col;
+      *reinterpret_cast<u16x4*>(&sm.vt[(ch * 8 + d) * VTS + kq * 4]) = col;
     }
   }
 }
@@ -117,9 +171,9 @@ BSA_DEV void qk_tile(const AttnSmem<D>& sm, const bf16x8 (&qf)[D / 16], f32x16& 
 }
 
 // O^T (D x 32 queries) += V^T P^T for one 64-key tile; p0/p1 hold P^T in the
-// S^T result layout.
+// S^T result layout.  With `first` the accumulators start from zero.
 template <int D>
-BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, f32x16 (&o)[D / 32]) {
+BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, f32x16 (&o)[D / 32], bool first) {
   const int lane = lane_id();
   const int r = lane & 31, h = lane >> 5;
   bf16x8 pb[4];
@@ -134,11 +188,14 @@ BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, 
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const uint16_t* vr = &sm.vt[(dt * 32 + r) * (KT + 8) + kk * 16 + 4 * h];
+      const uint16_t* vr = &sm.vt[(dt * 32 + r) * VTS + kk * 16 + 4 * h];
       const u16x4 lo = *reinterpret_cast<const u16x4*>(vr);
       const u16x4 hi = *reinterpret_cast<const u16x4*>(vr + 8);
       const u16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      o[dt] = mfma32(as_bf(a), pb[kk], o[dt]);
+      if (kk == 0 && first)
+        o[dt] = mfma32(as_bf(a), pb[kk], f32x16{});
+      else
+        o[dt] = mfma32(as_bf(a), pb[kk], o[dt]);
     }
   }
 }
@@ -146,16 +203,18 @@ BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, 
 // key index (within a 64-key tile) held by result register i of this lane
 BSA_DEV int krow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
-// Online-softmax update of one lane's query column with a masked S^T tile
-// (masked entries already -inf).  Returns false when every entry is masked
-// for this query (state unchanged, p = 0).
+// Online-softmax update of one lane's query column.  s0/s1 hold raw scores
+// (masked entries already -inf); sl2 = softmax scale * log2(e) is applied
+// inside the exponent.  On return s0/s1 hold the probabilities P (0 where
+// masked).  `first` skips rescaling the still-zero accumulators.
 template <int D>
-BSA_DEV void softmax_update(f32x16& s0, f32x16& s1, float& m, float& l, f32x16 (&o)[D / 32]) {
+BSA_DEV void softmax_update(f32x16& s0, f32x16& s1, float& m, float& l, f32x16 (&o)[D / 32], float sl2,
+                            bool first) {
   float tmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, fmaxf(s0[i], s1[i]));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-  const float mnew = fmaxf(m, tmax);
+  const float mnew = fmaxf(m, tmax * sl2);
   if (mnew == -INFINITY) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -164,19 +223,23 @@ BSA_DEV void softmax_update(f32x16& s0, f32x16& s1, float& m, float& l, f32x16 (
     }
     return;
   }
-  const float corr = exp2f(m - mnew);
   float rs = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    s0[i] = exp2f(s0[i] - mnew);
-    s1[i] = exp2f(s1[i] - mnew);
+    s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], sl2, -mnew));
+    s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], sl2, -mnew));
     rs += s0[i] + s1[i];
   }
   rs += __shfl_xor(rs, 32, 64);
-  l = l * corr + rs;
-  m = mnew;
+  if (first) {
+    l = rs;
+  } else {
+    const float corr = __builtin_amdgcn_exp2f(m - mnew);
+    l = l * corr + rs;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] *= corr;
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] *= corr;
+  }
+  m = mnew;
 }
 
 template <int D>
@@ -191,34 +254,42 @@ BSA_DEV void load_qf(const uint16_t* qrow, bool ok, bf16x8 (&qf)[D / 16]) {
 }
 
 // ---------------------------------------------------------------------------
-// Row metadata of one lane's query row in a work item; lr is the row's index
-// inside the item (the item record holds the tile's first entry and its row
-// count).
+// Row metadata of one lane's query row in a work item.  An item record holds
+// {bucket, first entry, rows, tile}; lr is the row's index inside the item.
 struct GRow {
   int t, slot, qh, hs, rr;
   bool valid;
 };
 
-BSA_DEV GRow grow_of(const AttnParams& p, int4 rec, int hk, int lr) {
+// raw entry word of row lr of item `rec` (speculative load guarded by validity)
+BSA_DEV uint32_t entry_of(const AttnParams& p, int4 rec, int lr) {
+  return lr < rec.z ? p.entries[rec.y + (lr >> p.lgR)] : 0u;
+}
+
+// entry word = slot | head-in-group << sh_h | token << sh_t; record w = b << 16 | hk
+BSA_DEV GRow grow_of(const AttnParams& p, int4 rec, uint32_t ent, int lr) {
   GRow g;
+  const int hk = rec.w & 0xFFFF;
   g.valid = lr < rec.z;
-  g.t = 0;
-  g.slot = 0;
-  g.rr = 0;
-  int hh = 0;
-  if (g.valid) {
-    const uint32_t ent = p.entries[rec.y + lr / p.R];
-    g.rr = lr % p.R;
-    g.slot = (int)(ent % (uint32_t)p.kslot);
-    const uint32_t th = ent / (uint32_t)p.kslot;
-    hh = (int)(th % (uint32_t)p.Gs);
-    g.t = (int)(th / (uint32_t)p.Gs);
-  }
+  g.rr = g.valid ? lr & ((1 << p.lgR) - 1) : 0;
+  g.slot = (int)(ent & ((1u << p.sh_h) - 1u));
+  const int hh = (int)((ent >> p.sh_h) & ((1u << (p.sh_t - p.sh_h)) - 1u));
+  g.t = g.valid ? (int)(ent >> p.sh_t) : 0;
   g.qh = p.per_group ? hk * p.G + g.rr : hk * p.G + hh;
   g.hs = p.per_group ? hk : hk * p.G + hh;
   return g;
 }
 
+template <int D>
+BSA_DEV const uint16_t* q_row(const AttnParams& p, int4 rec, const GRow& g) {
+  const int b = rec.w >> 16;
+  return p.q + (int64_t)b * p.qs_b + (int64_t)g.t * p.qs_t + (int64_t)g.qh * p.qs_h;
+}
+
+// Software pipeline per workgroup (contiguous item range): the next item's
+// record and entry word are loaded at the top of the current item, and its
+// queries are staged global -> LDS after the current item's first score
+// tile, to be read back once the current item's last PV tile is issued.
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
@@ -240,26 +311,26 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
   int staged = -1;  // bucket whose single key tile sits in LDS
 
   int4 rec = p.items[it_begin];
-  GRow g = grow_of(p, rec, (rec.x / p.Nb) % p.Hkv, lrow);
+  GRow g = grow_of(p, rec, entry_of(p, rec, lrow), lrow);
   bf16x8 qf[D / 16];
-  {
-    const int b = rec.x / (p.Nb * p.Hkv);
-    load_qf<D>(p.q + (int64_t)b * p.qs_b + (int64_t)g.t * p.qs_t + (int64_t)g.qh * p.qs_h, g.valid, qf);
-  }
+  load_qf<D>(q_row<D>(p, rec, g), g.valid, qf);
 
   for (int it = it_begin; it < it_end; ++it) {
     const int bucket = rec.x;
-    const int j = bucket % p.Nb;
-    const int hk = (bucket / p.Nb) % p.Hkv;
-    const int b = bucket / (p.Nb * p.Hkv);
+    const int hk = rec.w & 0xFFFF;
+    const int b = rec.w >> 16;
+    const int j = bucket - (b * p.Hkv + hk) * p.Nb;
     const bool wave_on = w * 32 < rec.z;
-    // next item: its record now, its rows after staging, its queries (into
-    // LDS) after the first score tile
     const bool has_next = it + 1 < it_end;
+    // next item: its record, and its entry word -- a workgroup's items cover
+    // one contiguous run of entries, so the next item starts right after this
+    // one's entries (read speculatively; the entries array is padded)
     const int4 rec_n = has_next ? p.items[it + 1] : rec;
+    const uint32_t ent_n =
+        has_next ? p.entries[rec.y + ((rec.z + (1 << p.lgR) - 1) >> p.lgR) + (lrow >> p.lgR)] : 0u;
     GRow g_n = g;
 
-    const int64_t qpos = (int64_t)p.Lk - p.Lq + g.t;
+    const int qpos = p.Lk - p.Lq + g.t;
     float m = -INFINITY, l = 0.f;
     f32x16 o[D / 32];
 #pragma unroll
@@ -276,52 +347,46 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
         __syncthreads();
         staged = single ? bucket : -1;
       }
-      const bool first = kt0 == 0;
-      if (first && has_next) g_n = grow_of(p, rec_n, (rec_n.x / p.Nb) % p.Hkv, lrow);
       f32x16 s0, s1;
       if (wave_on) qk_tile<D>(sm, qf, s0, s1);
-      if (first && has_next) {
-        const int b_n = rec_n.x / (p.Nb * p.Hkv);
-        prefetch_q_lds<D>(qst, p.q + (int64_t)b_n * p.qs_b + (int64_t)g_n.t * p.qs_t + (int64_t)g_n.qh * p.qs_h,
-                          g_n.valid);
+      if (kt0 == 0 && has_next) {
+        // queries of the next item into this wave's LDS staging area
+        g_n = grow_of(p, rec_n, ent_n, lrow);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the staging area are done
+        prefetch_q_lds<D>(qst, q_row<D>(p, rec_n, g_n), g_n.valid);
       }
       if (wave_on) {
+        // mask only where a key can be past the end or after the query
+        // (ragged last tile, or the query's own block); wave-uniform test
+        const int lim = min(n_keys - kt0, p.causal ? qpos - key0 - kt0 + 1 : KT);
+        if (__ballot(g.valid && lim < KT) != 0ull) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kr = kt0 + krow(i, hq);
-          const int64_t ka = key0 + kr;
-          const bool ok0 = kr < n_keys && (!p.causal || ka <= qpos);
-          const bool ok1 = kr + 32 < n_keys && (!p.causal || ka + 32 <= qpos);
-          s0[i] = ok0 ? s0[i] * p.sl2 : -INFINITY;
-          s1[i] = ok1 ? s1[i] * p.sl2 : -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int kr = krow(i, hq);
+            s0[i] = kr < lim ? s0[i] : -INFINITY;
+            s1[i] = kr + 32 < lim ? s1[i] : -INFINITY;
+          }
         }
-        softmax_update<D>(s0, s1, m, l, o);
-        pv_tile<D>(sm, s0, s1, o);
+        softmax_update<D>(s0, s1, m, l, o, p.sl2, kt0 == 0);
+        pv_tile<D>(sm, s0, s1, o, kt0 == 0);
       }
     }
-    // the next item's queries: wait for the LDS-bound loads, then read back
+    // epilogue: pack this item's outputs, take the next item's queries out of
+    // the staging area, then reuse the area to write whole partial rows
+    u16x4_t pk[D / 8];
+    pack_partials<D>(o, pk);
     if (has_next) {
       __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_wave_barrier();
       asm volatile("" ::: "memory");
       read_q_lds<D>(qst, g_n.valid, qf);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-    if (g.valid) {
-      const float inv = 1.0f / l;
+    {
       const int64_t srow = ((int64_t)b * p.Hs + g.hs) * p.Lq + g.t;
       const int64_t pidx = (srow * p.kslot + g.slot) * p.R + g.rr;
-      uint16_t* dst = p.part_o + pidx * D;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const int d0 = dt * 32 + 8 * gg + 4 * hq;
-          u16x4 v4 = {f2bf(o[dt][4 * gg] * inv), f2bf(o[dt][4 * gg + 1] * inv), f2bf(o[dt][4 * gg + 2] * inv),
-                      f2bf(o[dt][4 * gg + 3] * inv)};
-          *reinterpret_cast<u16x4*>(dst + d0) = v4;
-        }
-      }
-      if (hq == 0) p.part_lse[pidx] = m + log2f(l);
+      if (wave_on) store_partials<D>(qst, pk, pidx * D, min(32, rec.z - w * 32), p.part_o);
+      if (g.valid && hq == 0) p.part_ml[pidx] = make_float2(m, l);
     }
     rec = rec_n;
     g = g_n;
@@ -360,35 +425,36 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   }
 #pragma unroll
   for (int m2 = 1; m2 < LPR; m2 <<= 1) n += __shfl_xor(n, m2, 64);
+  // partial s holds sum_k p_k v_k with p = 2^(score*sl2 - m_s) and sum_k p_k = l_s
   float M = -INFINITY, W = 0.f;
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   for (int s0 = 0; s0 < n; s0 += SB) {
-    float ls[SB];
+    float2 ml[SB];
     u16x8 ov[SB];
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
       const int s = s0 + u;
-      ls[u] = -INFINITY;
+      ml[u] = make_float2(-INFINITY, 0.f);
       ov[u] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (s < n) {
         const int64_t pidx = (srow * p.kslot + s) * p.R + rr;
-        ls[u] = p.part_lse[pidx];
+        ml[u] = p.part_ml[pidx];
         ov[u] = ld16(p.part_o + pidx * D + li * 8);
       }
     }
     float mb = M;
 #pragma unroll
-    for (int u = 0; u < SB; ++u) mb = fmaxf(mb, ls[u]);
-    const float c = exp2f(M - mb);
+    for (int u = 0; u < SB; ++u) mb = fmaxf(mb, ml[u].x);
+    const float c = __builtin_amdgcn_exp2f(M - mb);
     W *= c;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= c;
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const float wu = exp2f(ls[u] - mb);  // 0 for unused slots
-      W += wu;
+      const float wu = __builtin_amdgcn_exp2f(ml[u].x - mb);  // 0 for unused slots
+      W = fmaf(wu, ml[u].y, W);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = fmaf(wu, bf2f(ov[u][e]), acc[e]);
     }
@@ -404,13 +470,27 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     p.lse_out[((int64_t)b * p.Hq + h) * p.Lq + t] = W > 0.f ? (M + log2f(W)) * 0.69314718055994530942f : -INFINITY;
 }
 
+// Persistent grid = the workgroups the device holds at once (a multiple of 8,
+// one range per XCD).
+template <int D>
+static int gather_grid() {
+  static int cached = 0;
+  if (cached) return cached;
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, attn_gather_kernel<D>, 256, 0) != hipSuccess || per < 1)
+    return 2048;
+  cached = ((cus * per + 7) / 8) * 8;
+  return cached;
+}
+
 bool launch_attn_gather(const AttnParams& p, hipStream_t s) {
   {
     LaunchScope ls("attn_gather", s);
     if (p.D == 128)
-      hipLaunchKernelGGL(attn_gather_kernel<128>, dim3(p.grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(attn_gather_kernel<128>, dim3(gather_grid<128>()), dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL(attn_gather_kernel<64>, dim3(p.grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(attn_gather_kernel<64>, dim3(gather_grid<64>()), dim3(256), 0, s, p);
   }
   return launch_ok("attn_gather");
 }

@@ -96,7 +96,8 @@ struct CsrParams {
   int B, Lq, Lk, Hkv, G, Hs, per_group, Nb, block, causal;
   const int32_t* sel;
   int sel_w;
-  int kslot;      // gate slots per selection row
+  int kslot;      // partial slots per selection row
+  int sh_h, sh_t; // entry bit fields: slot | head << sh_h | token << sh_t
   int R;          // attention rows per entry (G per group, else 1)
   int rows_item;  // attention rows per work item
   int32_t* counts;      // [nbk]
@@ -114,6 +115,7 @@ bool launch_csr(const CsrParams& p, hipStream_t s);
 // ---- attention ------------------------------------------------------------
 struct AttnParams {
   int B, Lq, Lk, Hq, Hkv, G, D, block, Nb, Hs, per_group, Gs, R, kslot, causal;
+  int sh_h, sh_t, lgR;  // entry bit fields; R = 1 << lgR
   const uint16_t* q;
   int64_t qs_b, qs_t, qs_h;
   const uint16_t* k;
@@ -124,11 +126,11 @@ struct AttnParams {
   const uint32_t* entries;
   const int32_t* bucket_off;
   const int32_t* tile_off;
-  const int4* items;  // {bucket, first entry, rows, tile}
+  const int4* items;  // {bucket, first entry, rows, b << 16 | kv head}
   const int32_t* n_items;  // device scalar
   int grid;                // persistent workgroups
-  uint16_t* part_o;        // [rows * kslot * R, D] bf16 (normalised)
-  float* part_lse;         // log2-domain lse
+  uint16_t* part_o;        // [rows * kslot * R, D] bf16, sum_k p_k v_k with p = 2^(s*sl2 - m)
+  float2* part_ml;         // (m, l): log2-domain running max and sum of p
   // combine
   const int32_t* sel;
   int sel_w;

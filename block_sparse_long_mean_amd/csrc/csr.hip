@@ -48,7 +48,8 @@ BSA_DEV SelEntry decode_sel(const CsrParams& p, int64_t idx) {
   const int Gs = p.per_group ? 1 : p.G;
   r.valid = true;
   r.bucket = (b * p.Hkv + hk) * p.Nb + j;
-  r.packed = ((uint32_t)t * (uint32_t)Gs + (uint32_t)hh) * (uint32_t)p.kslot + (uint32_t)slot;
+  (void)Gs;
+  r.packed = ((uint32_t)t << p.sh_t) | ((uint32_t)hh << p.sh_h) | (uint32_t)slot;
   return r;
 }
 
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(256) void scan_apply_kernel(CsrParams p) {
   }
 }
 
-// one thread per bucket: write its work items {bucket, first entry, rows, tile}
+// one thread per bucket: write its work items {bucket, first entry, rows, b << 16 | kv head}
 __global__ __launch_bounds__(256) void expand_items_kernel(CsrParams p) {
   const int ept = p.rows_item / p.R;  // entries per tile
   for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < p.nbk; g += (int64_t)gridDim.x * 256) {
@@ -196,7 +197,9 @@ __global__ __launch_bounds__(256) void expand_items_kernel(CsrParams p) {
     const int rows = (p.bucket_off[g + 1] - e0) * p.R;
     for (int t = t0; t < t1; ++t) {
       const int k = t - t0;
-      p.items[t] = make_int4((int)g, e0 + k * ept, min(p.rows_item, rows - k * p.rows_item), k);
+      const int bh = (int)(g / p.Nb);
+      p.items[t] = make_int4((int)g, e0 + k * ept, min(p.rows_item, rows - k * p.rows_item),
+                             ((bh / p.Hkv) << 16) | (bh % p.Hkv));
     }
   }
 }

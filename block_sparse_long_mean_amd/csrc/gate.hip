@@ -158,6 +158,44 @@ BSA_DEV void list_insert(uint64_t (&L)[KR], uint64_t c, bool active, int lane, i
   }
 }
 
+// Bitonic sort, descending, of the 64 keys a 16-lane group holds for one row
+// (element e = 16*r + lane%16 in register r); every group sorts its own row.
+BSA_DEV void group_sort64_desc(uint64_t (&v)[4], int lane) {
+  const int li = lane & 15;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= 16) {
+        const int rs = stride >> 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = r ^ rs;
+          if (q > r) {
+            const int e = r * 16 + li;
+            const bool desc = (e & size) == 0;
+            const uint64_t a = v[r], b = v[q];
+            const bool sw = desc ? (a < b) : (a > b);
+            v[r] = sw ? b : a;
+            v[q] = sw ? a : b;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint64_t o = shfl_xor64(v[r], stride);
+          const int e = r * 16 + li;
+          const bool lower = (li & stride) == 0;
+          const bool desc = (e & size) == 0;
+          const uint64_t mx = v[r] > o ? v[r] : o;
+          const uint64_t mn = v[r] > o ? o : v[r];
+          v[r] = (lower == desc) ? mx : mn;
+        }
+      }
+    }
+  }
+}
+
 // k-th best key of the row held by this lane's group (0 while fewer than k).
 template <int KR>
 BSA_DEV uint64_t list_kth(const uint64_t (&L)[KR], int lane, int topk) {
@@ -288,6 +326,14 @@ __global__ __launch_bounds__(64 * W) void gate_kernel(GateParams p) {
         const bool ok = j < c_hi && j < ncand[i];
         key[ct] = ok ? make_key(acc[ct][i], (uint32_t)j) : 0ull;
         if (key[ct] > thr[i]) pend |= 1 << ct;
+      }
+      if (c0 == c_lo) {
+        // first chunk: sort its 64 candidates and keep the best k
+        group_sort64_desc(key, lane);
+#pragma unroll
+        for (int m = 0; m < KR; ++m) L[i][m] = (m * 16 + r16) < p.topk ? key[m] : 0ull;
+        thr[i] = list_kth<KR>(L[i], lane, p.topk);
+        continue;
       }
       while (true) {
         const uint64_t bal = __ballot(pend != 0);

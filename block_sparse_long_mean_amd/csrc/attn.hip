@@ -53,6 +53,7 @@ struct QStage {
   static constexpr int OELEMS = 32 * RS;
   static constexpr int ELEMS = QELEMS > OELEMS ? QELEMS : OELEMS;
   uint16_t buf[4][ELEMS];
+  int64_t dst[4][32];  // destination element offset of each of the wave's 32 rows
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -69,14 +70,13 @@ BSA_DEV void prefetch_q_lds(QStage<D>& st, const uint16_t* qrow, bool ok) {
   }
 }
 
+// Rows past the item's end read whatever the staging area holds; their
+// result columns are never stored.
 template <int D>
-BSA_DEV void read_q_lds(const QStage<D>& st, bool ok, bf16x8 (&qf)[D / 16]) {
+BSA_DEV void read_q_lds(const QStage<D>& st, bf16x8 (&qf)[D / 16]) {
   const int w = threadIdx.x >> 6, l = lane_id();
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const u16x8 x = *reinterpret_cast<const u16x8*>(&st.buf[w][(s * 64 + l) * 8]);
-    qf[s] = as_bf(ok ? x : u16x8{0, 0, 0, 0, 0, 0, 0, 0});
-  }
+  for (int s = 0; s < D / 16; ++s) qf[s] = as_bf(*reinterpret_cast<const u16x8*>(&st.buf[w][(s * 64 + l) * 8]));
 }
 
 // O^T tile of the wave's 32 rows -> bf16 rows in LDS -> global:
@@ -105,14 +105,15 @@ BSA_DEV void store_partials(QStage<D>& st, const u16x4_t (&pk)[D / 8], int64_t d
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg) *reinterpret_cast<u16x4_t*>(sb + r * RS + dt * 32 + 8 * gg + 4 * h) = pk[dt * 4 + gg];
+  if (h == 0) st.dst[w][r] = dst_mine;
   __builtin_amdgcn_wave_barrier();
   constexpr int CPR = D / 8, RPI = 64 / CPR;
   const int c = lane % CPR;
 #pragma unroll
   for (int n = 0; n < 32 / RPI; ++n) {
     const int rr = n * RPI + lane / CPR;
-    const int64_t dst = (int64_t)shfl64((uint64_t)dst_mine, rr);
     if (rr < nvalid) {
+      const int64_t dst = st.dst[w][rr];
       const u16x4_t a = *reinterpret_cast<const u16x4_t*>(sb + rr * RS + c * 8);
       const u16x4_t b = *reinterpret_cast<const u16x4_t*>(sb + rr * RS + c * 8 + 4);
       const u16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -171,9 +172,13 @@ BSA_DEV void qk_tile(const AttnSmem<D>& sm, const bf16x8 (&qf)[D / 16], f32x16& 
 }
 
 // O^T (D x 32 queries) += V^T P^T for one 64-key tile; p0/p1 hold P^T in the
-// S^T result layout.  With `first` the accumulators start from zero.
+// S^T result layout.  With `first` the accumulators start from zero.  The
+// tile's per-query sum of the (bf16) probabilities -- the same weights the
+// product uses -- comes from four more MFMAs with an all-ones A operand and is
+// added to l.
 template <int D>
-BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, f32x16 (&o)[D / 32], bool first) {
+BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, f32x16 (&o)[D / 32], bool first,
+                     float& l) {
   const int lane = lane_id();
   const int r = lane & 31, h = lane >> 5;
   bf16x8 pb[4];
@@ -183,6 +188,14 @@ BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, 
     pb[1][e] = (__bf16)p0[8 + e];
     pb[2][e] = (__bf16)p1[e];
     pb[3][e] = (__bf16)p1[8 + e];
+  }
+  {
+    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+    f32x16 rsum = mfma32(ones, pb[0], f32x16{});
+#pragma unroll
+    for (int kk = 1; kk < 4; ++kk) rsum = mfma32(ones, pb[kk], rsum);
+    l += rsum[0];
   }
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
@@ -206,7 +219,9 @@ BSA_DEV int krow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 // Online-softmax update of one lane's query column.  s0/s1 hold raw scores
 // (masked entries already -inf); sl2 = softmax scale * log2(e) is applied
 // inside the exponent.  On return s0/s1 hold the probabilities P (0 where
-// masked).  `first` skips rescaling the still-zero accumulators.
+// masked) and the running sum l and accumulators o are rescaled to the new
+// max; the tile's own sum of P is added by pv_tile.  `first` skips rescaling
+// the still-zero state.
 template <int D>
 BSA_DEV void softmax_update(f32x16& s0, f32x16& s1, float& m, float& l, f32x16 (&o)[D / 32], float sl2,
                             bool first) {
@@ -223,19 +238,14 @@ BSA_DEV void softmax_update(f32x16& s0, f32x16& s1, float& m, float& l, f32x16 (
     }
     return;
   }
-  float rs = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], sl2, -mnew));
     s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], sl2, -mnew));
-    rs += s0[i] + s1[i];
   }
-  rs += __shfl_xor(rs, 32, 64);
-  if (first) {
-    l = rs;
-  } else {
+  if (!first) {
     const float corr = __builtin_amdgcn_exp2f(m - mnew);
-    l = l * corr + rs;
+    l *= corr;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) o[dt] *= corr;
   }
@@ -368,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
           }
         }
         softmax_update<D>(s0, s1, m, l, o, p.sl2, kt0 == 0);
-        pv_tile<D>(sm, s0, s1, o, kt0 == 0);
+        pv_tile<D>(sm, s0, s1, o, kt0 == 0, l);
       }
     }
     // epilogue: pack this item's outputs, take the next item's queries out of
@@ -379,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
       __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_wave_barrier();
       asm volatile("" ::: "memory");
-      read_q_lds<D>(qst, g_n.valid, qf);
+      read_q_lds<D>(qst, qf);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     {

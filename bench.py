@@ -232,7 +232,7 @@ def main():
          f"(host wall {wall * 1e3 / args.steps:.3f} ms/step)")
 
     kernels = ["doc_chunk_last", "doc_positions", "rope_q", "block_summary", "pooled_to_planes", "gate_topk",
-               "gate_merge", "decode_gate", "decode_gate_merge", "csr_fill", "csr_count", "csr_scan", "csr_scatter", "attn_gather", "attn_merge",
+               "gate_merge", "decode_scores", "decode_topk", "csr_fill", "csr_count", "csr_scan", "csr_scatter", "attn_gather", "attn_merge",
                "decode_union", "decode_attend", "decode_combine"]
     per_kernel = {}
     for name in kernels:

@@ -415,9 +415,8 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
 // decode plan
 // ---------------------------------------------------------------------------
 struct DecodePlan {
-  int Nb, Hs, G, topk, umax, nsplit, span, sel_w, ntiles, rows_per_bh;
-  uint16_t *p_hi, *p_lo;
-  uint64_t* part_keys;
+  int Nb, Hs, G, topk, umax, sel_w;
+  float* scores;
   int32_t* sel;
   int32_t *ulist, *ucount;
   float *part_o, *part_lse;
@@ -453,25 +452,10 @@ static bsa_status plan_decode(const bsa_decode_args* a, DecodePlan& P, char* ws)
   if (!strides_ok(a->q_stride, 2, a->D, 2) || !strides_ok(a->k_stride, 3, a->D, 2) || !strides_ok(a->v_stride, 3, a->D, 2) ||
       !strides_ok(a->o_stride, 2, a->D, 2) || !strides_ok(a->p_stride, 3, a->D, pe))
     return fail(BSA_ERR_INVALID_ARG, "strides must be non-negative and keep rows 16-byte aligned");
-  P.rows_per_bh = per_group ? 1 : P.G;
-  P.ntiles = 1;
-  const int64_t base = (int64_t)a->B * a->Hkv;
-  const int ncand = P.Nb;
-  int want = (int)std::min<int64_t>((4096 + base - 1) / base, (ncand + 255) / 256);
-  want = std::max(want, 1);
-  P.span = ((ncand + want - 1) / want + 63) / 64 * 64;
-  P.nsplit = std::max(1, (ncand + P.span - 1) / P.span);
   Carver c;
   c.base = ws;
-  if (a->pooled_dtype == BSA_DTYPE_F32) {
-    const int64_t n = (int64_t)a->B * a->Hkv * P.Nb * a->D;
-    P.p_hi = c.take<uint16_t>(n);
-    P.p_lo = c.take<uint16_t>(n);
-  } else {
-    P.p_hi = P.p_lo = nullptr;
-  }
   const int64_t nrows = (int64_t)a->B * P.Hs;
-  P.part_keys = P.nsplit > 1 ? c.take<uint64_t>(nrows * P.nsplit * std::max(P.topk, 1)) : nullptr;
+  P.scores = c.take<float>(nrows * P.Nb);
   P.sel = a->sel_out ? a->sel_out : c.take<int32_t>(nrows * P.sel_w);
   P.ulist = c.take<int32_t>((int64_t)a->B * a->Hkv * P.umax);
   P.ucount = c.take<int32_t>((int64_t)a->B * a->Hkv);
@@ -490,27 +474,14 @@ static bsa_status run_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes
   plan_decode(a, P, reinterpret_cast<char*>(ws));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool per_group = a->gate_mode == BSA_GATE_PER_GROUP;
-  GateParams g;
-  g.B = a->B; g.Lq = 1; g.Lk = a->Lc; g.Hkv = a->Hkv; g.G = P.G; g.Hs = P.Hs; g.per_group = per_group;
-  g.rows_per_bh = P.rows_per_bh; g.ntiles = P.ntiles;
-  g.q = a->q; g.qs_b = a->q_stride[0]; g.qs_t = 0; g.qs_h = a->q_stride[1];
-  g.qkind = per_group ? 2 : 0;
-  g.Dg = a->D;
-  if (a->pooled_dtype == BSA_DTYPE_F32) {
-    if (!launch_pooled_to_planes(a->pooled, 0, a->p_stride[0], a->p_stride[1], a->p_stride[2], a->B, P.Nb, a->Hkv, a->D,
-                                 P.p_hi, P.p_lo, s))
-      return BSA_ERR_HIP;
-    g.p_hi = P.p_hi; g.p_lo = P.p_lo;
-    g.ps_h = (int64_t)P.Nb * a->D; g.ps_b = (int64_t)a->Hkv * g.ps_h; g.ps_j = a->D;
-  } else {
-    g.p_hi = reinterpret_cast<const uint16_t*>(a->pooled); g.p_lo = nullptr;
-    g.ps_b = a->p_stride[0]; g.ps_j = a->p_stride[1]; g.ps_h = a->p_stride[2];
-  }
-  g.Nb = P.Nb; g.causal = 1; g.block = a->block; g.lens = a->cache_lens;
-  g.topk = P.topk; g.nsplit = P.nsplit; g.span = P.span;
-  g.sel = P.sel; g.sel_w = P.sel_w; g.part = P.part_keys; g.tag = "decode_gate";
-  if (!launch_gate(g, s)) return BSA_ERR_HIP;
-  if (P.nsplit > 1 && !launch_gate_merge(g, s)) return BSA_ERR_HIP;
+  DecodeGateParams g;
+  g.B = a->B; g.Lc = a->Lc; g.Hq = a->Hq; g.Hkv = a->Hkv; g.G = P.G; g.D = a->D; g.block = a->block; g.Nb = P.Nb;
+  g.Hs = P.Hs; g.per_group = per_group; g.topk = P.topk; g.sel_w = P.sel_w; g.lens = a->cache_lens;
+  g.q = reinterpret_cast<const uint16_t*>(a->q); g.qs_b = a->q_stride[0]; g.qs_h = a->q_stride[1];
+  g.pooled = a->pooled; g.pooled_bf16 = a->pooled_dtype == BSA_DTYPE_BF16;
+  g.ps_b = a->p_stride[0]; g.ps_j = a->p_stride[1]; g.ps_h = a->p_stride[2];
+  g.scores = P.scores; g.sel = P.sel;
+  if (!launch_decode_gate(g, s)) return BSA_ERR_HIP;
   DecodeAttnParams d;
   d.B = a->B; d.Lc = a->Lc; d.Hq = a->Hq; d.Hkv = a->Hkv; d.G = P.G; d.D = a->D; d.block = a->block; d.Hs = P.Hs;
   d.per_group = per_group; d.topk = a->topk; d.umax = P.umax; d.lens = a->cache_lens;

@@ -178,6 +178,18 @@ struct DecodeAttnParams {
   int64_t os_b, os_h;
   float* lse_out;
 };
+struct DecodeGateParams {
+  int B, Lc, Hq, Hkv, G, D, block, Nb, Hs, per_group, topk, sel_w;
+  const int32_t* lens;
+  const uint16_t* q;
+  int64_t qs_b, qs_h;
+  const void* pooled;  // [B, Nb, Hkv, D] summaries, bf16 or fp32
+  int pooled_bf16;
+  int64_t ps_b, ps_j, ps_h;
+  float* scores;  // [B, Hs, Nb] workspace
+  int32_t* sel;   // [B, Hs, sel_w]
+};
+bool launch_decode_gate(const DecodeGateParams& p, hipStream_t s);
 bool launch_decode_union(const DecodeAttnParams& p, hipStream_t s);
 bool launch_decode_attend(const DecodeAttnParams& p, hipStream_t s);
 bool launch_decode_combine(const DecodeAttnParams& p, hipStream_t s);

@@ -70,6 +70,67 @@ __global__ __launch_bounds__(256) void csr_scatter_kernel(CsrParams p, int64_t n
   }
 }
 
+// LDS-histogram variants.  All selection rows of one (b, kv head) are
+// contiguous in sel ([B, Hs, Lq, w] with the group's heads adjacent), and they
+// only touch that (b, kv head)'s Nb buckets.  A workgroup takes a run of
+// those rows, counts its entries per block in LDS, and touches global
+// counters once per block it saw.
+constexpr int kHistMax = 8192;   // blocks per (b, kv head) handled in LDS
+constexpr int kRowsPerWG = 1024; // selection rows per workgroup
+
+BSA_DEV void bh_rows(const CsrParams& p, int bh, int64_t& r0, int64_t& nr) {
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int per = p.per_group ? 1 : p.G;
+  nr = (int64_t)per * p.Lq;
+  r0 = ((int64_t)b * p.Hs + (int64_t)hk * per) * p.Lq;
+}
+
+__global__ __launch_bounds__(256) void csr_count_lds_kernel(CsrParams p) {
+  __shared__ int hist[kHistMax];
+  const int bh = blockIdx.y;
+  int64_t r0, nr;
+  bh_rows(p, bh, r0, nr);
+  const int64_t ra = r0 + (int64_t)blockIdx.x * kRowsPerWG;
+  const int64_t rb = min(r0 + nr, ra + kRowsPerWG);
+  if (ra >= rb) return;  // uniform
+  for (int j = threadIdx.x; j < p.Nb; j += 256) hist[j] = 0;
+  __syncthreads();
+  for (int64_t i = ra * p.sel_w + threadIdx.x; i < rb * p.sel_w; i += 256) {
+    const SelEntry e = decode_sel(p, i);
+    if (e.valid) atomicAdd(&hist[e.bucket - bh * p.Nb], 1);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < p.Nb; j += 256)
+    if (hist[j]) atomicAdd(&p.counts[bh * p.Nb + j], hist[j]);
+}
+
+__global__ __launch_bounds__(256) void csr_scatter_lds_kernel(CsrParams p) {
+  __shared__ int hist[kHistMax];
+  const int bh = blockIdx.y;
+  int64_t r0, nr;
+  bh_rows(p, bh, r0, nr);
+  const int64_t ra = r0 + (int64_t)blockIdx.x * kRowsPerWG;
+  const int64_t rb = min(r0 + nr, ra + kRowsPerWG);
+  if (ra >= rb) return;  // uniform
+  for (int j = threadIdx.x; j < p.Nb; j += 256) hist[j] = 0;
+  __syncthreads();
+  for (int64_t i = ra * p.sel_w + threadIdx.x; i < rb * p.sel_w; i += 256) {
+    const SelEntry e = decode_sel(p, i);
+    if (e.valid) atomicAdd(&hist[e.bucket - bh * p.Nb], 1);
+  }
+  __syncthreads();
+  // reserve this workgroup's range in every bucket it touches
+  for (int j = threadIdx.x; j < p.Nb; j += 256) {
+    const int c = hist[j];
+    if (c) hist[j] = p.bucket_off[bh * p.Nb + j] + atomicAdd(&p.cursor[bh * p.Nb + j], c);
+  }
+  __syncthreads();
+  for (int64_t i = ra * p.sel_w + threadIdx.x; i < rb * p.sel_w; i += 256) {
+    const SelEntry e = decode_sel(p, i);
+    if (e.valid) p.entries[atomicAdd(&hist[e.bucket - bh * p.Nb], 1)] = e.packed;
+  }
+}
+
 BSA_DEV int tiles_of(const CsrParams& p, int count) {
   const int rows = count * p.R;
   return (rows + p.rows_item - 1) / p.rows_item;
@@ -215,9 +276,15 @@ bool launch_csr(const CsrParams& p, hipStream_t s) {
     hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(p.nbk)), dim3(256), 0, s, p.cursor, (int64_t)p.nbk, 0);
   }
   if (!launch_ok("csr_fill")) return false;
+  const bool lds = p.Nb <= kHistMax;
+  const int64_t rows_bh = (int64_t)(p.per_group ? 1 : p.G) * p.Lq;
+  const dim3 lgrid((unsigned)((rows_bh + kRowsPerWG - 1) / kRowsPerWG), (unsigned)(p.B * p.Hkv));
   {
     LaunchScope ls("csr_count", s);
-    hipLaunchKernelGGL(csr_count_kernel, dim3(grid_for(nsel)), dim3(256), 0, s, p, nsel);
+    if (lds)
+      hipLaunchKernelGGL(csr_count_lds_kernel, lgrid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(csr_count_kernel, dim3(grid_for(nsel)), dim3(256), 0, s, p, nsel);
   }
   if (!launch_ok("csr_count")) return false;
   {
@@ -229,7 +296,10 @@ bool launch_csr(const CsrParams& p, hipStream_t s) {
   if (!launch_ok("csr_scan")) return false;
   {
     LaunchScope ls("csr_scatter", s);
-    hipLaunchKernelGGL(csr_scatter_kernel, dim3(grid_for(nsel)), dim3(256), 0, s, p, nsel);
+    if (lds)
+      hipLaunchKernelGGL(csr_scatter_lds_kernel, lgrid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(csr_scatter_kernel, dim3(grid_for(nsel)), dim3(256), 0, s, p, nsel);
     hipLaunchKernelGGL(expand_items_kernel, dim3(grid_for(p.nbk)), dim3(256), 0, s, p);
   }
   return launch_ok("csr_scatter");

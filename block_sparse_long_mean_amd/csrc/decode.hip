@@ -21,6 +21,165 @@ BSA_DEV int dec_len(const DecodeAttnParams& p, int b) {
   return n < 1 ? 1 : (n > p.Lc ? p.Lc : n);
 }
 
+// ---------------------------------------------------------------------------
+// Decode gate, pass 1: stream the routing keys once.  A wave scores 16
+// summary rows per step on a 16x16x32 bf16 MFMA: A = 16 rows x 32 head dims
+// (lanes read 16-byte pieces, four lanes per row per step), B = the group's
+// query heads as columns (G of 16 used; per group their fp32 sum, split into
+// bf16 hi + lo).  bf16 summaries times bf16 queries are exact products; fp32
+// summaries are split into hi + lo as well.  Writes fp32 scores [B, Hs, Nb].
+template <typename PT, int D>
+__global__ __launch_bounds__(256) void decode_scores_kernel(DecodeGateParams p) {
+  constexpr int KS = D / 32;
+  constexpr int ROWS_PER_WAVE = 64;  // 4 MFMA row tiles
+  const int bh = blockIdx.y;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, kq = lane >> 4;
+  const int nq = p.per_group ? 1 : p.G;
+  // B operand: column `col` = query head (or the group sum) for k = 8*kq + 32*ks
+  bf16x8 qh[KS], ql[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = ks * 32 + kq * 8 + e;
+      float x = 0.f;
+      if (col < nq) {
+        if (p.per_group) {
+          for (int g = 0; g < p.G; ++g) x += bf2f(p.q[(int64_t)b * p.qs_b + (int64_t)(hk * p.G + g) * p.qs_h + d]);
+        } else {
+          x = bf2f(p.q[(int64_t)b * p.qs_b + (int64_t)(hk * p.G + col) * p.qs_h + d]);
+        }
+      }
+      __bf16 h, l;
+      split_bf(x, h, l);
+      qh[ks][e] = h;
+      ql[ks][e] = l;
+    }
+  }
+  const int j0 = (blockIdx.x * 4 + w) * ROWS_PER_WAVE;
+  const PT* base = reinterpret_cast<const PT*>(p.pooled) + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h;
+  // A operands for 4 row tiles, all loads issued before the MFMAs
+  u32x4 raw[4][KS][sizeof(PT) / 2];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int j = j0 + rt * 16 + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int hpart = 0; hpart < (int)(sizeof(PT) / 2); ++hpart) {
+        raw[rt][ks][hpart] = u32x4{0u, 0u, 0u, 0u};
+        if (j < p.Nb)
+          raw[rt][ks][hpart] = *reinterpret_cast<const u32x4*>(base + (int64_t)j * p.ps_j + ks * 32 + kq * 8 + hpart * 4);
+      }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (sizeof(PT) == 2) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, raw[rt][ks][0]);
+        acc = mfma16(a, qh[ks], acc);
+        if (p.per_group) acc = mfma16(a, ql[ks], acc);
+      } else {
+        bf16x8 ah, al;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = __uint_as_float(raw[rt][ks][e >> 2][e & 3]);
+          __bf16 h, l;
+          split_bf(x, h, l);
+          ah[e] = h;
+          al[e] = l;
+        }
+        acc = mfma16(ah, qh[ks], acc);
+        acc = mfma16(al, qh[ks], acc);
+        if (p.per_group) acc = mfma16(ah, ql[ks], acc);
+      }
+    }
+    // result: lane holds column `col` (query head) of rows 4*kq + i
+    if (col < nq) {
+      const int hs = p.per_group ? hk : hk * p.G + col;
+      float* out = p.scores + ((int64_t)b * p.Hs + hs) * p.Nb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + rt * 16 + 4 * kq + i;
+        if (j < p.Nb) out[j] = acc[i];
+      }
+    }
+  }
+}
+
+// Decode gate, pass 2: one wave per selection row (b, hs) keeps the top-k of
+// the candidates j < cur by (score desc, index asc) -- a threshold filter
+// plus an LDS buffer compacted by a wave-wide bitonic sort -- and writes the
+// row ascending with the forced own block last, -1 padded.
+template <int V>
+__global__ __launch_bounds__(256) void decode_topk_kernel(DecodeGateParams p) {
+  constexpr int CAP = 64 * V;
+  __shared__ uint64_t s_buf[4][CAP];
+  __shared__ int s_cnt[4];
+  __shared__ uint64_t s_thr[4];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + w;
+  if (row >= p.B * p.Hs) return;  // wave-uniform; no workgroup barrier follows
+  const int b = row / p.Hs;
+  int n = p.lens ? p.lens[b] : p.Lc;
+  n = n < 1 ? 1 : (n > p.Lc ? p.Lc : n);
+  const int cur = (n - 1) / p.block;
+  const float* sc = p.scores + (int64_t)row * p.Nb;
+  if (lane == 0) {
+    s_cnt[w] = 0;
+    s_thr[w] = 0ull;
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int c0 = 0; c0 < cur; c0 += 64) {
+    const int j = c0 + lane;
+    const uint64_t key = j < cur ? make_key(sc[j], (uint32_t)j) : 0ull;
+    const bool hit = key > s_thr[w];
+    const uint64_t m = __ballot(hit);
+    if (m) {
+      const int c = s_cnt[w];
+      if (hit) s_buf[w][c + __popcll(m & ((1ull << lane) - 1ull))] = key;
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 0) s_cnt[w] = c + __popcll(m);
+      __builtin_amdgcn_wave_barrier();
+      if (s_cnt[w] > CAP - 64) row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+    }
+  }
+  row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+  const int cnt = s_cnt[w];
+  int idx = lane < cnt ? (int)key_index(s_buf[w][lane]) : 0x7FFFFFFF;
+  idx = wave_sort_asc_i32(idx);
+  int32_t* out = p.sel + (int64_t)row * p.sel_w;
+  for (int e = lane; e < p.sel_w; e += 64) out[e] = e < cnt ? idx : (e == cnt ? cur : -1);
+}
+
+bool launch_decode_gate(const DecodeGateParams& p, hipStream_t s) {
+  {
+    LaunchScope ls("decode_scores", s);
+    const dim3 grid((unsigned)((p.Nb + 255) / 256), (unsigned)(p.B * p.Hkv));  // 4 waves x 64 rows
+    if (p.pooled_bf16) {
+      if (p.D == 128) hipLaunchKernelGGL((decode_scores_kernel<uint16_t, 128>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((decode_scores_kernel<uint16_t, 64>), grid, dim3(256), 0, s, p);
+    } else {
+      if (p.D == 128) hipLaunchKernelGGL((decode_scores_kernel<float, 128>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((decode_scores_kernel<float, 64>), grid, dim3(256), 0, s, p);
+    }
+  }
+  if (!launch_ok("decode_scores")) return false;
+  {
+    LaunchScope ls("decode_topk", s);
+    const unsigned grid = (unsigned)((p.B * p.Hs + 3) / 4);
+    if (2 * p.topk + 64 <= 128)
+      hipLaunchKernelGGL(decode_topk_kernel<2>, dim3(grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(decode_topk_kernel<4>, dim3(grid), dim3(256), 0, s, p);
+  }
+  return launch_ok("decode_topk");
+}
+
 // Union of the selections of the heads of one (b, kv head): distinct block ids
 // ascending, each with a bit mask of the heads that chose it.
 __global__ __launch_bounds__(64) void decode_union_kernel(DecodeAttnParams p) {
@@ -76,7 +235,7 @@ __global__ __launch_bounds__(64) void decode_union_kernel(DecodeAttnParams p) {
 
 // One workgroup per (b, kv head, distinct block): scores for the heads that
 // chose the block, softmax over its keys, weighted sum of its values.
-template <int D>
+template <int D, int NH>
 __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeAttnParams p) {
   constexpr int KC = 128;  // keys per pass
   constexpr int CH = D / 8;
@@ -116,41 +275,58 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeAttnParams p) 
   const uint16_t* kb = p.k + (int64_t)b * p.ks_b + (int64_t)hk * p.ks_h;
   const uint16_t* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
   const int dc = tid % CH, kg = tid / CH;
-  float acc[8][8];
+  float acc[NH][8];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int a = 0; a < NH; ++a)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
   __syncthreads();
 
+  constexpr int KPG = KC / KG;
   for (int k0 = ka; k0 < ke; k0 += KC) {
     const int nk = min(KC, ke - k0);
-    // scores: two threads per key, each half of the head dimension
+    // this chunk's values, loaded now so they are in flight with the keys
+    u16x8 vx[KPG];
+#pragma unroll
+    for (int kk = 0; kk < KPG; ++kk) {
+      const int key = kg * KPG + kk;
+      vx[kk] = key < nk ? ld16(vb + (int64_t)(k0 + key) * p.vs_t + dc * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    // scores: 16 lanes per key row (8 head dims each), 16 rows per pass;
+    // the partial dot products are summed across the row's 16 lanes
     {
-      const int key = tid >> 1, half = tid & 1;
-      float part[8];
+      constexpr int CPR = D / 8;   // lanes per key row
+      constexpr int RPP = 256 / CPR;  // rows per pass
+      const int c = tid % CPR, rsub = tid / CPR;
+      float qv[NH][8];
 #pragma unroll
-      for (int a = 0; a < 8; ++a) part[a] = 0.f;
-      if (key < nk) {
-        const uint16_t* kr = kb + (int64_t)(k0 + key) * p.ks_t + half * (D / 2);
+      for (int a = 0; a < NH; ++a)
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          const u16x8 x = ld16(kr + c * 8);
+        for (int e = 0; e < 8; ++e) qv[a][e] = a < nh ? s_q[a][c * 8 + e] : 0.f;
+      u16x8 kx[KC / RPP];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float kv = bf2f(x[e]);
-            const int d = half * (D / 2) + c * 8 + e;
-#pragma unroll
-            for (int a = 0; a < 8; ++a)
-              if (a < nh) part[a] = fmaf(s_q[a][d], kv, part[a]);
-          }
-        }
+      for (int ps = 0; ps < KC / RPP; ++ps) {
+        const int key = ps * RPP + rsub;
+        kx[ps] = key < nk ? ld16(kb + (int64_t)(k0 + key) * p.ks_t + c * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        if (a < nh) {
-          const float tot = part[a] + __shfl_xor(part[a], 1, 64);
-          if (half == 0 && key < KC) s_s[a][key] = key < nk ? tot * p.sl2 : -INFINITY;
+      for (int ps = 0; ps < KC / RPP; ++ps) {
+        const int key = ps * RPP + rsub;
+        float part[NH];
+#pragma unroll
+        for (int a = 0; a < NH; ++a) {
+          part[a] = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part[a] = fmaf(qv[a][e], bf2f(kx[ps][e]), part[a]);
+        }
+#pragma unroll
+        for (int a = 0; a < NH; ++a) {
+          if (a < nh) {
+            float tot = part[a];
+#pragma unroll
+            for (int m2 = 1; m2 < CPR; m2 <<= 1) tot += __shfl_xor(tot, m2, 64);
+            if (c == 0) s_s[a][key] = key < nk ? tot * p.sl2 : -INFINITY;
+          }
         }
       }
     }
@@ -175,21 +351,21 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeAttnParams p) 
     __syncthreads();
     // weighted values: thread = (key group kg, 8-wide d chunk dc)
     {
-      constexpr int KPG = KC / KG;
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
+      for (int a = 0; a < NH; ++a) {
         if (a < nh) {
           const float c = s_c[a];
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[a][e] *= c;
         }
       }
+#pragma unroll
       for (int kk = 0; kk < KPG; ++kk) {
         const int key = kg * KPG + kk;
         if (key < nk) {
-          const u16x8 x = ld16(vb + (int64_t)(k0 + key) * p.vs_t + dc * 8);
+          const u16x8 x = vx[kk];
 #pragma unroll
-          for (int a = 0; a < 8; ++a) {
+          for (int a = 0; a < NH; ++a) {
             if (a < nh) {
               const float pw = s_s[a][key];
 #pragma unroll
@@ -203,7 +379,7 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeAttnParams p) 
   }
   // reduce the key groups and write the per-head partials
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
+  for (int a = 0; a < NH; ++a) {
     if (a >= nh) break;  // nh is uniform across the workgroup
 #pragma unroll
     for (int e = 0; e < 8; ++e) s_red[kg][dc * 8 + e] = acc[a][e];
@@ -263,10 +439,13 @@ bool launch_decode_attend(const DecodeAttnParams& p, hipStream_t s) {
   const int grid = p.B * p.Hkv * p.umax;
   {
     LaunchScope ls("decode_attend", s);
-    if (p.D == 128)
-      hipLaunchKernelGGL(decode_attend_kernel<128>, dim3(grid), dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL(decode_attend_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+    if (p.D == 128) {
+      if (p.G <= 4) hipLaunchKernelGGL((decode_attend_kernel<128, 4>), dim3(grid), dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((decode_attend_kernel<128, 8>), dim3(grid), dim3(256), 0, s, p);
+    } else {
+      if (p.G <= 4) hipLaunchKernelGGL((decode_attend_kernel<64, 4>), dim3(grid), dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((decode_attend_kernel<64, 8>), dim3(grid), dim3(256), 0, s, p);
+    }
   }
   return launch_ok("decode_attend");
 }

@@ -134,18 +134,28 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(DecodeGateParams p) {
     s_thr[w] = 0ull;
   }
   __builtin_amdgcn_wave_barrier();
-  for (int c0 = 0; c0 < cur; c0 += 64) {
-    const int j = c0 + lane;
-    const uint64_t key = j < cur ? make_key(sc[j], (uint32_t)j) : 0ull;
-    const bool hit = key > s_thr[w];
-    const uint64_t m = __ballot(hit);
-    if (m) {
-      const int c = s_cnt[w];
-      if (hit) s_buf[w][c + __popcll(m & ((1ull << lane) - 1ull))] = key;
-      __builtin_amdgcn_wave_barrier();
-      if (lane == 0) s_cnt[w] = c + __popcll(m);
-      __builtin_amdgcn_wave_barrier();
-      if (s_cnt[w] > CAP - 64) row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+  constexpr int U = 32;  // chunks of 64 candidates loaded together
+  for (int c0 = 0; c0 < cur; c0 += 64 * U) {
+    float sv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = c0 + u * 64 + lane;
+      sv[u] = j < cur ? sc[j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = c0 + u * 64 + lane;
+      const uint64_t key = j < cur ? make_key(sv[u], (uint32_t)j) : 0ull;
+      const bool hit = key > s_thr[w];
+      const uint64_t m = __ballot(hit);
+      if (m) {
+        const int c = s_cnt[w];
+        if (hit) s_buf[w][c + __popcll(m & ((1ull << lane) - 1ull))] = key;
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0) s_cnt[w] = c + __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+        if (s_cnt[w] > CAP - 64) row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+      }
     }
   }
   row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
@@ -211,26 +221,35 @@ __global__ __launch_bounds__(64) void decode_union_kernel(DecodeAttnParams p) {
   for (int i = 0; i < V; ++i) s_v[i * 64 + lane] = v[i];
   __builtin_amdgcn_wave_barrier();
   __syncthreads();
-  if (lane == 0) {
-    int n = 0;
-    int lastj = -1, mask = 0;
-    int32_t* out = p.ulist + (int64_t)bh * p.umax;
-    for (int e = 0; e < 64 * V; ++e) {
-      const uint64_t key = s_v[e];
-      if (key == 0ull) break;
-      const uint64_t val = ~key;
-      const int j = (int)(val >> 8), hh = (int)(val & 255);
-      const int bits = p.per_group ? ((1 << p.G) - 1) : (1 << hh);
-      if (j != lastj) {
-        if (lastj >= 0) out[n++] = (lastj << 8) | mask;
-        lastj = j;
-        mask = 0;
+  // element e starts a run of equal block ids when its id differs from
+  // element e-1's; a run holds at most G entries (one per head)
+  int32_t* out = p.ulist + (int64_t)bh * p.umax;
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = i * 64 + lane;
+    const uint64_t key = s_v[e];
+    bool head = false;
+    int val = 0;
+    if (key != 0ull) {
+      const uint64_t vv = ~key;
+      const int j = (int)(vv >> 8);
+      head = e == 0 || (int)((~s_v[e - 1]) >> 8) != j;
+      if (head) {
+        int mask = 0;
+        for (int f = e; f < 64 * V && f < e + 8; ++f) {
+          const uint64_t kf = s_v[f];
+          if (kf == 0ull || (int)((~kf) >> 8) != j) break;
+          mask |= p.per_group ? ((1 << p.G) - 1) : (1 << (int)((~kf) & 255));
+        }
+        val = (j << 8) | mask;
       }
-      mask |= bits;
     }
-    if (lastj >= 0) out[n++] = (lastj << 8) | mask;
-    p.ucount[bh] = n;
+    const uint64_t hm = __ballot(head);
+    if (head) out[total + __popcll(hm & ((1ull << lane) - 1ull))] = val;
+    total += __popcll(hm);
   }
+  if (lane == 0) p.ucount[bh] = total;
 }
 
 // One workgroup per (b, kv head, distinct block): scores for the heads that
@@ -406,18 +425,54 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnParams p)
   const int bh = b * p.Hkv + hk;
   const int n = p.ucount[bh];
   float m = -INFINITY, l = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int u = 0; u < n; ++u) {
-    const int ent = p.ulist[(int64_t)bh * p.umax + u];
-    if (!((ent & 255) & (1 << hh))) continue;
-    const int64_t pidx = ((int64_t)bh * p.umax + u) * p.G + hh;
-    const float ls = p.part_lse[pidx];
-    const float mnew = fmaxf(m, ls);
-    const float c1 = exp2f(m - mnew), c2 = exp2f(ls - mnew);
-    const float* src = p.part_o + pidx * p.D;
-    a0 = a0 * c1 + c2 * (lane < p.D ? src[lane] : 0.f);
-    a1 = a1 * c1 + c2 * (lane + 64 < p.D ? src[lane + 64] : 0.f);
-    l = l * c1 + c2;
-    m = mnew;
+  const int32_t* ul = p.ulist + (int64_t)bh * p.umax;
+  for (int u0 = 0; u0 < n; u0 += 64) {
+    // which of the next 64 union entries this head chose
+    const int u = u0 + lane;
+    const bool mine = u < n && ((ul[u] & 255) & (1 << hh));
+    uint64_t bm = __ballot(mine);
+    while (bm) {
+      int us[8];
+      int k = 0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        us[t] = -1;
+        if (bm) {
+          us[t] = u0 + __ffsll((unsigned long long)bm) - 1;
+          bm &= bm - 1;
+          ++k;
+        }
+      }
+      float ls[8], x0[8], x1[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        ls[t] = -INFINITY;
+        x0[t] = x1[t] = 0.f;
+        if (us[t] >= 0) {
+          const int64_t pidx = ((int64_t)bh * p.umax + us[t]) * p.G + hh;
+          ls[t] = p.part_lse[pidx];
+          const float* src = p.part_o + pidx * p.D;
+          x0[t] = lane < p.D ? src[lane] : 0.f;
+          x1[t] = lane + 64 < p.D ? src[lane + 64] : 0.f;
+        }
+      }
+      float mb = m;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) mb = fmaxf(mb, ls[t]);
+      const float c1 = __builtin_amdgcn_exp2f(m - mb);
+      a0 *= c1;
+      a1 *= c1;
+      l *= c1;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float c2 = __builtin_amdgcn_exp2f(ls[t] - mb);
+        a0 = fmaf(c2, x0[t], a0);
+        a1 = fmaf(c2, x1[t], a1);
+        l += c2;
+      }
+      m = mb;
+      (void)k;
+    }
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   uint16_t* dst = p.o + (int64_t)b * p.os_b + (int64_t)h * p.os_h;

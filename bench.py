@@ -147,6 +147,56 @@ def cpu_baseline(q, k, v, iq, ik, budget_s=20.0):
     }
 
 
+def copy_calibration(mib):
+    """A kernel of known traffic: neg over `mib` MiB of bf16 reads and writes
+    exactly that many bytes; its counter readings scale the gather's."""
+    import torch
+
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n * 2, "bytes_written": n * 2, "launches": 3}}), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_gather_128k_traffic.md")
+GATHER_SOURCES = ["attn.hip", "bsa_device.h", "bsa_internal.h"]
+
+
+def gather_sources_digest():
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in GATHER_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_long_mean_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per gather launch from the committed counter summary, or None
+    when the gather's sources have changed since the counters were taken."""
+    import re
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    got = {}
+    for key in ("sources_digest", "hbm_bytes_per_launch"):
+        mt = re.search(rf"^{key}:\s*(\S+)\s*$", text, re.M)
+        if not mt:
+            return None
+        got[key] = mt.group(1)
+    if got["sources_digest"] != gather_sources_digest():
+        return None
+    return float(got["hbm_bytes_per_launch"])
+
+
 class _RowView:
     """Presents sampled query rows at their true positions to the oracle."""
 
@@ -167,6 +217,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run an elementwise negation over MIB MiB (read once, written once) -- the "
+                         "known-size kernel that scales the HBM byte counters -- and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the path shards by KV head or "
@@ -174,6 +227,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import block_sparse_long_mean_amd as m
 
@@ -256,7 +313,7 @@ def main():
         # the gather attends every selected block, the own block included
         achieved = flops_total / (per_kernel[dom]["ms_avg"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(), "kernel": dom,
                 "kernel_ms": per_kernel[dom]["ms_avg"]}
     else:
         roof = {"bound": "unknown", "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None,

@@ -407,7 +407,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
     if (!launch_csr(cp, s)) return BSA_ERR_HIP;
     if (!launch_attn_gather(ap, s)) return BSA_ERR_HIP;
   }
-  if (!launch_attn_combine(ap, s)) return BSA_ERR_HIP;
+  if (!launch_attn_merge(ap, s)) return BSA_ERR_HIP;
   return BSA_OK;
 }
 

@@ -14,14 +14,15 @@
 //    block's keys and values are staged in LDS (V transposed) in 64-key tiles
 //    and kept there across consecutive items of the same bucket; each wave
 //    holds 32 gathered query rows.  S^T = K Q^T and O^T += V^T P^T run on
-//    v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the result is one
-//    normalised partial output (bf16) plus its log2-domain LSE per
-//    (row, slot).  Persistent workgroups walk contiguous item ranges and
-//    prefetch the next item's row metadata and queries during the current
-//    item's MFMAs.
-//  * attn_merge: streaming.  Sixteen lanes per output row read the row's
-//    partials (8 head dims each), merge them with LSE weights and write o (and
-//    lse).
+//    v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the result per
+//    (row, slot) is an unnormalised partial output sum_k p_k v_k (bf16) with
+//    p_k = 2^(s_k * scale * log2(e) - m) and its pair (m, l = sum_k p_k) in
+//    fp32.  Persistent workgroups walk contiguous item ranges and prefetch
+//    the next item's row metadata and queries during the current item's
+//    MFMAs.
+//  * attn_merge: streaming.  D/8 lanes per output row read the row's
+//    partials (8 head dims each), merge them with weights 2^(m_s - max m)
+//    and write o (and lse).
 #include <math.h>
 
 #include "bsa_device.h"
@@ -505,7 +506,7 @@ bool launch_attn_gather(const AttnParams& p, hipStream_t s) {
   return launch_ok("attn_gather");
 }
 
-bool launch_attn_combine(const AttnParams& p, hipStream_t s) {
+bool launch_attn_merge(const AttnParams& p, hipStream_t s) {
   const int64_t nrows = (int64_t)p.B * p.Lq * p.Hq;
   const int rpw = 64 / (p.D / 8);
   const int64_t grid = (nrows + 4 * rpw - 1) / (4 * rpw);

@@ -139,7 +139,7 @@ struct AttnParams {
   float* lse_out;  // natural log, [B, Hq, Lq] or null
 };
 bool launch_attn_gather(const AttnParams& p, hipStream_t s);
-bool launch_attn_combine(const AttnParams& p, hipStream_t s);
+bool launch_attn_merge(const AttnParams& p, hipStream_t s);
 
 struct AttnF32Params {
   int B, Lq, Lk, Hq, Hkv, G, D, block, Hs, per_group, causal;

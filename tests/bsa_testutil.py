@@ -98,3 +98,60 @@ def to_np(t):
 
 def ln2():
     return math.log(2.0)
+
+
+class RowView:
+    """Sampled query rows presented to the oracle at their true positions.
+
+    rows: CPU tensor [B, T, ...] holding the rows of `toks` (in that order) of a
+    [B, L, ...] tensor; only [b, t] indexing with t in `toks` is supported.
+    """
+
+    def __init__(self, rows, toks, L):
+        self.rows = rows
+        self.index = {int(t): i for i, t in enumerate(toks)}
+        self.shape = (rows.shape[0], L) + tuple(rows.shape[2:])
+
+    def __getitem__(self, key):
+        b, t = key
+        return self.rows[b, self.index[int(t)]]
+
+
+class HostSlices:
+    """A device tensor presented to the oracle as host copies of the slices it
+    asks for (the oracle reads only the blocks it needs from a large cache)."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, key):
+        import torch
+
+        if not isinstance(key, tuple):
+            key = (key,)
+        key = tuple(k.to(self.t.device) if isinstance(k, torch.Tensor) else k for k in key)
+        return self.t[key].cpu()
+
+
+def ref_with_gpu_sel(ref, diff_rows, gpu_sel, run_oracle, tokens=None):
+    """Recompute the oracle outputs of the evaluated tokens whose selection
+    legitimately differs (near-ties), on the GPU's own selection.
+
+    ref: oracle prefill result over evaluated tokens (index ti); diff_rows:
+    (b, hs, ti) from check_selection; gpu_sel [B, Hs, T, W] for the same
+    evaluated tokens; tokens[ti] = the query index of evaluated token ti
+    (default ti itself); run_oracle(tokens=..., force_sel=...) reruns the oracle.
+    """
+    if not diff_rows:
+        return ref
+    tis = sorted({ti for (_, _, ti) in diff_rows})
+    toks = [int(tokens[ti]) if tokens is not None else ti for ti in tis]
+    fs = np.asarray(gpu_sel)[:, :, tis]
+    r2 = run_oracle(tokens=toks, force_sel=fs)
+    o = ref["o"].copy()
+    lse = ref["lse"].copy()
+    for i, ti in enumerate(tis):
+        o[:, ti] = r2["o"][:, i]
+        lse[:, :, ti] = r2["lse"][:, :, i]
+    return {"o": o, "lse": lse}

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from bsa_testutil import assert_close, check_selection, to_np
+from bsa_testutil import assert_close, check_selection, ref_with_gpu_sel, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -26,22 +26,6 @@ def bsa():
 
 def _say(msg):
     print(msg, flush=True)
-
-
-def _ref_with_gpu_sel(ref, diff_rows, gpu_sel, run_oracle):
-    """Recompute oracle outputs of the tokens whose selection legitimately
-    differs (near-ties), on the GPU's selection."""
-    if not diff_rows:
-        return ref
-    toks = sorted({t for (_, _, t) in diff_rows})
-    fs = np.asarray(gpu_sel)[:, :, toks]
-    r2 = run_oracle(tokens=toks, force_sel=fs)
-    o = ref["o"].copy()
-    lse = ref["lse"].copy()
-    for i, t in enumerate(toks):
-        o[:, t] = r2["o"][:, i]
-        lse[:, :, t] = r2["lse"][:, :, i]
-    return {"o": o, "lse": lse}
 
 
 def run_prefill_case(bsa, *, dtype, B, Lq, Lk, Hq, Hkv, D, block, topk, causal, gate="head", sigma=1.0, seed=0,
@@ -77,7 +61,7 @@ def run_prefill_case(bsa, *, dtype, B, Lq, Lk, Hq, Hkv, D, block, topk, causal, 
     gsel = sel.cpu().numpy()
     diff = check_selection(gsel, ref["sel"], ref["scores"], topk, causal)
     _say(f"  selection rows {gsel.shape[0] * gsel.shape[1] * gsel.shape[2]}, near-tie differences {len(diff)}")
-    ref = _ref_with_gpu_sel(ref, diff, gsel, run_oracle)
+    ref = ref_with_gpu_sel(ref, diff, gsel, run_oracle)
     st = assert_close(to_np(o), ref["o"], atol, rel, bf16_storage=(dtype == "bf16"))
     assert_close(to_np(lse), ref["lse"], lse_atol, None, what="lse")
     return st
@@ -116,6 +100,13 @@ def test_bf16_memory_doc_rope_noncausal(bsa):
     """MSA-style: a memory of short documents with document-wise RoPE, one query chunk, non-causal top-16."""
     run_prefill_case(bsa, dtype="bf16", B=1, Lq=128, Lk=20000, Hq=8, Hkv=2, D=128, block=64, topk=16, causal=False,
                      seed=5, doc_mean=400.0, atol=1e-2, rel=1e-2, lse_atol=5e-3)
+
+
+def test_bf16_memory_topk64_global_buckets(bsa):
+    """Non-causal top-64 over a 600K-token memory of documents with document-wise RoPE: more blocks
+    per KV head (9375) than the bucket histogram keeps on chip, and a 64-entry top-k."""
+    run_prefill_case(bsa, dtype="bf16", B=1, Lq=64, Lk=600000, Hq=8, Hkv=2, D=128, block=64, topk=64, causal=False,
+                     seed=13, doc_mean=3000.0, atol=1e-2, rel=1e-2, lse_atol=5e-3)
 
 
 def test_bf16_topk_zero_and_full(bsa):
@@ -183,6 +174,31 @@ def test_decode_ragged_lengths(bsa, gate):
     diff = check_selection(gsel, ref["sel"][:, :, None], scores, topk, True)
     if diff:
         ref = oracle.decode(q, k, v, pooled, block=block, topk=topk, gate=gate, cache_lens=lens, force_sel=gsel[:, :, 0])
+    assert_close(to_np(o), ref["o"], 1e-2, 1e-2, bf16_storage=True)
+    assert_close(to_np(lse), ref["lse"], 5e-3, None, what="lse")
+
+
+def test_decode_topk60_group_of_8(bsa):
+    """Eight query heads per KV head with top-60 each: 488 (head, block) pairs per group to unite."""
+    B, Hq, Hkv, Lc, D, block, topk = 2, 16, 2, 20000, 128, 64, 60
+    _say(f"case decode B2 H16/2 Lc20000 block64 topk60")
+    q = synth.host_tensor((B, Hq, D), 1.0, 14, 0, "bf16")
+    k = synth.host_tensor((B, Lc, Hkv, D), 1.0, 14, 1, "bf16")
+    v = synth.host_tensor((B, Lc, Hkv, D), 1.0, 14, 2, "bf16")
+    lens = np.array([20000, 12345], dtype=np.int32)
+    pooled = torch.from_numpy(oracle.block_pool(k, block)).float()
+    o, sel, lse = bsa.sparse_attn_decode(q.cuda(), k.cuda(), v.cuda(), pooled.cuda(), topk, block,
+                                         cache_lens=torch.from_numpy(lens).cuda(), return_sel=True, return_lse=True)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q, k, v, pooled, block=block, topk=topk, cache_lens=lens, return_scores=True)
+    nb = pooled.shape[1]
+    scores = np.full((B, Hq, 1, nb), np.nan)
+    for (b, hs), s in ref["scores"].items():
+        scores[b, hs, 0, : len(s)] = s
+    gsel = sel.cpu().numpy()[:, :, None]
+    diff = check_selection(gsel, ref["sel"][:, :, None], scores, topk, True)
+    if diff:
+        ref = oracle.decode(q, k, v, pooled, block=block, topk=topk, cache_lens=lens, force_sel=gsel[:, :, 0])
     assert_close(to_np(o), ref["o"], 1e-2, 1e-2, bf16_storage=True)
     assert_close(to_np(lse), ref["lse"], 5e-3, None, what="lse")
 

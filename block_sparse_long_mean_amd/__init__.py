@@ -59,6 +59,7 @@ class PrefillArgs(ctypes.Structure):
         ("pooled", VP),
         ("sel_out", VP),
         ("lse_out", VP),
+        ("chunk_tokens", ctypes.c_int32),
     ]
 
 
@@ -202,7 +203,7 @@ def _doc(d, B, L, device):
 
 
 def _prefill_args(q, k, v, o, *, block, topk, causal, gate, index_q, index_k, doc_ids_q, doc_ids_k,
-                  rope_theta, scale, pooled, sel, lse):
+                  rope_theta, scale, pooled, sel, lse, chunk_tokens=0):
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     a = PrefillArgs()
@@ -227,6 +228,7 @@ def _prefill_args(q, k, v, o, *, block, topk, causal, gate, index_q, index_k, do
     a.pooled = _ptr(pooled)
     a.sel_out = _ptr(sel)
     a.lse_out = _ptr(lse)
+    a.chunk_tokens = int(chunk_tokens)
     return a
 
 
@@ -235,12 +237,12 @@ def _prefill_args(q, k, v, o, *, block, topk, causal, gate, index_q, index_k, do
 # --------------------------------------------------------------------------
 
 def prefill_workspace_bytes(q, k, *, block, topk, causal=True, gate="head", index_q=None, index_k=None,
-                            doc_ids_q=None, doc_ids_k=None, pooled=None) -> int:
+                            doc_ids_q=None, doc_ids_k=None, pooled=None, chunk_tokens: int = 0) -> int:
     dq = _doc(doc_ids_q, q.shape[0], q.shape[1], q.device)
     dk = _doc(doc_ids_k, k.shape[0], k.shape[1], k.device)
     a = _prefill_args(q, k, k, q, block=block, topk=topk, causal=causal, gate=gate, index_q=index_q,
                       index_k=index_k, doc_ids_q=dq, doc_ids_k=dk, rope_theta=10000.0, scale=None,
-                      pooled=pooled, sel=None, lse=None)
+                      pooled=pooled, sel=None, lse=None, chunk_tokens=chunk_tokens)
     n = lib().bsa_prefill_workspace_bytes(ctypes.byref(a))
     if n == 0:
         raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())
@@ -250,7 +252,7 @@ def prefill_workspace_bytes(q, k, *, block, topk, causal=True, gate="head", inde
 def sparse_attn_prefill(q, k, v, block: int, topk: int, causal: bool = True, doc_ids=None, *, gate: str = "head",
                         index_q=None, index_k=None, doc_ids_q=None, doc_ids_k=None, rope_theta: float = 10000.0,
                         scale: float | None = None, pooled=None, return_sel: bool = False,
-                        return_lse: bool = False, out=None, workspace=None, stream=None):
+                        return_lse: bool = False, out=None, workspace=None, stream=None, chunk_tokens: int = 0):
     """Block-sparse attention prefill (see include/bsa.h for the semantics).
 
     q [B, Lq, Hq, D], k/v [B, Lk, Hkv, D] device tensors (bf16 or fp32).
@@ -270,7 +272,8 @@ def sparse_attn_prefill(q, k, v, block: int, topk: int, causal: bool = True, doc
     dq = _doc(doc_ids_q, B, Lq, q.device)
     dk = _doc(doc_ids_k, B, Lk, k.device)
     a = _prefill_args(q, k, v, o, block=block, topk=topk, causal=causal, gate=gate, index_q=index_q, index_k=index_k,
-                      doc_ids_q=dq, doc_ids_k=dk, rope_theta=rope_theta, scale=scale, pooled=pooled, sel=sel, lse=lse)
+                      doc_ids_q=dq, doc_ids_k=dk, rope_theta=rope_theta, scale=scale, pooled=pooled, sel=sel, lse=lse,
+                      chunk_tokens=chunk_tokens)
     n = lib().bsa_prefill_workspace_bytes(ctypes.byref(a))
     if n == 0:
         raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())
@@ -403,8 +406,9 @@ def block_summary(k, block: int, doc_ids=None, *, rope_theta: float = 10000.0, o
     return res[0] if len(res) == 1 else tuple(res)
 
 
-def timer_enable(on: bool = True):
-    lib().bsa_timer_enable(1 if on else 0)
+def timer_enable(level=1):
+    """0/False: off; 1/True: every launch, the attention passes as one "attn" phase; 2: every launch."""
+    lib().bsa_timer_enable(int(level))
 
 
 def timer_reset():

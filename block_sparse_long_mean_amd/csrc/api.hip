@@ -40,11 +40,11 @@ struct TimerRec {
   std::string name;
   hipEvent_t a, b;
 };
-static bool g_timer_on = false;
+static int g_timer_level = 0;
 static std::vector<TimerRec> g_timer;
 
-LaunchScope::LaunchScope(const char* n, hipStream_t s) : name(n), stream(s), slot(-1) {
-  if (!g_timer_on) return;
+LaunchScope::LaunchScope(const char* n, hipStream_t s, int level) : name(n), stream(s), slot(-1) {
+  if (g_timer_level < level) return;
   TimerRec r;
   r.name = n;
   if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
@@ -103,6 +103,7 @@ struct PrefillPlan {
   int nsplit, span, gate_qkind, ntiles, rows_per_bh;
   int64_t nsel_rows, max_entries, max_items;
   int attn_grid;
+  int NC, CT, CPL;  // query chunks per (b, kv head), tokens per chunk, chunks per attention pass
   // workspace pointers
   int32_t *pos_q, *pos_k, *chunk_q, *chunk_k;
   uint16_t *q16, *k16;
@@ -185,7 +186,34 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
   if (P.sh_t >= 31 || (int64_t)(a->Lq - 1) >= ((int64_t)1 << (32 - P.sh_t)))
     return fail(BSA_ERR_UNSUPPORTED, "Lq too large for the packed selection entries");
   if ((int64_t)a->B * a->Hkv * P.Nb >= (int64_t)1 << 30) return fail(BSA_ERR_UNSUPPORTED, "too many KV blocks");
-  P.nbk = a->B * a->Hkv * P.Nb;
+  if (a->chunk_tokens < 0) return fail(BSA_ERR_INVALID_ARG, "chunk_tokens must be >= 0");
+  {
+    // Attention runs in passes over chunks of query tokens so that the
+    // partial outputs of one pass stay within a workspace budget.  One pass
+    // over everything is fastest (a chunk of fewer tokens gives each block
+    // fewer rows per work item and re-stages its keys per chunk; the partials
+    // written by a gather are not kept by the memory-side cache for the
+    // merge), so the budget is large: it only bounds the workspace of very
+    // long inputs.
+    const int64_t per_tok = (int64_t)P.G * P.kslot * (2 * a->D + 8);  // partial bytes per (token, kv head)
+    const int64_t budget = (int64_t)40 << 30;
+    const int64_t nbh = (int64_t)a->B * a->Hkv;
+    if (a->chunk_tokens > 0) {
+      P.CT = std::min(a->chunk_tokens, a->Lq);
+      P.CPL = 1;
+    } else if (per_tok * a->Lq <= budget) {
+      P.CT = a->Lq;
+      P.CPL = (int)std::max<int64_t>(1, std::min<int64_t>(nbh, budget / std::max<int64_t>(1, per_tok * a->Lq)));
+    } else {
+      int ct = 1024;
+      while ((int64_t)ct * 2 * per_tok <= budget && ct * 2 < a->Lq) ct *= 2;
+      P.CT = ct;
+      P.CPL = 1;
+    }
+    P.NC = (a->Lq + P.CT - 1) / P.CT;
+    if (nbh * P.NC * P.Nb >= (int64_t)1 << 30) return fail(BSA_ERR_UNSUPPORTED, "too many (chunk, block) buckets");
+  }
+  P.nbk = a->B * a->Hkv * P.NC * P.Nb;
   P.max_entries = P.nsel_rows * (P.topk + (a->causal ? 1 : 0));
   if (P.per_group && (128 % P.G) != 0) return fail(BSA_ERR_UNSUPPORTED, "per-group gating needs G dividing 128");
   const int rows_item = 128;
@@ -237,8 +265,9 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
     P.scan_tmp = c.take<int32_t>(scan_tmp_len(P.nbk));
     P.entries = c.take<uint32_t>(P.max_entries + 256);  // speculative reads past the end stay inside
     P.items = c.take<int4>(P.max_items);
-    P.part_o = c.take<uint16_t>(P.max_entries * P.R * a->D);
-    P.part_ml = c.take<float2>(P.max_entries * P.R);
+    const int64_t part_rows = (int64_t)P.CPL * P.Gs * P.CT * P.kslot * P.R;
+    P.part_o = c.take<uint16_t>(part_rows * a->D);
+    P.part_ml = c.take<float2>(part_rows);
   } else {
     P.counts = P.cursor = P.bucket_off = P.tile_off = P.scan_tmp = nullptr;
     P.entries = nullptr;
@@ -390,7 +419,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
   ap.v = reinterpret_cast<const uint16_t*>(a->v); ap.vs_b = a->v_stride[0]; ap.vs_t = a->v_stride[1]; ap.vs_h = a->v_stride[2];
   ap.sl2 = (float)((double)scale * 1.4426950408889634074);
   ap.entries = P.entries; ap.bucket_off = P.bucket_off; ap.tile_off = P.tile_off; ap.items = P.items;
-  ap.n_items = P.tile_off + P.nbk;
+  ap.NC = P.NC; ap.CT = P.CT;
   ap.grid = P.attn_grid;
   ap.part_o = P.part_o; ap.part_ml = P.part_ml;
   ap.sel = P.sel; ap.sel_w = P.sel_w;
@@ -400,14 +429,22 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
     CsrParams cp;
     cp.B = a->B; cp.Lq = a->Lq; cp.Lk = a->Lk; cp.Hkv = a->Hkv; cp.G = P.G; cp.Hs = P.Hs; cp.per_group = P.per_group;
     cp.Nb = P.Nb; cp.block = a->block; cp.causal = a->causal;
+    cp.Gs = P.Gs; cp.NC = P.NC; cp.CT = P.CT;
     cp.sel = P.sel; cp.sel_w = P.sel_w; cp.kslot = P.kslot; cp.R = P.R; cp.rows_item = 128;
     cp.sh_h = P.sh_h; cp.sh_t = P.sh_t;
     cp.counts = P.counts; cp.cursor = P.cursor; cp.bucket_off = P.bucket_off; cp.tile_off = P.tile_off;
     cp.scan_tmp = P.scan_tmp; cp.entries = P.entries; cp.items = P.items; cp.nbk = P.nbk;
     if (!launch_csr(cp, s)) return BSA_ERR_HIP;
-    if (!launch_attn_gather(ap, s)) return BSA_ERR_HIP;
   }
-  if (!launch_attn_merge(ap, s)) return BSA_ERR_HIP;
+  // attention passes: gather then merge, CPL chunks at a time
+  LaunchScope phase("attn", s);
+  const int nchunks = a->B * a->Hkv * P.NC;
+  for (int c0 = 0; c0 < nchunks; c0 += P.CPL) {
+    ap.c0 = c0;
+    ap.c1 = std::min(nchunks, c0 + P.CPL);
+    if (P.max_entries > 0 && !launch_attn_gather(ap, s)) return BSA_ERR_HIP;
+    if (!launch_attn_merge(ap, s)) return BSA_ERR_HIP;
+  }
   return BSA_OK;
 }
 
@@ -594,7 +631,7 @@ BSA_API const char* bsa_last_error(void) { return g_err.c_str(); }
 
 BSA_API int32_t bsa_version(void) { return 100; }  // 0.1.0
 
-BSA_API void bsa_timer_enable(int32_t on) { g_timer_on = on != 0; }
+BSA_API void bsa_timer_enable(int32_t level) { g_timer_level = level < 0 ? 0 : level; }
 
 BSA_API void bsa_timer_reset(void) { timer_clear(); }
 

@@ -118,7 +118,8 @@ BSA_DEV void store_partials(QStage<D>& st, const u16x4_t (&pk)[D / 8], int64_t d
       const u16x4_t a = *reinterpret_cast<const u16x4_t*>(sb + rr * RS + c * 8);
       const u16x4_t b = *reinterpret_cast<const u16x4_t*>(sb + rr * RS + c * 8 + 4);
       const u16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      st16(part_o + dst + c * 8, v);
+      // streaming store: partials are read once, by the merge, long after
+      __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(part_o + dst + c * 8));
     }
   }
 }
@@ -307,13 +308,15 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) QStage<D> qst;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hq = lane >> 5;
-  const int nitems = *p.n_items;
+  // work items of this launch's chunks (buckets c0*Nb .. c1*Nb)
+  const int it_lo = p.tile_off[(int64_t)p.c0 * p.Nb];
+  const int nitems = p.tile_off[(int64_t)p.c1 * p.Nb] - it_lo;
   // XCD x owns items [off_x, off_x + cnt_x); its workgroups split that range
   // into contiguous runs so that consecutive items mostly share a bucket.
   const int x = blockIdx.x & 7, wi = blockIdx.x >> 3, nw = gridDim.x >> 3;
   const int per = nitems >> 3, rem = nitems & 7;
   const int cnt_x = per + (x < rem ? 1 : 0);
-  const int off_x = x * per + (x < rem ? x : rem);
+  const int off_x = it_lo + x * per + (x < rem ? x : rem);
   const int it_begin = off_x + (int)(((int64_t)cnt_x * wi) / nw);
   const int it_end = off_x + (int)(((int64_t)cnt_x * (wi + 1)) / nw);
   if (it_begin >= it_end) return;  // uniform for the workgroup
@@ -330,7 +333,10 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
     const int bucket = rec.x;
     const int hk = rec.w & 0xFFFF;
     const int b = rec.w >> 16;
-    const int j = bucket - (b * p.Hkv + hk) * p.Nb;
+    const int cid = bucket / p.Nb;  // chunk id
+    const int j = bucket - cid * p.Nb;
+    const int t_base = (cid % p.NC) * p.CT;
+    const int64_t prow_base = (int64_t)(cid - p.c0) * p.Gs;
     const bool wave_on = w * 32 < rec.z;
     const bool has_next = it + 1 < it_end;
     // next item: its record, and its entry word -- a workgroup's items cover
@@ -394,10 +400,14 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     {
-      const int64_t srow = ((int64_t)b * p.Hs + g.hs) * p.Lq + g.t;
-      const int64_t pidx = (srow * p.kslot + g.slot) * p.R + g.rr;
+      const int hsel = p.per_group ? 0 : g.hs - hk * p.G;
+      const int64_t prow = (prow_base + hsel) * p.CT + (g.t - t_base);
+      const int64_t pidx = (prow * p.kslot + g.slot) * p.R + g.rr;
       if (wave_on) store_partials<D>(qst, pk, pidx * D, min(32, rec.z - w * 32), p.part_o);
-      if (g.valid && hq == 0) p.part_ml[pidx] = make_float2(m, l);
+      if (g.valid && hq == 0) {
+        __builtin_nontemporal_store(m, &p.part_ml[pidx].x);
+        __builtin_nontemporal_store(l, &p.part_ml[pidx].y);
+      }
     }
     rec = rec_n;
     g = g_n;
@@ -416,17 +426,24 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   constexpr int SB = 8;               // slots per batch
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int li = lane % LPR;
-  const int64_t nrows = (int64_t)p.B * p.Lq * p.Hq;
+  // rows of this launch: (chunk - c0, token in chunk, head in group), so a
+  // token's G output heads are adjacent
+  const int64_t nrows = (int64_t)(p.c1 - p.c0) * p.CT * p.G;
   const int64_t row = ((int64_t)blockIdx.x * 4 + w) * RPW + lane / LPR;
-  const bool ok = row < nrows;
-  const int64_t rr_ = ok ? row : 0;
-  const int h = (int)(rr_ % p.Hq);
-  const int t = (int)((rr_ / p.Hq) % p.Lq);
-  const int b = (int)(rr_ / ((int64_t)p.Hq * p.Lq));
-  const int hk = h / p.G;
+  const int64_t rr_ = row < nrows ? row : 0;
+  const int hh = (int)(rr_ % p.G);
+  const int t_loc = (int)((rr_ / p.G) % p.CT);
+  const int c_rel = (int)(rr_ / ((int64_t)p.G * p.CT));
+  const int cid = p.c0 + c_rel;
+  const int bh = cid / p.NC;
+  const int t = (cid % p.NC) * p.CT + t_loc;
+  const bool ok = row < nrows && t < p.Lq;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int h = hk * p.G + hh;
   const int hs = p.per_group ? hk : h;
-  const int rr = p.per_group ? h % p.G : 0;
-  const int64_t srow = ((int64_t)b * p.Hs + hs) * p.Lq + t;
+  const int rr = p.per_group ? hh : 0;
+  const int64_t prow = ((int64_t)c_rel * p.Gs + (p.per_group ? 0 : hh)) * p.CT + t_loc;
+  const int64_t srow = ((int64_t)b * p.Hs + hs) * p.Lq + (ok ? t : 0);
   const int32_t* sr = p.sel + srow * p.sel_w;
   // number of valid slots (valid entries come first, -1 after): the row's
   // lanes count a strided share each, then sum across the row's lanes
@@ -450,9 +467,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
       ml[u] = make_float2(-INFINITY, 0.f);
       ov[u] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (s < n) {
-        const int64_t pidx = (srow * p.kslot + s) * p.R + rr;
-        ml[u] = p.part_ml[pidx];
-        ov[u] = ld16(p.part_o + pidx * D + li * 8);
+        const int64_t pidx = (prow * p.kslot + s) * p.R + rr;
+        // streaming loads: every partial is read exactly once
+        ml[u].x = __builtin_nontemporal_load(&p.part_ml[pidx].x);
+        ml[u].y = __builtin_nontemporal_load(&p.part_ml[pidx].y);
+        ov[u] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p.part_o + pidx * D + li * 8));
       }
     }
     float mb = M;
@@ -497,7 +516,7 @@ static int gather_grid() {
 
 bool launch_attn_gather(const AttnParams& p, hipStream_t s) {
   {
-    LaunchScope ls("attn_gather", s);
+    LaunchScope ls("attn_gather", s, 2);
     if (p.D == 128)
       hipLaunchKernelGGL(attn_gather_kernel<128>, dim3(gather_grid<128>()), dim3(256), 0, s, p);
     else
@@ -507,11 +526,11 @@ bool launch_attn_gather(const AttnParams& p, hipStream_t s) {
 }
 
 bool launch_attn_merge(const AttnParams& p, hipStream_t s) {
-  const int64_t nrows = (int64_t)p.B * p.Lq * p.Hq;
+  const int64_t nrows = (int64_t)(p.c1 - p.c0) * p.CT * p.G;
   const int rpw = 64 / (p.D / 8);
   const int64_t grid = (nrows + 4 * rpw - 1) / (4 * rpw);
   {
-    LaunchScope ls("attn_merge", s);
+    LaunchScope ls("attn_merge", s, 2);
     if (p.D == 128)
       hipLaunchKernelGGL(attn_merge_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, p);
     else

@@ -9,7 +9,8 @@ namespace bsa {
 
 // ---- launch bookkeeping (timer + error capture), defined in api.hip -------
 struct LaunchScope {
-  LaunchScope(const char* name, hipStream_t s);
+  // level: the timer level from which this scope records (1 = every level)
+  LaunchScope(const char* name, hipStream_t s, int level = 1);
   ~LaunchScope();
   const char* name;
   hipStream_t stream;
@@ -92,8 +93,13 @@ struct GateF32Params {
 bool launch_gate_f32(const GateF32Params& p, hipStream_t s);
 
 // ---- selection inversion (CSR) --------------------------------------------
+// Query tokens of one (b, kv head) are attended in chunks of CT tokens (NC
+// chunks; chunk id = (b * Hkv + hk) * NC + c).  Buckets are per (chunk id,
+// block): bucket = chunk id * Nb + j, so a chunk's work items are contiguous.
 struct CsrParams {
   int B, Lq, Lk, Hkv, G, Hs, per_group, Nb, block, causal;
+  int Gs;         // selection rows per (b, kv head, token): G per head, 1 per group
+  int NC, CT;     // chunks per (b, kv head) and tokens per chunk
   const int32_t* sel;
   int sel_w;
   int kslot;      // partial slots per selection row
@@ -127,8 +133,10 @@ struct AttnParams {
   const int32_t* bucket_off;
   const int32_t* tile_off;
   const int4* items;  // {bucket, first entry, rows, b << 16 | kv head}
-  const int32_t* n_items;  // device scalar
+  int NC, CT;              // query chunks per (b, kv head), tokens per chunk
+  int c0, c1;              // chunk ids of this launch; its partial buffer holds c1 - c0 chunks
   int grid;                // persistent workgroups
+  // partials of the launch's chunks, row ((c - c0) * Gs + head-sel) * CT + token-in-chunk
   uint16_t* part_o;        // [rows * kslot * R, D] bf16, sum_k p_k v_k with p = 2^(s*sl2 - m)
   float2* part_ml;         // (m, l): log2-domain running max and sum of p
   // combine

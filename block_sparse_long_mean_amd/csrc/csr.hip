@@ -45,10 +45,8 @@ BSA_DEV SelEntry decode_sel(const CsrParams& p, int64_t idx) {
   const int b = (int)(srow / ((int64_t)p.Lq * p.Hs));
   const int hk = p.per_group ? hs : hs / p.G;
   const int hh = p.per_group ? 0 : hs % p.G;
-  const int Gs = p.per_group ? 1 : p.G;
   r.valid = true;
-  r.bucket = (b * p.Hkv + hk) * p.Nb + j;
-  (void)Gs;
+  r.bucket = ((b * p.Hkv + hk) * p.NC + t / p.CT) * p.Nb + j;
   r.packed = ((uint32_t)t << p.sh_t) | ((uint32_t)hh << p.sh_h) | (uint32_t)slot;
   return r;
 }
@@ -70,64 +68,69 @@ __global__ __launch_bounds__(256) void csr_scatter_kernel(CsrParams p, int64_t n
   }
 }
 
-// LDS-histogram variants.  All selection rows of one (b, kv head) are
-// contiguous in sel ([B, Hs, Lq, w] with the group's heads adjacent), and they
-// only touch that (b, kv head)'s Nb buckets.  A workgroup takes a run of
-// those rows, counts its entries per block in LDS, and touches global
-// counters once per block it saw.
+// LDS-histogram variants.  A segment is the run of selection rows of one
+// (b, kv head, head of the group, chunk): consecutive tokens of one selection
+// head whose entries all land in the chunk's Nb buckets.  A workgroup takes up
+// to kRowsPerWG rows of a segment, counts its entries per block in LDS, and
+// touches global counters once per block it saw.
 constexpr int kHistMax = 8192;   // blocks per (b, kv head) handled in LDS
 constexpr int kRowsPerWG = 1024; // selection rows per workgroup
 
-BSA_DEV void bh_rows(const CsrParams& p, int bh, int64_t& r0, int64_t& nr) {
-  const int b = bh / p.Hkv, hk = bh % p.Hkv;
-  const int per = p.per_group ? 1 : p.G;
-  nr = (int64_t)per * p.Lq;
-  r0 = ((int64_t)b * p.Hs + (int64_t)hk * per) * p.Lq;
+// rows [ra, rb) of sel and the first bucket of segment `seg`, piece `piece`
+BSA_DEV bool seg_rows(const CsrParams& p, int seg, int piece, int64_t& ra, int64_t& rb, int& base) {
+  const int c = seg % p.NC;
+  int rest = seg / p.NC;
+  const int hh = rest % p.Gs;
+  rest /= p.Gs;
+  const int hk = rest % p.Hkv;
+  const int b = rest / p.Hkv;
+  const int hs = p.per_group ? hk : hk * p.G + hh;
+  const int t0 = c * p.CT + piece * kRowsPerWG;
+  const int t1 = min(min(t0 + kRowsPerWG, c * p.CT + p.CT), p.Lq);
+  const int64_t r0 = ((int64_t)b * p.Hs + hs) * p.Lq;
+  ra = r0 + t0;
+  rb = r0 + t1;
+  base = ((b * p.Hkv + hk) * p.NC + c) * p.Nb;
+  return t0 < t1;
 }
 
 __global__ __launch_bounds__(256) void csr_count_lds_kernel(CsrParams p) {
   __shared__ int hist[kHistMax];
-  const int bh = blockIdx.y;
-  int64_t r0, nr;
-  bh_rows(p, bh, r0, nr);
-  const int64_t ra = r0 + (int64_t)blockIdx.x * kRowsPerWG;
-  const int64_t rb = min(r0 + nr, ra + kRowsPerWG);
-  if (ra >= rb) return;  // uniform
+  int64_t ra, rb;
+  int base;
+  if (!seg_rows(p, blockIdx.x, blockIdx.y, ra, rb, base)) return;  // uniform
   for (int j = threadIdx.x; j < p.Nb; j += 256) hist[j] = 0;
   __syncthreads();
   for (int64_t i = ra * p.sel_w + threadIdx.x; i < rb * p.sel_w; i += 256) {
     const SelEntry e = decode_sel(p, i);
-    if (e.valid) atomicAdd(&hist[e.bucket - bh * p.Nb], 1);
+    if (e.valid) atomicAdd(&hist[e.bucket - base], 1);
   }
   __syncthreads();
   for (int j = threadIdx.x; j < p.Nb; j += 256)
-    if (hist[j]) atomicAdd(&p.counts[bh * p.Nb + j], hist[j]);
+    if (hist[j]) atomicAdd(&p.counts[base + j], hist[j]);
 }
 
 __global__ __launch_bounds__(256) void csr_scatter_lds_kernel(CsrParams p) {
   __shared__ int hist[kHistMax];
-  const int bh = blockIdx.y;
-  int64_t r0, nr;
-  bh_rows(p, bh, r0, nr);
-  const int64_t ra = r0 + (int64_t)blockIdx.x * kRowsPerWG;
-  const int64_t rb = min(r0 + nr, ra + kRowsPerWG);
-  if (ra >= rb) return;  // uniform
+  int64_t ra, rb;
+  int base;
+  if (!seg_rows(p, blockIdx.x, blockIdx.y, ra, rb, base)) return;  // uniform
   for (int j = threadIdx.x; j < p.Nb; j += 256) hist[j] = 0;
   __syncthreads();
   for (int64_t i = ra * p.sel_w + threadIdx.x; i < rb * p.sel_w; i += 256) {
     const SelEntry e = decode_sel(p, i);
-    if (e.valid) atomicAdd(&hist[e.bucket - bh * p.Nb], 1);
+    if (e.valid) atomicAdd(&hist[e.bucket - base], 1);
   }
   __syncthreads();
   // reserve this workgroup's range in every bucket it touches
   for (int j = threadIdx.x; j < p.Nb; j += 256) {
     const int c = hist[j];
-    if (c) hist[j] = p.bucket_off[bh * p.Nb + j] + atomicAdd(&p.cursor[bh * p.Nb + j], c);
+    if (c) hist[j] = p.bucket_off[base + j] + atomicAdd(&p.cursor[base + j], c);
   }
   __syncthreads();
   for (int64_t i = ra * p.sel_w + threadIdx.x; i < rb * p.sel_w; i += 256) {
     const SelEntry e = decode_sel(p, i);
-    if (e.valid) p.entries[atomicAdd(&hist[e.bucket - bh * p.Nb], 1)] = e.packed;
+    if (e.valid) p.entries[atomicAdd(&hist[e.bucket - base], 1)] = e.packed;
   }
 }
 
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(256) void expand_items_kernel(CsrParams p) {
     const int rows = (p.bucket_off[g + 1] - e0) * p.R;
     for (int t = t0; t < t1; ++t) {
       const int k = t - t0;
-      const int bh = (int)(g / p.Nb);
+      const int bh = (int)(g / ((int64_t)p.NC * p.Nb));
       p.items[t] = make_int4((int)g, e0 + k * ept, min(p.rows_item, rows - k * p.rows_item),
                              ((bh / p.Hkv) << 16) | (bh % p.Hkv));
     }
@@ -276,9 +279,10 @@ bool launch_csr(const CsrParams& p, hipStream_t s) {
     hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(p.nbk)), dim3(256), 0, s, p.cursor, (int64_t)p.nbk, 0);
   }
   if (!launch_ok("csr_fill")) return false;
-  const bool lds = p.Nb <= kHistMax;
-  const int64_t rows_bh = (int64_t)(p.per_group ? 1 : p.G) * p.Lq;
-  const dim3 lgrid((unsigned)((rows_bh + kRowsPerWG - 1) / kRowsPerWG), (unsigned)(p.B * p.Hkv));
+  const int64_t nseg = (int64_t)p.B * p.Hkv * p.Gs * p.NC;
+  const int pieces = (std::min(p.CT, p.Lq) + kRowsPerWG - 1) / kRowsPerWG;
+  const dim3 lgrid((unsigned)nseg, (unsigned)pieces);
+  const bool lds = p.Nb <= kHistMax && pieces <= 65535 && nseg < ((int64_t)1 << 31);
   {
     LaunchScope ls("csr_count", s);
     if (lds)

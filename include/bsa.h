@@ -106,6 +106,11 @@ typedef struct bsa_prefill_args {
                                       or Hkv (per group): chosen blocks ascending, the forced
                                       block last when causal, -1 padded */
     float* lse_out;                /* optional [B, Hq, Lq] natural-log softmax normaliser */
+    int32_t chunk_tokens;          /* scheduling only, results do not depend on it: 0 lets the
+                                      library pick how many query tokens of one (b, kv head) it
+                                      attends per pass (all of them when their partial outputs fit
+                                      a cache-sized budget); > 0 forces passes of that many tokens,
+                                      one (b, kv head) at a time */
 } bsa_prefill_args;
 
 /* Workspace bytes bsa_sparse_attn_prefill needs for `a` (0 if `a` is invalid;
@@ -184,12 +189,17 @@ int32_t bsa_version(void);
 
 /*
  * Optional launch timer (off by default; host-side state, not thread-safe).
- * While enabled, every kernel launch is bracketed by HIP events recorded on
- * the launch stream.  bsa_timer_report synchronises on those events and
- * returns, for the kernel named `kernel` (HOST string), the summed duration in
- * milliseconds and the launch count since the last reset.
+ * Level 1: every kernel launch is bracketed by HIP events recorded on the
+ * launch stream, except inside the prefill's attention passes, which are
+ * bracketed as one phase named "attn" (gathers and merges of every pass, so
+ * that hundreds of short launches are not each charged the events' cost).
+ * Level 2: every launch, the attention passes' "attn_gather" / "attn_merge"
+ * launches included (and "attn" as well).  0 turns it off.
+ * bsa_timer_report synchronises on the events and returns, for the kernel or
+ * phase named `kernel` (HOST string), the summed duration in milliseconds and
+ * the launch count since the last reset.
  */
-void bsa_timer_enable(int32_t on);
+void bsa_timer_enable(int32_t level);
 void bsa_timer_reset(void);
 bsa_status bsa_timer_report(const char* kernel, double* total_ms, int64_t* launches);
 

@@ -67,6 +67,42 @@ BSA_DEV uint64_t shfl64(uint64_t v, int src) {
   hi = (uint32_t)__shfl((int)hi, src, 64);
   return ((uint64_t)hi << 32) | lo;
 }
+// Lane exchanges inside the 16-lane rows of a wave through DPP (a VALU
+// operand modifier, no LDS round trip).  Controls: quad_perm [1,0,3,2] = 0xB1,
+// quad_perm [2,3,0,1] = 0x4E, row_shl:n = 0x100+n (lane i reads i+n),
+// row_shr:n = 0x110+n (lane i reads i-n), row_ror:n = 0x120+n (lane i reads
+// (i-n) mod 16).  Lanes whose source falls outside the row keep `old`.
+template <int CTRL>
+BSA_DEV uint32_t dpp32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+BSA_DEV uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  return ((uint64_t)dpp32<CTRL>(hi, hi) << 32) | dpp32<CTRL>(lo, lo);
+}
+// value held by lane (li ^ M) of the same row, M in {1, 2, 4, 8}; li = lane % 16
+template <int M>
+BSA_DEV uint64_t row_xor64(uint64_t v, int li) {
+  if constexpr (M == 1) return dpp64<0xB1>(v);
+  else if constexpr (M == 2) return dpp64<0x4E>(v);
+  else if constexpr (M == 8) return dpp64<0x128>(v);
+  else {
+    static_assert(M == 4, "row_xor64 takes 1, 2, 4 or 8");
+    const uint64_t up = dpp64<0x104>(v);
+    const uint64_t dn = dpp64<0x114>(v);
+    return (li & 4) ? dn : up;
+  }
+}
+// value held by lane (li - 1) mod 16 of the same row
+BSA_DEV uint64_t row_ror1_64(uint64_t v) { return dpp64<0x121>(v); }
+// value held by lane `src` (wave-uniform)
+BSA_DEV uint64_t readlane64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 BSA_DEV float wave_max(float v) {
   for (int m = 32; m > 0; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
   return v;

@@ -142,19 +142,28 @@ BSA_DEV void list_insert(uint64_t (&L)[KR], uint64_t c, bool active, int lane, i
     pos += __popc((uint32_t)(bal >> (16 * g)) & 0xFFFFu);
   }
   active = active && pos < topk;
-  uint64_t prev[KR];
+  // element e-1 of the row: lane li-1 of the same register, or lane 15 of
+  // the previous register for li = 0 (a rotation inside the 16-lane row)
+  uint64_t r[KR];
+#pragma unroll
+  for (int m = 0; m < KR; ++m) r[m] = row_ror1_64(L[m]);
 #pragma unroll
   for (int m = 0; m < KR; ++m) {
-    const uint64_t up = shfl64(L[m], (lane + 63) & 63);
-    const uint64_t carry = m > 0 ? shfl64(L[m > 0 ? m - 1 : 0], (lane + 15) & 63) : 0ull;
-    prev[m] = li > 0 ? up : carry;
-  }
-#pragma unroll
-  for (int m = 0; m < KR; ++m) {
+    const uint64_t prev = li > 0 ? r[m] : (m > 0 ? r[m > 0 ? m - 1 : 0] : 0ull);
     const int e = m * 16 + li;
-    uint64_t nv = e < pos ? L[m] : (e == pos ? c : prev[m]);
+    uint64_t nv = e < pos ? L[m] : (e == pos ? c : prev);
     if (e >= topk) nv = 0ull;
     if (active) L[m] = nv;
+  }
+}
+
+// row_xor64 with a stride that is a constant once the caller's loops unroll
+BSA_DEV uint64_t row_xor64_any(uint64_t v, int m, int li) {
+  switch (m) {
+    case 1: return row_xor64<1>(v, li);
+    case 2: return row_xor64<2>(v, li);
+    case 4: return row_xor64<4>(v, li);
+    default: return row_xor64<8>(v, li);
   }
 }
 
@@ -183,7 +192,7 @@ BSA_DEV void group_sort64_desc(uint64_t (&v)[4], int lane) {
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint64_t o = shfl_xor64(v[r], stride);
+          const uint64_t o = row_xor64_any(v[r], stride, li);
           const int e = r * 16 + li;
           const bool lower = (li & stride) == 0;
           const bool desc = (e & size) == 0;
@@ -196,7 +205,7 @@ BSA_DEV void group_sort64_desc(uint64_t (&v)[4], int lane) {
   }
 }
 
-// k-th best key of the row held by this lane's group (0 while fewer than k).
+// k-th best key of the row held by this lane's group (0 while fewer than k)
 template <int KR>
 BSA_DEV uint64_t list_kth(const uint64_t (&L)[KR], int lane, int topk) {
   const int e = topk - 1;
@@ -208,7 +217,7 @@ BSA_DEV uint64_t list_kth(const uint64_t (&L)[KR], int lane, int topk) {
 }
 
 template <int W, int DG, int KR, int QK, bool LO>
-__global__ __launch_bounds__(64 * W) void gate_kernel(GateParams p) {
+__global__ __launch_bounds__(64 * W, 4) void gate_kernel(GateParams p) {
   constexpr int ROWS = 16 * W;
   constexpr int PADR = DG + 8;  // padded LDS row (bf16 elements)
   constexpr int KS = DG / 32;
@@ -338,13 +347,14 @@ __global__ __launch_bounds__(64 * W) void gate_kernel(GateParams p) {
       while (true) {
         const uint64_t bal = __ballot(pend != 0);
         if (bal == 0ull) break;
-        const uint32_t gm = (uint32_t)(bal >> (16 * kh)) & 0xFFFFu;
-        const int src = gm ? 16 * kh + __ffs((int)gm) - 1 : lane;
         const int ct0 = pend ? __ffs(pend) - 1 : 0;
         const uint64_t mine = ct0 == 0 ? key[0] : ct0 == 1 ? key[1] : ct0 == 2 ? key[2] : key[3];
+        const uint32_t gm = (uint32_t)(bal >> (16 * kh)) & 0xFFFFu;
+        const int src = gm ? 16 * kh + __ffs((int)gm) - 1 : lane;
         const uint64_t cnd = shfl64(pend ? mine : 0ull, src);
         const uint64_t c = gm ? cnd : 0ull;
-        if (gm && lane == src) pend &= pend - 1;
+        const int src_me = gm ? src : -1;
+        if (lane == src_me) pend &= pend - 1;
         list_insert<KR>(L[i], c, c > thr[i], lane, p.topk);
         thr[i] = list_kth<KR>(L[i], lane, p.topk);
 #pragma unroll

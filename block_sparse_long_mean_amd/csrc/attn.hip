@@ -58,6 +58,14 @@ struct QStage {
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// Work-item records are read-only while the gather runs: reading them through
+// the constant address space makes them scalar loads, whose wait does not
+// also wait for the partial-output stores still in flight (vector memory
+// operations complete in order).
+typedef const __attribute__((address_space(4))) int* const_int_ptr;
+BSA_DEV int4 load_item(const_int_ptr items, int i) {
+  return make_int4(items[4 * i], items[4 * i + 1], items[4 * i + 2], items[4 * i + 3]);
+}
 
 template <int D>
 BSA_DEV void prefetch_q_lds(QStage<D>& st, const uint16_t* qrow, bool ok) {
@@ -324,7 +332,8 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
   const int lrow = w * 32 + (lane & 31);
   int staged = -1;  // bucket whose single key tile sits in LDS
 
-  int4 rec = p.items[it_begin];
+  const const_int_ptr items = (const_int_ptr)p.items;
+  int4 rec = load_item(items, it_begin);
   GRow g = grow_of(p, rec, entry_of(p, rec, lrow), lrow);
   bf16x8 qf[D / 16];
   load_qf<D>(q_row<D>(p, rec, g), g.valid, qf);
@@ -342,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
     // next item: its record, and its entry word -- a workgroup's items cover
     // one contiguous run of entries, so the next item starts right after this
     // one's entries (read speculatively; the entries array is padded)
-    const int4 rec_n = has_next ? p.items[it + 1] : rec;
+    const int4 rec_n = has_next ? load_item(items, it + 1) : rec;
     const uint32_t ent_n =
         has_next ? p.entries[rec.y + ((rec.z + (1 << p.lgR) - 1) >> p.lgR) + (lrow >> p.lgR)] : 0u;
     GRow g_n = g;

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(64) void decode_union_kernel(DecodeAttnParams p) {
 // chose the block, softmax over its keys, weighted sum of its values.
 template <int D, int NH>
 __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeAttnParams p) {
-  constexpr int KC = 128;  // keys per pass
+  constexpr int KC = 64;  // keys per pass (a small pass keeps registers low: 4 waves per SIMD)
   constexpr int CH = D / 8;
   constexpr int KG = 256 / CH;  // key groups in the value pass
   __shared__ float s_q[8][D];
@@ -352,13 +352,14 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeAttnParams p) 
     __syncthreads();
     // softmax statistics per head (wave a handles heads a, a+4)
     for (int a = w; a < nh; a += 4) {
-      const float x0 = s_s[a][lane], x1 = s_s[a][lane + 64];
+      const float x0 = lane < KC ? s_s[a][lane] : -INFINITY;
+      const float x1 = KC > 64 ? s_s[a][(lane + 64) % KC] : -INFINITY;
       const float mx = wave_max(fmaxf(x0, x1));
       const float mold = s_m[a];
       const float mnew = fmaxf(mold, mx);
       const float e0 = exp2f(x0 - mnew), e1 = exp2f(x1 - mnew);
-      s_s[a][lane] = e0;
-      s_s[a][lane + 64] = e1;
+      if (lane < KC) s_s[a][lane] = e0;
+      if (KC > 64) s_s[a][(lane + 64) % KC] = e1;
       const float sum = wave_sum(e0 + e1);
       if (lane == 0) {
         const float c = exp2f(mold - mnew);

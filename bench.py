@@ -68,6 +68,79 @@ def make_decode_inputs(m):
     return q, kc, vc, pooled
 
 
+MOBA = dict(B=1, L=32768, Hq=32, Hkv=8, D=128, block=512, topk=3, sigma=128 ** -0.5)
+MEMORY = dict(Lk=10_000_000, docs=2000, doc_mean=5000.0, doc_sigma=0.8, Lq=512, Hq=32, Hkv=8, D=128, block=64,
+              topk=64)
+
+
+def causal_pairs(L, bs, k):
+    """(query, key) pairs a causal top-k + own-block prefill attends per head."""
+    n = 0
+    for t in range(L):
+        cur = t // bs
+        n += min(k, cur) * bs + (t - cur * bs + 1)
+    return n
+
+
+def time_call(fn, reps):
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def other_workloads(m, reps):
+    """Times the MoBA-style 32K prefill and the 10M-token memory-bank prefill
+    (reported beside the benchmark step, not part of it)."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    t = synth.TID
+    out = {}
+    c = MOBA
+    q = synth.device_tensor((c["B"], c["L"], c["Hq"], c["D"]), c["sigma"], SEED, t["q"], "bf16")
+    k = synth.device_tensor((c["B"], c["L"], c["Hkv"], c["D"]), c["sigma"], SEED, t["k"], "bf16")
+    v = synth.device_tensor((c["B"], c["L"], c["Hkv"], c["D"]), c["sigma"], SEED, t["v"], "bf16")
+    o = torch.empty_like(q)
+    ws = torch.empty(m.prefill_workspace_bytes(q, k, block=c["block"], topk=c["topk"], causal=True),
+                     dtype=torch.uint8, device="cuda")
+    ms = time_call(lambda: m.sparse_attn_prefill(q, k, v, c["block"], c["topk"], True, out=o, workspace=ws), reps)
+    flops = 4.0 * c["D"] * c["Hq"] * causal_pairs(c["L"], c["block"], c["topk"])
+    out["moba_32k_prefill"] = {"ms": round(ms, 4), "tokens_per_s": round(c["L"] / (ms * 1e-3), 1),
+                               "attended_tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+    _log(f"MoBA-style 32K prefill: {ms:.3f} ms")
+    del q, k, v, o, ws
+    c = MEMORY
+    ids = synth.doc_ids_from_lengths(synth.doc_lengths(c["Lk"], c["docs"], c["doc_mean"], c["doc_sigma"], SEED))
+    dk = torch.from_numpy(ids[None]).cuda()
+    dq = torch.zeros((1, c["Lq"]), dtype=torch.int32, device="cuda")
+    q = synth.device_tensor((1, c["Lq"], c["Hq"], c["D"]), 1.0, SEED, t["q"], "bf16")
+    k = synth.device_tensor((1, c["Lk"], c["Hkv"], c["D"]), 1.0, SEED, t["k"], "bf16")
+    v = synth.device_tensor((1, c["Lk"], c["Hkv"], c["D"]), 1.0, SEED, t["v"], "bf16")
+    ms_sum = time_call(lambda: m.block_summary(k, c["block"], doc_ids=dk), reps)
+    pooled = m.block_summary(k, c["block"], doc_ids=dk)  # the memory's stored routing keys
+    o = torch.empty_like(q)
+    kw = dict(doc_ids_q=dq, doc_ids_k=dk, pooled=pooled)
+    ws = torch.empty(m.prefill_workspace_bytes(q, k, block=c["block"], topk=c["topk"], causal=False, **kw),
+                     dtype=torch.uint8, device="cuda")
+    ms = time_call(lambda: m.sparse_attn_prefill(q, k, v, c["block"], c["topk"], False, out=o, workspace=ws, **kw),
+                   reps)
+    out["memory_10m_summary"] = {"ms": round(ms_sum, 4),
+                                 "read_gbs": round(2 * c["Lk"] * c["Hkv"] * c["D"] / (ms_sum * 1e-3) / 1e9, 1)}
+    out["memory_10m_query_chunk"] = {"ms": round(ms, 4), "query_tokens_per_s": round(c["Lq"] / (ms * 1e-3), 1)}
+    _log(f"memory bank: summaries {ms_sum:.3f} ms, 512-token query chunk {ms:.3f} ms")
+    return out
+
+
 def prefill_pairs():
     """Exact attended (query, key) pair counts of the prefill workload:
     (pairs in gate-chosen blocks, pairs in own blocks)."""
@@ -218,6 +291,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--also", action="store_true",
+                    help="also time the MoBA-style 32K prefill and the 10M-token memory bank (extra field)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run an elementwise negation over MIB MiB (read once, written once) -- the "
                          "known-size kernel that scales the HBM byte counters -- and exit")
@@ -336,6 +411,12 @@ def main():
         _log("timing the float64 oracle on a sample of the prefill (CPU)")
         cpu = cpu_baseline(q, k, v, iq, ik, args.cpu_budget)
 
+    others = None
+    if args.also:
+        del q, k, v, iq, ik, o, pws, dq, kc, vc, pooled, dws
+        torch.cuda.empty_cache()
+        others = other_workloads(m, max(1, args.steps))
+
     out = {
         "metric": "block-sparse attn prefill tokens/s + MFMA TFLOP/s at 128K; decode HBM GB/s",
         "value": round(value, 1),
@@ -372,6 +453,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if others is not None:
+        out["other_workloads"] = others
     print(json.dumps(out), flush=True)
 
 

@@ -205,6 +205,57 @@ BSA_DEV void group_sort64_desc(uint64_t (&v)[4], int lane) {
   }
 }
 
+// 32-bit value held by lane (li ^ m) of the same 16-lane row, m in {1, 2, 4, 8}
+BSA_DEV int row_xor32_any(int v, int m, int li) {
+  const uint32_t u = (uint32_t)v;
+  switch (m) {
+    case 1: return (int)dpp32<0xB1>(u, u);
+    case 2: return (int)dpp32<0x4E>(u, u);
+    case 4: {
+      // both exchanges run on every lane (a lane must not read a lane that a
+      // branch has switched off), then each lane keeps its partner's value
+      const uint32_t up = dpp32<0x104>(u, u), dn = dpp32<0x114>(u, u);
+      return (int)((li & 4) ? dn : up);
+    }
+    default: return (int)dpp32<0x128>(u, u);
+  }
+}
+
+// Ascending bitonic sort of the 16*NR ints a 16-lane group holds (element
+// e = 16*r + lane%16 in register r); every group sorts its own row.
+template <int NR>
+BSA_DEV void group_sort_asc(int (&v)[NR], int li) {
+#pragma unroll
+  for (int size = 2; size <= 16 * NR; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= 16) {
+        const int rs = stride >> 4;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const int q = r ^ rs;
+          if (q > r) {
+            const bool asc = ((r * 16 + li) & size) == 0;
+            const int a = v[r], b = v[q];
+            const bool sw = asc ? (a > b) : (a < b);
+            v[r] = sw ? b : a;
+            v[q] = sw ? a : b;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const int o = row_xor32_any(v[r], stride, li);
+          const bool lower = (li & stride) == 0;
+          const bool asc = ((r * 16 + li) & size) == 0;
+          const int mn = v[r] < o ? v[r] : o, mx = v[r] < o ? o : v[r];
+          v[r] = (lower == asc) ? mn : mx;
+        }
+      }
+    }
+  }
+}
+
 // k-th best key of the row held by this lane's group (0 while fewer than k)
 template <int KR>
 BSA_DEV uint64_t list_kth(const uint64_t (&L)[KR], int lane, int topk) {
@@ -217,15 +268,14 @@ BSA_DEV uint64_t list_kth(const uint64_t (&L)[KR], int lane, int topk) {
 }
 
 template <int W, int DG, int KR, int QK, bool LO>
-__global__ __launch_bounds__(64 * W, 4) void gate_kernel(GateParams p) {
+__global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParams p) {
   constexpr int ROWS = 16 * W;
   constexpr int PADR = DG + 8;  // padded LDS row (bf16 elements)
   constexpr int KS = DG / 32;
   constexpr int CPR = DG / 8;                       // 16-byte chunks per summary row
   constexpr int NPF = (64 * CPR + 64 * W - 1) / (64 * W);  // chunks per thread per plane
   constexpr int STAGE_BYTES = (LO ? 2 : 1) * 64 * PADR * 2;
-  constexpr int EMIT_BYTES = W * 16 * 64 * 8;
-  constexpr int SMEM = STAGE_BYTES > EMIT_BYTES ? STAGE_BYTES : EMIT_BYTES;
+  constexpr int SMEM = STAGE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   uint16_t* s_hi = reinterpret_cast<uint16_t*>(smem);
   uint16_t* s_lo = s_hi + 64 * PADR;
@@ -363,23 +413,45 @@ __global__ __launch_bounds__(64 * W, 4) void gate_kernel(GateParams p) {
       }
     }
   }
-  // emit: each wave writes its 16 rows' lists to LDS, then finishes them row by row
-  __syncthreads();
-  uint64_t* s_emit = reinterpret_cast<uint64_t*>(smem) + w * 16 * 64;
+  // emit: each lane group finishes its four rows from registers -- chosen
+  // block ids sorted ascending inside the group, the forced block after them
+  constexpr int NR = KR == 1 ? 1 : (KR == 2 ? 2 : 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int row = rbase + 4 * kh + i;
+    const bool row_ok = row < p.rows_per_bh;
+    int cnt = 0;
 #pragma unroll
-    for (int m = 0; m < KR; ++m) s_emit[(4 * kh + i) * 64 + m * 16 + r16] = L[i][m];
-  __syncthreads();
-  for (int r = 0; r < 16; ++r) {
-    const int row = rbase + r;
-    if (row >= p.rows_per_bh) break;
-    const uint64_t* buf = s_emit + r * 64;
-    const bool has = lane < p.topk && lane < KR * 16 && buf[lane] != 0ull;
-    const int cnt = __popcll(__ballot(has));
-    const RowInfo ri = row_to_th(row, p);
+    for (int m = 0; m < KR; ++m) {
+      const bool valid = m * 16 + r16 < p.topk && L[i][m] != 0ull;
+      cnt += __popc((uint32_t)(__ballot(valid) >> (16 * kh)) & 0xFFFFu);
+    }
+    const RowInfo ri = row_to_th(row_ok ? row : 0, p);
     const int hs = p.per_group ? hk : hk * p.G + ri.hh;
-    emit_row<1>(p, buf, cnt, b, hs, ri.t, split);
+    const int64_t srow = ((int64_t)b * p.Hs + hs) * p.Lq + ri.t;
+    if (p.nsplit == 1) {
+      int idx[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        idx[r] = (r < KR && r * 16 + r16 < cnt) ? (int)key_index(L[i][r < KR ? r : 0]) : 0x7FFFFFFF;
+      group_sort_asc<NR>(idx, r16);
+      if (row_ok) {
+        int32_t* out = p.sel + srow * p.sel_w;
+        const int cur = p.causal ? (int)(qpos_of(p, b, ri.t) / p.block) : -1;
+#pragma unroll
+        for (int r = 0; r <= NR; ++r) {
+          const int e = r * 16 + r16;
+          if (e < p.sel_w) out[e] = e < cnt ? idx[r < NR ? r : 0] : (e == cnt && p.causal ? cur : -1);
+        }
+      }
+    } else if (row_ok) {
+      uint64_t* out = p.part + (srow * p.nsplit + split) * p.topk;
+#pragma unroll
+      for (int m = 0; m < KR; ++m) {
+        const int e = m * 16 + r16;
+        if (e < p.topk) out[e] = e < cnt ? L[i][m] : 0ull;
+      }
+    }
   }
 }
 

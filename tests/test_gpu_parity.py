@@ -235,6 +235,25 @@ def test_decode_topk60_group_of_8(bsa):
     assert_close(to_np(lse), ref["lse"], 5e-3, None, what="lse")
 
 
+def test_prerotated_keys_equal_internal_rotation(bsa):
+    """A memory stored with its keys already rotated (the block summary's k_rot output) gives the
+    same attention as rotating them inside the call."""
+    B, Lq, Lk, Hq, Hkv, D, block, topk = 1, 96, 9000, 8, 2, 128, 64, 8
+    _say("case pre-rotated keys vs in-call doc-RoPE")
+    q = synth.host_tensor((B, Lq, Hq, D), 1.0, 19, 0, "bf16").cuda()
+    k = synth.host_tensor((B, Lk, Hkv, D), 1.0, 19, 1, "bf16").cuda()
+    v = synth.host_tensor((B, Lk, Hkv, D), 1.0, 19, 2, "bf16").cuda()
+    dk = torch.from_numpy(synth.random_doc_ids(Lk, 700.0, 19)[None]).cuda()
+    dq = torch.zeros((B, Lq), dtype=torch.int32, device="cuda")
+    pooled, k_rot = bsa.block_summary(k, block, doc_ids=dk, return_k_rot=True)
+    o1, s1 = bsa.sparse_attn_prefill(q, k, v, block, topk, False, doc_ids_q=dq, doc_ids_k=dk, pooled=pooled,
+                                     return_sel=True)
+    o2, s2 = bsa.sparse_attn_prefill(q, k_rot, v, block, topk, False, doc_ids_q=dq, pooled=pooled, return_sel=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 def test_deterministic_bitwise(bsa):
     B, L, Hq, Hkv, D = 1, 4096, 8, 2, 128
     _say("case determinism L4096 H8/2 block128 topk4")

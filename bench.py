@@ -5,7 +5,8 @@ A step is one pass of the whole path over one batch of synthetic input:
     tokens, 64 query heads / 8 KV heads, head dim 128, block 64, index q/k of
     dim 64, gate scores summed over each group's 8 heads, top-16 blocks per
     group plus the own block, causal, bf16 N(0,1);
-  * decode -- 16 sequences x 1 new token over 1,048,576-token caches,
+  * decode -- 16 sequences x 1 new token over 1,048,576-token caches
+    (stored head-major),
     32/8 heads, head dim 128, block 128, bf16 routing keys (8192 blocks)
     precomputed once by the library's block summary, top-32 per query head
     plus the own block, bf16 N(0,1).
@@ -60,8 +61,10 @@ def make_decode_inputs(m):
     t = synth.TID
     # distinct seed stream from the prefill inputs
     q = synth.device_tensor((c["B"], c["Hq"], c["D"]), c["sigma"], SEED + 1, t["q"], "bf16")
-    kc = synth.device_tensor((c["B"], c["Lc"], c["Hkv"], c["D"]), c["sigma"], SEED + 1, t["k"], "bf16")
-    vc = synth.device_tensor((c["B"], c["Lc"], c["Hkv"], c["D"]), c["sigma"], SEED + 1, t["v"], "bf16")
+    # caches stored head-major ([B, Hkv, Lc, D], passed as [B, Lc, Hkv, D]
+    # views): a block of one KV head is then 32 contiguous KB in HBM
+    kc = synth.device_tensor((c["B"], c["Hkv"], c["Lc"], c["D"]), c["sigma"], SEED + 1, t["k"], "bf16").transpose(1, 2)
+    vc = synth.device_tensor((c["B"], c["Hkv"], c["Lc"], c["D"]), c["sigma"], SEED + 1, t["v"], "bf16").transpose(1, 2)
     import torch
 
     pooled = m.block_summary(kc, c["block"], out_dtype=torch.bfloat16)  # routing keys, computed once
@@ -436,8 +439,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "128K MiniMax-style prefill (B1 L131072 H64/8 D128 block64 index-dim64 group-summed "
-                        "top16+own causal) + decode (B16 x 1 token, 1,048,576-token caches, H32/8 D128 block128 "
-                        "top32+own)",
+                        "top16+own causal) + decode (B16 x 1 token, 1,048,576-token head-major caches, H32/8 D128 "
+                        "block128 top32+own)",
             "global_batch": c["B"],
             "seq_len": c["L"],
             "parallelism": "single GPU",

@@ -254,6 +254,38 @@ def test_prerotated_keys_equal_internal_rotation(bsa):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+def test_decode_head_major_cache(bsa):
+    """Caches stored head-major ([B, Hkv, Lc, D]) and passed as strided [B, Lc, Hkv, D] views."""
+    B, Hq, Hkv, Lc, D, block, topk = 2, 8, 2, 3000, 128, 128, 6
+    _say("case decode head-major caches B2 H8/2 Lc3000 block128 topk6")
+    q = synth.host_tensor((B, Hq, D), 1.0, 20, 0, "bf16")
+    k = synth.host_tensor((B, Lc, Hkv, D), 1.0, 20, 1, "bf16")
+    v = synth.host_tensor((B, Lc, Hkv, D), 1.0, 20, 2, "bf16")
+    kd = k.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    vd = v.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    assert not kd.is_contiguous()
+    lens = np.array([3000, 1777], dtype=np.int32)
+    pooled = bsa.block_summary(kd, block, out_dtype=torch.bfloat16)  # checked against the oracle below
+    ref_pool = oracle.block_pool(k, block)
+    got_pool = pooled.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got_pool - ref_pool) <= np.abs(ref_pool) * 2.0 ** -8 + 1e-7)
+    ph = torch.from_numpy(ref_pool).to(torch.bfloat16)  # the oracle's own routing keys, rounded like the input
+    o, sel, lse = bsa.sparse_attn_decode(q.cuda(), kd, vd, ph.cuda(), topk, block,
+                                         cache_lens=torch.from_numpy(lens).cuda(), return_sel=True, return_lse=True)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q, k, v, ph, block=block, topk=topk, cache_lens=lens, return_scores=True)
+    nb = ph.shape[1]
+    scores = np.full((B, Hq, 1, nb), np.nan)
+    for (b, hs), sc in ref["scores"].items():
+        scores[b, hs, 0, : len(sc)] = sc
+    gsel = sel.cpu().numpy()[:, :, None]
+    diff = check_selection(gsel, ref["sel"][:, :, None], scores, topk, True)
+    if diff:
+        ref = oracle.decode(q, k, v, ph, block=block, topk=topk, cache_lens=lens, force_sel=gsel[:, :, 0])
+    assert_close(to_np(o), ref["o"], 1e-2, 1e-2, bf16_storage=True)
+    assert_close(to_np(lse), ref["lse"], 5e-3, None, what="lse")
+
+
 def test_deterministic_bitwise(bsa):
     B, L, Hq, Hkv, D = 1, 4096, 8, 2, 128
     _say("case determinism L4096 H8/2 block128 topk4")

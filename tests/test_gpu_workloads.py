@@ -157,8 +157,9 @@ def test_decode_1m_cache_fullsize(bsa):
     nb = Lc // block
     _say("case decode B16 Lc1048576 H32/8 D128 block128 topk32 (68.7 GB of cache)")
     q = synth.device_tensor((B, Hq, D), 1.0, SEED + 1, T["q"], "bf16")
-    kc = synth.device_tensor((B, Lc, Hkv, D), 1.0, SEED + 1, T["k"], "bf16")
-    vc = synth.device_tensor((B, Lc, Hkv, D), 1.0, SEED + 1, T["v"], "bf16")
+    # head-major caches as the benchmark stores them, seen as [B, Lc, Hkv, D]
+    kc = synth.device_tensor((B, Hkv, Lc, D), 1.0, SEED + 1, T["k"], "bf16").transpose(1, 2)
+    vc = synth.device_tensor((B, Hkv, Lc, D), 1.0, SEED + 1, T["v"], "bf16").transpose(1, 2)
     pooled = synth.device_tensor((B, nb, Hkv, D), 128 ** -0.5, SEED + 1, T["pooled"], "bf16")
     _decode_check(bsa, q, kc, vc, pooled, topk, block, None)
     lens = np.array([1, 2, 127, 128, 129, 256, 257, 33 * 128, 33 * 128 + 1, 500_000, 777_777,
@@ -186,11 +187,11 @@ def _check_summary_blocks(got, k, block, blocks, pos=None, bf16_out=False, atol=
 
 
 def test_block_summary_1m_cache_fullsize(bsa):
-    """The routing keys of the decode caches: bf16 block means of 16 x 1,048,576 keys, block 128,
-    sampled blocks of every sequence against the oracle."""
+    """The routing keys of the decode caches (head-major, as the benchmark stores them): bf16 block
+    means of 16 x 1,048,576 keys, block 128, sampled blocks of every sequence against the oracle."""
     B, Lc, Hkv, D, block = 16, 1 << 20, 8, 128, 128
     _say("case block_summary B16 L1048576 H8 D128 block128 bf16 out")
-    kc = synth.device_tensor((B, Lc, Hkv, D), 1.0, SEED + 1, T["k"], "bf16")
+    kc = synth.device_tensor((B, Hkv, Lc, D), 1.0, SEED + 1, T["k"], "bf16").transpose(1, 2)
     pooled = bsa.block_summary(kc, block, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     nb = Lc // block

@@ -216,7 +216,7 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
   P.nbk = a->B * a->Hkv * P.NC * P.Nb;
   P.max_entries = P.nsel_rows * (P.topk + (a->causal ? 1 : 0));
   if (P.per_group && (128 % P.G) != 0) return fail(BSA_ERR_UNSUPPORTED, "per-group gating needs G dividing 128");
-  const int rows_item = 128;
+  const int rows_item = 32 * gather_waves(a->block);
   P.max_items = (P.max_entries * P.R + rows_item - 1) / rows_item + std::min<int64_t>(P.nbk, P.max_entries);
   // gate geometry
   P.rows_per_bh = P.per_group ? a->Lq : a->Lq * P.G;
@@ -421,6 +421,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
   ap.entries = P.entries; ap.bucket_off = P.bucket_off; ap.tile_off = P.tile_off; ap.items = P.items;
   ap.NC = P.NC; ap.CT = P.CT;
   ap.grid = P.attn_grid;
+  ap.rows_item = 32 * gather_waves(a->block);
   ap.part_o = P.part_o; ap.part_ml = P.part_ml;
   ap.sel = P.sel; ap.sel_w = P.sel_w;
   ap.o = reinterpret_cast<uint16_t*>(a->o); ap.os_b = a->o_stride[0]; ap.os_t = a->o_stride[1]; ap.os_h = a->o_stride[2];
@@ -430,7 +431,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
     cp.B = a->B; cp.Lq = a->Lq; cp.Lk = a->Lk; cp.Hkv = a->Hkv; cp.G = P.G; cp.Hs = P.Hs; cp.per_group = P.per_group;
     cp.Nb = P.Nb; cp.block = a->block; cp.causal = a->causal;
     cp.Gs = P.Gs; cp.NC = P.NC; cp.CT = P.CT;
-    cp.sel = P.sel; cp.sel_w = P.sel_w; cp.kslot = P.kslot; cp.R = P.R; cp.rows_item = 128;
+    cp.sel = P.sel; cp.sel_w = P.sel_w; cp.kslot = P.kslot; cp.R = P.R; cp.rows_item = 32 * gather_waves(a->block);
     cp.sh_h = P.sh_h; cp.sh_t = P.sh_t;
     cp.counts = P.counts; cp.cursor = P.cursor; cp.bucket_off = P.bucket_off; cp.tile_off = P.tile_off;
     cp.scan_tmp = P.scan_tmp; cp.entries = P.entries; cp.items = P.items; cp.nbk = P.nbk;

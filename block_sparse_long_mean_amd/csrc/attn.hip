@@ -47,14 +47,14 @@ struct AttnSmem {
 //    writes lane l's data at the wave's LDS base + 16*l);
 //  * the finished partial outputs, row-major with rows padded by 8 bytes, so
 //    that every global store instruction writes whole 256-byte rows.
-template <int D>
+template <int D, int W>
 struct QStage {
   static constexpr int QELEMS = (D / 16) * 64 * 8;
   static constexpr int RS = D + 4;  // padded output row (bf16 elements)
   static constexpr int OELEMS = 32 * RS;
   static constexpr int ELEMS = QELEMS > OELEMS ? QELEMS : OELEMS;
-  uint16_t buf[4][ELEMS];
-  int64_t dst[4][32];  // destination element offset of each of the wave's 32 rows
+  uint16_t buf[W][ELEMS];
+  int64_t dst[W][32];  // destination element offset of each of the wave's 32 rows
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -67,8 +67,8 @@ BSA_DEV int4 load_item(const_int_ptr items, int i) {
   return make_int4(items[4 * i], items[4 * i + 1], items[4 * i + 2], items[4 * i + 3]);
 }
 
-template <int D>
-BSA_DEV void prefetch_q_lds(QStage<D>& st, const uint16_t* qrow, bool ok) {
+template <int D, int W>
+BSA_DEV void prefetch_q_lds(QStage<D, W>& st, const uint16_t* qrow, bool ok) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane_id() >> 5;
   if (ok) {
@@ -81,8 +81,8 @@ BSA_DEV void prefetch_q_lds(QStage<D>& st, const uint16_t* qrow, bool ok) {
 
 // Rows past the item's end read whatever the staging area holds; their
 // result columns are never stored.
-template <int D>
-BSA_DEV void read_q_lds(const QStage<D>& st, bf16x8 (&qf)[D / 16]) {
+template <int D, int W>
+BSA_DEV void read_q_lds(const QStage<D, W>& st, bf16x8 (&qf)[D / 16]) {
   const int w = threadIdx.x >> 6, l = lane_id();
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) qf[s] = as_bf(*reinterpret_cast<const u16x8*>(&st.buf[w][(s * 64 + l) * 8]));
@@ -104,11 +104,11 @@ BSA_DEV void pack_partials(const f32x16 (&o)[D / 32], u16x4_t (&pk)[D / 8]) {
                                 f2bf(o[dt][4 * gg + 3])};
 }
 
-template <int D>
-BSA_DEV void store_partials(QStage<D>& st, const u16x4_t (&pk)[D / 8], int64_t dst_mine, int nvalid,
+template <int D, int W>
+BSA_DEV void store_partials(QStage<D, W>& st, const u16x4_t (&pk)[D / 8], int64_t dst_mine, int nvalid,
                             uint16_t* part_o) {
   const int w = threadIdx.x >> 6, lane = lane_id(), r = lane & 31, h = lane >> 5;
-  constexpr int RS = QStage<D>::RS;
+  constexpr int RS = QStage<D, W>::RS;
   uint16_t* sb = st.buf[w];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -134,12 +134,12 @@ BSA_DEV void store_partials(QStage<D>& st, const u16x4_t (&pk)[D / 8], int64_t d
 
 // Stage keys [key0, key0 + KT) of one kv head (zero past n_valid) into LDS:
 // K row-major, V transposed.
-template <int D>
+template <int D, int NT>
 BSA_DEV void stage_kv(AttnSmem<D>& sm, const uint16_t* kb, int64_t ks_t, const uint16_t* vb, int64_t vs_t,
                       int key0, int n_valid) {
   const int tid = threadIdx.x;
   constexpr int CH = D / 8;
-  for (int idx = tid; idx < KT * CH; idx += 256) {
+  for (int idx = tid; idx < KT * CH; idx += NT) {
     const int kr = idx / CH, ch = idx % CH;
     u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
     if (kr < n_valid) x = ld16(kb + (int64_t)(key0 + kr) * ks_t + ch * 8);
@@ -148,7 +148,7 @@ BSA_DEV void stage_kv(AttnSmem<D>& sm, const uint16_t* kb, int64_t ks_t, const u
   // V: a thread takes 4 consecutive keys x 8 head dims and writes them
   // transposed; consecutive lanes take consecutive key quads so that their
   // LDS writes of one V^T row are contiguous
-  for (int idx = tid; idx < (KT / 4) * CH; idx += 256) {
+  for (int idx = tid; idx < (KT / 4) * CH; idx += NT) {
     const int kq = idx % (KT / 4), ch = idx / (KT / 4);
     u16x8 r[4];
 #pragma unroll
@@ -310,10 +310,10 @@ BSA_DEV const uint16_t* q_row(const AttnParams& p, int4 rec, const GRow& g) {
 // record and entry word are loaded at the top of the current item, and its
 // queries are staged global -> LDS after the current item's first score
 // tile, to be read back once the current item's last PV tile is issued.
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
+template <int D, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
-  __shared__ __attribute__((aligned(16))) QStage<D> qst;
+  __shared__ __attribute__((aligned(16))) QStage<D, W> qst;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hq = lane >> 5;
   // work items of this launch's chunks (buckets c0*Nb .. c1*Nb)
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
       const bool single = n_keys <= KT;
       if (!(single && staged == bucket)) {
         __syncthreads();
-        stage_kv<D>(sm, kb, p.ks_t, vb, p.vs_t, key0 + kt0, n_keys - kt0);
+        stage_kv<D, 64 * W>(sm, kb, p.ks_t, vb, p.vs_t, key0 + kt0, n_keys - kt0);
         __syncthreads();
         staged = single ? bucket : -1;
       }
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
         // queries of the next item into this wave's LDS staging area
         g_n = grow_of(p, rec_n, ent_n, lrow);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the staging area are done
-        prefetch_q_lds<D>(qst, q_row<D>(p, rec_n, g_n), g_n.valid);
+        prefetch_q_lds<D, W>(qst, q_row<D>(p, rec_n, g_n), g_n.valid);
       }
       if (wave_on) {
         // mask only where a key can be past the end or after the query
@@ -405,14 +405,14 @@ __global__ __launch_bounds__(256, 2) void attn_gather_kernel(AttnParams p) {
       __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_wave_barrier();
       asm volatile("" ::: "memory");
-      read_q_lds<D>(qst, qf);
+      read_q_lds<D, W>(qst, qf);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     {
       const int hsel = p.per_group ? 0 : g.hs - hk * p.G;
       const int64_t prow = (prow_base + hsel) * p.CT + (g.t - t_base);
       const int64_t pidx = (prow * p.kslot + g.slot) * p.R + g.rr;
-      if (wave_on) store_partials<D>(qst, pk, pidx * D, min(32, rec.z - w * 32), p.part_o);
+      if (wave_on) store_partials<D, W>(qst, pk, pidx * D, min(32, rec.z - w * 32), p.part_o);
       if (g.valid && hq == 0) {
         __builtin_nontemporal_store(m, &p.part_ml[pidx].x);
         __builtin_nontemporal_store(l, &p.part_ml[pidx].y);
@@ -511,25 +511,35 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 
 // Persistent grid = the workgroups the device holds at once (a multiple of 8,
 // one range per XCD).
-template <int D>
+template <int D, int W>
 static int gather_grid() {
   static int cached = 0;
   if (cached) return cached;
   int dev = 0, cus = 0, per = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, attn_gather_kernel<D>, 256, 0) != hipSuccess || per < 1)
-    return 2048;
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, attn_gather_kernel<D, W>, 64 * W, 0) != hipSuccess || per < 1)
+    return 2048 / W;
   cached = ((cus * per + 7) / 8) * 8;
   return cached;
 }
 
+// Work items hold 32 * gather_waves rows: 4 waves for blocks of one 64-key
+// tile (a workgroup keeps the tile staged across consecutive items of the
+// same block), 8 waves for longer blocks (every item re-stages the block's
+// tiles, so a larger item stages them for twice the rows).
+int gather_waves(int block) { return block > KT ? 8 : 4; }
+
 bool launch_attn_gather(const AttnParams& p, hipStream_t s) {
   {
     LaunchScope ls("attn_gather", s, 2);
-    if (p.D == 128)
-      hipLaunchKernelGGL(attn_gather_kernel<128>, dim3(gather_grid<128>()), dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL(attn_gather_kernel<64>, dim3(gather_grid<64>()), dim3(256), 0, s, p);
+    const int W = p.rows_item / 32;
+    if (p.D == 128) {
+      if (W == 8) hipLaunchKernelGGL((attn_gather_kernel<128, 8>), dim3(gather_grid<128, 8>()), dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((attn_gather_kernel<128, 4>), dim3(gather_grid<128, 4>()), dim3(256), 0, s, p);
+    } else {
+      if (W == 8) hipLaunchKernelGGL((attn_gather_kernel<64, 8>), dim3(gather_grid<64, 8>()), dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((attn_gather_kernel<64, 4>), dim3(gather_grid<64, 4>()), dim3(256), 0, s, p);
+    }
   }
   return launch_ok("attn_gather");
 }

@@ -136,6 +136,7 @@ struct AttnParams {
   int NC, CT;              // query chunks per (b, kv head), tokens per chunk
   int c0, c1;              // chunk ids of this launch; its partial buffer holds c1 - c0 chunks
   int grid;                // persistent workgroups
+  int rows_item;           // rows per work item: 32 per wave of a gather workgroup
   // partials of the launch's chunks, row ((c - c0) * Gs + head-sel) * CT + token-in-chunk
   uint16_t* part_o;        // [rows * kslot * R, D] bf16, sum_k p_k v_k with p = 2^(s*sl2 - m)
   float2* part_ml;         // (m, l): log2-domain running max and sum of p
@@ -146,6 +147,7 @@ struct AttnParams {
   int64_t os_b, os_t, os_h;
   float* lse_out;  // natural log, [B, Hq, Lq] or null
 };
+int gather_waves(int block);  // waves per gather workgroup for this block size
 bool launch_attn_gather(const AttnParams& p, hipStream_t s);
 bool launch_attn_merge(const AttnParams& p, hipStream_t s);
 

@@ -60,6 +60,7 @@ class PrefillArgs(ctypes.Structure):
         ("sel_out", VP),
         ("lse_out", VP),
         ("chunk_tokens", ctypes.c_int32),
+        ("chunks_per_pass", ctypes.c_int32),
     ]
 
 
@@ -203,7 +204,7 @@ def _doc(d, B, L, device):
 
 
 def _prefill_args(q, k, v, o, *, block, topk, causal, gate, index_q, index_k, doc_ids_q, doc_ids_k,
-                  rope_theta, scale, pooled, sel, lse, chunk_tokens=0):
+                  rope_theta, scale, pooled, sel, lse, chunk_tokens=0, chunks_per_pass=0):
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     a = PrefillArgs()
@@ -229,6 +230,7 @@ def _prefill_args(q, k, v, o, *, block, topk, causal, gate, index_q, index_k, do
     a.sel_out = _ptr(sel)
     a.lse_out = _ptr(lse)
     a.chunk_tokens = int(chunk_tokens)
+    a.chunks_per_pass = int(chunks_per_pass)
     return a
 
 
@@ -237,12 +239,14 @@ def _prefill_args(q, k, v, o, *, block, topk, causal, gate, index_q, index_k, do
 # --------------------------------------------------------------------------
 
 def prefill_workspace_bytes(q, k, *, block, topk, causal=True, gate="head", index_q=None, index_k=None,
-                            doc_ids_q=None, doc_ids_k=None, pooled=None, chunk_tokens: int = 0) -> int:
+                            doc_ids_q=None, doc_ids_k=None, pooled=None, chunk_tokens: int = 0,
+                            chunks_per_pass: int = 0) -> int:
     dq = _doc(doc_ids_q, q.shape[0], q.shape[1], q.device)
     dk = _doc(doc_ids_k, k.shape[0], k.shape[1], k.device)
     a = _prefill_args(q, k, k, q, block=block, topk=topk, causal=causal, gate=gate, index_q=index_q,
                       index_k=index_k, doc_ids_q=dq, doc_ids_k=dk, rope_theta=10000.0, scale=None,
-                      pooled=pooled, sel=None, lse=None, chunk_tokens=chunk_tokens)
+                      pooled=pooled, sel=None, lse=None, chunk_tokens=chunk_tokens,
+                      chunks_per_pass=chunks_per_pass)
     n = lib().bsa_prefill_workspace_bytes(ctypes.byref(a))
     if n == 0:
         raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())
@@ -252,7 +256,8 @@ def prefill_workspace_bytes(q, k, *, block, topk, causal=True, gate="head", inde
 def sparse_attn_prefill(q, k, v, block: int, topk: int, causal: bool = True, doc_ids=None, *, gate: str = "head",
                         index_q=None, index_k=None, doc_ids_q=None, doc_ids_k=None, rope_theta: float = 10000.0,
                         scale: float | None = None, pooled=None, return_sel: bool = False,
-                        return_lse: bool = False, out=None, workspace=None, stream=None, chunk_tokens: int = 0):
+                        return_lse: bool = False, out=None, workspace=None, stream=None, chunk_tokens: int = 0,
+                        chunks_per_pass: int = 0):
     """Block-sparse attention prefill (see include/bsa.h for the semantics).
 
     q [B, Lq, Hq, D], k/v [B, Lk, Hkv, D] device tensors (bf16 or fp32).
@@ -273,7 +278,7 @@ def sparse_attn_prefill(q, k, v, block: int, topk: int, causal: bool = True, doc
     dk = _doc(doc_ids_k, B, Lk, k.device)
     a = _prefill_args(q, k, v, o, block=block, topk=topk, causal=causal, gate=gate, index_q=index_q, index_k=index_k,
                       doc_ids_q=dq, doc_ids_k=dk, rope_theta=rope_theta, scale=scale, pooled=pooled, sel=sel, lse=lse,
-                      chunk_tokens=chunk_tokens)
+                      chunk_tokens=chunk_tokens, chunks_per_pass=chunks_per_pass)
     n = lib().bsa_prefill_workspace_bytes(ctypes.byref(a))
     if n == 0:
         raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())

@@ -121,6 +121,12 @@ struct PrefillPlan {
   size_t bytes;
 };
 
+// consecutive work items a gather workgroup takes at a time (runs are dealt
+// round-robin to the workgroups of an XCD)
+constexpr int kGatherRun = 64;
+// query bytes of one (b, kv head) chunk of the default chunk size
+constexpr int64_t kChunkQueryBytes = (int64_t)64 << 20;
+
 static int ceil_log2(int x) {
   int b = 0;
   while ((1 << b) < x) ++b;
@@ -187,30 +193,30 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
     return fail(BSA_ERR_UNSUPPORTED, "Lq too large for the packed selection entries");
   if ((int64_t)a->B * a->Hkv * P.Nb >= (int64_t)1 << 30) return fail(BSA_ERR_UNSUPPORTED, "too many KV blocks");
   if (a->chunk_tokens < 0) return fail(BSA_ERR_INVALID_ARG, "chunk_tokens must be >= 0");
+  if (a->chunks_per_pass < 0) return fail(BSA_ERR_INVALID_ARG, "chunks_per_pass must be >= 0");
   {
-    // Attention runs in passes over chunks of query tokens so that the
-    // partial outputs of one pass stay within a workspace budget.  One pass
-    // over everything is fastest (a chunk of fewer tokens gives each block
-    // fewer rows per work item and re-stages its keys per chunk; the partials
-    // written by a gather are not kept by the memory-side cache for the
-    // merge), so the budget is large: it only bounds the workspace of very
-    // long inputs.
+    // Query tokens of one (b, kv head) are attended in chunks of CT tokens:
+    // the gather works through its items chunk by chunk, and a chunk's query
+    // rows (re-read once per block they chose) stay in the memory-side cache
+    // while it does.  The default chunk holds about 64 MiB of queries.
+    // Chunks run in passes (gather + merge) whose partial outputs fit a
+    // workspace budget; the budget is large, one pass over everything is
+    // fastest (the cache does not keep the gather's written partials for
+    // the merge), so it only bounds the workspace of very long inputs.
     const int64_t per_tok = (int64_t)P.G * P.kslot * (2 * a->D + 8);  // partial bytes per (token, kv head)
     const int64_t budget = (int64_t)40 << 30;
     const int64_t nbh = (int64_t)a->B * a->Hkv;
     if (a->chunk_tokens > 0) {
       P.CT = std::min(a->chunk_tokens, a->Lq);
-      P.CPL = 1;
-    } else if (per_tok * a->Lq <= budget) {
-      P.CT = a->Lq;
-      P.CPL = (int)std::max<int64_t>(1, std::min<int64_t>(nbh, budget / std::max<int64_t>(1, per_tok * a->Lq)));
     } else {
-      int ct = 1024;
-      while ((int64_t)ct * 2 * per_tok <= budget && ct * 2 < a->Lq) ct *= 2;
-      P.CT = ct;
-      P.CPL = 1;
+      const int64_t q_bytes = (int64_t)P.G * a->D * 2;  // query bytes per (token, kv head)
+      int64_t ct = 1024;
+      while (ct * 2 * q_bytes <= kChunkQueryBytes && ct * 2 * per_tok <= budget) ct *= 2;
+      P.CT = (int)std::min<int64_t>(ct, a->Lq);
     }
     P.NC = (a->Lq + P.CT - 1) / P.CT;
+    const int64_t fit = std::max<int64_t>(1, budget / std::max<int64_t>(1, per_tok * P.CT));
+    P.CPL = (int)std::min<int64_t>(nbh * P.NC, a->chunks_per_pass > 0 ? a->chunks_per_pass : fit);
     if (nbh * P.NC * P.Nb >= (int64_t)1 << 30) return fail(BSA_ERR_UNSUPPORTED, "too many (chunk, block) buckets");
   }
   P.nbk = a->B * a->Hkv * P.NC * P.Nb;
@@ -246,7 +252,7 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
   P.q32 = (P.rope_q && (!P.bf16 || !P.use_index)) ? c.take<float>(B * Lq * a->Hq * a->D) : nullptr;
   P.k16 = (P.rope_k && P.bf16) ? c.take<uint16_t>(B * Lk * a->Hkv * a->D) : nullptr;
   P.k32 = (P.rope_k && !P.bf16) ? c.take<float>(B * Lk * a->Hkv * a->D) : nullptr;
-  const int64_t npool = (int64_t)P.nbk * P.Dg;
+  const int64_t npool = (int64_t)a->B * a->Hkv * P.Nb * P.Dg;
   if (P.bf16) {
     P.p_hi = c.take<uint16_t>(npool);
     P.p_lo = c.take<uint16_t>(npool);
@@ -422,6 +428,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
   ap.NC = P.NC; ap.CT = P.CT;
   ap.grid = P.attn_grid;
   ap.rows_item = 32 * gather_waves(a->block);
+  ap.run_items = kGatherRun;
   ap.part_o = P.part_o; ap.part_ml = P.part_ml;
   ap.sel = P.sel; ap.sel_w = P.sel_w;
   ap.o = reinterpret_cast<uint16_t*>(a->o); ap.os_b = a->o_stride[0]; ap.os_t = a->o_stride[1]; ap.os_h = a->o_stride[2];

@@ -58,6 +58,17 @@ struct QStage {
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS reads of the staged key / value tiles go through inline asm that waits
+// for its own data inside the same asm block.  While a global_load_lds copy
+// of the next item's queries is in flight, the compiler cannot tell these
+// reads from that copy's LDS area and would make each of them wait for the
+// copy (and, in order, for every vector store issued before it).  Each block
+// issues the reads of two (keys) or four (values) MFMA steps from one base
+// address with immediate offsets, so that their latencies overlap.
+typedef const __attribute__((address_space(3))) void* lds_cptr_t;
+BSA_DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_cptr_t)p; }
+
 // Work-item records are read-only while the gather runs: reading them through
 // the constant address space makes them scalar loads, whose wait does not
 // also wait for the partial-output stores still in flight (vector memory
@@ -66,16 +77,40 @@ typedef const __attribute__((address_space(4))) int* const_int_ptr;
 BSA_DEV int4 load_item(const_int_ptr items, int i) {
   return make_int4(items[4 * i], items[4 * i + 1], items[4 * i + 2], items[4 * i + 3]);
 }
+// Entry word of a lane's row for the item whose entries start at e_item.
+// With R >= 4 rows per entry a wave's 32 rows use at most 8 entries: they are
+// read with scalar loads (a wave-uniform address) and each lane picks its
+// own, so waiting for them does not wait for the vector stores in flight;
+// otherwise (R < 4) each lane loads its entry.
+template <bool SCALAR>
+BSA_DEV uint32_t next_entry(const uint32_t* entries, int e_item, int wave, int lane, int lgR) {
+  if constexpr (SCALAR) {
+    const const_int_ptr ents = (const const_int_ptr)entries;
+    const int e0 = e_item + ((wave * 32) >> lgR);
+    const int sel = (lane & 31) >> lgR;
+    int v = ents[e0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      const int x = ents[e0 + i];
+      v = sel == i ? x : v;
+    }
+    return (uint32_t)v;
+  }
+  return entries[e_item + ((wave * 32 + (lane & 31)) >> lgR)];
+}
 
 template <int D, int W>
 BSA_DEV void prefetch_q_lds(QStage<D, W>& st, const uint16_t* qrow, bool ok) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = lane_id() >> 5;
   if (ok) {
+    // byte offset of the lane's half row, 16 * (lane >> 5): derived here, in
+    // asm, so that it is not held live (and spilled) across the item loop
+    uint32_t hb;
+    asm volatile("v_and_b32 %0, 32, %1\n\tv_lshrrev_b32 %0, 1, %0" : "=v"(hb) : "v"(lane_id()));
+    const char* src = reinterpret_cast<const char*>(qrow) + hb;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
-      __builtin_amdgcn_global_load_lds((const void*)(qrow + 16 * s + 8 * h), (lds_ptr_t)(&st.buf[w][s * 64 * 8]), 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(src + 32 * s), (lds_ptr_t)(&st.buf[w][s * 64 * 8]), 16, 0, 0);
   }
 }
 
@@ -104,6 +139,30 @@ BSA_DEV void pack_partials(const f32x16 (&o)[D / 32], u16x4_t (&pk)[D / 8]) {
                                 f2bf(o[dt][4 * gg + 3])};
 }
 
+// Stores rows N*RPI + lr (N = 0..NMAX-1) of the wave's staged partial rows:
+// the LDS reads (destination offset, 16 bytes of the row) go through asm with
+// immediate offsets from two base addresses, so the stores of earlier rows
+// stay in flight (see the key / value tile reads).
+template <int N, int NMAX, int RPI, int RS>
+BSA_DEV void store_rows(uint32_t dst_base, uint32_t row_base, int lr, int nvalid, uint16_t* part_o) {
+  if constexpr (N < NMAX) {
+    if (N * RPI + lr < nvalid) {
+      int64_t dst;
+      u16x4_t a, b;
+      asm volatile(
+          "ds_read_b64 %0, %3 offset:%5\n\tds_read_b64 %1, %4 offset:%6\n\tds_read_b64 %2, %4 offset:%7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=v"(dst), "=v"(a), "=v"(b)
+          : "v"(dst_base), "v"(row_base), "n"(N * RPI * 8), "n"(N * RPI * RS * 2), "n"(N * RPI * RS * 2 + 8)
+          : "memory");
+      const u16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      // streaming store: partials are read once, by the merge, long after
+      __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(part_o + dst));
+    }
+    store_rows<N + 1, NMAX, RPI, RS>(dst_base, row_base, lr, nvalid, part_o);
+  }
+}
+
 template <int D, int W>
 BSA_DEV void store_partials(QStage<D, W>& st, const u16x4_t (&pk)[D / 8], int64_t dst_mine, int nvalid,
                             uint16_t* part_o) {
@@ -117,19 +176,9 @@ BSA_DEV void store_partials(QStage<D, W>& st, const u16x4_t (&pk)[D / 8], int64_
   if (h == 0) st.dst[w][r] = dst_mine;
   __builtin_amdgcn_wave_barrier();
   constexpr int CPR = D / 8, RPI = 64 / CPR;
-  const int c = lane % CPR;
-#pragma unroll
-  for (int n = 0; n < 32 / RPI; ++n) {
-    const int rr = n * RPI + lane / CPR;
-    if (rr < nvalid) {
-      const int64_t dst = st.dst[w][rr];
-      const u16x4_t a = *reinterpret_cast<const u16x4_t*>(sb + rr * RS + c * 8);
-      const u16x4_t b = *reinterpret_cast<const u16x4_t*>(sb + rr * RS + c * 8 + 4);
-      const u16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      // streaming store: partials are read once, by the merge, long after
-      __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(part_o + dst + c * 8));
-    }
-  }
+  const int c = lane % CPR, lr = lane / CPR;
+  store_rows<0, 32 / RPI, RPI, RS>(lds_addr(&st.dst[w][lr]), lds_addr(sb + lr * RS + c * 8), lr, nvalid,
+                                    part_o + c * 8);
 }
 
 // Stage keys [key0, key0 + KT) of one kv head (zero past n_valid) into LDS:
@@ -165,6 +214,27 @@ BSA_DEV void stage_kv(AttnSmem<D>& sm, const uint16_t* kb, int64_t ks_t, const u
   }
 }
 
+// Score steps S and S+1 (head dims 16S .. 16S+31) of qk_tile, then the rest.
+// base = LDS byte address of this lane's 16 bytes in key row r, step 0.
+template <int S, int D>
+BSA_DEV void qk_steps(uint32_t base, const bf16x8 (&qf)[D / 16], f32x16& s0, f32x16& s1) {
+  if constexpr (S < D / 16) {
+    constexpr int R32 = 32 * (D + 8) * 2;  // byte distance from key row r to r + 32
+    u16x8 a0, a1, b0, b1;
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%5\n\tds_read_b128 %1, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %4 offset:%7\n\tds_read_b128 %3, %4 offset:%8\n\ts_waitcnt lgkmcnt(0)"
+        : "=v"(a0), "=v"(a1), "=v"(b0), "=v"(b1)
+        : "v"(base), "n"(S * 32), "n"(R32 + S * 32), "n"(S * 32 + 32), "n"(R32 + S * 32 + 32)
+        : "memory");
+    s0 = mfma32(as_bf(a0), qf[S], s0);
+    s1 = mfma32(as_bf(a1), qf[S], s1);
+    s0 = mfma32(as_bf(b0), qf[S + 1], s0);
+    s1 = mfma32(as_bf(b1), qf[S + 1], s1);
+    qk_steps<S + 2, D>(base, qf, s0, s1);
+  }
+}
+
 // S^T (64 keys x 32 queries) for this wave: s0 keys 0..31, s1 keys 32..63.
 template <int D>
 BSA_DEV void qk_tile(const AttnSmem<D>& sm, const bf16x8 (&qf)[D / 16], f32x16& s0, f32x16& s1) {
@@ -172,12 +242,35 @@ BSA_DEV void qk_tile(const AttnSmem<D>& sm, const bf16x8 (&qf)[D / 16], f32x16& 
   const int r = lane & 31, h = lane >> 5;
   s0 = f32x16{};
   s1 = f32x16{};
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const bf16x8 a0 = as_bf(ld16(&sm.k[r * (D + 8) + 16 * s + 8 * h]));
-    const bf16x8 a1 = as_bf(ld16(&sm.k[(32 + r) * (D + 8) + 16 * s + 8 * h]));
-    s0 = mfma32(a0, qf[s], s0);
-    s1 = mfma32(a1, qf[s], s1);
+  qk_steps<0, D>(lds_addr(&sm.k[r * (D + 8) + 8 * h]), qf, s0, s1);
+}
+
+// Head-dim tile DT (rows 32 DT + r of V^T) of pv_tile over the tile's 64
+// keys, then the rest.  base = LDS byte address of V^T row r, key 4h.
+template <int DT, int D>
+BSA_DEV void pv_steps(uint32_t base, const bf16x8 (&pb)[4], f32x16 (&o)[D / 32], bool first) {
+  if constexpr (DT < D / 32) {
+    constexpr int OFF = DT * 32 * VTS * 2;
+    u16x4 x0, x1, x2, x3, x4, x5, x6, x7;
+    // keys 16kk + 4h .. +3 and 16kk + 8 + 4h .. +3 for kk = 0..3
+    asm volatile(
+        "ds_read_b64 %0, %8 offset:%9\n\tds_read_b64 %1, %8 offset:%10\n\t"
+        "ds_read_b64 %2, %8 offset:%11\n\tds_read_b64 %3, %8 offset:%12\n\t"
+        "ds_read_b64 %4, %8 offset:%13\n\tds_read_b64 %5, %8 offset:%14\n\t"
+        "ds_read_b64 %6, %8 offset:%15\n\tds_read_b64 %7, %8 offset:%16\n\ts_waitcnt lgkmcnt(0)"
+        : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3), "=v"(x4), "=v"(x5), "=v"(x6), "=v"(x7)
+        : "v"(base), "n"(OFF), "n"(OFF + 16), "n"(OFF + 32), "n"(OFF + 48), "n"(OFF + 64), "n"(OFF + 80),
+          "n"(OFF + 96), "n"(OFF + 112)
+        : "memory");
+    const u16x8 a0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    const u16x8 a1 = {x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
+    const u16x8 a2 = {x4[0], x4[1], x4[2], x4[3], x5[0], x5[1], x5[2], x5[3]};
+    const u16x8 a3 = {x6[0], x6[1], x6[2], x6[3], x7[0], x7[1], x7[2], x7[3]};
+    o[DT] = first ? mfma32(as_bf(a0), pb[0], f32x16{}) : mfma32(as_bf(a0), pb[0], o[DT]);
+    o[DT] = mfma32(as_bf(a1), pb[1], o[DT]);
+    o[DT] = mfma32(as_bf(a2), pb[2], o[DT]);
+    o[DT] = mfma32(as_bf(a3), pb[3], o[DT]);
+    pv_steps<DT + 1, D>(base, pb, o, first);
   }
 }
 
@@ -207,20 +300,7 @@ BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, 
     for (int kk = 1; kk < 4; ++kk) rsum = mfma32(ones, pb[kk], rsum);
     l += rsum[0];
   }
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint16_t* vr = &sm.vt[(dt * 32 + r) * VTS + kk * 16 + 4 * h];
-      const u16x4 lo = *reinterpret_cast<const u16x4*>(vr);
-      const u16x4 hi = *reinterpret_cast<const u16x4*>(vr + 8);
-      const u16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      if (kk == 0 && first)
-        o[dt] = mfma32(as_bf(a), pb[kk], f32x16{});
-      else
-        o[dt] = mfma32(as_bf(a), pb[kk], o[dt]);
-    }
-  }
+  pv_steps<0, D>(lds_addr(&sm.vt[r * VTS + 4 * h]), pb, o, first);
 }
 
 // key index (within a 64-key tile) held by result register i of this lane
@@ -278,7 +358,7 @@ BSA_DEV void load_qf(const uint16_t* qrow, bool ok, bf16x8 (&qf)[D / 16]) {
 // {bucket, first entry, rows, tile}; lr is the row's index inside the item.
 struct GRow {
   int t, slot, qh, hs, rr;
-  bool valid;
+  int valid;  // an int, not a bool: a padded struct's copy keeps a private-memory temporary
 };
 
 // raw entry word of row lr of item `rec` (speculative load guarded by validity)
@@ -306,11 +386,12 @@ BSA_DEV const uint16_t* q_row(const AttnParams& p, int4 rec, const GRow& g) {
   return p.q + (int64_t)b * p.qs_b + (int64_t)g.t * p.qs_t + (int64_t)g.qh * p.qs_h;
 }
 
-// Software pipeline per workgroup (contiguous item range): the next item's
+// Software pipeline per workgroup (its sequence of items): the next item's
 // record and entry word are loaded at the top of the current item, and its
 // queries are staged global -> LDS after the current item's first score
 // tile, to be read back once the current item's last PV tile is issued.
-template <int D, int W>
+// SE: entry words through scalar loads (requires R >= 4)
+template <int D, int W, bool SE>
 __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
   __shared__ __attribute__((aligned(16))) QStage<D, W> qst;
@@ -319,26 +400,38 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
   // work items of this launch's chunks (buckets c0*Nb .. c1*Nb)
   const int it_lo = p.tile_off[(int64_t)p.c0 * p.Nb];
   const int nitems = p.tile_off[(int64_t)p.c1 * p.Nb] - it_lo;
-  // XCD x owns items [off_x, off_x + cnt_x); its workgroups split that range
-  // into contiguous runs so that consecutive items mostly share a bucket.
+  // XCD x owns items [off_x, end_x); its workgroups take runs of run_items
+  // consecutive items round-robin, so that at any time the XCD works on a
+  // narrow window of buckets (one query chunk: its query rows are re-read
+  // by every block they chose, from the memory-side cache while the window
+  // stays on the chunk) and consecutive items of a run mostly share a bucket.
   const int x = blockIdx.x & 7, wi = blockIdx.x >> 3, nw = gridDim.x >> 3;
   const int per = nitems >> 3, rem = nitems & 7;
-  const int cnt_x = per + (x < rem ? 1 : 0);
   const int off_x = it_lo + x * per + (x < rem ? x : rem);
-  const int it_begin = off_x + (int)(((int64_t)cnt_x * wi) / nw);
-  const int it_end = off_x + (int)(((int64_t)cnt_x * (wi + 1)) / nw);
-  if (it_begin >= it_end) return;  // uniform for the workgroup
+  const int end_x = off_x + per + (x < rem ? 1 : 0);
+  const int RUN = p.run_items > 0 ? p.run_items : max(1, (end_x - off_x + nw - 1) / nw);
+  int it = off_x + wi * RUN;
+  if (it >= end_x) return;  // uniform for the workgroup
+  int run_end = min(it + RUN, end_x);
 
   const int lrow = w * 32 + (lane & 31);
   int staged = -1;  // bucket whose single key tile sits in LDS
 
   const const_int_ptr items = (const_int_ptr)p.items;
-  int4 rec = load_item(items, it_begin);
+  int4 rec = load_item(items, it);
   GRow g = grow_of(p, rec, entry_of(p, rec, lrow), lrow);
+  // the first item's queries take the same LDS path as every later item's,
+  // so that the query registers never wait on a vector load (a wait on one
+  // would also wait for the partial stores issued before it)
   bf16x8 qf[D / 16];
-  load_qf<D>(q_row<D>(p, rec, g), g.valid, qf);
+  prefetch_q_lds<D, W>(qst, q_row<D>(p, rec, g), g.valid);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+  read_q_lds<D, W>(qst, qf);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-  for (int it = it_begin; it < it_end; ++it) {
+  while (true) {
     const int bucket = rec.x;
     const int hk = rec.w & 0xFFFF;
     const int b = rec.w >> 16;
@@ -347,13 +440,19 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
     const int t_base = (cid % p.NC) * p.CT;
     const int64_t prow_base = (int64_t)(cid - p.c0) * p.Gs;
     const bool wave_on = w * 32 < rec.z;
-    const bool has_next = it + 1 < it_end;
-    // next item: its record, and its entry word -- a workgroup's items cover
-    // one contiguous run of entries, so the next item starts right after this
-    // one's entries (read speculatively; the entries array is padded)
-    const int4 rec_n = has_next ? load_item(items, it + 1) : rec;
-    const uint32_t ent_n =
-        has_next ? p.entries[rec.y + ((rec.z + (1 << p.lgR) - 1) >> p.lgR) + (lrow >> p.lgR)] : 0u;
+    // next item: within the run the next one; after it the first of the
+    // workgroup's next run
+    const bool in_run = it + 1 < run_end;
+    const int it_n = in_run ? it + 1 : it + 1 + (nw - 1) * RUN;
+    const bool has_next = it_n < end_x;
+    // its record, and its entry word: within a run, items cover contiguous
+    // entries, so the next item starts right after this one's (read
+    // speculatively; the entries array is padded); a new run starts where its
+    // record says
+    const int4 rec_n = has_next ? load_item(items, it_n) : rec;
+    const int w_u = __builtin_amdgcn_readfirstlane(w);
+    const int e_n = in_run ? rec.y + ((rec.z + (1 << p.lgR) - 1) >> p.lgR) : rec_n.y;
+    const uint32_t ent_n = has_next ? next_entry<SE>(p.entries, e_n, w_u, lane, p.lgR) : 0u;
     GRow g_n = g;
 
     const int qpos = p.Lk - p.Lq + g.t;
@@ -418,6 +517,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
         __builtin_nontemporal_store(l, &p.part_ml[pidx].y);
       }
     }
+    if (!has_next) break;
+    if (!in_run) run_end = min(it_n + RUN, end_x);
+    it = it_n;
     rec = rec_n;
     g = g_n;
   }
@@ -511,13 +613,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 
 // Persistent grid = the workgroups the device holds at once (a multiple of 8,
 // one range per XCD).
-template <int D, int W>
+template <int D, int W, bool SE>
 static int gather_grid() {
   static int cached = 0;
   if (cached) return cached;
   int dev = 0, cus = 0, per = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, attn_gather_kernel<D, W>, 64 * W, 0) != hipSuccess || per < 1)
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, attn_gather_kernel<D, W, SE>, 64 * W, 0) != hipSuccess || per < 1)
     return 2048 / W;
   cached = ((cus * per + 7) / 8) * 8;
   return cached;
@@ -529,16 +631,24 @@ static int gather_grid() {
 // tiles, so a larger item stages them for twice the rows).
 int gather_waves(int block) { return block > KT ? 8 : 4; }
 
+template <int D, int W>
+static void launch_gather_dw(const AttnParams& p, hipStream_t s) {
+  if (p.lgR >= 2)
+    hipLaunchKernelGGL((attn_gather_kernel<D, W, true>), dim3(gather_grid<D, W, true>()), dim3(64 * W), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_gather_kernel<D, W, false>), dim3(gather_grid<D, W, false>()), dim3(64 * W), 0, s, p);
+}
+
 bool launch_attn_gather(const AttnParams& p, hipStream_t s) {
   {
     LaunchScope ls("attn_gather", s, 2);
     const int W = p.rows_item / 32;
     if (p.D == 128) {
-      if (W == 8) hipLaunchKernelGGL((attn_gather_kernel<128, 8>), dim3(gather_grid<128, 8>()), dim3(512), 0, s, p);
-      else hipLaunchKernelGGL((attn_gather_kernel<128, 4>), dim3(gather_grid<128, 4>()), dim3(256), 0, s, p);
+      if (W == 8) launch_gather_dw<128, 8>(p, s);
+      else launch_gather_dw<128, 4>(p, s);
     } else {
-      if (W == 8) hipLaunchKernelGGL((attn_gather_kernel<64, 8>), dim3(gather_grid<64, 8>()), dim3(512), 0, s, p);
-      else hipLaunchKernelGGL((attn_gather_kernel<64, 4>), dim3(gather_grid<64, 4>()), dim3(256), 0, s, p);
+      if (W == 8) launch_gather_dw<64, 8>(p, s);
+      else launch_gather_dw<64, 4>(p, s);
     }
   }
   return launch_ok("attn_gather");

@@ -137,6 +137,7 @@ struct AttnParams {
   int c0, c1;              // chunk ids of this launch; its partial buffer holds c1 - c0 chunks
   int grid;                // persistent workgroups
   int rows_item;           // rows per work item: 32 per wave of a gather workgroup
+  int run_items;           // consecutive items a gather workgroup takes at a time
   // partials of the launch's chunks, row ((c - c0) * Gs + head-sel) * CT + token-in-chunk
   uint16_t* part_o;        // [rows * kslot * R, D] bf16, sum_k p_k v_k with p = 2^(s*sl2 - m)
   float2* part_ml;         // (m, l): log2-domain running max and sum of p

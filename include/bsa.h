@@ -106,11 +106,14 @@ typedef struct bsa_prefill_args {
                                       or Hkv (per group): chosen blocks ascending, the forced
                                       block last when causal, -1 padded */
     float* lse_out;                /* optional [B, Hq, Lq] natural-log softmax normaliser */
-    int32_t chunk_tokens;          /* scheduling only, results do not depend on it: 0 lets the
-                                      library pick how many query tokens of one (b, kv head) it
-                                      attends per pass (all of them when their partial outputs fit
-                                      a cache-sized budget); > 0 forces passes of that many tokens,
-                                      one (b, kv head) at a time */
+    int32_t chunk_tokens;          /* scheduling only, results do not depend on it: query tokens
+                                      of one (b, kv head) per chunk (the attention works through
+                                      its blocks chunk by chunk); 0 lets the library pick (about
+                                      64 MiB of queries per chunk), > 0 forces that many */
+    int32_t chunks_per_pass;       /* scheduling only: chunks per attention pass (one gather and
+                                      one merge launch); 0 = as many as a 40 GiB partial-output
+                                      budget holds, > 0 forces that many (the last pass may hold
+                                      fewer) */
 } bsa_prefill_args;
 
 /* Workspace bytes bsa_sparse_attn_prefill needs for `a` (0 if `a` is invalid;

@@ -66,6 +66,7 @@ def _args(m, **kw):
 @pytest.mark.parametrize("field,value,status", [
     ("B", 0, 1), ("Hq", 3, 1), ("D", 96, 2), ("block", 0, 1), ("topk", -1, 1), ("topk", 65, 2),
     ("causal", 2, 1), ("gate_mode", 7, 1), ("dtype", 5, 1), ("chunk_tokens", -1, 1),
+    ("chunks_per_pass", -2, 1),
 ])
 def test_prefill_rejects_bad_arguments(m, field, value, status):
     a, _buf = _args(m, **{field: value})
@@ -118,16 +119,12 @@ def test_query_chunks_bound_the_workspace(m):
     """Passes over chunks of query tokens keep only one pass's partial outputs."""
     a, _buf = _args(m, Lq=4096, Lk=4096)
     full = m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a))
-    a.chunk_tokens = 512
+    a.chunk_tokens, a.chunks_per_pass = 512, 1
     chunked = m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a))
-    a.chunk_tokens = 100000  # more than Lq: one pass per (b, kv head)
+    a.chunks_per_pass = 3
+    three = m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a))
+    a.chunk_tokens, a.chunks_per_pass = 100000, 1  # more than Lq: one pass per (b, kv head)
     capped = m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a))
-    assert 0 < chunked < capped <= full, (chunked, capped, full)
-
-
-def test_timer_levels_are_host_state(m):
-    for level in (2, 1, 0):
-        m.timer_enable(level)
-        m.timer_reset()
-        assert m.timer_report("attn") == (0.0, 0)
-    m.timer_enable(0)
+    a.chunk_tokens, a.chunks_per_pass = 512, 0  # every chunk in one pass
+    single = m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a))
+    assert 0 < chunked < three < capped <= full <= single, (chunked, three, capped, full, single)

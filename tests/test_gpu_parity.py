@@ -29,9 +29,9 @@ def _say(msg):
 
 
 def run_prefill_case(bsa, *, dtype, B, Lq, Lk, Hq, Hkv, D, block, topk, causal, gate="head", sigma=1.0, seed=0,
-                     Di=None, doc_mean=None, atol, rel, lse_atol, chunk_tokens=0):
+                     Di=None, doc_mean=None, atol, rel, lse_atol, chunk_tokens=0, chunks_per_pass=0):
     name = (f"prefill dtype={dtype} B{B} Lq{Lq} Lk{Lk} H{Hq}/{Hkv} D{D} block{block} topk{topk} causal{causal} "
-            f"gate={gate} Di={Di} doc={doc_mean} seed{seed} chunk{chunk_tokens}")
+            f"gate={gate} Di={Di} doc={doc_mean} seed{seed} chunk{chunk_tokens} per_pass{chunks_per_pass}")
     _say("case " + name)
     q = synth.host_tensor((B, Lq, Hq, D), sigma, seed, synth.TID["q"], dtype)
     k = synth.host_tensor((B, Lk, Hkv, D), sigma, seed, synth.TID["k"], dtype)
@@ -49,10 +49,10 @@ def run_prefill_case(bsa, *, dtype, B, Lq, Lk, Hq, Hkv, D, block, topk, causal, 
         dev(q), dev(k), dev(v), block, topk, causal, gate=gate, index_q=dev(iq), index_k=dev(ik),
         doc_ids_q=None if dq is None else torch.from_numpy(dq).cuda(),
         doc_ids_k=None if dk is None else torch.from_numpy(dk).cuda(),
-        return_sel=True, return_lse=True, chunk_tokens=chunk_tokens)
+        return_sel=True, return_lse=True, chunk_tokens=chunk_tokens, chunks_per_pass=chunks_per_pass)
     torch.cuda.synchronize()
     _say("  gpu done")
-    if chunk_tokens:
+    if chunk_tokens or chunks_per_pass:
         # the attention schedule changes nothing in the results
         o1, sel1, lse1 = bsa.sparse_attn_prefill(
             dev(q), dev(k), dev(v), block, topk, causal, gate=gate, index_q=dev(iq), index_k=dev(ik),
@@ -63,7 +63,7 @@ def run_prefill_case(bsa, *, dtype, B, Lq, Lk, Hq, Hkv, D, block, topk, causal, 
         assert torch.equal(sel, sel1)
         assert torch.equal(o.view(torch.int16) if o.dtype == torch.bfloat16 else o, o1.view(torch.int16) if o1.dtype == torch.bfloat16 else o1)
         assert torch.equal(lse, lse1)
-        _say("  chunked == single pass, bitwise")
+        _say("  chunked == default schedule, bitwise")
 
     def run_oracle(tokens=None, force_sel=None, scores=False):
         return oracle.prefill(q, k, v, block=block, topk=topk, causal=causal, gate=gate, index_q=iq, index_k=ik,
@@ -122,23 +122,24 @@ def test_bf16_memory_topk64_global_buckets(bsa):
                      seed=13, doc_mean=3000.0, atol=1e-2, rel=1e-2, lse_atol=5e-3)
 
 
-@pytest.mark.parametrize("case", ["head_l3000_c512", "group_l2085_c256", "offset_b2_c64", "memory_c32"])
+@pytest.mark.parametrize("case", ["head_l3000_c512_p1", "group_l2085_c256_all", "offset_b2_c64_p3", "memory_c32_p1"])
 def test_bf16_query_chunks(bsa, case):
-    """Attention in passes over chunks of query tokens (one (b, kv head) chunk per pass, a ragged
-    last chunk): same results as one pass, and the oracle's."""
+    """Attention over chunks of query tokens (a ragged last chunk), in passes of one chunk, of
+    three chunks (a ragged last pass) or of all chunks: same results as the default schedule,
+    and the oracle's."""
     kw = dict(dtype="bf16", atol=1e-2, rel=1e-2, lse_atol=5e-3)
-    if case == "head_l3000_c512":
+    if case == "head_l3000_c512_p1":
         run_prefill_case(bsa, B=1, Lq=3000, Lk=3000, Hq=8, Hkv=2, D=128, block=256, topk=3, causal=True,
-                         sigma=128 ** -0.5, seed=15, chunk_tokens=512, **kw)
-    elif case == "group_l2085_c256":
+                         sigma=128 ** -0.5, seed=15, chunk_tokens=512, chunks_per_pass=1, **kw)
+    elif case == "group_l2085_c256_all":
         run_prefill_case(bsa, B=1, Lq=2085, Lk=2085, Hq=16, Hkv=2, D=128, block=64, topk=16, causal=True,
                          gate="group", Di=64, seed=16, chunk_tokens=256, **kw)
-    elif case == "offset_b2_c64":
+    elif case == "offset_b2_c64_p3":
         run_prefill_case(bsa, B=2, Lq=200, Lk=1500, Hq=4, Hkv=4, D=64, block=32, topk=5, causal=True,
-                         seed=17, chunk_tokens=64, **kw)
+                         seed=17, chunk_tokens=64, chunks_per_pass=3, **kw)
     else:
         run_prefill_case(bsa, B=1, Lq=128, Lk=20000, Hq=8, Hkv=2, D=128, block=64, topk=16, causal=False,
-                         seed=18, doc_mean=400.0, chunk_tokens=32, **kw)
+                         seed=18, doc_mean=400.0, chunk_tokens=32, chunks_per_pass=1, **kw)
 
 
 def test_bf16_topk_zero_and_full(bsa):

@@ -277,6 +277,8 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
   constexpr int STAGE_BYTES = (LO ? 2 : 1) * 64 * PADR * 2;
   constexpr int SMEM = STAGE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  // per (wave, lane group): the chunk's candidates that beat the row's k-th key
+  __shared__ __attribute__((aligned(16))) uint64_t s_cand[W][4][72];  // 64 + read-ahead pad
   uint16_t* s_hi = reinterpret_cast<uint16_t*>(smem);
   uint16_t* s_lo = s_hi + 64 * PADR;
 
@@ -373,8 +375,11 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
         if constexpr (QK != 0) acc[ct] = mfma16(ql[ks], bh16, acc[ct]);
       }
     }
-    // merge this chunk into the running lists, one candidate per lane group
-    // per step, until no lane holds a candidate that beats its row's k-th key
+    // merge this chunk into the running lists: each lane group packs its
+    // row's candidates that beat the row's k-th key into an LDS list, then all
+    // groups insert from their lists in lockstep.  The k-th key is refreshed
+    // once per chunk; a candidate that an earlier insertion of the same chunk
+    // has pushed below it is rejected by the insertion itself.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint64_t key[4];
@@ -394,23 +399,39 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
         thr[i] = list_kth<KR>(L[i], lane, p.topk);
         continue;
       }
-      while (true) {
-        const uint64_t bal = __ballot(pend != 0);
-        if (bal == 0ull) break;
-        const int ct0 = pend ? __ffs(pend) - 1 : 0;
-        const uint64_t mine = ct0 == 0 ? key[0] : ct0 == 1 ? key[1] : ct0 == 2 ? key[2] : key[3];
-        const uint32_t gm = (uint32_t)(bal >> (16 * kh)) & 0xFFFFu;
-        const int src = gm ? 16 * kh + __ffs((int)gm) - 1 : lane;
-        const uint64_t cnd = shfl64(pend ? mine : 0ull, src);
-        const uint64_t c = gm ? cnd : 0ull;
-        const int src_me = gm ? src : -1;
-        if (lane == src_me) pend &= pend - 1;
-        list_insert<KR>(L[i], c, c > thr[i], lane, p.topk);
-        thr[i] = list_kth<KR>(L[i], lane, p.topk);
+      // slots: exclusive scan of the per-lane counts over the 16-lane group
+      const int n_me = __popc(pend);
+      int inc = n_me;
+      inc += (int)dpp32<0x111>(0u, (uint32_t)inc);  // row_shr:1
+      inc += (int)dpp32<0x112>(0u, (uint32_t)inc);  // row_shr:2
+      inc += (int)dpp32<0x114>(0u, (uint32_t)inc);  // row_shr:4
+      inc += (int)dpp32<0x118>(0u, (uint32_t)inc);  // row_shr:8
+      // group totals (lane 15 of each group) and the longest list
+      const int n0 = __builtin_amdgcn_readlane(inc, 15), n1 = __builtin_amdgcn_readlane(inc, 31);
+      const int n2 = __builtin_amdgcn_readlane(inc, 47), n3 = __builtin_amdgcn_readlane(inc, 63);
+      const int nmax = max(max(n0, n1), max(n2, n3));
+      if (nmax == 0) continue;
+      const int ng = kh == 0 ? n0 : kh == 1 ? n1 : kh == 2 ? n2 : n3;
+      uint64_t* lst = s_cand[w][kh];
+      int slot = inc - n_me;
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          if (key[ct] <= thr[i]) pend &= ~(1 << ct);
+      for (int ct = 0; ct < 4; ++ct)
+        if (pend & (1 << ct)) lst[slot++] = key[ct];
+      // every lane of a group reads the same entries (an LDS broadcast), four
+      // at a time, the next four before the current ones are inserted
+      typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+      u64x2 e01 = *reinterpret_cast<const u64x2*>(lst), e23 = *reinterpret_cast<const u64x2*>(lst + 2);
+      for (int s = 0; s < nmax; s += 4) {
+        const u64x2 n01 = *reinterpret_cast<const u64x2*>(lst + s + 4);
+        const u64x2 n23 = *reinterpret_cast<const u64x2*>(lst + s + 6);
+        const uint64_t e[4] = {e01[0], e01[1], e23[0], e23[1]};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (s + u < nmax) list_insert<KR>(L[i], s + u < ng ? e[u] : 0ull, s + u < ng, lane, p.topk);
+        e01 = n01;
+        e23 = n23;
       }
+      thr[i] = list_kth<KR>(L[i], lane, p.topk);
     }
   }
   // emit: each lane group finishes its four rows from registers -- chosen

@@ -399,6 +399,7 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
         thr[i] = list_kth<KR>(L[i], lane, p.topk);
         continue;
       }
+      if (__ballot(pend != 0) == 0ull) continue;  // nothing to insert in any group
       // slots: exclusive scan of the per-lane counts over the 16-lane group
       const int n_me = __popc(pend);
       int inc = n_me;
@@ -410,7 +411,6 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
       const int n0 = __builtin_amdgcn_readlane(inc, 15), n1 = __builtin_amdgcn_readlane(inc, 31);
       const int n2 = __builtin_amdgcn_readlane(inc, 47), n3 = __builtin_amdgcn_readlane(inc, 63);
       const int nmax = max(max(n0, n1), max(n2, n3));
-      if (nmax == 0) continue;
       const int ng = kh == 0 ? n0 : kh == 1 ? n1 : kh == 2 ? n2 : n3;
       uint64_t* lst = s_cand[w][kh];
       int slot = inc - n_me;

@@ -411,7 +411,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
   const int end_x = off_x + per + (x < rem ? 1 : 0);
   // runs no longer than an even share, so that small launches still spread
   // over every workgroup
-  const int share = max(1, (end_x - off_x) / nw);
+  const int share = max(1, (end_x - off_x + nw - 1) / nw);
   const int RUN = p.run_items > 0 ? min(p.run_items, share) : share;
   int it = off_x + wi * RUN;
   if (it >= end_x) return;  // uniform for the workgroup

@@ -94,8 +94,6 @@ BSA_DEV uint64_t row_xor64(uint64_t v, int li) {
     return (li & 4) ? dn : up;
   }
 }
-// value held by lane (li - 1) mod 16 of the same row
-BSA_DEV uint64_t row_ror1_64(uint64_t v) { return dpp64<0x121>(v); }
 // value held by lane `src` (wave-uniform)
 BSA_DEV uint64_t readlane64(uint64_t v, int src) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);

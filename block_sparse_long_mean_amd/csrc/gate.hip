@@ -128,35 +128,9 @@ BSA_DEV void emit_row(const GateParams& p, const uint64_t* buf, int cnt, int b, 
 // lanes of lane group g = lane/16 hold rows 4g..4g+3, each row's candidates
 // spread over those 16 lanes.  Each row keeps its best k keys in the same 16
 // lanes: element e = 16*m + (lane % 16) lives in register m, sorted
-// descending; unused elements are 0.  Inserting a candidate is a 16-lane
-// ballot (how many held keys beat it), a one-place shift and a write; all four
-// lane groups insert into their own rows at once.
+// descending; unused elements are 0.  New candidates are merged 16 at a time
+// with a bitonic merge; all four lane groups merge into their own rows at once.
 // ---------------------------------------------------------------------------
-template <int KR>
-BSA_DEV void list_insert(uint64_t (&L)[KR], uint64_t c, bool active, int lane, int topk) {
-  const int g = lane >> 4, li = lane & 15;
-  int pos = 0;
-#pragma unroll
-  for (int m = 0; m < KR; ++m) {
-    const uint64_t bal = __ballot(L[m] > c);
-    pos += __popc((uint32_t)(bal >> (16 * g)) & 0xFFFFu);
-  }
-  active = active && pos < topk;
-  // element e-1 of the row: lane li-1 of the same register, or lane 15 of
-  // the previous register for li = 0 (a rotation inside the 16-lane row)
-  uint64_t r[KR];
-#pragma unroll
-  for (int m = 0; m < KR; ++m) r[m] = row_ror1_64(L[m]);
-#pragma unroll
-  for (int m = 0; m < KR; ++m) {
-    const uint64_t prev = li > 0 ? r[m] : (m > 0 ? r[m > 0 ? m - 1 : 0] : 0ull);
-    const int e = m * 16 + li;
-    uint64_t nv = e < pos ? L[m] : (e == pos ? c : prev);
-    if (e >= topk) nv = 0ull;
-    if (active) L[m] = nv;
-  }
-}
-
 // row_xor64 with a stride that is a constant once the caller's loops unroll
 BSA_DEV uint64_t row_xor64_any(uint64_t v, int m, int li) {
   switch (m) {
@@ -167,42 +141,59 @@ BSA_DEV uint64_t row_xor64_any(uint64_t v, int m, int li) {
   }
 }
 
-// Bitonic sort, descending, of the 64 keys a 16-lane group holds for one row
-// (element e = 16*r + lane%16 in register r); every group sorts its own row.
-BSA_DEV void group_sort64_desc(uint64_t (&v)[4], int lane) {
-  const int li = lane & 15;
+// Bitonic sort, ascending, of the 16 keys a 16-lane group holds (one per
+// lane); every group sorts its own keys.
+BSA_DEV uint64_t group_sort16_asc(uint64_t v, int li) {
 #pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
+  for (int size = 2; size <= 16; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride >= 16) {
-        const int rs = stride >> 4;
+      const uint64_t o = row_xor64_any(v, stride, li);
+      const bool lower = (li & stride) == 0;
+      const bool asc = (li & size) == 0 || size == 16;
+      const uint64_t mx = v > o ? v : o, mn = v > o ? o : v;
+      v = (lower == asc) ? mn : mx;
+    }
+  }
+  return v;
+}
+
+// Merges up to 16 keys per lane group (b, one per lane, any order, 0 = none)
+// into the group's list L (16*KR keys, element e = 16m + li in register m,
+// descending, elements >= topk zero) and keeps the best topk.  With b sorted
+// ascending, max(L[e], b[e - (16KR - 16)]) over the last register is a
+// bitonic sequence holding the 16KR best keys of both; a bitonic merge sorts
+// it descending.
+template <int KR>
+BSA_DEV void list_merge16(uint64_t (&L)[KR], uint64_t b, int li, int topk) {
+  b = group_sort16_asc(b, li);
+  L[KR - 1] = L[KR - 1] > b ? L[KR - 1] : b;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = r ^ rs;
-          if (q > r) {
-            const int e = r * 16 + li;
-            const bool desc = (e & size) == 0;
-            const uint64_t a = v[r], b = v[q];
-            const bool sw = desc ? (a < b) : (a > b);
-            v[r] = sw ? b : a;
-            v[q] = sw ? a : b;
-          }
-        }
-      } else {
+  for (int stride = 8 * KR; stride > 0; stride >>= 1) {
+    if (stride >= 16) {
+      const int rs = stride >> 4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint64_t o = row_xor64_any(v[r], stride, li);
-          const int e = r * 16 + li;
-          const bool lower = (li & stride) == 0;
-          const bool desc = (e & size) == 0;
-          const uint64_t mx = v[r] > o ? v[r] : o;
-          const uint64_t mn = v[r] > o ? o : v[r];
-          v[r] = (lower == desc) ? mx : mn;
+      for (int r = 0; r < KR; ++r) {
+        const int q = r ^ rs;
+        if (q > r) {
+          const uint64_t a = L[r], c = L[q];
+          L[r] = a > c ? a : c;
+          L[q] = a > c ? c : a;
         }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < KR; ++r) {
+        const uint64_t o = row_xor64_any(L[r], stride, li);
+        const bool lower = (li & stride) == 0;
+        const uint64_t mx = L[r] > o ? L[r] : o, mn = L[r] > o ? o : L[r];
+        L[r] = lower ? mx : mn;
       }
     }
   }
+#pragma unroll
+  for (int m = 0; m < KR; ++m)
+    if (m * 16 + li >= topk) L[m] = 0ull;
 }
 
 // 32-bit value held by lane (li ^ m) of the same 16-lane row, m in {1, 2, 4, 8}
@@ -278,7 +269,7 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
   constexpr int SMEM = STAGE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   // per (wave, lane group): the chunk's candidates that beat the row's k-th key
-  __shared__ __attribute__((aligned(16))) uint64_t s_cand[W][4][72];  // 64 + read-ahead pad
+  __shared__ uint64_t s_cand[W][4][80];  // < 16 left over + up to 64 new
   uint16_t* s_hi = reinterpret_cast<uint16_t*>(smem);
   uint16_t* s_lo = s_hi + 64 * PADR;
 
@@ -321,10 +312,13 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
   const uint16_t* plo = LO ? p.p_lo + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h : nullptr;
 
   uint64_t L[4][KR];
-  uint64_t thr[4];
+  uint64_t thr[4], left[4];
+  int nleft[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     thr[i] = 0ull;
+    left[i] = 0ull;
+    nleft[i] = 0;
 #pragma unroll
     for (int m = 0; m < KR; ++m) L[i][m] = 0ull;
   }
@@ -375,11 +369,12 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
         if constexpr (QK != 0) acc[ct] = mfma16(ql[ks], bh16, acc[ct]);
       }
     }
-    // merge this chunk into the running lists: each lane group packs its
-    // row's candidates that beat the row's k-th key into an LDS list, then all
-    // groups insert from their lists in lockstep.  The k-th key is refreshed
-    // once per chunk; a candidate that an earlier insertion of the same chunk
-    // has pushed below it is rejected by the insertion itself.
+    // merge this chunk into the running lists: each lane group appends its
+    // row's candidates that beat the row's k-th key to an LDS list (after the
+    // fewer than 16 left over from earlier chunks, which wait in a register),
+    // then merges the list into the row's top-k 16 keys at a time.  The k-th
+    // key is refreshed after each merge; candidates that pass a stale one are
+    // simply merged and dropped.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint64_t key[4];
@@ -391,15 +386,7 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
         key[ct] = ok ? make_key(acc[ct][i], (uint32_t)j) : 0ull;
         if (key[ct] > thr[i]) pend |= 1 << ct;
       }
-      if (c0 == c_lo) {
-        // first chunk: sort its 64 candidates and keep the best k
-        group_sort64_desc(key, lane);
-#pragma unroll
-        for (int m = 0; m < KR; ++m) L[i][m] = (m * 16 + r16) < p.topk ? key[m] : 0ull;
-        thr[i] = list_kth<KR>(L[i], lane, p.topk);
-        continue;
-      }
-      if (__ballot(pend != 0) == 0ull) continue;  // nothing to insert in any group
+      if (__ballot(pend != 0) == 0ull) continue;  // nothing new in any group
       // slots: exclusive scan of the per-lane counts over the 16-lane group
       const int n_me = __popc(pend);
       int inc = n_me;
@@ -407,33 +394,31 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
       inc += (int)dpp32<0x112>(0u, (uint32_t)inc);  // row_shr:2
       inc += (int)dpp32<0x114>(0u, (uint32_t)inc);  // row_shr:4
       inc += (int)dpp32<0x118>(0u, (uint32_t)inc);  // row_shr:8
-      // group totals (lane 15 of each group) and the longest list
+      // group totals (lane 15 of each group)
       const int n0 = __builtin_amdgcn_readlane(inc, 15), n1 = __builtin_amdgcn_readlane(inc, 31);
       const int n2 = __builtin_amdgcn_readlane(inc, 47), n3 = __builtin_amdgcn_readlane(inc, 63);
-      const int nmax = max(max(n0, n1), max(n2, n3));
       const int ng = kh == 0 ? n0 : kh == 1 ? n1 : kh == 2 ? n2 : n3;
       uint64_t* lst = s_cand[w][kh];
-      int slot = inc - n_me;
+      if (r16 < nleft[i]) lst[r16] = left[i];
+      int slot = nleft[i] + inc - n_me;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
         if (pend & (1 << ct)) lst[slot++] = key[ct];
-      // every lane of a group reads the same entries (an LDS broadcast), four
-      // at a time, the next four before the current ones are inserted
-      typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
-      u64x2 e01 = *reinterpret_cast<const u64x2*>(lst), e23 = *reinterpret_cast<const u64x2*>(lst + 2);
-      for (int s = 0; s < nmax; s += 4) {
-        const u64x2 n01 = *reinterpret_cast<const u64x2*>(lst + s + 4);
-        const u64x2 n23 = *reinterpret_cast<const u64x2*>(lst + s + 6);
-        const uint64_t e[4] = {e01[0], e01[1], e23[0], e23[1]};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (s + u < nmax) list_insert<KR>(L[i], s + u < ng ? e[u] : 0ull, s + u < ng, lane, p.topk);
-        e01 = n01;
-        e23 = n23;
-      }
-      thr[i] = list_kth<KR>(L[i], lane, p.topk);
+      const int cnt = nleft[i] + ng;
+      const int m0 = __builtin_amdgcn_readlane(cnt, 0), m1 = __builtin_amdgcn_readlane(cnt, 16);
+      const int m2 = __builtin_amdgcn_readlane(cnt, 32), m3 = __builtin_amdgcn_readlane(cnt, 48);
+      const int nb = max(max(m0, m1), max(m2, m3)) >> 4;  // whole batches of the fullest list
+      for (int q = 0; q < nb; ++q)
+        list_merge16<KR>(L[i], 16 * q + r16 < cnt ? lst[16 * q + r16] : 0ull, r16, p.topk);
+      nleft[i] = max(0, cnt - 16 * nb);
+      left[i] = r16 < nleft[i] ? lst[16 * nb + r16] : 0ull;
+      if (nb > 0) thr[i] = list_kth<KR>(L[i], lane, p.topk);
     }
   }
+  // the candidates still waiting
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (__ballot(nleft[i] > 0) != 0ull) list_merge16<KR>(L[i], left[i], r16, p.topk);
   // emit: each lane group finishes its four rows from registers -- chosen
   // block ids sorted ascending inside the group, the forced block after them
   constexpr int NR = KR == 1 ? 1 : (KR == 2 ? 2 : 4);

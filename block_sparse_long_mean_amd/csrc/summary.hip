@@ -113,11 +113,13 @@ struct Elt;
 template <>
 struct Elt<uint16_t> {
   static constexpr int E = 8;
-  static BSA_DEV void load(const uint16_t* p, float* x) {
-    u16x8 v = ld16(p);
+  typedef u16x8 Raw;
+  static BSA_DEV Raw raw(const uint16_t* p) { return ld16(p); }
+  static BSA_DEV void cvt(Raw v, float* x) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = bf2f(v[e]);
   }
+  static BSA_DEV void load(const uint16_t* p, float* x) { cvt(raw(p), x); }
   static BSA_DEV void store(uint16_t* p, const float* x) {
     u16x8 v;
 #pragma unroll
@@ -128,11 +130,13 @@ struct Elt<uint16_t> {
 template <>
 struct Elt<float> {
   static constexpr int E = 4;
-  static BSA_DEV void load(const float* p, float* x) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  typedef f32x4 Raw;
+  static BSA_DEV Raw raw(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  static BSA_DEV void cvt(Raw v, float* x) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = v[e];
   }
+  static BSA_DEV void load(const float* p, float* x) { cvt(raw(p), x); }
   static BSA_DEV void store(float* p, const float* x) {
     f32x4 v;
 #pragma unroll
@@ -143,12 +147,14 @@ struct Elt<float> {
 
 template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(256) void block_summary_kernel(SummaryParams p, int hpw) {
+  typedef typename Elt<T>::Raw Raw;
   constexpr int E = Elt<T>::E;
   constexpr int UPH = D / (2 * E);
   constexpr int HALF = D / 2;
-  constexpr int TPMAX = 256 / UPH;  // tokens per pass when a workgroup holds one head
-  __shared__ float s_cos[ROPE ? TPMAX : 1][ROPE ? HALF : 1];
-  __shared__ float s_sin[ROPE ? TPMAX : 1][ROPE ? HALF : 1];
+  constexpr int SUB = 64;  // tokens per rotation table
+  constexpr int UNR = 4;   // passes whose rows are loaded together
+  __shared__ float s_cos[ROPE ? SUB : 1][ROPE ? HALF : 1];
+  __shared__ float s_sin[ROPE ? SUB : 1][ROPE ? HALF : 1];
   __shared__ float s_red[2 * E][256];
   const int U = hpw * UPH;
   const int TP = 256 / U;
@@ -165,43 +171,73 @@ __global__ __launch_bounds__(256) void block_summary_kernel(SummaryParams p, int
 #pragma unroll
   for (int e = 0; e < 2 * E; ++e) acc[e] = 0.f;
 
-  for (int p0 = 0; p0 < n; p0 += TP) {
+  // rows of passes p0 .. p0 + UNR - 1 (token p0*TP + q*TP + tl of the sub-block)
+  auto load_rows = [&](int tbase, int lim, Raw (&lo)[UNR], Raw (&hi)[UNR]) {
+#pragma unroll
+    for (int q = 0; q < UNR; ++q) {
+      const int tt = tbase + q * TP + tl;
+      lo[q] = Raw{};
+      hi[q] = Raw{};
+      if (tt < lim) {
+        const T* row = kb + (int64_t)(t0 + tt) * p.ks_t;
+        lo[q] = Elt<T>::raw(row + c * E);
+        hi[q] = Elt<T>::raw(row + HALF + c * E);
+      }
+    }
+  };
+  // Sub-blocks of SUB tokens: the next rows are loaded before the rotation
+  // table is built and before the current rows are used, so that every
+  // thread keeps 2*UNR row loads in flight.
+  for (int s0 = 0; s0 < n; s0 += SUB) {
+    const int ns = min(SUB, n - s0);
+    Raw lo[UNR], hi[UNR];
+    load_rows(s0, s0 + ns, lo, hi);
     if constexpr (ROPE) {
-      __syncthreads();
-      for (int idx = tid; idx < TP * HALF; idx += 256) {
+      __syncthreads();  // the previous sub-block's table is no longer read
+      for (int idx = tid; idx < ns * HALF; idx += 256) {
         const int tt = idx / HALF, i = idx % HALF;
-        float cc = 1.f, ss = 0.f;
-        if (p0 + tt < n) rope_sincos(p.pos[(int64_t)b * p.L + t0 + p0 + tt], p.omega[i], cc, ss);
+        float cc, ss;
+        rope_sincos(p.pos[(int64_t)b * p.L + t0 + s0 + tt], p.omega[i], cc, ss);
         s_cos[tt][i] = cc;
         s_sin[tt][i] = ss;
       }
       __syncthreads();
     }
-    const int tt = p0 + tl;
-    if (tt < n) {
-      const int t = t0 + tt;
-      const T* row = kb + (int64_t)t * p.ks_t;
-      float xl[E], xh[E];
-      Elt<T>::load(row + c * E, xl);
-      Elt<T>::load(row + HALF + c * E, xh);
-      if constexpr (ROPE) {
+    for (int p0 = 0; p0 < ns; p0 += UNR * TP) {
+      Raw nlo[UNR], nhi[UNR];
+      load_rows(s0 + p0 + UNR * TP, s0 + ns, nlo, nhi);
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float cs = s_cos[tl][c * E + e], sn = s_sin[tl][c * E + e];
-          const float a = xl[e], bb = xh[e];
-          xl[e] = a * cs - bb * sn;
-          xh[e] = a * sn + bb * cs;
-        }
-        if (p.k_rot) {
-          T* kr = reinterpret_cast<T*>(p.k_rot) + (((int64_t)b * p.L + t) * p.H + h) * D;
-          Elt<T>::store(kr + c * E, xl);
-          Elt<T>::store(kr + HALF + c * E, xh);
+      for (int q = 0; q < UNR; ++q) {
+        const int tt = p0 + q * TP + tl;  // token within the sub-block
+        if (tt < ns) {
+          float xl[E], xh[E];
+          Elt<T>::cvt(lo[q], xl);
+          Elt<T>::cvt(hi[q], xh);
+          if constexpr (ROPE) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const float cs = s_cos[tt][c * E + e], sn = s_sin[tt][c * E + e];
+              const float a = xl[e], bb = xh[e];
+              xl[e] = a * cs - bb * sn;
+              xh[e] = a * sn + bb * cs;
+            }
+            if (p.k_rot) {
+              T* kr = reinterpret_cast<T*>(p.k_rot) + (((int64_t)b * p.L + t0 + s0 + tt) * p.H + h) * D;
+              Elt<T>::store(kr + c * E, xl);
+              Elt<T>::store(kr + HALF + c * E, xh);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            acc[e] += xl[e];
+            acc[E + e] += xh[e];
+          }
         }
       }
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        acc[e] += xl[e];
-        acc[E + e] += xh[e];
+      for (int q = 0; q < UNR; ++q) {
+        lo[q] = nlo[q];
+        hi[q] = nhi[q];
       }
     }
   }

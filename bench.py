@@ -381,8 +381,8 @@ def main():
     m.timer_enable(0)
 
     kernels = ["doc_chunk_last", "doc_positions", "rope_q", "block_summary", "pooled_to_planes", "gate_topk",
-               "gate_merge", "decode_scores", "decode_topk", "csr_fill", "csr_count", "csr_scan", "csr_scatter",
-               "attn", "decode_union", "decode_attend", "decode_combine"]
+               "gate_merge", "decode_scores", "decode_select", "csr_fill", "csr_count", "csr_scan", "csr_scatter",
+               "attn", "decode_attend", "decode_combine"]
     per_kernel = {}
     for name in kernels:
         ms, n = m.timer_report(name)

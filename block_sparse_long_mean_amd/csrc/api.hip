@@ -525,7 +525,7 @@ static bsa_status run_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes
   g.q = reinterpret_cast<const uint16_t*>(a->q); g.qs_b = a->q_stride[0]; g.qs_h = a->q_stride[1];
   g.pooled = a->pooled; g.pooled_bf16 = a->pooled_dtype == BSA_DTYPE_BF16;
   g.ps_b = a->p_stride[0]; g.ps_j = a->p_stride[1]; g.ps_h = a->p_stride[2];
-  g.scores = P.scores; g.sel = P.sel;
+  g.scores = P.scores; g.sel = P.sel; g.ulist = P.ulist; g.ucount = P.ucount; g.umax = P.umax;
   if (!launch_decode_gate(g, s)) return BSA_ERR_HIP;
   DecodeAttnParams d;
   d.B = a->B; d.Lc = a->Lc; d.Hq = a->Hq; d.Hkv = a->Hkv; d.G = P.G; d.D = a->D; d.block = a->block; d.Hs = P.Hs;
@@ -538,7 +538,6 @@ static bsa_status run_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes
   d.sel = P.sel; d.ulist = P.ulist; d.ucount = P.ucount; d.part_o = P.part_o; d.part_lse = P.part_lse;
   d.o = reinterpret_cast<uint16_t*>(a->o); d.os_b = a->o_stride[0]; d.os_h = a->o_stride[1];
   d.lse_out = a->lse_out;
-  if (!launch_decode_union(d, s)) return BSA_ERR_HIP;
   if (!launch_decode_attend(d, s)) return BSA_ERR_HIP;
   if (!launch_decode_combine(d, s)) return BSA_ERR_HIP;
   return BSA_OK;

@@ -609,7 +609,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   u16x8 out;
 #pragma unroll
   for (int e = 0; e < 8; ++e) out[e] = f2bf(acc[e] * inv);
-  st16(p.o + (int64_t)b * p.os_b + (int64_t)t * p.os_t + (int64_t)h * p.os_h + li * 8, out);
+  // streaming store: the output is written once and not read back here
+  __builtin_nontemporal_store(out, reinterpret_cast<u16x8*>(p.o + (int64_t)b * p.os_b + (int64_t)t * p.os_t +
+                                                            (int64_t)h * p.os_h + li * 8));
   if (p.lse_out && li == 0)
     p.lse_out[((int64_t)b * p.Hq + h) * p.Lq + t] = W > 0.f ? (M + log2f(W)) * 0.69314718055994530942f : -INFINITY;
 }

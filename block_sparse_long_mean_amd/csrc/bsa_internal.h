@@ -199,9 +199,11 @@ struct DecodeGateParams {
   int64_t ps_b, ps_j, ps_h;
   float* scores;  // [B, Hs, Nb] workspace
   int32_t* sel;   // [B, Hs, sel_w]
+  int32_t* ulist;  // [B * Hkv, umax] union of a (b, kv head)'s rows (j << 8 | head mask)
+  int32_t* ucount; // [B * Hkv]
+  int umax;
 };
 bool launch_decode_gate(const DecodeGateParams& p, hipStream_t s);
-bool launch_decode_union(const DecodeAttnParams& p, hipStream_t s);
 bool launch_decode_attend(const DecodeAttnParams& p, hipStream_t s);
 bool launch_decode_combine(const DecodeAttnParams& p, hipStream_t s);
 

@@ -111,59 +111,148 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(DecodeGateParams p) 
   }
 }
 
-// Decode gate, pass 2: one wave per selection row (b, hs) keeps the top-k of
-// the candidates j < cur by (score desc, index asc) -- a threshold filter
-// plus an LDS buffer compacted by a wave-wide bitonic sort -- and writes the
-// row ascending with the forced own block last, -1 padded.
+// Union of the selections of one (b, kv head) by one wave: sel[r][s] for
+// rows r < nrow, slots s < w (-1 = none) -> distinct block ids ascending,
+// each with a bit mask of the heads that chose it, packed (j << 8 | mask).
+BSA_DEV int unite_rows(const int32_t (*sel)[65], int nrow, int w, int G, bool per_group, uint64_t* s_v,
+                       int32_t* out) {
+  constexpr int V = 8;  // up to 512 (head, block) pairs
+  const int lane = lane_id();
+  uint64_t v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = i * 64 + lane;
+    uint64_t key = 0ull;
+    if (e < nrow * w) {
+      const int hh = e / w, sl = e % w;
+      const int j = sel[hh][sl];
+      if (j >= 0) key = ~(((uint64_t)(uint32_t)j << 8) | (uint64_t)hh);  // descending ~val = ascending val
+    }
+    v[i] = key;
+  }
+  wave_sort_desc<V>(v);
+#pragma unroll
+  for (int i = 0; i < V; ++i) s_v[i * 64 + lane] = v[i];
+  __builtin_amdgcn_wave_barrier();
+  // element e starts a run of equal block ids when its id differs from
+  // element e-1's; a run holds at most G entries (one per head)
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = i * 64 + lane;
+    const uint64_t key = s_v[e];
+    bool head = false;
+    int val = 0;
+    if (key != 0ull) {
+      const int j = (int)((~key) >> 8);
+      head = e == 0 || (int)((~s_v[e - 1]) >> 8) != j;
+      if (head) {
+        int mask = 0;
+        for (int f = e; f < 64 * V && f < e + 8; ++f) {
+          const uint64_t kf = s_v[f];
+          if (kf == 0ull || (int)((~kf) >> 8) != j) break;
+          mask |= per_group ? ((1 << G) - 1) : (1 << (int)((~kf) & 255));
+        }
+        val = (j << 8) | mask;
+      }
+    }
+    const uint64_t hm = __ballot(head);
+    if (head) out[total + __popcll(hm & ((1ull << lane) - 1ull))] = val;
+    total += __popcll(hm);
+  }
+  return total;
+}
+
+// Decode gate, pass 2, and the union, for one (b, kv head) per workgroup.
+// Its 16 waves split the candidates j < cur of the selection rows (G rows
+// per head, one per group): each wave keeps the top-k of its share by (score
+// desc, index asc) -- a threshold filter plus an LDS buffer compacted by a
+// wave-wide bitonic sort -- the shares of a row are merged pairwise, each row
+// is written ascending with the forced own block last, -1 padded, and wave 0
+// unites the rows' blocks for the attention.
 template <int V>
-__global__ __launch_bounds__(256) void decode_topk_kernel(DecodeGateParams p) {
+__global__ __launch_bounds__(1024) void decode_select_kernel(DecodeGateParams p) {
   constexpr int CAP = 64 * V;
-  __shared__ uint64_t s_buf[4][CAP];
-  __shared__ int s_cnt[4];
-  __shared__ uint64_t s_thr[4];
+  constexpr int NW = 16;
+  __shared__ uint64_t s_buf[NW][CAP];
+  __shared__ int s_cnt[NW];
+  __shared__ uint64_t s_thr[NW];
+  __shared__ int32_t s_sel[8][65];
+  __shared__ uint64_t s_v[512];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + w;
-  if (row >= p.B * p.Hs) return;  // wave-uniform; no workgroup barrier follows
-  const int b = row / p.Hs;
+  const int bh = blockIdx.x;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int nrow = p.per_group ? 1 : p.G;
+  const int wpr = NW / nrow;  // waves per row
+  const int r = w / wpr, q = w % wpr;
+  const bool active = r < nrow;
   int n = p.lens ? p.lens[b] : p.Lc;
   n = n < 1 ? 1 : (n > p.Lc ? p.Lc : n);
   const int cur = (n - 1) / p.block;
-  const float* sc = p.scores + (int64_t)row * p.Nb;
+  const int hs = p.per_group ? hk : hk * p.G + (active ? r : 0);
+  const int64_t row = (int64_t)b * p.Hs + hs;
   if (lane == 0) {
     s_cnt[w] = 0;
     s_thr[w] = 0ull;
   }
   __builtin_amdgcn_wave_barrier();
-  constexpr int U = 32;  // chunks of 64 candidates loaded together
-  for (int c0 = 0; c0 < cur; c0 += 64 * U) {
-    float sv[U];
+  if (active) {
+    const float* sc = p.scores + row * p.Nb;
+    constexpr int U = 32;  // chunks of 64 candidates loaded together
+    for (int c0 = q * 64 * U; c0 < cur; c0 += wpr * 64 * U) {
+      float sv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = c0 + u * 64 + lane;
-      sv[u] = j < cur ? sc[j] : 0.f;
-    }
+      for (int u = 0; u < U; ++u) {
+        const int j = c0 + u * 64 + lane;
+        sv[u] = j < cur ? sc[j] : 0.f;
+      }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = c0 + u * 64 + lane;
-      const uint64_t key = j < cur ? make_key(sv[u], (uint32_t)j) : 0ull;
-      const bool hit = key > s_thr[w];
-      const uint64_t m = __ballot(hit);
-      if (m) {
-        const int c = s_cnt[w];
-        if (hit) s_buf[w][c + __popcll(m & ((1ull << lane) - 1ull))] = key;
-        __builtin_amdgcn_wave_barrier();
-        if (lane == 0) s_cnt[w] = c + __popcll(m);
-        __builtin_amdgcn_wave_barrier();
-        if (s_cnt[w] > CAP - 64) row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+      for (int u = 0; u < U; ++u) {
+        const int j = c0 + u * 64 + lane;
+        const uint64_t key = j < cur ? make_key(sv[u], (uint32_t)j) : 0ull;
+        const bool hit = key > s_thr[w];
+        const uint64_t m = __ballot(hit);
+        if (m) {
+          const int c = s_cnt[w];
+          if (hit) s_buf[w][c + __popcll(m & ((1ull << lane) - 1ull))] = key;
+          __builtin_amdgcn_wave_barrier();
+          if (lane == 0) s_cnt[w] = c + __popcll(m);
+          __builtin_amdgcn_wave_barrier();
+          if (s_cnt[w] > CAP - 64) row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+        }
       }
     }
+    row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
   }
-  row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
-  const int cnt = s_cnt[w];
-  int idx = lane < cnt ? (int)key_index(s_buf[w][lane]) : 0x7FFFFFFF;
-  idx = wave_sort_asc_i32(idx);
-  int32_t* out = p.sel + (int64_t)row * p.sel_w;
-  for (int e = lane; e < p.sel_w; e += 64) out[e] = e < cnt ? idx : (e == cnt ? cur : -1);
+  // pairwise merges of a row's shares: wave q absorbs wave q + st (at most
+  // 2k keys, within the buffer), keeps the best k
+  for (int st = 1; st < wpr; st <<= 1) {
+    __syncthreads();
+    if (active && (q % (2 * st)) == 0 && q + st < wpr) {
+      const int c = s_cnt[w], co = s_cnt[w + st];
+      for (int e = lane; e < co; e += 64) s_buf[w][c + e] = s_buf[w + st][e];
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 0) s_cnt[w] = c + co;
+      __builtin_amdgcn_wave_barrier();
+      row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+    }
+  }
+  if (active && q == 0) {
+    const int cnt = s_cnt[w];
+    int idx = lane < cnt ? (int)key_index(s_buf[w][lane]) : 0x7FFFFFFF;
+    idx = wave_sort_asc_i32(idx);
+    int32_t* out = p.sel + row * p.sel_w;
+    for (int e = lane; e < p.sel_w; e += 64) {
+      const int val = e < cnt ? idx : (e == cnt ? cur : -1);
+      out[e] = val;
+      s_sel[r][e] = val;
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int total = unite_rows(s_sel, nrow, p.sel_w, p.G, p.per_group != 0, s_v, p.ulist + (int64_t)bh * p.umax);
+    if (lane == 0) p.ucount[bh] = total;
+  }
 }
 
 bool launch_decode_gate(const DecodeGateParams& p, hipStream_t s) {
@@ -180,76 +269,14 @@ bool launch_decode_gate(const DecodeGateParams& p, hipStream_t s) {
   }
   if (!launch_ok("decode_scores")) return false;
   {
-    LaunchScope ls("decode_topk", s);
-    const unsigned grid = (unsigned)((p.B * p.Hs + 3) / 4);
+    LaunchScope ls("decode_select", s);
+    const unsigned grid = (unsigned)(p.B * p.Hkv);
     if (2 * p.topk + 64 <= 128)
-      hipLaunchKernelGGL(decode_topk_kernel<2>, dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(decode_select_kernel<2>, dim3(grid), dim3(1024), 0, s, p);
     else
-      hipLaunchKernelGGL(decode_topk_kernel<4>, dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(decode_select_kernel<4>, dim3(grid), dim3(1024), 0, s, p);
   }
-  return launch_ok("decode_topk");
-}
-
-// Union of the selections of the heads of one (b, kv head): distinct block ids
-// ascending, each with a bit mask of the heads that chose it.
-__global__ __launch_bounds__(64) void decode_union_kernel(DecodeAttnParams p) {
-  constexpr int V = 8;  // up to 512 (head, block) pairs
-  __shared__ uint64_t s_v[64 * V];
-  const int lane = threadIdx.x;
-  const int bh = blockIdx.x;
-  const int b = bh / p.Hkv, hk = bh % p.Hkv;
-  const int nrow = p.per_group ? 1 : p.G;
-  const int w = p.topk + 1;
-  uint64_t v[V];
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int e = i * 64 + lane;
-    uint64_t key = 0ull;
-    if (e < nrow * w) {
-      const int hh = e / w, s = e % w;
-      const int hs = p.per_group ? hk : hk * p.G + hh;
-      const int j = p.sel[((int64_t)b * p.Hs + hs) * w + s];
-      if (j >= 0) {
-        const uint64_t val = ((uint64_t)(uint32_t)j << 8) | (uint64_t)hh;
-        key = ~val;  // descending sort of ~val = ascending val; empty slots (0) last
-      }
-    }
-    v[i] = key;
-  }
-  wave_sort_desc<V>(v);
-#pragma unroll
-  for (int i = 0; i < V; ++i) s_v[i * 64 + lane] = v[i];
-  __builtin_amdgcn_wave_barrier();
-  __syncthreads();
-  // element e starts a run of equal block ids when its id differs from
-  // element e-1's; a run holds at most G entries (one per head)
-  int32_t* out = p.ulist + (int64_t)bh * p.umax;
-  int total = 0;
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int e = i * 64 + lane;
-    const uint64_t key = s_v[e];
-    bool head = false;
-    int val = 0;
-    if (key != 0ull) {
-      const uint64_t vv = ~key;
-      const int j = (int)(vv >> 8);
-      head = e == 0 || (int)((~s_v[e - 1]) >> 8) != j;
-      if (head) {
-        int mask = 0;
-        for (int f = e; f < 64 * V && f < e + 8; ++f) {
-          const uint64_t kf = s_v[f];
-          if (kf == 0ull || (int)((~kf) >> 8) != j) break;
-          mask |= p.per_group ? ((1 << p.G) - 1) : (1 << (int)((~kf) & 255));
-        }
-        val = (j << 8) | mask;
-      }
-    }
-    const uint64_t hm = __ballot(head);
-    if (head) out[total + __popcll(hm & ((1ull << lane) - 1ull))] = val;
-    total += __popcll(hm);
-  }
-  if (lane == 0) p.ucount[bh] = total;
+  return launch_ok("decode_select");
 }
 
 // One workgroup per (b, kv head, distinct block): scores for the heads that
@@ -481,14 +508,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnParams p)
   if (lane + 64 < p.D) dst[lane + 64] = f2bf(a1 * inv);
   if (p.lse_out && lane == 0)
     p.lse_out[(int64_t)b * p.Hq + h] = l > 0.f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY;
-}
-
-bool launch_decode_union(const DecodeAttnParams& p, hipStream_t s) {
-  {
-    LaunchScope ls("decode_union", s);
-    hipLaunchKernelGGL(decode_union_kernel, dim3(p.B * p.Hkv), dim3(64), 0, s, p);
-  }
-  return launch_ok("decode_union");
 }
 
 bool launch_decode_attend(const DecodeAttnParams& p, hipStream_t s) {

@@ -76,8 +76,14 @@ __global__ __launch_bounds__(256) void csr_scatter_kernel(CsrParams p, int64_t n
 constexpr int kHistMax = 8192;   // blocks per (b, kv head) handled in LDS
 constexpr int kRowsPerWG = 1024; // selection rows per workgroup
 
-// rows [ra, rb) of sel and the first bucket of segment `seg`, piece `piece`
-BSA_DEV bool seg_rows(const CsrParams& p, int seg, int piece, int64_t& ra, int64_t& rb, int& base) {
+// A workgroup's piece of a segment: rows [ra, ra + nrows) of sel (tokens
+// t0 ..), the segment's first bucket and head-in-group field.
+struct SegPiece {
+  int64_t ra;
+  int nrows, t0, base, hh;
+};
+
+BSA_DEV bool seg_rows(const CsrParams& p, int seg, int piece, SegPiece& sp) {
   const int c = seg % p.NC;
   int rest = seg / p.NC;
   const int hh = rest % p.Gs;
@@ -87,50 +93,71 @@ BSA_DEV bool seg_rows(const CsrParams& p, int seg, int piece, int64_t& ra, int64
   const int hs = p.per_group ? hk : hk * p.G + hh;
   const int t0 = c * p.CT + piece * kRowsPerWG;
   const int t1 = min(min(t0 + kRowsPerWG, c * p.CT + p.CT), p.Lq);
-  const int64_t r0 = ((int64_t)b * p.Hs + hs) * p.Lq;
-  ra = r0 + t0;
-  rb = r0 + t1;
-  base = ((b * p.Hkv + hk) * p.NC + c) * p.Nb;
+  sp.ra = ((int64_t)b * p.Hs + hs) * p.Lq + t0;
+  sp.nrows = t1 - t0;
+  sp.t0 = t0;
+  sp.base = ((b * p.Hkv + hk) * p.NC + c) * p.Nb;
+  sp.hh = p.per_group ? 0 : hh;
   return t0 < t1;
+}
+
+// Entry li (row li / sel_w, slot li % sel_w) of a piece; the quotient comes
+// from a float reciprocal corrected by one step (li < 2^24).
+BSA_DEV bool piece_entry(const CsrParams& p, const SegPiece& sp, int li, float inv_w, int& bucket, uint32_t& packed) {
+  int lr = (int)((float)li * inv_w);
+  if (lr * p.sel_w > li) --lr;
+  else if ((lr + 1) * p.sel_w <= li) ++lr;
+  const int slot = li - lr * p.sel_w;
+  if (slot >= p.kslot) return false;
+  const int j = p.sel[sp.ra * p.sel_w + li];
+  if (j < 0) return false;
+  bucket = sp.base + j;
+  packed = ((uint32_t)(sp.t0 + lr) << p.sh_t) | ((uint32_t)sp.hh << p.sh_h) | (uint32_t)slot;
+  return true;
 }
 
 __global__ __launch_bounds__(256) void csr_count_lds_kernel(CsrParams p) {
   __shared__ int hist[kHistMax];
-  int64_t ra, rb;
-  int base;
-  if (!seg_rows(p, blockIdx.x, blockIdx.y, ra, rb, base)) return;  // uniform
+  SegPiece sp;
+  if (!seg_rows(p, blockIdx.x, blockIdx.y, sp)) return;  // uniform
   for (int j = threadIdx.x; j < p.Nb; j += 256) hist[j] = 0;
   __syncthreads();
-  for (int64_t i = ra * p.sel_w + threadIdx.x; i < rb * p.sel_w; i += 256) {
-    const SelEntry e = decode_sel(p, i);
-    if (e.valid) atomicAdd(&hist[e.bucket - base], 1);
+  const float inv_w = 1.0f / (float)p.sel_w;
+  const int ne = sp.nrows * p.sel_w;
+  for (int li = threadIdx.x; li < ne; li += 256) {
+    int bucket;
+    uint32_t packed;
+    if (piece_entry(p, sp, li, inv_w, bucket, packed)) atomicAdd(&hist[bucket - sp.base], 1);
   }
   __syncthreads();
   for (int j = threadIdx.x; j < p.Nb; j += 256)
-    if (hist[j]) atomicAdd(&p.counts[base + j], hist[j]);
+    if (hist[j]) atomicAdd(&p.counts[sp.base + j], hist[j]);
 }
 
 __global__ __launch_bounds__(256) void csr_scatter_lds_kernel(CsrParams p) {
   __shared__ int hist[kHistMax];
-  int64_t ra, rb;
-  int base;
-  if (!seg_rows(p, blockIdx.x, blockIdx.y, ra, rb, base)) return;  // uniform
+  SegPiece sp;
+  if (!seg_rows(p, blockIdx.x, blockIdx.y, sp)) return;  // uniform
   for (int j = threadIdx.x; j < p.Nb; j += 256) hist[j] = 0;
   __syncthreads();
-  for (int64_t i = ra * p.sel_w + threadIdx.x; i < rb * p.sel_w; i += 256) {
-    const SelEntry e = decode_sel(p, i);
-    if (e.valid) atomicAdd(&hist[e.bucket - base], 1);
+  const float inv_w = 1.0f / (float)p.sel_w;
+  const int ne = sp.nrows * p.sel_w;
+  for (int li = threadIdx.x; li < ne; li += 256) {
+    int bucket;
+    uint32_t packed;
+    if (piece_entry(p, sp, li, inv_w, bucket, packed)) atomicAdd(&hist[bucket - sp.base], 1);
   }
   __syncthreads();
   // reserve this workgroup's range in every bucket it touches
   for (int j = threadIdx.x; j < p.Nb; j += 256) {
     const int c = hist[j];
-    if (c) hist[j] = p.bucket_off[base + j] + atomicAdd(&p.cursor[base + j], c);
+    if (c) hist[j] = p.bucket_off[sp.base + j] + atomicAdd(&p.cursor[sp.base + j], c);
   }
   __syncthreads();
-  for (int64_t i = ra * p.sel_w + threadIdx.x; i < rb * p.sel_w; i += 256) {
-    const SelEntry e = decode_sel(p, i);
-    if (e.valid) p.entries[atomicAdd(&hist[e.bucket - base], 1)] = e.packed;
+  for (int li = threadIdx.x; li < ne; li += 256) {
+    int bucket;
+    uint32_t packed;
+    if (piece_entry(p, sp, li, inv_w, bucket, packed)) p.entries[atomicAdd(&hist[bucket - sp.base], 1)] = packed;
   }
 }
 

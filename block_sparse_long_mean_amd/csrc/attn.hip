@@ -516,8 +516,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
       const int64_t pidx = (prow * p.kslot + g.slot) * p.R + g.rr;
       if (wave_on) store_partials<D, W>(qst, pk, pidx * D, min(32, rec.z - w * 32), p.part_o);
       if (g.valid && hq == 0) {
-        __builtin_nontemporal_store(m, &p.part_ml[pidx].x);
-        __builtin_nontemporal_store(l, &p.part_ml[pidx].y);
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(f32x2{m, l}, reinterpret_cast<f32x2*>(&p.part_ml[pidx]));
       }
     }
     if (!has_next) break;
@@ -583,8 +583,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
       if (s < n) {
         const int64_t pidx = (prow * p.kslot + s) * p.R + rr;
         // streaming loads: every partial is read exactly once
-        ml[u].x = __builtin_nontemporal_load(&p.part_ml[pidx].x);
-        ml[u].y = __builtin_nontemporal_load(&p.part_ml[pidx].y);
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 v2 = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(&p.part_ml[pidx]));
+        ml[u] = make_float2(v2[0], v2[1]);
         ov[u] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p.part_o + pidx * D + li * 8));
       }
     }

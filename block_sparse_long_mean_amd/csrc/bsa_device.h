@@ -94,6 +94,32 @@ BSA_DEV uint64_t row_xor64(uint64_t v, int li) {
     return (li & 4) ? dn : up;
   }
 }
+// row_xor64 with a stride that is a constant once the caller's loops unroll
+BSA_DEV uint64_t row_xor64_any(uint64_t v, int m, int li) {
+  switch (m) {
+    case 1: return row_xor64<1>(v, li);
+    case 2: return row_xor64<2>(v, li);
+    case 4: return row_xor64<4>(v, li);
+    default: return row_xor64<8>(v, li);
+  }
+}
+
+// 32-bit value held by lane (li ^ m) of the same 16-lane row, m in {1, 2, 4, 8}
+BSA_DEV int row_xor32_any(int v, int m, int li) {
+  const uint32_t u = (uint32_t)v;
+  switch (m) {
+    case 1: return (int)dpp32<0xB1>(u, u);
+    case 2: return (int)dpp32<0x4E>(u, u);
+    case 4: {
+      // both exchanges run on every lane (a lane must not read a lane that a
+      // branch has switched off), then each lane keeps its partner's value
+      const uint32_t up = dpp32<0x104>(u, u), dn = dpp32<0x114>(u, u);
+      return (int)((li & 4) ? dn : up);
+    }
+    default: return (int)dpp32<0x128>(u, u);
+  }
+}
+
 // value held by lane `src` (wave-uniform)
 BSA_DEV uint64_t readlane64(uint64_t v, int src) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
@@ -151,7 +177,8 @@ BSA_DEV void wave_sort_desc(uint64_t (&v)[V]) {
       } else {
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-          const uint64_t o = shfl_xor64(v[i], stride);
+          // strides inside a 16-lane row through DPP, wider ones through LDS
+          const uint64_t o = stride < 16 ? row_xor64_any(v[i], stride, lane & 15) : shfl_xor64(v[i], stride);
           const int e = i * 64 + lane;
           const bool lower = (lane & stride) == 0;
           const bool desc = (e & size) == 0;
@@ -172,7 +199,7 @@ BSA_DEV int wave_sort_asc_i32(int v) {
   for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int o = __shfl_xor(v, stride, 64);
+      const int o = stride < 16 ? row_xor32_any(v, stride, lane & 15) : __shfl_xor(v, stride, 64);
       const bool lower = (lane & stride) == 0;
       const bool asc = (lane & size) == 0;
       const bool keep_min = (lower == asc);

@@ -131,16 +131,6 @@ BSA_DEV void emit_row(const GateParams& p, const uint64_t* buf, int cnt, int b, 
 // descending; unused elements are 0.  New candidates are merged 16 at a time
 // with a bitonic merge; all four lane groups merge into their own rows at once.
 // ---------------------------------------------------------------------------
-// row_xor64 with a stride that is a constant once the caller's loops unroll
-BSA_DEV uint64_t row_xor64_any(uint64_t v, int m, int li) {
-  switch (m) {
-    case 1: return row_xor64<1>(v, li);
-    case 2: return row_xor64<2>(v, li);
-    case 4: return row_xor64<4>(v, li);
-    default: return row_xor64<8>(v, li);
-  }
-}
-
 // Bitonic sort, ascending, of the 16 keys a 16-lane group holds (one per
 // lane); every group sorts its own keys.
 BSA_DEV uint64_t group_sort16_asc(uint64_t v, int li) {
@@ -194,22 +184,6 @@ BSA_DEV void list_merge16(uint64_t (&L)[KR], uint64_t b, int li, int topk) {
 #pragma unroll
   for (int m = 0; m < KR; ++m)
     if (m * 16 + li >= topk) L[m] = 0ull;
-}
-
-// 32-bit value held by lane (li ^ m) of the same 16-lane row, m in {1, 2, 4, 8}
-BSA_DEV int row_xor32_any(int v, int m, int li) {
-  const uint32_t u = (uint32_t)v;
-  switch (m) {
-    case 1: return (int)dpp32<0xB1>(u, u);
-    case 2: return (int)dpp32<0x4E>(u, u);
-    case 4: {
-      // both exchanges run on every lane (a lane must not read a lane that a
-      // branch has switched off), then each lane keeps its partner's value
-      const uint32_t up = dpp32<0x104>(u, u), dn = dpp32<0x114>(u, u);
-      return (int)((li & 4) ? dn : up);
-    }
-    default: return (int)dpp32<0x128>(u, u);
-  }
 }
 
 // Ascending bitonic sort of the 16*NR ints a 16-lane group holds (element

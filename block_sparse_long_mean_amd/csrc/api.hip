@@ -124,6 +124,9 @@ struct PrefillPlan {
 // consecutive work items a gather workgroup takes at a time (runs are dealt
 // round-robin to the workgroups of an XCD)
 constexpr int kGatherRun = 64;
+// below this many rows per selected (b, kv head, block) on average, the
+// gather takes the sparse-bucket kernel
+constexpr int kSparseRows = 8;
 // query bytes of one (b, kv head) chunk of the default chunk size
 constexpr int64_t kChunkQueryBytes = (int64_t)64 << 20;
 
@@ -429,6 +432,14 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
   ap.grid = P.attn_grid;
   ap.rows_item = 32 * gather_waves(a->block);
   ap.run_items = kGatherRun;
+  // a few rows per selected block on average (a short query chunk over a very
+  // long memory): the sparse-bucket gather streams each block from HBM
+  // instead of staging it for an MFMA tile of mostly empty rows.  The test
+  // counts blocks per (b, kv head), not buckets, so that the query chunking
+  // (a scheduling choice) never changes which kernel computes a result.
+  const double blocks = (double)a->B * a->Hkv * P.Nb;
+  ap.sparse_items = (double)P.max_entries * P.R < kSparseRows * blocks && P.max_items < ((int64_t)1 << 31)
+                        ? P.max_items : 0;
   ap.part_o = P.part_o; ap.part_ml = P.part_ml;
   ap.sel = P.sel; ap.sel_w = P.sel_w;
   ap.o = reinterpret_cast<uint16_t*>(a->o); ap.os_b = a->o_stride[0]; ap.os_t = a->o_stride[1]; ap.os_h = a->o_stride[2];

@@ -138,6 +138,7 @@ struct AttnParams {
   int grid;                // persistent workgroups
   int rows_item;           // rows per work item: 32 per wave of a gather workgroup
   int run_items;           // consecutive items a gather workgroup takes at a time
+  int64_t sparse_items;    // > 0: sparse-bucket gather, one workgroup per item (grid = this bound)
   // partials of the launch's chunks, row ((c - c0) * Gs + head-sel) * CT + token-in-chunk
   uint16_t* part_o;        // [rows * kslot * R, D] bf16, sum_k p_k v_k with p = 2^(s*sl2 - m)
   float2* part_ml;         // (m, l): log2-domain running max and sum of p

@@ -531,29 +531,25 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
 // ---------------------------------------------------------------------------
 // Gather for sparse buckets (a few rows per selected block, as when a short
 // query chunk selects from a very long memory): the MFMA gather would stage
-// each block for one or two rows.  Here one workgroup takes one work item
-// and streams its block's keys and values straight from HBM, flash-decoding
-// style: 16 lanes per key row for the scores (8 head dims each, summed
-// across the row's lanes), an fp32 online softmax per row, and (key group,
-// 8-dim chunk) threads for the weighted values, reduced through LDS.  Rows go
-// four at a time; the partials have the gather's format.
+// each block for one or two rows.  Here one wave takes one work item and
+// streams its block's keys and values straight from HBM, flash-decoding
+// style, with no workgroup barrier (so many items per CU are in flight):
+// lane k scores key k of a 64-key pass against the rows' queries (read from
+// LDS by broadcast), an fp32 online softmax per row runs across the wave, and
+// for the weighted values each lane owns D/64 head dims and takes every key's
+// probability by v_readlane.  Rows go four at a time; the partials have the
+// gather's format.
 template <int D>
 __global__ __launch_bounds__(256) void attn_sparse_kernel(AttnParams p) {
-  constexpr int NR = 4;          // rows per pass
-  constexpr int KC = 64;         // keys per pass
-  constexpr int CPR = D / 8;     // lanes per key row (scores) / dim chunks (values)
-  constexpr int RPP = 256 / CPR; // key rows per score step
-  constexpr int KG = 256 / CPR;  // key groups (values)
-  constexpr int KPG = KC / KG;   // keys per group
-  __shared__ float s_q[NR][D];
-  __shared__ float s_s[NR][KC];
-  __shared__ float s_m[NR], s_l[NR], s_c[NR];
-  __shared__ float s_red[KG][D];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int NR = 4;        // rows per pass
+  constexpr int DPL = D / 64;  // head dims per lane (values)
+  __shared__ __attribute__((aligned(16))) float s_q[4][NR][D];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int it_lo = p.tile_off[(int64_t)p.c0 * p.Nb];
   const int nitems = p.tile_off[(int64_t)p.c1 * p.Nb] - it_lo;
-  if ((int)blockIdx.x >= nitems) return;  // uniform
-  const int4 rec = load_item((const_int_ptr)p.items, it_lo + (int)blockIdx.x);
+  const int item = (int)blockIdx.x * 4 + w;
+  if (item >= nitems) return;  // wave-uniform; no workgroup barrier follows
+  const int4 rec = load_item((const_int_ptr)p.items, it_lo + item);
   const int bucket = rec.x, hk = rec.w & 0xFFFF, b = rec.w >> 16;
   const int cid = bucket / p.Nb;
   const int j = bucket - cid * p.Nb;
@@ -563,137 +559,121 @@ __global__ __launch_bounds__(256) void attn_sparse_kernel(AttnParams p) {
   const int n_keys = min(p.block, p.Lk - key0);
   const uint16_t* kb = p.k + (int64_t)b * p.ks_b + (int64_t)hk * p.ks_h;
   const uint16_t* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
-  const int dc = tid % CPR, kg = tid / CPR;
   for (int r0 = 0; r0 < rec.z; r0 += NR) {
     const int nr = min(NR, rec.z - r0);
-    __syncthreads();  // the previous rows' LDS state is no longer read
-    for (int idx = tid; idx < NR * D; idx += 256) {
-      const int a = idx / D, d = idx % D;
-      float x = 0.f;
-      if (a < nr) {
-        const int lr = r0 + a;
-        const GRow g = grow_of(p, rec, entry_of(p, rec, lr), lr);
-        x = bf2f(q_row<D>(p, rec, g)[d]);
-      }
-      s_q[a][d] = x;
-    }
-    if (tid < NR) {
-      s_m[tid] = -INFINITY;
-      s_l[tid] = 0.f;
-    }
-    // each lane's row positions, for the causal mask
+    GRow g[NR];
     int qpos[NR];
 #pragma unroll
     for (int a = 0; a < NR; ++a) {
       const int lr = r0 + (a < nr ? a : 0);
-      const GRow g = grow_of(p, rec, entry_of(p, rec, lr), lr);
-      qpos[a] = p.causal ? p.Lk - p.Lq + g.t : 0x7FFFFFFF;
+      g[a] = grow_of(p, rec, entry_of(p, rec, lr), lr);
+      qpos[a] = p.causal ? p.Lk - p.Lq + g[a].t : 0x7FFFFFFF;
     }
-    float acc[NR][8];
+    __builtin_amdgcn_wave_barrier();  // the previous rows' queries are no longer read
 #pragma unroll
-    for (int a = 0; a < NR; ++a)
+    for (int a = 0; a < NR; ++a) {
+      const uint16_t* qr = q_row<D>(p, rec, g[a]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
-    __syncthreads();
-    for (int k0 = 0; k0 < n_keys; k0 += KC) {
-      const int nk = min(KC, n_keys - k0);
-      // this pass's values, loaded now so they are in flight with the keys
-      u16x8 vx[KPG];
+      for (int d = lane; d < D; d += 64) s_q[w][a][d] = a < nr ? bf2f(qr[d]) : 0.f;
+    }
+    __builtin_amdgcn_wave_barrier();
+    float m[NR], l[NR], acc[NR][DPL];
 #pragma unroll
-      for (int kk = 0; kk < KPG; ++kk) {
-        const int key = kg * KPG + kk;
-        vx[kk] = key < nk ? ld16(vb + (int64_t)(key0 + k0 + key) * p.vs_t + dc * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-      {
-        const int c = tid % CPR, rsub = tid / CPR;
-        float qv[NR][8];
+    for (int a = 0; a < NR; ++a) {
+      m[a] = -INFINITY;
+      l[a] = 0.f;
 #pragma unroll
-        for (int a = 0; a < NR; ++a)
+      for (int e = 0; e < DPL; ++e) acc[a][e] = 0.f;
+    }
+    for (int k0 = 0; k0 < n_keys; k0 += 64) {
+      asm volatile("" ::: "memory");  // the query reads below stay in the pass (not hoisted: 4 rows x D floats)
+      const int key = k0 + lane;
+      const bool kv = key < n_keys;
+      const uint16_t* krow = kb + (int64_t)(key0 + (kv ? key : 0)) * p.ks_t;
+      // scores of this lane's key against the rows, 8 head dims at a time
+      float sc[NR];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qv[a][e] = s_q[a][c * 8 + e];
-        u16x8 kx[KC / RPP];
+      for (int a = 0; a < NR; ++a) sc[a] = 0.f;
+      // four 16-byte pieces of the key row at a time, the next four in flight
+      u16x8 kx[4], kn[4];
 #pragma unroll
-        for (int ps = 0; ps < KC / RPP; ++ps) {
-          const int key = ps * RPP + rsub;
-          kx[ps] = key < nk ? ld16(kb + (int64_t)(key0 + k0 + key) * p.ks_t + c * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
+      for (int c = 0; c < 4; ++c) kx[c] = kv ? ld16(krow + c * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 1
+      for (int c0 = 0; c0 < D / 8; c0 += 4) {
 #pragma unroll
-        for (int ps = 0; ps < KC / RPP; ++ps) {
-          const int key = ps * RPP + rsub;
-          float kf[8];
+        for (int c = 0; c < 4; ++c)
+          kn[c] = (kv && c0 + 4 < D / 8) ? ld16(krow + (c0 + 4 + c) * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kf[e] = bf2f(kx[ps][e]);
+        for (int c = 0; c < 4; ++c) {
 #pragma unroll
           for (int a = 0; a < NR; ++a) {
-            float part = 0.f;
+            const f32x4 q0 = *reinterpret_cast<const f32x4*>(&s_q[w][a][(c0 + c) * 8]);
+            const f32x4 q1 = *reinterpret_cast<const f32x4*>(&s_q[w][a][(c0 + c) * 8 + 4]);
+            float part = sc[a];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) part = fmaf(qv[a][e], kf[e], part);
+            for (int e = 0; e < 4; ++e) part = fmaf(q0[e], bf2f(kx[c][e]), part);
 #pragma unroll
-            for (int m2 = 1; m2 < CPR; m2 <<= 1) part += __shfl_xor(part, m2, 64);
-            const int kpos = key0 + k0 + key;
-            if (c == 0) s_s[a][key] = (key < nk && kpos <= qpos[a]) ? part * p.sl2 : -INFINITY;
+            for (int e = 0; e < 4; ++e) part = fmaf(q1[e], bf2f(kx[c][4 + e]), part);
+            sc[a] = part;
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kx[c] = kn[c];
+      }
+      // this pass's values: lane owns head dims lane*DPL .. +DPL-1 of every key
+      const int nk = min(64, n_keys - k0);
+      float pr[NR];
+#pragma unroll
+      for (int a = 0; a < NR; ++a) {
+        const float x = (kv && key0 + key <= qpos[a]) ? sc[a] * p.sl2 : -INFINITY;
+        const float mnew = fmaxf(m[a], wave_max(x));
+        const float e0 = mnew == -INFINITY ? 0.f : exp2f(x - mnew);
+        const float c = mnew == -INFINITY ? 1.f : exp2f(m[a] - mnew);
+        l[a] = l[a] * c + wave_sum(e0);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[a][e] *= c;
+        m[a] = mnew;
+        pr[a] = e0;
+      }
+      for (int kk0 = 0; kk0 < nk; kk0 += 16) {
+        uint32_t vx[16];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const int kq = kk0 + kk;
+          const uint16_t* vr = vb + (int64_t)(key0 + k0 + (kq < nk ? kq : 0)) * p.vs_t + lane * DPL;
+          vx[kk] = kq < nk ? (DPL == 2 ? *reinterpret_cast<const uint32_t*>(vr) : (uint32_t)*vr) : 0u;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const int kq = kk0 + kk;
+          if (kq < nk) {  // wave-uniform
+            const float v0 = bf2f((uint16_t)(vx[kk] & 0xFFFFu)), v1 = bf2f((uint16_t)(vx[kk] >> 16));
+#pragma unroll
+            for (int a = 0; a < NR; ++a) {
+              const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr[a]), kq));
+              acc[a][0] = fmaf(pw, v0, acc[a][0]);
+              if constexpr (DPL == 2) acc[a][1] = fmaf(pw, v1, acc[a][1]);
+            }
           }
         }
       }
-      __syncthreads();
-      // softmax statistics per row (wave w handles rows w and w + 4)
-      for (int a = w; a < NR; a += 4) {
-        const float x = lane < KC ? s_s[a][lane] : -INFINITY;
-        const float mx = wave_max(x);
-        const float mold = s_m[a];
-        const float mnew = fmaxf(mold, mx);
-        const float e0 = mnew == -INFINITY ? 0.f : exp2f(x - mnew);
-        if (lane < KC) s_s[a][lane] = e0;
-        const float sum = wave_sum(e0);
-        if (lane == 0) {
-          const float c = mnew == -INFINITY ? 1.f : exp2f(mold - mnew);
-          s_c[a] = c;
-          s_l[a] = s_l[a] * c + sum;
-          s_m[a] = mnew;
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int a = 0; a < NR; ++a) {
-        const float c = s_c[a];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[a][e] *= c;
-      }
-#pragma unroll
-      for (int kk = 0; kk < KPG; ++kk) {
-        const int key = kg * KPG + kk;
-        float vf[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[e] = bf2f(vx[kk][e]);
-#pragma unroll
-        for (int a = 0; a < NR; ++a) {
-          const float pw = s_s[a][key];  // 0 past nk and for masked keys
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(pw, vf[e], acc[a][e]);
-        }
-      }
-      __syncthreads();
     }
-    // reduce the key groups; write each row's partial (sum p v, m, l)
+    // partial rows: lane writes its head dims; lane 0 writes (m, l)
     for (int a = 0; a < nr; ++a) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_red[kg][dc * 8 + e] = acc[a][e];
-      __syncthreads();
-      const int lr = r0 + a;
-      const GRow g = grow_of(p, rec, entry_of(p, rec, lr), lr);
-      const int hsel = p.per_group ? 0 : g.hs - hk * p.G;
-      const int64_t prow = (prow_base + hsel) * p.CT + (g.t - t_base);
-      const int64_t pidx = (prow * p.kslot + g.slot) * p.R + g.rr;
-      if (tid < D) {
-        float sum = 0.f;
-        for (int q = 0; q < KG; ++q) sum += s_red[q][tid];
-        __builtin_nontemporal_store(f2bf(sum), p.part_o + pidx * D + tid);
+      const int hsel = p.per_group ? 0 : g[a].hs - hk * p.G;
+      const int64_t prow = (prow_base + hsel) * p.CT + (g[a].t - t_base);
+      const int64_t pidx = (prow * p.kslot + g[a].slot) * p.R + g[a].rr;
+      uint16_t* dst = p.part_o + pidx * D + lane * DPL;
+      if constexpr (DPL == 2) {
+        const uint32_t packed = (uint32_t)f2bf(acc[a][0]) | ((uint32_t)f2bf(acc[a][1]) << 16);
+        __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t*>(dst));
+      } else {
+        __builtin_nontemporal_store(f2bf(acc[a][0]), dst);
       }
-      if (tid == 0) {
+      if (lane == 0) {
         typedef float f32x2 __attribute__((ext_vector_type(2)));
-        __builtin_nontemporal_store(f32x2{s_m[a], s_l[a]}, reinterpret_cast<f32x2*>(&p.part_ml[pidx]));
+        __builtin_nontemporal_store(f32x2{m[a], l[a]}, reinterpret_cast<f32x2*>(&p.part_ml[pidx]));
       }
-      __syncthreads();
     }
   }
 }
@@ -818,10 +798,11 @@ static void launch_gather_dw(const AttnParams& p, hipStream_t s) {
 bool launch_attn_gather(const AttnParams& p, hipStream_t s) {
   if (p.sparse_items > 0) {
     LaunchScope ls("attn_gather", s, 2);
+    const unsigned grid = (unsigned)((p.sparse_items + 3) / 4);  // one wave per item
     if (p.D == 128)
-      hipLaunchKernelGGL(attn_sparse_kernel<128>, dim3((unsigned)p.sparse_items), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(attn_sparse_kernel<128>, dim3(grid), dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL(attn_sparse_kernel<64>, dim3((unsigned)p.sparse_items), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(attn_sparse_kernel<64>, dim3(grid), dim3(256), 0, s, p);
     return launch_ok("attn_gather");
   }
   {

@@ -537,11 +537,11 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
 // lane k scores key k of a 64-key pass against the rows' queries (read from
 // LDS by broadcast), an fp32 online softmax per row runs across the wave, and
 // for the weighted values each lane owns D/64 head dims and takes every key's
-// probability by v_readlane.  Rows go four at a time; the partials have the
+// probability by v_readlane.  Rows go two at a time; the partials have the
 // gather's format.
 template <int D>
 __global__ __launch_bounds__(256) void attn_sparse_kernel(AttnParams p) {
-  constexpr int NR = 4;        // rows per pass
+  constexpr int NR = 2;        // rows per pass (most sparse buckets hold one or two)
   constexpr int DPL = D / 64;  // head dims per lane (values)
   __shared__ __attribute__((aligned(16))) float s_q[4][NR][D];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(256) void attn_sparse_kernel(AttnParams p) {
       for (int e = 0; e < DPL; ++e) acc[a][e] = 0.f;
     }
     for (int k0 = 0; k0 < n_keys; k0 += 64) {
-      asm volatile("" ::: "memory");  // the query reads below stay in the pass (not hoisted: 4 rows x D floats)
+      asm volatile("" ::: "memory");  // the query reads below stay in the pass (not hoisted: NR rows x D floats)
       const int key = k0 + lane;
       const bool kv = key < n_keys;
       const uint16_t* krow = kb + (int64_t)(key0 + (kv ? key : 0)) * p.ks_t;

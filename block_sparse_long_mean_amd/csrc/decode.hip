@@ -206,6 +206,22 @@ __global__ __launch_bounds__(1024) void decode_select_kernel(DecodeGateParams p)
         const int j = c0 + u * 64 + lane;
         sv[u] = j < cur ? sc[j] : 0.f;
       }
+      if (c0 == q * 64 * U && p.topk > 0) {
+        // starting threshold: the k-th best of the 64 lanes' maxima is a
+        // lower bound of the share's k-th best key (k distinct keys reach
+        // it), so only keys at or above it need to enter the buffer
+        uint64_t lm[1] = {0ull};
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = c0 + u * 64 + lane;
+          const uint64_t key = j < cur ? make_key(sv[u], (uint32_t)j) : 0ull;
+          lm[0] = key > lm[0] ? key : lm[0];
+        }
+        wave_sort_desc<1>(lm);
+        const uint64_t tk = shfl64(lm[0], p.topk - 1);
+        if (lane == 0 && tk > 0ull) s_thr[w] = tk - 1ull;
+        __builtin_amdgcn_wave_barrier();
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = c0 + u * 64 + lane;

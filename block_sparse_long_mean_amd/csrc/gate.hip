@@ -358,8 +358,23 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
         const int j = c0 + ct * 16 + r16;
         const bool ok = j < c_hi && j < ncand[i];
         key[ct] = ok ? make_key(acc[ct][i], (uint32_t)j) : 0ull;
-        if (key[ct] > thr[i]) pend |= 1 << ct;
       }
+      if (KR == 1 && c0 == c_lo) {
+        // first chunk, k <= 16: the smallest of the 16 lanes' maxima is a
+        // lower bound of the row's k-th best key (16 distinct keys reach it)
+        uint64_t lm = key[0];
+#pragma unroll
+        for (int ct = 1; ct < 4; ++ct) lm = key[ct] > lm ? key[ct] : lm;
+#pragma unroll
+        for (int st = 1; st < 16; st <<= 1) {
+          const uint64_t o = row_xor64_any(lm, st, r16);
+          lm = o < lm ? o : lm;
+        }
+        if (lm > 0ull) thr[i] = lm - 1ull;
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        if (key[ct] > thr[i]) pend |= 1 << ct;
       if (__ballot(pend != 0) == 0ull) continue;  // nothing new in any group
       // slots: exclusive scan of the per-lane counts over the 16-lane group
       const int n_me = __popc(pend);

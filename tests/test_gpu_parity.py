@@ -142,15 +142,18 @@ def test_bf16_query_chunks(bsa, case):
                          seed=18, doc_mean=400.0, chunk_tokens=32, chunks_per_pass=1, **kw)
 
 
-@pytest.mark.parametrize("case", ["group_d64_causal_offset", "head_block128_causal"])
+@pytest.mark.parametrize("case", ["group_d64_causal_offset", "head_block128_causal", "group_d64_passes"])
 def test_bf16_sparse_buckets(bsa, case):
     """A few query tokens over a long key sequence: a handful of rows per selected block, so the
     gather takes its sparse-bucket kernel (keys streamed from HBM, causal mask inside the query's
-    own block, blocks longer than one 64-key pass)."""
+    own block, blocks longer than one 64-key pass, query chunks in passes of three)."""
     kw = dict(dtype="bf16", atol=1e-2, rel=1e-2, lse_atol=5e-3)
     if case == "group_d64_causal_offset":
         run_prefill_case(bsa, B=2, Lq=48, Lk=40000, Hq=8, Hkv=2, D=64, block=64, topk=6, causal=True,
                          gate="group", seed=21, **kw)
+    elif case == "group_d64_passes":
+        run_prefill_case(bsa, B=2, Lq=48, Lk=40000, Hq=8, Hkv=2, D=64, block=64, topk=6, causal=True,
+                         gate="group", seed=23, chunk_tokens=16, chunks_per_pass=3, **kw)
     else:
         run_prefill_case(bsa, B=1, Lq=40, Lk=50000, Hq=4, Hkv=4, D=128, block=128, topk=5, causal=True,
                          sigma=128 ** -0.5, seed=22, **kw)

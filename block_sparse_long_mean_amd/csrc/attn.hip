@@ -214,6 +214,58 @@ BSA_DEV void stage_kv(AttnSmem<D>& sm, const uint16_t* kb, int64_t ks_t, const u
   }
 }
 
+// Blocks longer than one key tile: the next tile's keys and values are
+// copied global -> LDS by DMA in their natural layout (rows of D elements)
+// while the current tile is computed, then repacked LDS -> LDS into the
+// padded key rows and the transposed values the MFMA reads.  Rows past
+// n_valid copy row 0 of the tile (in bounds); the repack zeroes them.
+template <int D, int NT>
+BSA_DEV void dma_kv(uint16_t* nat, const uint16_t* kb, int64_t ks_t, const uint16_t* vb, int64_t vs_t, int key0,
+                    int n_valid) {
+  constexpr int CPR = D / 8;       // 16-byte pieces per row
+  constexpr int RPI = 64 / CPR;    // rows per DMA instruction (64 lanes x 16 bytes)
+  constexpr int NW = NT / 64;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int r_in = lane / CPR, c = lane % CPR;
+  for (int i = w; i < KT / RPI; i += NW) {
+    const int r = i * RPI + r_in;
+    const int rr = r < n_valid ? r : 0;
+    __builtin_amdgcn_global_load_lds((const void*)(kb + (int64_t)(key0 + rr) * ks_t + c * 8),
+                                     (lds_ptr_t)(nat + i * RPI * D), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(vb + (int64_t)(key0 + rr) * vs_t + c * 8),
+                                     (lds_ptr_t)(nat + KT * D + i * RPI * D), 16, 0, 0);
+  }
+}
+
+template <int D, int NT>
+BSA_DEV void repack_kv(AttnSmem<D>& sm, const uint16_t* nat, int n_valid) {
+  const int tid = threadIdx.x;
+  constexpr int CH = D / 8;
+  for (int idx = tid; idx < KT * CH; idx += NT) {
+    const int kr = idx / CH, ch = idx % CH;
+    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (kr < n_valid) x = *reinterpret_cast<const u16x8*>(nat + kr * D + ch * 8);
+    st16(&sm.k[kr * (D + 8) + ch * 8], x);
+  }
+  // values transposed as stage_kv writes them
+  for (int idx = tid; idx < (KT / 4) * CH; idx += NT) {
+    const int kq = idx % (KT / 4), ch = idx / (KT / 4);
+    u16x8 r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kr = kq * 4 + i;
+      r[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (kr < n_valid) r[i] = *reinterpret_cast<const u16x8*>(nat + KT * D + kr * D + ch * 8);
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      u16x4 col = {r[0][d], r[1][d], r[2][d], r[3][d]};
+      *reinterpret_cast<u16x4*>(&sm.vt[(ch * 8 + d) * VTS + kq * 4]) = col;
+    }
+  }
+}
+
 // Score steps S and S+1 (head dims 16S .. 16S+31) of qk_tile, then the rest.
 // base = LDS byte address of this lane's 16 bytes in key row r, step 0.
 template <int S, int D>
@@ -395,6 +447,8 @@ template <int D, int W, bool SE>
 __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
   __shared__ __attribute__((aligned(16))) QStage<D, W> qst;
+  // natural-layout keys + values of the next tile (blocks longer than a tile)
+  __shared__ __attribute__((aligned(16))) uint16_t s_nat[W == 8 ? 2 * KT * D : 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hq = lane >> 5;
   // work items of this launch's chunks (buckets c0*Nb .. c1*Nb)
@@ -469,7 +523,17 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
     const uint16_t* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
     for (int kt0 = 0; kt0 < n_keys; kt0 += KT) {
       const bool single = n_keys <= KT;
-      if (!(single && staged == bucket)) {
+      if (W == 8 && !single) {
+        // tile kt0 arrives by DMA (issued during the previous tile, or now
+        // for the first), is repacked, and the next tile's DMA starts
+        if (kt0 == 0) dma_kv<D, 64 * W>(s_nat, kb, p.ks_t, vb, p.vs_t, key0, n_keys);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        repack_kv<D, 64 * W>(sm, s_nat, n_keys - kt0);
+        __syncthreads();
+        if (kt0 + KT < n_keys) dma_kv<D, 64 * W>(s_nat, kb, p.ks_t, vb, p.vs_t, key0 + kt0 + KT, n_keys - kt0 - KT);
+        staged = -1;
+      } else if (!(single && staged == bucket)) {
         __syncthreads();
         stage_kv<D, 64 * W>(sm, kb, p.ks_t, vb, p.vs_t, key0 + kt0, n_keys - kt0);
         __syncthreads();

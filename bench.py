@@ -145,6 +145,38 @@ def other_workloads(m, reps):
     out["memory_10m_query_chunk"] = {"ms": round(ms, 4), "query_tokens_per_s": round(c["Lq"] / (ms * 1e-3), 1),
                                      "note": "keys stored rotated with their routing keys (offline encoding)"}
     _log(f"memory bank: summaries {ms_sum:.3f} ms, 512-token query chunk {ms:.3f} ms")
+    del q, k_rot, v, o, ws, pooled, dk, dq
+    torch.cuda.empty_cache()
+    # the decode workload over a paged cache: the same 1,048,576-token caches
+    # cut into 128-token pages (head-major inside a page) stored in a seeded
+    # random order, one table row of 8192 pages per sequence
+    c = DECODE
+    nb = c["Lc"] // c["block"]
+    npg = c["B"] * nb
+    kp = synth.device_tensor((npg, c["Hkv"], c["block"], c["D"]), c["sigma"], SEED + 2, t["k"], "bf16").transpose(1, 2)
+    vp = synth.device_tensor((npg, c["Hkv"], c["block"], c["D"]), c["sigma"], SEED + 2, t["v"], "bf16").transpose(1, 2)
+    perm = np.random.default_rng(SEED + 2).permutation(npg).astype(np.int32)
+    table = torch.from_numpy(perm.reshape(c["B"], nb)).cuda()
+    qd = synth.device_tensor((c["B"], c["Hq"], c["D"]), c["sigma"], SEED + 2, t["q"], "bf16")
+    # routing keys: each page summarised as a one-block sequence, then laid out by the table
+    page_sum = m.block_summary(kp, c["block"], out_dtype=torch.bfloat16)  # [pages, 1, Hkv, D]
+    pooled = page_sum[table.long(), 0]  # [B, nb, Hkv, D]
+    od = torch.empty_like(qd)
+    ws = torch.empty(m.decode_workspace_bytes(qd, kp, vp, pooled, block=c["block"], topk=c["topk"], block_table=table),
+                     dtype=torch.uint8, device="cuda")
+
+    def paged():
+        return m.sparse_attn_decode(qd, kp, vp, pooled, c["topk"], c["block"], out=od, workspace=ws,
+                                    block_table=table, return_sel=True)
+
+    ms = time_call(paged, max(reps, 10))
+    _, sel = paged()
+    torch.cuda.synchronize()
+    nbytes, distinct = decode_bytes(sel)
+    out["paged_decode_1m"] = {"ms": round(ms, 4), "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                              "algorithmic_gb": round(nbytes / 1e9, 4), "distinct_blocks": distinct,
+                              "note": "128-token pages in a random order, block table per sequence"}
+    _log(f"paged decode (1M caches, shuffled 128-token pages): {ms:.3f} ms, {nbytes / (ms * 1e-3) / 1e9:.1f} GB/s")
     return out
 
 
@@ -299,7 +331,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--also", action="store_true",
-                    help="also time the MoBA-style 32K prefill and the 10M-token memory bank (extra field)")
+                    help="also time the MoBA-style 32K prefill, the 10M-token memory bank and the paged decode "
+                         "(extra field)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run an elementwise negation over MIB MiB (read once, written once) -- the "
                          "known-size kernel that scales the HBM byte counters -- and exit")

@@ -79,6 +79,8 @@ class DecodeArgs(ctypes.Structure):
         ("o", VP), ("o_stride", I64x2),
         ("sel_out", VP),
         ("lse_out", VP),
+        ("block_table", VP),
+        ("table_w", ctypes.c_int32), ("num_pages", ctypes.c_int32),
     ]
 
 
@@ -318,10 +320,15 @@ def select_blocks(q, k, block: int, topk: int, causal: bool = True, *, gate: str
     return sel
 
 
-def _decode_args(q, kcache, vcache, pooled, o, *, block, topk, gate, cache_lens, scale, sel, lse):
+def _decode_args(q, kcache, vcache, pooled, o, *, block, topk, gate, cache_lens, scale, sel, lse, block_table=None):
     B, Hq, D = q.shape
     Lc, Hkv = kcache.shape[1], kcache.shape[2]
     a = DecodeArgs()
+    if block_table is not None:
+        # paged caches [pages, block, Hkv, D]; the logical capacity is one block per routing key
+        Lc = pooled.shape[1] * int(block)
+        a.block_table = _ptr(block_table)
+        a.table_w, a.num_pages = block_table.shape[1], kcache.shape[0]
     a.dtype = _dtype_code(q)
     a.B, a.Lc, a.Hq, a.Hkv, a.D = B, Lc, Hq, Hkv, D
     a.q, a.q_stride = _ptr(q), I64x2(*_strides(q, 2))
@@ -340,9 +347,9 @@ def _decode_args(q, kcache, vcache, pooled, o, *, block, topk, gate, cache_lens,
     return a
 
 
-def decode_workspace_bytes(q, kcache, vcache, pooled, *, block, topk, gate="head") -> int:
+def decode_workspace_bytes(q, kcache, vcache, pooled, *, block, topk, gate="head", block_table=None) -> int:
     a = _decode_args(q, kcache, vcache, pooled, q, block=block, topk=topk, gate=gate, cache_lens=None, scale=None,
-                     sel=None, lse=None)
+                     sel=None, lse=None, block_table=block_table)
     n = lib().bsa_decode_workspace_bytes(ctypes.byref(a))
     if n == 0:
         raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())
@@ -351,9 +358,17 @@ def decode_workspace_bytes(q, kcache, vcache, pooled, *, block, topk, gate="head
 
 def sparse_attn_decode(q, kcache, vcache, pooled, topk: int, block: int, *, gate: str = "head", cache_lens=None,
                        scale: float | None = None, return_sel: bool = False, return_lse: bool = False, out=None,
-                       workspace=None, stream=None):
-    """One decode step: q [B, Hq, D], caches [B, Lc, Hkv, D], pooled [B, Nb, Hkv, D]."""
+                       workspace=None, stream=None, block_table=None):
+    """One decode step: q [B, Hq, D], caches [B, Lc, Hkv, D], pooled [B, Nb, Hkv, D].
+
+    With block_table (int32 [B, >= Nb] on the device) the caches are pages [P, block, Hkv, D]
+    (any strides) and block j of sequence b is page block_table[b, j]."""
     torch = _torch()
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise BsaError(BSA_ERR_INVALID_ARG, "block_table must be int32 [B, table_w] with unit inner stride")
+        if block_table.stride(0) != block_table.shape[1]:
+            block_table = block_table.contiguous()
     B, Hq, D = q.shape
     Hkv = kcache.shape[2]
     o = out if out is not None else torch.empty_like(q, memory_format=torch.contiguous_format)
@@ -363,7 +378,7 @@ def sparse_attn_decode(q, kcache, vcache, pooled, topk: int, block: int, *, gate
     if cache_lens is not None:
         cache_lens = cache_lens.to(device=q.device, dtype=torch.int32).contiguous()
     a = _decode_args(q, kcache, vcache, pooled, o, block=block, topk=topk, gate=gate, cache_lens=cache_lens,
-                     scale=scale, sel=sel, lse=lse)
+                     scale=scale, sel=sel, lse=lse, block_table=block_table)
     n = lib().bsa_decode_workspace_bytes(ctypes.byref(a))
     if n == 0:
         raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())

@@ -493,9 +493,12 @@ static bsa_status plan_decode(const bsa_decode_args* a, DecodePlan& P, char* ws)
   if (!a->q || !a->kcache || !a->vcache || !a->pooled || !a->o) return fail(BSA_ERR_INVALID_ARG, "q, kcache, vcache, pooled and o are required");
   P.G = a->Hq / a->Hkv;
   if (P.G > 8) return fail(BSA_ERR_UNSUPPORTED, "decode supports at most 8 query heads per KV head");
+  if (a->block_table && a->num_pages < 1) return fail(BSA_ERR_INVALID_ARG, "num_pages must be >= 1 with a block table");
+  if (a->block_table && ((uintptr_t)a->block_table & 3)) return fail(BSA_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
   if (a->block > (1 << 22)) return fail(BSA_ERR_UNSUPPORTED, "block too large");
   P.Nb = (int)(((int64_t)a->Lc + a->block - 1) / a->block);
   if (P.Nb >= (1 << 23)) return fail(BSA_ERR_UNSUPPORTED, "too many blocks for decode");
+  if (a->block_table && a->table_w < P.Nb) return fail(BSA_ERR_INVALID_ARG, "table_w must be >= ceil(Lc / block)");
   const bool per_group = a->gate_mode == BSA_GATE_PER_GROUP;
   P.Hs = per_group ? a->Hkv : a->Hq;
   P.topk = std::min(a->topk, P.Nb);
@@ -541,6 +544,7 @@ static bsa_status run_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes
   DecodeAttnParams d;
   d.B = a->B; d.Lc = a->Lc; d.Hq = a->Hq; d.Hkv = a->Hkv; d.G = P.G; d.D = a->D; d.block = a->block; d.Hs = P.Hs;
   d.per_group = per_group; d.topk = a->topk; d.umax = P.umax; d.lens = a->cache_lens;
+  d.table = a->block_table; d.table_w = a->table_w; d.num_pages = a->num_pages;
   d.q = reinterpret_cast<const uint16_t*>(a->q); d.qs_b = a->q_stride[0]; d.qs_h = a->q_stride[1];
   d.k = reinterpret_cast<const uint16_t*>(a->kcache); d.ks_b = a->k_stride[0]; d.ks_t = a->k_stride[1]; d.ks_h = a->k_stride[2];
   d.v = reinterpret_cast<const uint16_t*>(a->vcache); d.vs_b = a->v_stride[0]; d.vs_t = a->v_stride[1]; d.vs_h = a->v_stride[2];

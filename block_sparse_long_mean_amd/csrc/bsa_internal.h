@@ -174,10 +174,12 @@ bool launch_attn_rowwise_f32(const AttnF32Params& p, hipStream_t s);
 struct DecodeAttnParams {
   int B, Lc, Hq, Hkv, G, D, block, Hs, per_group, topk, umax;
   const int32_t* lens;
+  const int32_t* table;  // paged caches: [B, table_w] page per logical block, or null
+  int table_w, num_pages;
   const uint16_t* q;
   int64_t qs_b, qs_h;
   const uint16_t* k;
-  int64_t ks_b, ks_t, ks_h;
+  int64_t ks_b, ks_t, ks_h;  // with a table, ks_b is the page stride
   const uint16_t* v;
   int64_t vs_b, vs_t, vs_h;
   float sl2;

@@ -333,9 +333,20 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeAttnParams p) 
   }
   const int n = dec_len(p, b);
   const int ka = j * p.block;
-  const int ke = min(ka + p.block, n);
-  const uint16_t* kb = p.k + (int64_t)b * p.ks_b + (int64_t)hk * p.ks_h;
-  const uint16_t* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
+  int ke = min(ka + p.block, n);
+  // kb / vb: the block's first key and value row (token ka of sequence b)
+  int64_t ko, vo;
+  if (p.table) {
+    const int pg = p.table[(int64_t)b * p.table_w + j];
+    if (pg < 0 || pg >= p.num_pages) ke = ka;  // no keys: the sequence's output is undefined, nothing is read
+    ko = (int64_t)pg * p.ks_b;
+    vo = (int64_t)pg * p.vs_b;
+  } else {
+    ko = (int64_t)b * p.ks_b + (int64_t)ka * p.ks_t;
+    vo = (int64_t)b * p.vs_b + (int64_t)ka * p.vs_t;
+  }
+  const uint16_t* kb = p.k + ko + (int64_t)hk * p.ks_h;
+  const uint16_t* vb = p.v + vo + (int64_t)hk * p.vs_h;
   const int dc = tid % CH, kg = tid / CH;
   float acc[NH][8];
 #pragma unroll
@@ -352,7 +363,7 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeAttnParams p) 
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
       const int key = kg * KPG + kk;
-      vx[kk] = key < nk ? ld16(vb + (int64_t)(k0 + key) * p.vs_t + dc * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      vx[kk] = key < nk ? ld16(vb + (int64_t)(k0 - ka + key) * p.vs_t + dc * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
     // scores: 16 lanes per key row (8 head dims each), 16 rows per pass;
     // the partial dot products are summed across the row's 16 lanes
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(DecodeAttnParams p) 
 #pragma unroll
       for (int ps = 0; ps < KC / RPP; ++ps) {
         const int key = ps * RPP + rsub;
-        kx[ps] = key < nk ? ld16(kb + (int64_t)(k0 + key) * p.ks_t + c * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        kx[ps] = key < nk ? ld16(kb + (int64_t)(k0 - ka + key) * p.ks_t + c * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
 #pragma unroll
       for (int ps = 0; ps < KC / RPP; ++ps) {

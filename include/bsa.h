@@ -141,6 +141,15 @@ bsa_status bsa_select_blocks(const bsa_prefill_args* a, void* workspace, size_t 
  * to [1, Lc]); the new token is already cached at position n_b - 1, so its
  * block cur = (n_b - 1) / block is forced (keys up to n_b - 1) and blocks
  * 0..cur-1 compete for topk slots, ties to the lower index.
+ *
+ * Paged caches (block_table != NULL): kcache and vcache hold num_pages pages
+ * of `block` tokens each, strides (page, token in page, head); block j of
+ * sequence b (tokens j*block .. j*block + block - 1) is page
+ * block_table[b * table_w + j].  table_w >= Nb; pages may be shared or in
+ * any order, and only the pages of chosen blocks are read.  An entry outside
+ * [0, num_pages) reads nothing and leaves that sequence's output undefined.
+ * Lc is then the logical capacity (Nb = ceil(Lc / block) routing keys); the
+ * gate and the cache lengths work on logical blocks exactly as above.
  */
 typedef struct bsa_decode_args {
     int32_t dtype;                 /* BSA_DTYPE_BF16 (q, caches, o) */
@@ -156,6 +165,8 @@ typedef struct bsa_decode_args {
     void* o;            int64_t o_stride[2];   /* [B, Hq, D] output */
     int32_t* sel_out;              /* optional [B, Hs, topk + 1]: chosen ascending, forced last, -1 padded */
     float* lse_out;                /* optional [B, Hq] */
+    const int32_t* block_table;    /* optional [B, table_w] page of each logical block (device) */
+    int32_t table_w, num_pages;    /* used only with block_table */
 } bsa_decode_args;
 
 size_t bsa_decode_workspace_bytes(const bsa_decode_args* a);

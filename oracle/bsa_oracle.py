@@ -33,6 +33,9 @@ What it computes, step by step, and where each step comes from:
   block.  MoBA's card (card.what_it_is) adds that top-k covering every block
   is full attention.
 
+* Paged caches (PagedCache): a storage mapping only, defined in its
+  docstring; decode over it is decode over the logical cache it stands for.
+
 Every array is widened to float64 before any arithmetic; nothing is rounded
 in between.  Inputs may be NumPy arrays or CPU torch tensors (bfloat16 is
 widened exactly).
@@ -54,6 +57,7 @@ __all__ = [
     "attend",
     "prefill",
     "decode",
+    "PagedCache",
 ]
 
 
@@ -449,3 +453,38 @@ def decode(
     if return_scores:
         out["scores"] = scores
     return out
+
+
+class PagedCache:
+    """A paged KV cache presented as the logical [B, Lc, Hkv, D] cache that
+    decode() slices.
+
+    The pages describe no storage layout for the cache; this is the plain
+    definition of the paged one: the cache is split into pages of `block`
+    tokens, and token t of sequence b is row t mod block of page
+    table[b, t div block].  pages: [P, block, Hkv, D] (anything that slices as
+    pages[p, a:e, h], e.g. a lazily fetched device tensor); table: [B, >= Nb]
+    integers.  Only the slices decode() asks for are supported:
+    [b, a:e, h] with 0 <= a <= e <= Lc; a slice may cross page boundaries.
+    """
+
+    def __init__(self, pages, table, block: int, Lc: int):
+        self.pages = pages
+        self.table = _int(table)
+        self.block = int(block)
+        self.shape = (self.table.shape[0], int(Lc), pages.shape[2], pages.shape[3])
+
+    def __getitem__(self, key):
+        b, sl, h = key
+        a, e = sl.start, sl.stop
+        parts = []
+        t = a
+        while t < e:
+            j = t // self.block
+            stop = min(e, (j + 1) * self.block)
+            page = int(self.table[b, j])
+            parts.append(f64(self.pages[page, t - j * self.block:stop - j * self.block, h]))
+            t = stop
+        if not parts:
+            return np.zeros((0, self.shape[3]))
+        return np.concatenate(parts, axis=0)

@@ -110,6 +110,32 @@ def test_decode_and_summary_validation(m):
     assert m.lib().bsa_block_summary(ctypes.byref(s), None, 0, None) == m.BSA_ERR_INVALID_ARG
 
 
+def test_decode_block_table_validation(m):
+    """Paged caches: the table must cover every logical block and name at least one page."""
+    buf = ctypes.create_string_buffer(1 << 12)
+    base = (ctypes.addressof(buf) + 255) & ~255  # never dereferenced: only the workspace query runs
+    d = m.DecodeArgs()
+    d.dtype, d.pooled_dtype = m.BSA_DTYPE_BF16, m.BSA_DTYPE_BF16
+    d.B, d.Lc, d.Hq, d.Hkv, d.D, d.block, d.topk = 2, 1000, 8, 2, 128, 64, 4
+    d.q = d.kcache = d.vcache = d.pooled = d.o = base
+    d.q_stride = m.I64x2(8 * 128, 128)
+    d.k_stride = d.v_stride = m.I64x3(64 * 2 * 128, 2 * 128, 128)  # (page, token, head)
+    d.p_stride = m.I64x3(16 * 2 * 128, 2 * 128, 128)
+    d.o_stride = m.I64x2(8 * 128, 128)
+    contiguous = m.lib().bsa_decode_workspace_bytes(ctypes.byref(d))
+    assert contiguous > 0
+    d.block_table, d.table_w, d.num_pages = base, 16, 40
+    assert m.lib().bsa_decode_workspace_bytes(ctypes.byref(d)) == contiguous
+    d.table_w = 15  # ceil(1000 / 64) = 16 logical blocks
+    assert m.lib().bsa_decode_workspace_bytes(ctypes.byref(d)) == 0
+    assert b"table_w" in m.lib().bsa_last_error()
+    d.table_w, d.num_pages = 16, 0
+    assert m.lib().bsa_decode_workspace_bytes(ctypes.byref(d)) == 0
+    assert b"num_pages" in m.lib().bsa_last_error()
+    d.num_pages, d.block_table = 40, base + 2
+    assert m.lib().bsa_decode_workspace_bytes(ctypes.byref(d)) == 0
+
+
 def test_timer_report_unknown_kernel_is_empty(m):
     m.timer_reset()
     assert m.timer_report("no_such_kernel") == (0.0, 0)

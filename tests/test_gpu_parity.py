@@ -304,6 +304,56 @@ def test_decode_head_major_cache(bsa):
     assert_close(to_np(lse), ref["lse"], 5e-3, None, what="lse")
 
 
+@pytest.mark.parametrize("gate,layout,D", [("head", "token", 128), ("group", "head", 64), ("head", "head", 64)])
+def test_decode_paged_cache(bsa, gate, layout, D):
+    """Paged caches: 32-token pages drawn at random (with repeats) from a pool with spare pages, so
+    sequences share pages and the pages of one sequence are out of order; pages stored token-major
+    ([P, block, Hkv, D]) or head-major ([P, Hkv, block, D] passed as a strided view).  Checked
+    against the oracle over the paged view, and bitwise against the contiguous call on the logical
+    caches gathered on the host."""
+    B, Hq, Hkv, block, nb, topk = 3, 8, 2, 32, 40, 6
+    P = B * nb + 5
+    Lc = nb * block
+    _say(f"case paged decode gate={gate} layout={layout} D{D} B3 H8/2 pages{P} block32 topk6")
+    q = synth.host_tensor((B, Hq, D), 1.0, 33, 0, "bf16")
+    kp = synth.host_tensor((P, block, Hkv, D), 1.0, 33, 1, "bf16")
+    vp = synth.host_tensor((P, block, Hkv, D), 1.0, 33, 2, "bf16")
+    table = np.random.default_rng(33).integers(0, P, size=(B, nb)).astype(np.int32)
+    lens = np.array([Lc, 700, 33], dtype=np.int32)
+    # logical caches by plain indexing (host), their routing keys from the oracle
+    k_log = kp[torch.from_numpy(table).long()].reshape(B, Lc, Hkv, D)
+    v_log = vp[torch.from_numpy(table).long()].reshape(B, Lc, Hkv, D)
+    pooled = torch.from_numpy(oracle.block_pool(k_log, block)).to(torch.bfloat16)
+    if layout == "head":
+        kd = kp.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+        vd = vp.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    else:
+        kd, vd = kp.cuda(), vp.cuda()
+    tab = torch.from_numpy(table).cuda()
+    cl = torch.from_numpy(lens).cuda()
+    o, sel, lse = bsa.sparse_attn_decode(q.cuda(), kd, vd, pooled.cuda(), topk, block, gate=gate, cache_lens=cl,
+                                         block_table=tab, return_sel=True, return_lse=True)
+    o2, sel2, lse2 = bsa.sparse_attn_decode(q.cuda(), k_log.cuda(), v_log.cuda(), pooled.cuda(), topk, block,
+                                            gate=gate, cache_lens=cl, return_sel=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel2)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+    kv = (oracle.PagedCache(kp, table, block, Lc), oracle.PagedCache(vp, table, block, Lc))
+    ref = oracle.decode(q, *kv, pooled, block=block, topk=topk, gate=gate, cache_lens=lens, return_scores=True)
+    Hs = Hkv if gate == "group" else Hq
+    scores = np.full((B, Hs, 1, nb), np.nan)
+    for (b, hs), sc in ref["scores"].items():
+        scores[b, hs, 0, : len(sc)] = sc
+    gsel = sel.cpu().numpy()[:, :, None]
+    diff = check_selection(gsel, ref["sel"][:, :, None], scores, topk, True)
+    if diff:
+        ref = oracle.decode(q, *kv, pooled, block=block, topk=topk, gate=gate, cache_lens=lens,
+                            force_sel=gsel[:, :, 0])
+    assert_close(to_np(o), ref["o"], 1e-2, 1e-2, bf16_storage=True)
+    assert_close(to_np(lse), ref["lse"], 5e-3, None, what="lse")
+
+
 def test_deterministic_bitwise(bsa):
     B, L, Hq, Hkv, D = 1, 4096, 8, 2, 128
     _say("case determinism L4096 H8/2 block128 topk4")

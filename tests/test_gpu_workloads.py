@@ -123,14 +123,18 @@ def test_index_branch_prefill_128k_fullsize(bsa):
     _check_prefill_rows(o, sel, lse, toks, run_oracle, topk, True)
 
 
-def _decode_check(bsa, q, kc, vc, pooled, topk, block, lens):
+def _decode_check(bsa, q, kc, vc, pooled, topk, block, lens, table=None):
     o, sel, lse = bsa.sparse_attn_decode(q, kc, vc, pooled, topk, block, return_sel=True, return_lse=True,
-                                         cache_lens=None if lens is None else torch.from_numpy(lens).cuda())
+                                         cache_lens=None if lens is None else torch.from_numpy(lens).cuda(),
+                                         block_table=None if table is None else torch.from_numpy(table).cuda())
     torch.cuda.synchronize()
     _say("  gpu done")
     ph = pooled.cpu()
     qh = q.cpu()
     kv = (HostSlices(kc), HostSlices(vc))
+    if table is not None:
+        Lc = pooled.shape[1] * block
+        kv = (oracle.PagedCache(kv[0], table, block, Lc), oracle.PagedCache(kv[1], table, block, Lc))
     ref = oracle.decode(qh, *kv, ph, block=block, topk=topk, cache_lens=lens, return_scores=True)
     B, Hs = ref["sel"].shape[:2]
     nb = pooled.shape[1]
@@ -166,6 +170,26 @@ def test_decode_1m_cache_fullsize(bsa):
                      Lc - 129, Lc - 128, Lc - 1, Lc, 4097], dtype=np.int32)
     _say("case decode ragged lengths " + ",".join(str(int(x)) for x in lens))
     _decode_check(bsa, q, kc, vc, pooled, topk, block, lens)
+
+
+def test_paged_decode_1m_cache_fullsize(bsa):
+    """The long-context decode over a paged cache: the 16 sequences' 1,048,576-token caches cut
+    into 128-token pages (head-major inside a page), stored in a seeded random order, one table
+    row of 8192 pages per sequence; every (sequence, head) is compared, full and ragged lengths."""
+    B, Lc, Hq, Hkv, D, block, topk = 16, 1 << 20, 32, 8, 128, 128, 32
+    nb = Lc // block
+    P = B * nb
+    _say("case paged decode B16 Lc1048576 H32/8 D128 block128 topk32, 131072 shuffled pages")
+    q = synth.device_tensor((B, Hq, D), 1.0, SEED + 3, T["q"], "bf16")
+    kp = synth.device_tensor((P, Hkv, block, D), 1.0, SEED + 3, T["k"], "bf16").transpose(1, 2)
+    vp = synth.device_tensor((P, Hkv, block, D), 1.0, SEED + 3, T["v"], "bf16").transpose(1, 2)
+    pooled = synth.device_tensor((B, nb, Hkv, D), 128 ** -0.5, SEED + 3, T["pooled"], "bf16")
+    table = np.random.default_rng(SEED + 3).permutation(P).astype(np.int32).reshape(B, nb)
+    _decode_check(bsa, q, kp, vp, pooled, topk, block, None, table)
+    lens = np.array([1, 2, 127, 128, 129, 256, 257, 33 * 128, 33 * 128 + 1, 500_000, 777_777,
+                     Lc - 129, Lc - 128, Lc - 1, Lc, 4097], dtype=np.int32)
+    _say("case paged decode ragged lengths")
+    _decode_check(bsa, q, kp, vp, pooled, topk, block, lens, table)
 
 
 def _check_summary_blocks(got, k, block, blocks, pos=None, bf16_out=False, atol=2e-6):

@@ -366,6 +366,57 @@ def test_decode_equals_last_prefill_row(gate):
         np.testing.assert_allclose(dc2["o"][b], p2["o"][0, -1], atol=1e-12)
 
 
+def _paged_from_contiguous(cache, block, perm, spare):
+    """Pages of `cache` [B, Lc, Hkv, D] (Lc a multiple of block) stored at shuffled page slots
+    perm[b * Nb + j] among Nb * B + spare pages (spare slots hold unrelated values), plus the
+    table that maps logical blocks back to them -- built with plain array indexing."""
+    B, Lc, Hkv, D = cache.shape
+    nb = Lc // block
+    blocks = cache.reshape(B * nb, block, Hkv, D)
+    pages = np.full((B * nb + spare, block, Hkv, D), 7.5)
+    pages[perm] = blocks
+    return pages, perm.reshape(B, nb)
+
+
+@pytest.mark.parametrize("gate", ["head", "group"])
+def test_paged_decode_equals_contiguous(gate):
+    """Token t of sequence b lives in row t mod block of page table[b, t div block]: decode over the
+    shuffled pages equals decode over the contiguous cache, for identity and shuffled tables."""
+    B, Lc, Hq, Hkv, D, block = 3, 48, 4, 2, 8, 8
+    q = _rand((B, Hq, D), 31, 0)
+    k, v = _rand((B, Lc, Hkv, D), 31, 1), _rand((B, Lc, Hkv, D), 31, 2)
+    pooled = oracle.block_pool(k, block)
+    lens = np.array([48, 21, 1])
+    ref = oracle.decode(q, k, v, pooled, block=block, topk=2, gate=gate, cache_lens=lens)
+    nb = Lc // block
+    rng = np.random.default_rng(5)
+    for perm in (np.arange(B * nb), rng.permutation(B * nb + 4)[: B * nb]):
+        kp, table = _paged_from_contiguous(k, block, perm, 4)
+        vp, _ = _paged_from_contiguous(v, block, perm, 4)
+        got = oracle.decode(q, oracle.PagedCache(kp, table, block, Lc), oracle.PagedCache(vp, table, block, Lc),
+                            pooled, block=block, topk=2, gate=gate, cache_lens=lens)
+        np.testing.assert_array_equal(got["sel"], ref["sel"])
+        np.testing.assert_array_equal(got["o"], ref["o"])
+        np.testing.assert_array_equal(got["lse"], ref["lse"])
+
+
+def test_paged_cache_slices_cross_pages():
+    """Every slice [b, a:e, h] of the paged view equals the contiguous cache's, including slices
+    that start or end inside a page and span several pages."""
+    B, Lc, Hkv, D, block = 2, 30, 2, 3, 4
+    Lp = -(-Lc // block) * block
+    cache = _rand((B, Lp, Hkv, D), 32, 1)
+    perm = np.random.default_rng(6).permutation(B * Lp // block)
+    pages, table = _paged_from_contiguous(cache, block, perm, 0)
+    view = oracle.PagedCache(pages, table, block, Lc)
+    assert view.shape == (B, Lc, Hkv, D)
+    for b in range(B):
+        for h in range(Hkv):
+            for a in range(Lc + 1):
+                for e in range(a, Lc + 1):
+                    np.testing.assert_array_equal(view[b, a:e, h], cache[b, a:e, h])
+
+
 # --------------------------------------------------------------------------
 # hand-derived golden cases
 # --------------------------------------------------------------------------

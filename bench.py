@@ -145,7 +145,46 @@ def other_workloads(m, reps):
     out["memory_10m_query_chunk"] = {"ms": round(ms, 4), "query_tokens_per_s": round(c["Lq"] / (ms * 1e-3), 1),
                                      "note": "keys stored rotated with their routing keys (offline encoding)"}
     _log(f"memory bank: summaries {ms_sum:.3f} ms, 512-token query chunk {ms:.3f} ms")
-    del q, k_rot, v, o, ws, pooled, dk, dq
+    # host content tier: the memory's rotated keys and its values (41 GB) in
+    # pinned host RAM, its routing keys in GPU memory; only the chosen blocks
+    # cross the host link
+    # (stored head-major there, so one block of one KV head is 16 contiguous KB)
+    _log("host tier: moving the memory's keys and values to pinned host RAM")
+    hm = (1, c["Hkv"], c["Lk"], c["D"])
+    kh = torch.empty(hm, dtype=k_rot.dtype, pin_memory=True)
+    kh.copy_(k_rot.transpose(1, 2))
+    del k_rot
+    vh = torch.empty(hm, dtype=v.dtype, pin_memory=True)
+    vh.copy_(v.transpose(1, 2))
+    del v
+    kh, vh = kh.transpose(1, 2), vh.transpose(1, 2)
+    torch.cuda.empty_cache()
+
+    def hosted_chunk():
+        return m.sparse_attn_prefill(q, kh, vh, c["block"], c["topk"], False, out=o, workspace=ws, **kw)
+
+    ms_h = time_call(hosted_chunk, reps)
+    sel = m.select_blocks(q, kh, c["block"], c["topk"], False, **kw)  # [1, Hq, Lq, topk]
+    hk = torch.arange(c["Hq"], device="cuda").view(1, c["Hq"], 1, 1) // (c["Hq"] // c["Hkv"])
+    nbm = pooled.shape[1]
+    keys = (hk * nbm + sel.long()).masked_select(sel >= 0)
+    distinct = int(torch.unique(keys).numel())
+    m.timer_enable(1)
+    m.timer_reset()
+    for _ in range(2):
+        hosted_chunk()
+    torch.cuda.synchronize()
+    att_ms = m.timer_report("attn")[0] / 2
+    m.timer_enable(0)
+    kv_bytes = distinct * c["block"] * c["D"] * 2 * 2
+    out["memory_10m_query_chunk_host_tier"] = {
+        "ms": round(ms_h, 4), "attn_ms": round(att_ms, 4), "host_bytes_gb": round(kv_bytes / 1e9, 3),
+        "host_link_gbs": round(kv_bytes / (att_ms * 1e-3) / 1e9, 1), "distinct_blocks": distinct,
+        "note": "memory keys/values in pinned host RAM (head-major), routing keys in HBM; host_link_gbs = chosen K/V bytes "
+                "(each distinct (kv head, block) once) / attention-phase time"}
+    _log(f"host-tier memory bank query chunk: {ms_h:.3f} ms, attention {att_ms:.3f} ms, "
+         f"{kv_bytes / (att_ms * 1e-3) / 1e9:.1f} GB/s over the host link")
+    del q, kh, vh, o, ws, pooled, dk, dq, sel, keys
     torch.cuda.empty_cache()
     # the decode workload over a paged cache: the same 1,048,576-token caches
     # cut into 128-token pages (head-major inside a page) stored in a seeded
@@ -177,6 +216,49 @@ def other_workloads(m, reps):
                               "algorithmic_gb": round(nbytes / 1e9, 4), "distinct_blocks": distinct,
                               "note": "128-token pages in a random order, block table per sequence"}
     _log(f"paged decode (1M caches, shuffled 128-token pages): {ms:.3f} ms, {nbytes / (ms * 1e-3) / 1e9:.1f} GB/s")
+    del kp, vp, od, ws
+    torch.cuda.empty_cache()
+    # host content tier: the same decode with its 68.7 GB of caches in pinned
+    # host RAM (read by the kernels over the host link, only the chosen blocks)
+    # and the routing keys in GPU memory
+    _log("host tier: filling 68.7 GB of pinned host caches")
+    shape = (c["B"], c["Hkv"], c["Lc"], c["D"])
+    host = []
+    for tid in (t["k"], t["v"]):
+        h = torch.empty(shape, dtype=torch.bfloat16, pin_memory=True)
+        for b in range(c["B"]):  # one sequence at a time through a device staging tensor
+            h[b].copy_(synth.device_tensor(shape[1:], c["sigma"], SEED + 4 + 16 * b, tid, "bf16"))
+        host.append(h.transpose(1, 2))
+    kh, vh = host
+    qd = synth.device_tensor((c["B"], c["Hq"], c["D"]), c["sigma"], SEED + 4, t["q"], "bf16")
+    pooled = m.block_summary(kh, c["block"], out_dtype=torch.bfloat16)
+    od = torch.empty_like(qd)
+    ws = torch.empty(m.decode_workspace_bytes(qd, kh, vh, pooled, block=c["block"], topk=c["topk"]),
+                     dtype=torch.uint8, device="cuda")
+
+    def hosted():
+        return m.sparse_attn_decode(qd, kh, vh, pooled, c["topk"], c["block"], out=od, workspace=ws,
+                                    return_sel=True)
+
+    ms = time_call(hosted, max(reps, 10))
+    _, sel = hosted()
+    torch.cuda.synchronize()
+    nbytes, distinct = decode_bytes(sel)
+    kv_bytes = distinct * c["block"] * c["D"] * 2 * 2
+    m.timer_enable(2)
+    m.timer_reset()
+    for _ in range(3):
+        hosted()
+    torch.cuda.synchronize()
+    att_ms = m.timer_report("decode_attend")[0] / 3
+    m.timer_enable(0)
+    out["host_tier_decode_1m"] = {
+        "ms": round(ms, 4), "decode_attend_ms": round(att_ms, 4),
+        "host_link_gbs": round(kv_bytes / (att_ms * 1e-3) / 1e9, 1), "host_bytes_gb": round(kv_bytes / 1e9, 4),
+        "distinct_blocks": distinct,
+        "note": "caches in pinned host RAM, routing keys in HBM; host_link_gbs = chosen K/V bytes / decode_attend time"}
+    _log(f"host-tier decode (1M caches in host RAM): {ms:.3f} ms, attend {att_ms:.3f} ms, "
+         f"{kv_bytes / (att_ms * 1e-3) / 1e9:.1f} GB/s over the host link")
     return out
 
 

@@ -195,6 +195,15 @@ def _workspace(nbytes: int, device, workspace=None):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+def _gpu(t):
+    """Where outputs and workspaces go: the tensor's GPU, or the current GPU when the tensor lives in
+    (pinned) host memory."""
+    if t.is_cuda:
+        return t.device
+    torch = _torch()
+    return torch.device("cuda", torch.cuda.current_device())
+
+
 def _doc(d, B, L, device):
     if d is None:
         return None
@@ -243,8 +252,8 @@ def _prefill_args(q, k, v, o, *, block, topk, causal, gate, index_q, index_k, do
 def prefill_workspace_bytes(q, k, *, block, topk, causal=True, gate="head", index_q=None, index_k=None,
                             doc_ids_q=None, doc_ids_k=None, pooled=None, chunk_tokens: int = 0,
                             chunks_per_pass: int = 0) -> int:
-    dq = _doc(doc_ids_q, q.shape[0], q.shape[1], q.device)
-    dk = _doc(doc_ids_k, k.shape[0], k.shape[1], k.device)
+    dq = _doc(doc_ids_q, q.shape[0], q.shape[1], _gpu(q))
+    dk = _doc(doc_ids_k, k.shape[0], k.shape[1], _gpu(k))
     a = _prefill_args(q, k, k, q, block=block, topk=topk, causal=causal, gate=gate, index_q=index_q,
                       index_k=index_k, doc_ids_q=dq, doc_ids_k=dk, rope_theta=10000.0, scale=None,
                       pooled=pooled, sel=None, lse=None, chunk_tokens=chunk_tokens,
@@ -272,19 +281,19 @@ def sparse_attn_prefill(q, k, v, block: int, topk: int, causal: bool = True, doc
         doc_ids_k = doc_ids if doc_ids_k is None else doc_ids_k
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
-    o = out if out is not None else torch.empty_like(q, memory_format=torch.contiguous_format)
+    o = out if out is not None else torch.empty(q.shape, dtype=q.dtype, device=_gpu(q))
     hs = Hkv if gate == "group" else Hq
-    sel = torch.empty((B, hs, Lq, topk + (1 if causal else 0)), dtype=torch.int32, device=q.device) if return_sel else None
-    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
-    dq = _doc(doc_ids_q, B, Lq, q.device)
-    dk = _doc(doc_ids_k, B, Lk, k.device)
+    sel = torch.empty((B, hs, Lq, topk + (1 if causal else 0)), dtype=torch.int32, device=_gpu(q)) if return_sel else None
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=_gpu(q)) if return_lse else None
+    dq = _doc(doc_ids_q, B, Lq, _gpu(q))
+    dk = _doc(doc_ids_k, B, Lk, _gpu(k))
     a = _prefill_args(q, k, v, o, block=block, topk=topk, causal=causal, gate=gate, index_q=index_q, index_k=index_k,
                       doc_ids_q=dq, doc_ids_k=dk, rope_theta=rope_theta, scale=scale, pooled=pooled, sel=sel, lse=lse,
                       chunk_tokens=chunk_tokens, chunks_per_pass=chunks_per_pass)
     n = lib().bsa_prefill_workspace_bytes(ctypes.byref(a))
     if n == 0:
         raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())
-    ws = _workspace(n, q.device, workspace)
+    ws = _workspace(n, _gpu(q), workspace)
     _check(lib().bsa_sparse_attn_prefill(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(n), _stream(stream)))
     res = [o]
     if return_sel:
@@ -302,9 +311,9 @@ def select_blocks(q, k, block: int, topk: int, causal: bool = True, *, gate: str
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     hs = Hkv if gate == "group" else Hq
-    sel = torch.empty((B, hs, Lq, topk + (1 if causal else 0)), dtype=torch.int32, device=q.device)
-    dq = _doc(doc_ids_q, B, Lq, q.device)
-    dk = _doc(doc_ids_k, B, Lk, k.device)
+    sel = torch.empty((B, hs, Lq, topk + (1 if causal else 0)), dtype=torch.int32, device=_gpu(q))
+    dq = _doc(doc_ids_q, B, Lq, _gpu(q))
+    dk = _doc(doc_ids_k, B, Lk, _gpu(k))
     a = _prefill_args(q, k, None, None, block=block, topk=topk, causal=causal, gate=gate, index_q=index_q,
                       index_k=index_k, doc_ids_q=dq, doc_ids_k=dk, rope_theta=rope_theta, scale=None, pooled=pooled,
                       sel=sel, lse=None)
@@ -315,7 +324,7 @@ def select_blocks(q, k, block: int, topk: int, causal: bool = True, *, gate: str
     n = lib().bsa_prefill_workspace_bytes(ctypes.byref(a_full))
     if n == 0:
         raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())
-    ws = _workspace(n, q.device, workspace)
+    ws = _workspace(n, _gpu(q), workspace)
     _check(lib().bsa_select_blocks(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(n), _stream(stream)))
     return sel
 
@@ -371,18 +380,18 @@ def sparse_attn_decode(q, kcache, vcache, pooled, topk: int, block: int, *, gate
             block_table = block_table.contiguous()
     B, Hq, D = q.shape
     Hkv = kcache.shape[2]
-    o = out if out is not None else torch.empty_like(q, memory_format=torch.contiguous_format)
+    o = out if out is not None else torch.empty(q.shape, dtype=q.dtype, device=_gpu(q))
     hs = Hkv if gate == "group" else Hq
-    sel = torch.empty((B, hs, topk + 1), dtype=torch.int32, device=q.device) if return_sel else None
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    sel = torch.empty((B, hs, topk + 1), dtype=torch.int32, device=_gpu(q)) if return_sel else None
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=_gpu(q)) if return_lse else None
     if cache_lens is not None:
-        cache_lens = cache_lens.to(device=q.device, dtype=torch.int32).contiguous()
+        cache_lens = cache_lens.to(device=_gpu(q), dtype=torch.int32).contiguous()
     a = _decode_args(q, kcache, vcache, pooled, o, block=block, topk=topk, gate=gate, cache_lens=cache_lens,
                      scale=scale, sel=sel, lse=lse, block_table=block_table)
     n = lib().bsa_decode_workspace_bytes(ctypes.byref(a))
     if n == 0:
         raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())
-    ws = _workspace(n, q.device, workspace)
+    ws = _workspace(n, _gpu(q), workspace)
     _check(lib().bsa_sparse_attn_decode(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(n), _stream(stream)))
     res = [o]
     if return_sel:
@@ -399,10 +408,10 @@ def block_summary(k, block: int, doc_ids=None, *, rope_theta: float = 10000.0, o
     B, L, H, D = k.shape
     nb = -(-L // block)
     out_dtype = torch.float32 if out_dtype is None else out_dtype
-    pooled = torch.empty((B, nb, H, D), dtype=out_dtype, device=k.device)
-    d = _doc(doc_ids, B, L, k.device)
-    k_rot = torch.empty((B, L, H, D), dtype=k.dtype, device=k.device) if return_k_rot else None
-    pos = torch.empty((B, L), dtype=torch.int32, device=k.device) if return_pos else None
+    pooled = torch.empty((B, nb, H, D), dtype=out_dtype, device=_gpu(k))
+    d = _doc(doc_ids, B, L, _gpu(k))
+    k_rot = torch.empty((B, L, H, D), dtype=k.dtype, device=_gpu(k)) if return_k_rot else None
+    pos = torch.empty((B, L), dtype=torch.int32, device=_gpu(k)) if return_pos else None
     a = SummaryArgs()
     a.dtype = _dtype_code(k)
     a.B, a.L, a.H, a.D, a.block = B, L, H, D, int(block)
@@ -416,7 +425,7 @@ def block_summary(k, block: int, doc_ids=None, *, rope_theta: float = 10000.0, o
     n = lib().bsa_summary_workspace_bytes(ctypes.byref(a))
     if n == 0:
         raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())
-    ws = _workspace(n, k.device)
+    ws = _workspace(n, _gpu(k))
     _check(lib().bsa_block_summary(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(n), _stream(stream)))
     res = [pooled]
     if return_k_rot:

@@ -3,6 +3,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -86,6 +87,33 @@ static void omega_table(double theta, int D, double* out) {
 static bool dim_ok(int D) { return D == 64 || D == 128; }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Every tensor may be device memory or pinned host memory mapped into the
+// device's address space at the same address (hipHostMalloc, a pinned
+// tensor); kernels then read the host copy over the host link.  This is how a
+// memory's content keys and values stay in host RAM while its routing keys
+// stay in HBM ("100 Millionen Token ...", section "Das Gehirn mit zwei
+// Geschwindigkeiten").  Pageable host memory cannot be read by a kernel: it
+// is rejected before anything is enqueued.
+static bool resident_one(const void* p) {
+  if (!p) return true;
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // the failed query must not surface as a later launch error
+    return false;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged || at.isManaged) return true;
+  if (at.type != hipMemoryTypeHost || !at.devicePointer || !at.hostPointer) return false;
+  const char* dev = (const char*)at.devicePointer + ((const char*)p - (const char*)at.hostPointer);
+  return dev == (const char*)p;
+}
+
+static bsa_status resident(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (!resident_one(p))
+      return fail(BSA_ERR_INVALID_ARG, "a tensor is neither device memory nor pinned host memory mapped for the device");
+  return BSA_OK;
+}
 
 static bool strides_ok(const int64_t* s, int n, int D, int elt) {
   for (int i = 0; i < n; ++i)
@@ -294,6 +322,9 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
   if (st != BSA_OK) return st;
   if (!ws || ws_bytes < P.bytes) return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_prefill_workspace_bytes");
   if (((uintptr_t)ws & 255) != 0) return fail(BSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  st = resident({a->q, a->k, a->v, a->o, a->index_q, a->index_k, a->doc_ids_q, a->doc_ids_k, a->pooled, a->sel_out,
+                 a->lse_out, ws});
+  if (st != BSA_OK) return st;
   plan_prefill(a, P, reinterpret_cast<char*>(ws), gate_only);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const double theta = a->rope_theta > 0.f ? (double)a->rope_theta : 10000.0;
@@ -530,6 +561,8 @@ static bsa_status run_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes
   if (st != BSA_OK) return st;
   if (!ws || ws_bytes < P.bytes) return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_decode_workspace_bytes");
   if (((uintptr_t)ws & 255) != 0) return fail(BSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  st = resident({a->q, a->kcache, a->vcache, a->pooled, a->cache_lens, a->o, a->sel_out, a->lse_out, a->block_table, ws});
+  if (st != BSA_OK) return st;
   plan_decode(a, P, reinterpret_cast<char*>(ws));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool per_group = a->gate_mode == BSA_GATE_PER_GROUP;
@@ -594,6 +627,8 @@ static bsa_status run_summary(const bsa_summary_args* a, void* ws, size_t ws_byt
     if (((uintptr_t)ws & 255) != 0) return fail(BSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     plan_summary(a, &chunk, &pos, reinterpret_cast<char*>(ws), &need);
   }
+  st = resident({a->k, a->doc_ids, a->pooled, a->k_rot, a->pos_out, a->doc_ids ? ws : nullptr});
+  if (st != BSA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (a->doc_ids && !launch_doc_positions(a->doc_ids, a->B, a->L, chunk, pos, s)) return BSA_ERR_HIP;
   SummaryParams sp;

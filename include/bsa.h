@@ -19,7 +19,16 @@
  *   block, the tie rule, the RoPE form) are stated at each call below.
  *
  * Conventions for every call:
- *   - Every pointer in an args struct is DEVICE memory unless marked HOST.
+ *   - Every pointer in an args struct is DEVICE memory unless marked HOST,
+ *     or pinned host memory mapped into the device's address space at the
+ *     same address (hipHostMalloc, a pinned tensor), which the kernels then
+ *     read over the host link.  This is the host content tier: a memory's
+ *     keys and values (prefill k / v, decode kcache / vcache) stay in host
+ *     RAM and only the chosen blocks cross the link, while the routing keys
+ *     (pooled) stay in GPU memory ("100 Millionen Token ...", section "Das
+ *     Gehirn mit zwei Geschwindigkeiten").  Other memory (pageable host
+ *     memory) fails validation with BSA_ERR_INVALID_ARG before anything is
+ *     enqueued.
  *     The caller owns all buffers, including the workspace; the library never
  *     allocates or frees device memory and keeps no state across calls other
  *     than the last error message and the optional launch timer.

@@ -354,6 +354,98 @@ def test_decode_paged_cache(bsa, gate, layout, D):
     assert_close(to_np(lse), ref["lse"], 5e-3, None, what="lse")
 
 
+def _pinned(t):
+    """A copy of a host tensor in pinned (page-locked, device-mapped) host memory."""
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    return h
+
+
+def test_host_tier_decode(bsa):
+    """Host content tier: the caches stay in pinned host RAM (the kernels read the chosen blocks over
+    the host link), the routing keys in GPU memory.  Routing keys summarised from the host caches,
+    the decode itself, and the decode over host pages are bitwise equal to the device-resident
+    calls, and the decode matches the oracle."""
+    B, Hq, Hkv, Lc, D, block, topk = 2, 8, 2, 3000, 128, 128, 6
+    _say("case host-tier decode B2 H8/2 Lc3000 block128 topk6")
+    q = synth.host_tensor((B, Hq, D), 1.0, 34, 0, "bf16")
+    k = synth.host_tensor((B, Lc, Hkv, D), 1.0, 34, 1, "bf16")
+    v = synth.host_tensor((B, Lc, Hkv, D), 1.0, 34, 2, "bf16")
+    kh, vh = _pinned(k), _pinned(v)
+    lens = torch.from_numpy(np.array([3000, 1777], dtype=np.int32)).cuda()
+    p_dev = bsa.block_summary(k.cuda(), block, out_dtype=torch.bfloat16)
+    p_host = bsa.block_summary(kh, block, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(p_dev.view(torch.int16), p_host.view(torch.int16))
+    qd = q.cuda()
+    o1, s1, l1 = bsa.sparse_attn_decode(qd, k.cuda(), v.cuda(), p_dev, topk, block, cache_lens=lens,
+                                        return_sel=True, return_lse=True)
+    o2, s2, l2 = bsa.sparse_attn_decode(qd, kh, vh, p_dev, topk, block, cache_lens=lens,
+                                        return_sel=True, return_lse=True)
+    # the same caches as host pages of 128 tokens, in order
+    nb = -(-Lc // block)
+    Lp = nb * block
+    kp = torch.zeros((B * nb, block, Hkv, D), dtype=torch.bfloat16, pin_memory=True)
+    vp = torch.zeros((B * nb, block, Hkv, D), dtype=torch.bfloat16, pin_memory=True)
+    kp.view(B, Lp, Hkv, D)[:, :Lc] = k
+    vp.view(B, Lp, Hkv, D)[:, :Lc] = v
+    table = torch.arange(B * nb, dtype=torch.int32).reshape(B, nb).cuda()
+    o3 = bsa.sparse_attn_decode(qd, kp, vp, p_dev, topk, block, cache_lens=lens, block_table=table)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(l1, l2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+    ph = p_dev.cpu()
+    ref = oracle.decode(q, k, v, ph, block=block, topk=topk, cache_lens=lens.cpu().numpy(),
+                        force_sel=s1.cpu().numpy())
+    assert_close(to_np(o2), ref["o"], 1e-2, 1e-2, bf16_storage=True)
+
+
+@pytest.mark.parametrize("case", ["memory_prerotated", "causal_gather"])
+def test_host_tier_prefill(bsa, case):
+    """Host content tier for prefill: keys and values in pinned host RAM.  The memory-bank flow (keys
+    stored rotated with their routing keys in GPU memory, a query chunk of its own document,
+    non-causal) and a causal prefill whose attention runs on the LDS-staged gather; both bitwise
+    equal to the device-resident call."""
+    if case == "memory_prerotated":
+        B, Lq, Lk, Hq, Hkv, D, block, topk, causal = 1, 96, 20000, 8, 2, 128, 64, 16, False
+    else:
+        B, Lq, Lk, Hq, Hkv, D, block, topk, causal = 1, 3000, 3000, 8, 2, 128, 128, 4, True
+    _say(f"case host-tier prefill {case} Lq{Lq} Lk{Lk} H8/2 block{block} topk{topk}")
+    q = synth.host_tensor((B, Lq, Hq, D), 1.0, 35, 0, "bf16").cuda()
+    k = synth.host_tensor((B, Lk, Hkv, D), 1.0, 35, 1, "bf16")
+    v = synth.host_tensor((B, Lk, Hkv, D), 1.0, 35, 2, "bf16")
+    kw = {}
+    if case == "memory_prerotated":
+        dk = torch.from_numpy(synth.random_doc_ids(Lk, 700.0, 35)[None]).cuda()
+        pooled, k_rot = bsa.block_summary(k.cuda(), block, doc_ids=dk, return_k_rot=True)
+        kd = k_rot
+        kw = dict(doc_ids_q=torch.zeros((B, Lq), dtype=torch.int32, device="cuda"), pooled=pooled)
+    else:
+        kd = k.cuda()
+    kh, vh = _pinned(kd.cpu()), _pinned(v)
+    o1, s1 = bsa.sparse_attn_prefill(q, kd, v.cuda(), block, topk, causal, return_sel=True, **kw)
+    o2, s2 = bsa.sparse_attn_prefill(q, kh, vh, block, topk, causal, return_sel=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_pageable_host_memory_rejected(bsa):
+    """Pageable host memory cannot be read by a kernel: the call fails validation and enqueues
+    nothing.  (The block table names no page, so even a launch would read no cache row.)"""
+    B, Hq, Hkv, D, block, topk, nb = 1, 4, 1, 128, 64, 2, 4
+    q = torch.zeros((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((nb, block, Hkv, D), dtype=torch.bfloat16)  # ordinary (pageable) host memory
+    vc = torch.zeros((nb, block, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    pooled = torch.zeros((B, nb, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    table = torch.full((B, nb), -1, dtype=torch.int32, device="cuda")
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.sparse_attn_decode(q, kc, vc, pooled, topk, block, block_table=table)
+    assert e.value.status == bsa.BSA_ERR_INVALID_ARG
+    assert "pinned host memory" in str(e.value)
+
+
 def test_deterministic_bitwise(bsa):
     B, L, Hq, Hkv, D = 1, 4096, 8, 2, 128
     _say("case determinism L4096 H8/2 block128 topk4")

@@ -35,6 +35,11 @@ What it computes, step by step, and where each step comes from:
 
 * Paged caches (PagedCache): a storage mapping only, defined in its
   docstring; decode over it is decode over the logical cache it stands for.
+* Gradients (attend_grad, prefill_backward): the plain derivative of the
+  exact attention above with the block selection held fixed -- the method is
+  trained end to end (MoBA card, card.what_it_is; "MSA: Memory Sparse
+  Attention", "Key Points"), and a top-k choice has no gradient, so the
+  gradient flows through the chosen keys only.
 
 Every array is widened to float64 before any arithmetic; nothing is rounded
 in between.  Inputs may be NumPy arrays or CPU torch tensors (bfloat16 is
@@ -58,6 +63,8 @@ __all__ = [
     "prefill",
     "decode",
     "PagedCache",
+    "attend_grad",
+    "prefill_backward",
 ]
 
 
@@ -488,3 +495,80 @@ class PagedCache:
         if not parts:
             return np.zeros((0, self.shape[3]))
         return np.concatenate(parts, axis=0)
+
+
+# ---------------------------------------------------------------------------
+# gradients through a fixed selection
+# ---------------------------------------------------------------------------
+
+def attend_grad(q_row, keys, values, do_row, scale: float):
+    """Gradient of o = sum_u p_u v_u, p = softmax_u(scale * q . k_u), for one
+    query, given g = dL/do.
+
+    Differentiating: dL/dv_u = p_u g; with d_u = g . v_u and
+    ds_u = p_u (d_u - sum_w p_w d_w) (the softmax Jacobian),
+    dL/dq = scale * sum_u ds_u k_u and dL/dk_u = scale * ds_u q.
+    Returns (dq [D], dK [n, D], dV [n, D]); an empty key set gives zeros.
+    """
+    q = f64(q_row)
+    K = f64(keys)
+    V = f64(values)
+    g = f64(do_row)
+    if K.shape[0] == 0:
+        return np.zeros_like(q), np.zeros_like(K), np.zeros_like(V)
+    z = (K @ q) * scale
+    w = np.exp(z - z.max())
+    pr = w / w.sum()
+    dV = pr[:, None] * g[None, :]
+    dpr = V @ g
+    ds = pr * (dpr - pr @ dpr)
+    return scale * (ds @ K), scale * ds[:, None] * q[None, :], dV
+
+
+def prefill_backward(q, k, v, dout, sel, *, block: int, causal: bool, gate: str = "head",
+                     scale: float | None = None):
+    """Gradients of the prefill output w.r.t. q, k and v with the selection
+    held fixed.
+
+    q: [B, Lq, Hq, D]; k, v: [B, Lk, Hkv, D]; dout = dL/do [B, Lq, Hq, D];
+    sel [B, Hs, Lq, w]: the blocks each selection row attended (-1 padded),
+    e.g. the prefill's own sel.  Each query (b, t, h) attends the union of its
+    selection row's blocks, with keys after the query masked inside its own
+    block when causal (absolute query position Lk - Lq + t), exactly as in
+    prefill(); its gradient contributions are summed into dk, dv over the
+    keys it attended.  q and k are the attended (already position-encoded)
+    tensors.  Returns dict dq [B, Lq, Hq, D], dk, dv [B, Lk, Hkv, D].
+    """
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    per_group = gate == "group"
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    sel = _int(sel)
+    dq = np.zeros((B, Lq, Hq, D))
+    dk = np.zeros((B, Lk, Hkv, D))
+    dv = np.zeros((B, Lk, Hkv, D))
+    for b in range(B):
+        for t in range(Lq):
+            qabs = Lk - Lq + t
+            cur = current_block(qabs, block) if causal else None
+            for h in range(Hq):
+                hk = h // G
+                hs = hk if per_group else h
+                idx = []
+                for j in sel[b, hs, t]:
+                    if j < 0:
+                        continue
+                    a, e = _block_tokens(int(j), block, Lk)
+                    if causal and j == cur:
+                        e = min(e, qabs + 1)
+                    idx.extend(range(a, e))
+                idx = np.asarray(idx, dtype=np.int64)
+                if idx.size == 0:
+                    continue
+                gq, gk, gv = attend_grad(q[b, t, h], _rows(k, b, idx, hk), _rows(v, b, idx, hk),
+                                         dout[b, t, h], scale)
+                dq[b, t, h] = gq
+                dk[b, idx, hk] += gk
+                dv[b, idx, hk] += gv
+    return {"dq": dq, "dk": dk, "dv": dv}

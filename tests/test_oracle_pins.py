@@ -418,6 +418,72 @@ def test_paged_cache_slices_cross_pages():
 
 
 # --------------------------------------------------------------------------
+# gradients through a fixed selection
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gate,causal", [("head", True), ("group", True), ("head", False)])
+def test_backward_matches_finite_differences(gate, causal):
+    """Central differences of L = sum(dO * O), with O from the forward oracle on the same fixed
+    selection, agree with every analytic gradient element."""
+    B, Lq, Lk, Hq, Hkv, D, block = 1, 7, 10, 4, 2, 3, 4
+    q, k, v = _rand((B, Lq, Hq, D), 40, 0), _rand((B, Lk, Hkv, D), 40, 1), _rand((B, Lk, Hkv, D), 40, 2)
+    g = _rand((B, Lq, Hq, D), 40, 3)
+    sel = oracle.prefill(q, k, v, block=block, topk=1, causal=causal, gate=gate)["sel"]
+    grads = oracle.prefill_backward(q, k, v, g, sel, block=block, causal=causal, gate=gate)
+
+    def loss(qq, kk, vv):
+        o = oracle.prefill(qq, kk, vv, block=block, topk=1, causal=causal, gate=gate, force_sel=sel)["o"]
+        return float((o * g).sum())
+
+    h = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        num = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[i] += h
+            xm[i] -= h
+            args = {"dq": (xp, k, v), "dk": (q, xp, v), "dv": (q, k, xp)}[name]
+            argm = {"dq": (xm, k, v), "dk": (q, xm, v), "dv": (q, k, xm)}[name]
+            num[i] = (loss(*args) - loss(*argm)) / (2 * h)
+        np.testing.assert_allclose(grads[name], num, atol=1e-7, rtol=1e-6, err_msg=name)
+
+
+def test_backward_dense_equals_torch_autograd():
+    """With every block selected, the gradients are those of dense causal attention (offset
+    queries, GQA): torch float64 autograd through scaled_dot_product_attention."""
+    B, Lq, Lk, Hq, Hkv, D, block = 2, 9, 13, 4, 2, 8, 4
+    q, k, v = _rand((B, Lq, Hq, D), 41, 0), _rand((B, Lk, Hkv, D), 41, 1), _rand((B, Lk, Hkv, D), 41, 2)
+    g = _rand((B, Lq, Hq, D), 41, 3)
+    nb = -(-Lk // block)
+    sel = oracle.prefill(q, k, v, block=block, topk=nb, causal=True)["sel"]
+    ours = oracle.prefill_backward(q, k, v, g, sel, block=block, causal=True)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    G = Hq // Hkv
+    kk = tk.repeat_interleave(G, dim=2).transpose(1, 2)
+    vv = tv.repeat_interleave(G, dim=2).transpose(1, 2)
+    mask = torch.arange(Lk)[None, :] <= (Lk - Lq + torch.arange(Lq))[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(tq.transpose(1, 2), kk, vv, attn_mask=mask)
+    (o.transpose(1, 2) * torch.from_numpy(g)).sum().backward()
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        np.testing.assert_allclose(ours[name], t.grad.numpy(), atol=1e-12, rtol=1e-10, err_msg=name)
+
+
+def test_backward_sum_rules():
+    """Each row's softmax weights sum to one, so summed over all keys dv equals the summed output
+    gradients of the heads that read them, and dk sums to zero (each row's ds sums to zero)."""
+    B, L, Hq, Hkv, D, block = 2, 40, 6, 2, 5, 8
+    q, k, v = _rand((B, L, Hq, D), 42, 0), _rand((B, L, Hkv, D), 42, 1), _rand((B, L, Hkv, D), 42, 2)
+    g = _rand((B, L, Hq, D), 42, 3)
+    sel = oracle.prefill(q, k, v, block=block, topk=2, causal=True, gate="group")["sel"]
+    r = oracle.prefill_backward(q, k, v, g, sel, block=block, causal=True, gate="group")
+    G = Hq // Hkv
+    for hk in range(Hkv):
+        np.testing.assert_allclose(r["dv"][:, :, hk].sum(axis=1), g[:, :, hk * G:(hk + 1) * G].sum(axis=(1, 2)),
+                                   atol=1e-12)
+        np.testing.assert_allclose(r["dk"][:, :, hk].sum(axis=1), 0.0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
 # hand-derived golden cases
 # --------------------------------------------------------------------------
 

@@ -18,6 +18,8 @@ __all__ = [
     "select_blocks",
     "sparse_attn_decode",
     "block_summary",
+    "sparse_attn_backward",
+    "backward_workspace_bytes",
     "prefill_workspace_bytes",
     "decode_workspace_bytes",
     "timer_enable",
@@ -98,6 +100,25 @@ class SummaryArgs(ctypes.Structure):
     ]
 
 
+class BackwardArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("Lq", ctypes.c_int32), ("Lk", ctypes.c_int32),
+        ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("q", VP), ("q_stride", I64x3),
+        ("k", VP), ("k_stride", I64x3),
+        ("v", VP), ("v_stride", I64x3),
+        ("o", VP), ("o_stride", I64x3),
+        ("dout", VP), ("do_stride", I64x3),
+        ("lse", VP),
+        ("sel", VP),
+        ("sel_w", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("causal", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("dq", VP), ("dk", VP), ("dv", VP),
+    ]
+
+
 class BsaError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"libbsa {_STATUS.get(status, status)}: {msg}")
@@ -128,6 +149,10 @@ def lib():
         L.bsa_summary_workspace_bytes.restype = ctypes.c_size_t
         L.bsa_block_summary.argtypes = [ctypes.POINTER(SummaryArgs), VP, ctypes.c_size_t, VP]
         L.bsa_block_summary.restype = ctypes.c_int32
+        L.bsa_backward_workspace_bytes.argtypes = [ctypes.POINTER(BackwardArgs)]
+        L.bsa_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.bsa_sparse_attn_backward.argtypes = [ctypes.POINTER(BackwardArgs), VP, ctypes.c_size_t, VP]
+        L.bsa_sparse_attn_backward.restype = ctypes.c_int32
         L.bsa_last_error.argtypes = []
         L.bsa_last_error.restype = ctypes.c_char_p
         L.bsa_version.argtypes = []
@@ -433,6 +458,63 @@ def block_summary(k, block: int, doc_ids=None, *, rope_theta: float = 10000.0, o
     if return_pos:
         res.append(pos)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def _backward_args(q, k, v, o, lse, sel, dout, dq, dk, dv, *, block, causal, gate, scale):
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    a = BackwardArgs()
+    a.dtype = _dtype_code(q)
+    a.B, a.Lq, a.Lk, a.Hq, a.Hkv, a.D = B, Lq, Lk, Hq, Hkv, D
+    a.q, a.q_stride = _ptr(q), I64x3(*_strides(q, 3))
+    a.k, a.k_stride = _ptr(k), I64x3(*_strides(k, 3))
+    a.v, a.v_stride = _ptr(v), I64x3(*_strides(v, 3))
+    a.o, a.o_stride = _ptr(o), I64x3(*_strides(o, 3))
+    a.dout, a.do_stride = _ptr(dout), I64x3(*_strides(dout, 3))
+    a.lse, a.sel, a.sel_w = _ptr(lse), _ptr(sel), int(sel.shape[-1])
+    a.block, a.causal = int(block), int(bool(causal))
+    a.gate_mode = BSA_GATE_PER_GROUP if gate == "group" else BSA_GATE_PER_HEAD
+    a.scale = 0.0 if scale is None else float(scale)
+    a.dq, a.dk, a.dv = _ptr(dq), _ptr(dk), _ptr(dv)
+    return a
+
+
+def backward_workspace_bytes(q, k, sel, *, block, causal, gate="head") -> int:
+    # only sizes are read by the query; any non-null pointer stands in for lse
+    a = _backward_args(q, k, k, q, q, sel, q, q, k, k, block=block, causal=causal, gate=gate, scale=None)
+    n = lib().bsa_backward_workspace_bytes(ctypes.byref(a))
+    if n == 0:
+        raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())
+    return int(n)
+
+
+def sparse_attn_backward(q, k, v, o, lse, sel, dout, block: int, causal: bool, *, gate: str = "head",
+                         scale: float | None = None, out=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv), fp32, of the prefill's output through its fixed selection.
+
+    q, k, v: the attended bf16 tensors; o, lse, sel: the forward call's outputs (o, lse [B, Hq, Lq],
+    sel [B, Hs, Lq, topk + causal]); dout: dL/do.  out: optional (dq, dk, dv) fp32 contiguous."""
+    torch = _torch()
+    dev = _gpu(q)
+    if out is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+        dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    else:
+        dq, dk, dv = out
+    for t in (dq, dk, dv):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise BsaError(BSA_ERR_INVALID_ARG, "dq, dk and dv must be contiguous float32")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or sel.dtype != torch.int32 or not sel.is_contiguous():
+        raise BsaError(BSA_ERR_INVALID_ARG, "lse must be contiguous float32 and sel contiguous int32")
+    a = _backward_args(q, k, v, o, lse, sel, dout, dq, dk, dv, block=block, causal=causal, gate=gate, scale=scale)
+    n = lib().bsa_backward_workspace_bytes(ctypes.byref(a))
+    if n == 0:
+        raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())
+    ws = _workspace(n, dev, workspace)
+    _check(lib().bsa_sparse_attn_backward(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(n),
+                                          _stream(stream)))
+    return dq, dk, dv
 
 
 def timer_enable(level=1):

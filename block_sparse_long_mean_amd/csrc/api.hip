@@ -592,6 +592,128 @@ static bsa_status run_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes
 }
 
 // ---------------------------------------------------------------------------
+// backward plan
+// ---------------------------------------------------------------------------
+struct BackwardPlan {
+  int G, Nb, Hs, Gs, R, kslot, sh_h, sh_t, lgR, NC, CT, rows_item;
+  int64_t nsel_rows, max_entries, max_items, nbk;
+  int32_t *counts, *cursor, *bucket_off, *tile_off, *scan_tmp;
+  uint32_t* entries;
+  int4* items;
+  float *delta, *dq_part, *dkv_part;
+  size_t bytes;
+};
+
+static bsa_status plan_backward(const bsa_backward_args* a, BackwardPlan& P, char* ws) {
+  if (!a) return fail(BSA_ERR_INVALID_ARG, "args is NULL");
+  if (a->dtype != BSA_DTYPE_BF16) return fail(BSA_ERR_UNSUPPORTED, "backward supports bf16 q/k/v");
+  if (a->B < 1 || a->Lq < 1 || a->Lk < 1 || a->Hq < 1 || a->Hkv < 1) return fail(BSA_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (a->Hq % a->Hkv) return fail(BSA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+  if (!dim_ok(a->D)) return fail(BSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (a->block < 1) return fail(BSA_ERR_INVALID_ARG, "block must be >= 1");
+  if (a->causal != 0 && a->causal != 1) return fail(BSA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (a->causal && a->Lq > a->Lk) return fail(BSA_ERR_INVALID_ARG, "causal needs Lq <= Lk");
+  if (a->gate_mode != BSA_GATE_PER_HEAD && a->gate_mode != BSA_GATE_PER_GROUP) return fail(BSA_ERR_INVALID_ARG, "gate_mode");
+  if (a->sel_w < 0 || a->sel_w > BSA_MAX_TOPK + 1) return fail(BSA_ERR_INVALID_ARG, "sel_w must be in [0, BSA_MAX_TOPK + 1]");
+  if (!a->q || !a->k || !a->v || !a->o || !a->dout || !a->lse || (!a->sel && a->sel_w > 0) || !a->dq || !a->dk || !a->dv)
+    return fail(BSA_ERR_INVALID_ARG, "q, k, v, o, dout, lse, sel, dq, dk and dv are required");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) || !aligned16(a->dout) ||
+      !aligned16(a->dq) || !aligned16(a->dk) || !aligned16(a->dv))
+    return fail(BSA_ERR_INVALID_ARG, "tensor base pointers must be 16-byte aligned");
+  if (!strides_ok(a->q_stride, 3, a->D, 2) || !strides_ok(a->k_stride, 3, a->D, 2) || !strides_ok(a->v_stride, 3, a->D, 2) ||
+      !strides_ok(a->o_stride, 3, a->D, 2) || !strides_ok(a->do_stride, 3, a->D, 2))
+    return fail(BSA_ERR_INVALID_ARG, "strides must be non-negative and keep rows 16-byte aligned");
+  const bool per_group = a->gate_mode == BSA_GATE_PER_GROUP;
+  P.G = a->Hq / a->Hkv;
+  if (per_group && (128 % P.G) != 0) return fail(BSA_ERR_UNSUPPORTED, "per-group gating needs G dividing 128");
+  P.Nb = (int)(((int64_t)a->Lk + a->block - 1) / a->block);
+  P.Hs = per_group ? a->Hkv : a->Hq;
+  P.Gs = per_group ? 1 : P.G;
+  P.R = per_group ? P.G : 1;
+  P.kslot = std::max(a->sel_w, 1);
+  P.sh_h = ceil_log2(P.kslot);
+  P.sh_t = P.sh_h + ceil_log2(P.Gs);
+  P.lgR = ceil_log2(P.R);
+  P.nsel_rows = (int64_t)a->B * P.Hs * a->Lq;
+  if (P.nsel_rows * std::max(a->sel_w, 1) >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "too many selection entries");
+  if (P.sh_t >= 31 || (int64_t)(a->Lq - 1) >= ((int64_t)1 << (32 - P.sh_t)))
+    return fail(BSA_ERR_UNSUPPORTED, "Lq too large for the packed selection entries");
+  // Query chunks: a (chunk, block) bucket is one work item whose entries are
+  // sorted in LDS (at most CT * Gs of them), and each non-empty bucket keeps a
+  // block-sized dk / dv partial; the longest chunks the sort holds keep the
+  // fewest partials.
+  P.CT = std::min(a->Lq, kBwdSortCap / P.Gs);
+  P.NC = (a->Lq + P.CT - 1) / P.CT;
+  P.nbk = (int64_t)a->B * a->Hkv * P.NC * P.Nb;
+  if (P.nbk >= (int64_t)1 << 30) return fail(BSA_ERR_UNSUPPORTED, "too many (chunk, block) buckets");
+  P.rows_item = P.CT * P.G;  // every row a bucket can hold: one item per bucket
+  P.max_entries = P.nsel_rows * a->sel_w;
+  P.max_items = (P.max_entries * P.R + P.rows_item - 1) / P.rows_item + std::min<int64_t>(P.nbk, P.max_entries);
+  if (P.max_items >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "too many work items");
+  Carver c;
+  c.base = ws;
+  P.counts = c.take<int32_t>(P.nbk);
+  P.cursor = c.take<int32_t>(P.nbk);
+  P.bucket_off = c.take<int32_t>(P.nbk + 1);
+  P.tile_off = c.take<int32_t>(P.nbk + 1);
+  P.scan_tmp = c.take<int32_t>(scan_tmp_len(P.nbk));
+  P.entries = c.take<uint32_t>(P.max_entries + 256);
+  P.items = c.take<int4>(std::max<int64_t>(P.max_items, 1));
+  P.delta = c.take<float>((int64_t)a->B * a->Hq * a->Lq);
+  // partial rows per (b, kv head, chunk, head of the group): CT each, the last chunk padded
+  P.dq_part = c.take<float>((int64_t)a->B * a->Hkv * P.NC * P.Gs * P.CT * P.kslot * P.R * a->D);
+  P.dkv_part = c.take<float>(std::max<int64_t>(P.max_items, 1) * 2 * a->block * a->D);
+  P.bytes = c.off + 256;
+  return BSA_OK;
+}
+
+static bsa_status run_backward(const bsa_backward_args* a, void* ws, size_t ws_bytes, void* stream) {
+  BackwardPlan P;
+  bsa_status st = plan_backward(a, P, nullptr);
+  if (st != BSA_OK) return st;
+  if (!ws || ws_bytes < P.bytes) return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_backward_workspace_bytes");
+  if (((uintptr_t)ws & 255) != 0) return fail(BSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  st = resident({a->q, a->k, a->v, a->o, a->dout, a->lse, a->sel, a->dq, a->dk, a->dv, ws});
+  if (st != BSA_OK) return st;
+  plan_backward(a, P, reinterpret_cast<char*>(ws));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool per_group = a->gate_mode == BSA_GATE_PER_GROUP;
+  const float scale = a->scale != 0.f ? a->scale : (float)(1.0 / sqrt((double)a->D));
+  AttnParams ap{};
+  ap.B = a->B; ap.Lq = a->Lq; ap.Lk = a->Lk; ap.Hq = a->Hq; ap.Hkv = a->Hkv; ap.G = P.G; ap.D = a->D;
+  ap.block = a->block; ap.Nb = P.Nb; ap.Hs = P.Hs; ap.per_group = per_group; ap.Gs = P.Gs; ap.R = P.R;
+  ap.kslot = P.kslot; ap.causal = a->causal; ap.sh_h = P.sh_h; ap.sh_t = P.sh_t; ap.lgR = P.lgR;
+  ap.q = reinterpret_cast<const uint16_t*>(a->q); ap.qs_b = a->q_stride[0]; ap.qs_t = a->q_stride[1]; ap.qs_h = a->q_stride[2];
+  ap.k = reinterpret_cast<const uint16_t*>(a->k); ap.ks_b = a->k_stride[0]; ap.ks_t = a->k_stride[1]; ap.ks_h = a->k_stride[2];
+  ap.v = reinterpret_cast<const uint16_t*>(a->v); ap.vs_b = a->v_stride[0]; ap.vs_t = a->v_stride[1]; ap.vs_h = a->v_stride[2];
+  ap.o = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a->o));
+  ap.os_b = a->o_stride[0]; ap.os_t = a->o_stride[1]; ap.os_h = a->o_stride[2];
+  ap.dout = reinterpret_cast<const uint16_t*>(a->dout);
+  ap.dos_b = a->do_stride[0]; ap.dos_t = a->do_stride[1]; ap.dos_h = a->do_stride[2];
+  ap.sl2 = (float)((double)scale * 1.4426950408889634074);
+  ap.scale = scale;
+  ap.entries = P.entries; ap.bucket_off = P.bucket_off; ap.tile_off = P.tile_off; ap.items = P.items;
+  ap.counts = P.counts;
+  ap.NC = P.NC; ap.CT = P.CT; ap.c0 = 0; ap.c1 = a->B * a->Hkv * P.NC;
+  ap.rows_item = P.rows_item;
+  ap.grid = P.max_entries > 0 ? (int)P.max_items : 0;
+  ap.sel = a->sel; ap.sel_w = a->sel_w;
+  ap.lse_in = a->lse; ap.delta = P.delta; ap.dq_part = P.dq_part; ap.dkv_part = P.dkv_part;
+  ap.dq = a->dq; ap.dk = a->dk; ap.dv = a->dv;
+  CsrParams cp;
+  cp.B = a->B; cp.Lq = a->Lq; cp.Lk = a->Lk; cp.Hkv = a->Hkv; cp.G = P.G; cp.Hs = P.Hs; cp.per_group = per_group;
+  cp.Nb = P.Nb; cp.block = a->block; cp.causal = a->causal;
+  cp.Gs = P.Gs; cp.NC = P.NC; cp.CT = P.CT;
+  cp.sel = a->sel; cp.sel_w = a->sel_w; cp.kslot = P.kslot; cp.R = P.R; cp.rows_item = P.rows_item;
+  cp.sh_h = P.sh_h; cp.sh_t = P.sh_t;
+  cp.counts = P.counts; cp.cursor = P.cursor; cp.bucket_off = P.bucket_off; cp.tile_off = P.tile_off;
+  cp.scan_tmp = P.scan_tmp; cp.entries = P.entries; cp.items = P.items; cp.nbk = (int)P.nbk;
+  if (P.max_entries > 0 && !launch_csr(cp, s)) return BSA_ERR_HIP;
+  if (!launch_attn_backward(ap, (int64_t)a->B * a->Lq * a->Hq, s)) return BSA_ERR_HIP;
+  return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
 // summary
 // ---------------------------------------------------------------------------
 static bsa_status plan_summary(const bsa_summary_args* a, int32_t** chunk, int32_t** pos, char* ws, size_t* bytes) {
@@ -672,6 +794,15 @@ BSA_API size_t bsa_decode_workspace_bytes(const bsa_decode_args* a) {
 
 BSA_API bsa_status bsa_sparse_attn_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes, void* stream) {
   return run_decode(a, ws, ws_bytes, stream);
+}
+
+BSA_API size_t bsa_backward_workspace_bytes(const bsa_backward_args* a) {
+  BackwardPlan P;
+  return plan_backward(a, P, nullptr) == BSA_OK ? P.bytes : 0;
+}
+
+BSA_API bsa_status bsa_sparse_attn_backward(const bsa_backward_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return run_backward(a, ws, ws_bytes, stream);
 }
 
 BSA_API size_t bsa_summary_workspace_bytes(const bsa_summary_args* a) {

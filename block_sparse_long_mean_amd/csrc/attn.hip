@@ -969,4 +969,307 @@ bool launch_attn_rowwise_f32(const AttnF32Params& p, hipStream_t s) {
   return launch_ok("attn_rowwise_f32");
 }
 
+// ---------------------------------------------------------------------------
+// Backward through the fixed selection.  Work items are whole buckets (one
+// query chunk's entries for one (b, kv head, block)); their entries are
+// sorted first so that every sum over the rows that chose a block runs in a
+// fixed order.
+// ---------------------------------------------------------------------------
+
+// delta[b, h, t] = dout . o of each output row, fp32 (D/8 lanes per row)
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(AttnParams p, int64_t nrows) {
+  constexpr int LPR = D / 8;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int li = threadIdx.x % LPR;
+  const int64_t rr = row < nrows ? row : 0;  // rows (b, t, h), h fastest
+  const int h = (int)(rr % p.Hq);
+  const int t = (int)((rr / p.Hq) % p.Lq);
+  const int b = (int)(rr / ((int64_t)p.Hq * p.Lq));
+  const u16x8 g = ld16(p.dout + (int64_t)b * p.dos_b + (int64_t)t * p.dos_t + (int64_t)h * p.dos_h + li * 8);
+  const u16x8 o = ld16(p.o + (int64_t)b * p.os_b + (int64_t)t * p.os_t + (int64_t)h * p.os_h + li * 8);
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = fmaf(bf2f(g[e]), bf2f(o[e]), acc);
+#pragma unroll
+  for (int m2 = 1; m2 < LPR; m2 <<= 1) acc += __shfl_xor(acc, m2, 64);
+  if (row < nrows && li == 0) p.delta[((int64_t)b * p.Hq + h) * p.Lq + t] = acc;
+}
+
+// Sort each bucket's entry words ascending (bitonic, in LDS); buckets hold at
+// most kBwdSortCap entries by construction of the query chunks.
+__global__ __launch_bounds__(256) void bwd_sort_kernel(AttnParams p, int nbk) {
+  __shared__ uint32_t s_e[kBwdSortCap];
+  const int bk = blockIdx.x;
+  if (bk >= nbk) return;
+  const int a = p.bucket_off[bk];
+  const int n = p.bucket_off[bk + 1] - a;
+  if (n <= 1 || n > kBwdSortCap) return;  // uniform (larger buckets cannot arise from a valid selection)
+  int n2 = 2;
+  while (n2 < n) n2 <<= 1;
+  uint32_t* ent = const_cast<uint32_t*>(p.entries) + a;
+  for (int i = threadIdx.x; i < n2; i += 256) s_e[i] = i < n ? ent[i] : 0xFFFFFFFFu;
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += 256) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t x = s_e[i], y = s_e[l];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            s_e[i] = y;
+            s_e[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < n; i += 256) ent[i] = s_e[i];
+}
+
+// One workgroup per work item (bucket): for each 64-key tile of the block,
+// stage K and V (fp32, LDS), then take the item's rows eight at a time.
+// Wave w owns keys 16w .. 16w+15 of the tile; lane (key, quarter) forms
+// quarter dot products q.k and g.v, completes them across the key's four
+// lanes, and accumulates dk and dv for its key and quarter in registers.
+// The rows' ds values go through LDS for dq = sum_u ds_u k_u, which each
+// (row, slot) partial accumulates over the block's tiles.
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnParams p) {
+  constexpr int KT = 64, RB = 8, DQ = D / 4, KP = D + 4;
+  __shared__ __attribute__((aligned(16))) float s_k[KT * KP];
+  __shared__ __attribute__((aligned(16))) float s_v[KT * KP];
+  __shared__ __attribute__((aligned(16))) float s_q[RB][D];
+  __shared__ __attribute__((aligned(16))) float s_g[RB][D];
+  __shared__ float s_ds[RB][KT];
+  __shared__ float s_lse2[RB], s_dl[RB];
+  __shared__ int s_qpos[RB];
+  __shared__ int64_t s_pidx[RB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int item = blockIdx.x;
+  if (item >= p.tile_off[(int64_t)p.B * p.Hkv * p.NC * p.Nb]) return;  // past the built items; uniform
+  const int4 rec = load_item((const_int_ptr)p.items, item);
+  const int bucket = rec.x, hk = rec.w & 0xFFFF, b = rec.w >> 16;
+  const int cid = bucket / p.Nb;
+  const int j = bucket - cid * p.Nb;
+  const int t_base = (cid % p.NC) * p.CT;
+  const int64_t prow_base = (int64_t)cid * p.Gs;
+  const int key0 = j * p.block;
+  const int n_keys = min(p.block, p.Lk - key0);
+  const uint16_t* kb = p.k + (int64_t)b * p.ks_b + (int64_t)hk * p.ks_h;
+  const uint16_t* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
+  const int ku = 16 * w + (lane >> 2), qc = lane & 3;  // this lane's key in the tile and quarter
+  float* dst = p.dkv_part + (int64_t)item * 2 * p.block * D;
+  const float L2E = 1.4426950408889634f;
+  for (int t0 = 0; t0 < n_keys; t0 += KT) {
+    const int nt = min(KT, n_keys - t0);
+    __syncthreads();  // the previous tile's K / V are no longer read
+    for (int i = tid; i < KT * (D / 8); i += 256) {
+      const int u = i / (D / 8), c8 = i % (D / 8);
+      u16x8 kx = u16x8{0, 0, 0, 0, 0, 0, 0, 0}, vx = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (u < nt) {
+        kx = ld16(kb + (int64_t)(key0 + t0 + u) * p.ks_t + c8 * 8);
+        vx = ld16(vb + (int64_t)(key0 + t0 + u) * p.vs_t + c8 * 8);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s_k[u * KP + c8 * 8 + e] = bf2f(kx[e]);
+        s_v[u * KP + c8 * 8 + e] = bf2f(vx[e]);
+      }
+    }
+    float dk[DQ], dv[DQ];
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) dk[e] = dv[e] = 0.f;
+    const int key = key0 + t0 + ku;
+    for (int r0 = 0; r0 < rec.z; r0 += RB) {
+      const int nr = min(RB, rec.z - r0);
+      __syncthreads();  // the previous rows' q, g and ds are no longer read
+      // stage the batch's rows: q, g (fp32), lse (log2), delta, position, partial index
+      for (int i = tid; i < RB * (D / 8); i += 256) {
+        const int r = i / (D / 8), c8 = i % (D / 8);
+        u16x8 qx = u16x8{0, 0, 0, 0, 0, 0, 0, 0}, gx = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (r < nr) {
+          const GRow g = grow_of(p, rec, entry_of(p, rec, r0 + r), r0 + r);
+          qx = ld16(q_row<D>(p, rec, g) + c8 * 8);
+          gx = ld16(p.dout + (int64_t)b * p.dos_b + (int64_t)g.t * p.dos_t + (int64_t)g.qh * p.dos_h + c8 * 8);
+          if (c8 == 0) {
+            const int64_t orow = ((int64_t)b * p.Hq + g.qh) * p.Lq + g.t;
+            s_lse2[r] = p.lse_in[orow] * L2E;
+            s_dl[r] = p.delta[orow];
+            s_qpos[r] = p.causal ? p.Lk - p.Lq + g.t : 0x7FFFFFFF;
+            const int hsel = p.per_group ? 0 : g.hs - hk * p.G;
+            const int64_t prow = (prow_base + hsel) * p.CT + (g.t - t_base);
+            s_pidx[r] = (prow * p.kslot + g.slot) * p.R + g.rr;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          s_q[r][c8 * 8 + e] = bf2f(qx[e]);
+          s_g[r][c8 * 8 + e] = bf2f(gx[e]);
+        }
+      }
+      __syncthreads();
+      for (int r = 0; r < nr; ++r) {
+        float sc = 0.f, dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < DQ; e += 4) {
+          const f32x4 kq = *reinterpret_cast<const f32x4*>(&s_k[ku * KP + qc * DQ + e]);
+          const f32x4 vq = *reinterpret_cast<const f32x4*>(&s_v[ku * KP + qc * DQ + e]);
+          const f32x4 qq = *reinterpret_cast<const f32x4*>(&s_q[r][qc * DQ + e]);
+          const f32x4 gq = *reinterpret_cast<const f32x4*>(&s_g[r][qc * DQ + e]);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            sc = fmaf(qq[x], kq[x], sc);
+            dp = fmaf(gq[x], vq[x], dp);
+          }
+        }
+        sc += __shfl_xor(sc, 1, 64);
+        sc += __shfl_xor(sc, 2, 64);
+        dp += __shfl_xor(dp, 1, 64);
+        dp += __shfl_xor(dp, 2, 64);
+        const bool ok = ku < nt && key <= s_qpos[r];
+        const float pr = ok ? exp2f(sc * p.sl2 - s_lse2[r]) : 0.f;
+        const float ds = pr * (dp - s_dl[r]);
+#pragma unroll
+        for (int e = 0; e < DQ; e += 4) {
+          const f32x4 qq = *reinterpret_cast<const f32x4*>(&s_q[r][qc * DQ + e]);
+          const f32x4 gq = *reinterpret_cast<const f32x4*>(&s_g[r][qc * DQ + e]);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            dk[e + x] = fmaf(ds, qq[x], dk[e + x]);
+            dv[e + x] = fmaf(pr, gq[x], dv[e + x]);
+          }
+        }
+        if (qc == 0) s_ds[r][ku] = ds;
+      }
+      __syncthreads();
+      // dq partials: thread (row, D/32 head dims) sums ds_u k_u over the tile
+      {
+        constexpr int DPT = D / 32;
+        const int r = tid >> 5, d0 = (tid & 31) * DPT;
+        if (r < nr) {
+          float acc[DPT];
+#pragma unroll
+          for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+          for (int u = 0; u < nt; ++u) {
+            const float dsu = s_ds[r][u];
+#pragma unroll
+            for (int e = 0; e < DPT; ++e) acc[e] = fmaf(dsu, s_k[u * KP + d0 + e], acc[e]);
+          }
+          float* dqp = p.dq_part + s_pidx[r] * D + d0;
+#pragma unroll
+          for (int e = 0; e < DPT; ++e) dqp[e] = t0 == 0 ? acc[e] : dqp[e] + acc[e];
+        }
+      }
+    }
+    // this item's dk / dv sums for the tile's keys
+    if (ku < nt) {
+      float* dkp = dst + (int64_t)(t0 + ku) * D + qc * DQ;
+      float* dvp = dst + (int64_t)(p.block + t0 + ku) * D + qc * DQ;
+#pragma unroll
+      for (int e = 0; e < DQ; e += 4) {
+        *reinterpret_cast<f32x4*>(dkp + e) = f32x4{dk[e], dk[e + 1], dk[e + 2], dk[e + 3]};
+        *reinterpret_cast<f32x4*>(dvp + e) = f32x4{dv[e], dv[e + 1], dv[e + 2], dv[e + 3]};
+      }
+    }
+  }
+}
+
+// dq row (b, t, h) = scale * sum of its selection row's slot partials, in slot
+// order (D/4 lanes per row, four head dims each)
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(AttnParams p, int64_t nrows) {
+  constexpr int LPR = D / 4;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+  if (row >= nrows) return;
+  const int li = threadIdx.x % LPR;
+  const int h = (int)(row % p.Hq);
+  const int t = (int)((row / p.Hq) % p.Lq);
+  const int b = (int)(row / ((int64_t)p.Hq * p.Lq));
+  const int hk = h / p.G, hh = h % p.G;
+  const int hs = p.per_group ? hk : h;
+  const int c = t / p.CT;
+  const int64_t cid = ((int64_t)b * p.Hkv + hk) * p.NC + c;
+  const int64_t prow = (cid * p.Gs + (p.per_group ? 0 : hh)) * p.CT + (t - c * p.CT);
+  const int rr = p.per_group ? hh : 0;
+  const int32_t* sr = p.sel + (((int64_t)b * p.Hs + hs) * p.Lq + t) * p.sel_w;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sl = 0; sl < p.sel_w; ++sl) {
+    const int jj = sr[sl];
+    if (jj < 0 || jj >= p.Nb) continue;
+    const int64_t pidx = (prow * p.kslot + sl) * p.R + rr;
+    acc += *reinterpret_cast<const f32x4*>(p.dq_part + pidx * D + li * 4);
+  }
+  *reinterpret_cast<f32x4*>(p.dq + row * D + li * 4) = acc * p.scale;
+}
+
+// dk / dv of one (b, kv head, block): the items of its buckets summed in
+// query-chunk order; blocks nobody chose get zeros
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(AttnParams p) {
+  const int64_t blk = blockIdx.x;  // (b * Hkv + hk) * Nb + j
+  const int j = (int)(blk % p.Nb);
+  const int64_t bh = blk / p.Nb;
+  const int hk = (int)(bh % p.Hkv), b = (int)(bh / p.Hkv);
+  const int key0 = j * p.block;
+  const int n_keys = min(p.block, p.Lk - key0);
+  for (int i = threadIdx.x; i < n_keys * (D / 4); i += 256) {
+    const int u = i / (D / 4), d4 = (i % (D / 4)) * 4;
+    f32x4 ak = f32x4{0.f, 0.f, 0.f, 0.f}, av = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < p.NC; ++c) {
+      const int64_t bk = (bh * p.NC + c) * p.Nb + j;
+      if (p.grid == 0 || p.counts[bk] == 0) continue;  // no selection entries at all: nothing was built
+      const float* src = p.dkv_part + (int64_t)p.tile_off[bk] * 2 * p.block * D;
+      ak += *reinterpret_cast<const f32x4*>(src + (int64_t)u * D + d4);
+      av += *reinterpret_cast<const f32x4*>(src + (int64_t)(p.block + u) * D + d4);
+    }
+    const int64_t orow = (((int64_t)b * p.Lk + key0 + u) * p.Hkv + hk) * D + d4;
+    *reinterpret_cast<f32x4*>(p.dk + orow) = ak * p.scale;
+    *reinterpret_cast<f32x4*>(p.dv + orow) = av;
+  }
+}
+
+bool launch_attn_backward(const AttnParams& p, int64_t nrows_out, hipStream_t s) {
+  const int nbk = p.B * p.Hkv * p.NC * p.Nb;
+  {
+    LaunchScope ls("bwd_delta", s);
+    const int64_t thr = nrows_out * (p.D / 8);
+    const unsigned grid = (unsigned)((thr + 255) / 256);
+    if (p.D == 128) hipLaunchKernelGGL(bwd_delta_kernel<128>, dim3(grid), dim3(256), 0, s, p, nrows_out);
+    else hipLaunchKernelGGL(bwd_delta_kernel<64>, dim3(grid), dim3(256), 0, s, p, nrows_out);
+  }
+  if (!launch_ok("bwd_delta")) return false;
+  if (p.grid > 0) {
+    LaunchScope ls("bwd_sort", s);
+    hipLaunchKernelGGL(bwd_sort_kernel, dim3((unsigned)nbk), dim3(256), 0, s, p, nbk);
+  }
+  if (!launch_ok("bwd_sort")) return false;
+  if (p.grid > 0) {
+    LaunchScope ls("attn_bwd", s);
+    // grid = the bound on the item count (items are built on the device);
+    // workgroups past the built items exit at once
+    const unsigned grid = (unsigned)p.grid;
+    if (p.D == 128) hipLaunchKernelGGL(attn_bwd_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(attn_bwd_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+  }
+  if (!launch_ok("attn_bwd")) return false;
+  {
+    LaunchScope ls("bwd_dq_reduce", s);
+    const int64_t thr = nrows_out * (p.D / 4);
+    const unsigned grid = (unsigned)((thr + 255) / 256);
+    if (p.D == 128) hipLaunchKernelGGL(bwd_dq_reduce_kernel<128>, dim3(grid), dim3(256), 0, s, p, nrows_out);
+    else hipLaunchKernelGGL(bwd_dq_reduce_kernel<64>, dim3(grid), dim3(256), 0, s, p, nrows_out);
+  }
+  if (!launch_ok("bwd_dq_reduce")) return false;
+  {
+    LaunchScope ls("bwd_dkv_reduce", s);
+    const unsigned grid = (unsigned)((int64_t)p.B * p.Hkv * p.Nb);
+    if (p.D == 128) hipLaunchKernelGGL(bwd_dkv_reduce_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(bwd_dkv_reduce_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+  }
+  return launch_ok("bwd_dkv_reduce");
+}
+
 }  // namespace bsa

@@ -148,10 +148,25 @@ struct AttnParams {
   uint16_t* o;
   int64_t os_b, os_t, os_h;
   float* lse_out;  // natural log, [B, Hq, Lq] or null
+  // backward through the fixed selection (one work item per bucket, entries sorted)
+  const uint16_t* dout;
+  int64_t dos_b, dos_t, dos_h;
+  const float* lse_in;      // [B, Hq, Lq] natural log
+  float* delta;             // [B, Hq, Lq]: dout . o per row
+  float* dq_part;           // [rows * kslot * R, D]: sum over the slot's keys of ds * k
+  float* dkv_part;          // [items, 2, block, D]: per item, sum over its rows of ds * q and p * dout
+  const int32_t* counts;    // entries per bucket
+  float* dq;                // [B, Lq, Hq, D]
+  float* dk;                // [B, Lk, Hkv, D]
+  float* dv;
+  float scale;
 };
 int gather_waves(int block);  // waves per gather workgroup for this block size
 bool launch_attn_gather(const AttnParams& p, hipStream_t s);
 bool launch_attn_merge(const AttnParams& p, hipStream_t s);
+// backward: delta, per-bucket entry sort, gradient partials, ordered reductions
+constexpr int kBwdSortCap = 8192;  // entries per bucket the LDS sort holds
+bool launch_attn_backward(const AttnParams& p, int64_t nrows_out, hipStream_t s);
 
 struct AttnF32Params {
   int B, Lq, Lk, Hq, Hkv, G, D, block, Hs, per_group, causal;

@@ -39,7 +39,7 @@ BSA_DEV SelEntry decode_sel(const CsrParams& p, int64_t idx) {
   if (slot >= p.kslot) return r;
   const int64_t srow = idx / p.sel_w;
   const int j = p.sel[idx];
-  if (j < 0) return r;
+  if (j < 0 || j >= p.Nb) return r;
   const int t = (int)(srow % p.Lq);
   const int hs = (int)((srow / p.Lq) % p.Hs);
   const int b = (int)(srow / ((int64_t)p.Lq * p.Hs));
@@ -110,7 +110,7 @@ BSA_DEV bool piece_entry(const CsrParams& p, const SegPiece& sp, int li, float i
   const int slot = li - lr * p.sel_w;
   if (slot >= p.kslot) return false;
   const int j = p.sel[sp.ra * p.sel_w + li];
-  if (j < 0) return false;
+  if (j < 0 || j >= p.Nb) return false;
   bucket = sp.base + j;
   packed = ((uint32_t)(sp.t0 + lr) << p.sh_t) | ((uint32_t)sp.hh << p.sh_h) | (uint32_t)slot;
   return true;

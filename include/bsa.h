@@ -205,6 +205,44 @@ typedef struct bsa_summary_args {
 size_t bsa_summary_workspace_bytes(const bsa_summary_args* a);
 bsa_status bsa_block_summary(const bsa_summary_args* a, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Backward of the prefill's attention through its block selection: the
+ * method is trained end to end (MoBA card, card.what_it_is; "MSA: Memory
+ * Sparse Attention", "Key Points"), and a top-k choice has no gradient, so
+ * with the selection held fixed the gradient is that of exact softmax
+ * attention over the chosen keys.  For query row (b, t, h) with weights p_u
+ * over the keys it attended (own block masked after the query when causal,
+ * query t at absolute position Lk - Lq + t) and g = dL/do:
+ *   dv_u += p_u g,  ds_u = p_u (g . v_u - g . o),
+ *   dq = scale * sum_u ds_u k_u,  dk_u += scale * ds_u q.
+ * q and k are the attended tensors (after RoPE when the forward applied it;
+ * the rotation's own backward is the caller's).  o, lse and sel are the
+ * forward call's outputs (sel entries -1 or in [0, Nb); entries outside that
+ * range are skipped).  bf16 inputs, fp32 outputs, fp32 arithmetic; outputs
+ * are bitwise deterministic (the rows that chose a block are summed in a
+ * fixed order).
+ */
+typedef struct bsa_backward_args {
+    int32_t dtype;                 /* BSA_DTYPE_BF16 */
+    int32_t B, Lq, Lk, Hq, Hkv, D; /* D 64 or 128 */
+    const void* q;    int64_t q_stride[3];   /* (b, t, h) element strides, as in prefill */
+    const void* k;    int64_t k_stride[3];
+    const void* v;    int64_t v_stride[3];
+    const void* o;    int64_t o_stride[3];   /* the forward's output */
+    const void* dout; int64_t do_stride[3];  /* dL/do, same shape as o */
+    const float* lse;              /* [B, Hq, Lq] the forward's lse_out (natural log) */
+    const int32_t* sel;            /* [B, Hs, Lq, sel_w] the forward's sel_out */
+    int32_t sel_w;                 /* the forward's topk + causal */
+    int32_t block, causal, gate_mode;
+    float scale;                   /* 0 means 1/sqrt(D) */
+    float* dq;                     /* [B, Lq, Hq, D] contiguous fp32 */
+    float* dk;                     /* [B, Lk, Hkv, D] contiguous fp32 */
+    float* dv;                     /* [B, Lk, Hkv, D] contiguous fp32 */
+} bsa_backward_args;
+
+size_t bsa_backward_workspace_bytes(const bsa_backward_args* a);
+bsa_status bsa_sparse_attn_backward(const bsa_backward_args* a, void* workspace, size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char* bsa_last_error(void);
 /* Library version, major * 10000 + minor * 100 + patch. */

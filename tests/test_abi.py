@@ -136,6 +136,34 @@ def test_decode_block_table_validation(m):
     assert m.lib().bsa_decode_workspace_bytes(ctypes.byref(d)) == 0
 
 
+def test_backward_validation_and_workspace(m):
+    """The backward entry point validates before anything else and sizes its workspace from the
+    shapes alone."""
+    buf = ctypes.create_string_buffer(1 << 12)
+    base = (ctypes.addressof(buf) + 255) & ~255  # never dereferenced: only validation and the query run
+    a = m.BackwardArgs()
+    a.dtype = m.BSA_DTYPE_BF16
+    a.B, a.Lq, a.Lk, a.Hq, a.Hkv, a.D = 1, 512, 512, 8, 2, 128
+    for f in ("q", "k", "v", "o", "dout", "lse", "sel", "dq", "dk", "dv"):
+        setattr(a, f, base)
+    a.q_stride = a.o_stride = a.do_stride = m.I64x3(512 * 8 * 128, 8 * 128, 128)
+    a.k_stride = a.v_stride = m.I64x3(512 * 2 * 128, 2 * 128, 128)
+    a.sel_w, a.block, a.causal, a.gate_mode = 4, 64, 1, m.BSA_GATE_PER_HEAD
+    n = m.lib().bsa_backward_workspace_bytes(ctypes.byref(a))
+    assert n > 0
+    assert m.lib().bsa_sparse_attn_backward(ctypes.byref(a), None, 0, None) == m.BSA_ERR_WORKSPACE
+    a.gate_mode = m.BSA_GATE_PER_GROUP
+    assert 0 < m.lib().bsa_backward_workspace_bytes(ctypes.byref(a)) < n  # one selection row per group
+    for field, value, status in (("dtype", m.BSA_DTYPE_F32, m.BSA_ERR_UNSUPPORTED), ("D", 96, m.BSA_ERR_UNSUPPORTED),
+                                 ("sel_w", 66, m.BSA_ERR_INVALID_ARG), ("causal", 2, m.BSA_ERR_INVALID_ARG),
+                                 ("dout", None, m.BSA_ERR_INVALID_ARG), ("Lk", 100, m.BSA_ERR_INVALID_ARG)):
+        old = getattr(a, field)
+        setattr(a, field, value)
+        assert m.lib().bsa_backward_workspace_bytes(ctypes.byref(a)) == 0
+        assert m.lib().bsa_sparse_attn_backward(ctypes.byref(a), None, 0, None) == status, field
+        setattr(a, field, old)
+
+
 def test_timer_report_unknown_kernel_is_empty(m):
     m.timer_reset()
     assert m.timer_report("no_such_kernel") == (0.0, 0)

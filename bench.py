@@ -121,7 +121,33 @@ def other_workloads(m, reps):
     out["moba_32k_prefill"] = {"ms": round(ms, 4), "tokens_per_s": round(c["L"] / (ms * 1e-3), 1),
                                "attended_tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
     _log(f"MoBA-style 32K prefill: {ms:.3f} ms")
-    del q, k, v, o, ws
+    # its backward through the selection (a training step's attention part)
+    g = synth.device_tensor((c["B"], c["L"], c["Hq"], c["D"]), 1.0, SEED, t["dout"], "bf16")
+    o, sel, lse = m.sparse_attn_prefill(q, k, v, c["block"], c["topk"], True, return_sel=True, return_lse=True)
+    grads = (torch.empty(q.shape, dtype=torch.float32, device="cuda"),
+             torch.empty(k.shape, dtype=torch.float32, device="cuda"),
+             torch.empty(v.shape, dtype=torch.float32, device="cuda"))
+    bws = torch.empty(m.backward_workspace_bytes(q, k, sel, block=c["block"], causal=True), dtype=torch.uint8,
+                      device="cuda")
+    bms = time_call(lambda: m.sparse_attn_backward(q, k, v, o, lse, sel, g, c["block"], True, out=grads,
+                                                   workspace=bws), reps)
+    m.timer_enable(1)
+    m.timer_reset()
+    for _ in range(2):
+        m.sparse_attn_backward(q, k, v, o, lse, sel, g, c["block"], True, out=grads, workspace=bws)
+    torch.cuda.synchronize()
+    kms = m.timer_report("attn_bwd")[0] / 2
+    m.timer_enable(0)
+    bflops = 2.5 * flops  # per attended pair: q.k, g.v, and the three rank-one updates (dq, dk, dv) = 10 D
+    out["moba_32k_backward"] = {"ms": round(bms, 4), "attn_bwd_ms": round(kms, 4),
+                                "attended_tflops": round(bflops / (bms * 1e-3) / 1e12, 2),
+                                "kernel_tflops": round(bflops / (kms * 1e-3) / 1e12, 2),
+                                "note": "gradients through the forward's selection; fp32 VALU (chip fp32 vector "
+                                        "peak 157.3 TFLOP/s with packed FP32, 78.6 without, which this build "
+                                        "does not emit)"}
+    _log(f"MoBA-style 32K backward: {bms:.3f} ms (gradient kernel {kms:.3f} ms, "
+         f"{bflops / (kms * 1e-3) / 1e12:.1f} TFLOP/s)")
+    del q, k, v, o, ws, g, sel, lse, grads, bws
     c = MEMORY
     ids = synth.doc_ids_from_lengths(synth.doc_lengths(c["Lk"], c["docs"], c["doc_mean"], c["doc_sigma"], SEED))
     dk = torch.from_numpy(ids[None]).cuda()

@@ -638,15 +638,17 @@ static bsa_status plan_backward(const bsa_backward_args* a, BackwardPlan& P, cha
   if (P.nsel_rows * std::max(a->sel_w, 1) >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "too many selection entries");
   if (P.sh_t >= 31 || (int64_t)(a->Lq - 1) >= ((int64_t)1 << (32 - P.sh_t)))
     return fail(BSA_ERR_UNSUPPORTED, "Lq too large for the packed selection entries");
-  // Query chunks: a (chunk, block) bucket is one work item whose entries are
-  // sorted in LDS (at most CT * Gs of them), and each non-empty bucket keeps a
-  // block-sized dk / dv partial; the longest chunks the sort holds keep the
-  // fewest partials.
+  // Query chunks: a (chunk, block) bucket's entries are sorted in LDS (at
+  // most CT * Gs of them); the longest chunks the sort holds.
   P.CT = std::min(a->Lq, kBwdSortCap / P.Gs);
   P.NC = (a->Lq + P.CT - 1) / P.CT;
   P.nbk = (int64_t)a->B * a->Hkv * P.NC * P.Nb;
   if (P.nbk >= (int64_t)1 << 30) return fail(BSA_ERR_UNSUPPORTED, "too many (chunk, block) buckets");
-  P.rows_item = P.CT * P.G;  // every row a bucket can hold: one item per bucket
+  // work items: consecutive runs of up to 512 rows of a bucket's sorted
+  // entries (a fixed split, so the sums stay in a fixed order); long buckets
+  // (early blocks that most tokens of a chunk choose) spread over several
+  // workgroups instead of one
+  P.rows_item = std::min(P.CT * P.G, 512);
   P.max_entries = P.nsel_rows * a->sel_w;
   P.max_items = (P.max_entries * P.R + P.rows_item - 1) / P.rows_item + std::min<int64_t>(P.nbk, P.max_entries);
   if (P.max_items >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "too many work items");

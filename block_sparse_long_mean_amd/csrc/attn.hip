@@ -970,10 +970,10 @@ bool launch_attn_rowwise_f32(const AttnF32Params& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Backward through the fixed selection.  Work items are whole buckets (one
-// query chunk's entries for one (b, kv head, block)); their entries are
-// sorted first so that every sum over the rows that chose a block runs in a
-// fixed order.
+// Backward through the fixed selection.  A bucket's entries (one query
+// chunk's rows that chose one (b, kv head, block)) are sorted first and cut
+// into work items of consecutive rows, so every sum over the rows that chose
+// a block runs in a fixed order.
 // ---------------------------------------------------------------------------
 
 // delta[b, h, t] = dout . o of each output row, fp32 (D/8 lanes per row)
@@ -1083,6 +1083,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnParams p) {
 #pragma unroll
     for (int e = 0; e < DQ; ++e) dk[e] = dv[e] = 0.f;
     const int key = key0 + t0 + ku;
+    __syncthreads();  // the tile is staged
+    // this lane's quarter of its key and value, held for every row of the item
+    float kr[DQ], vr[DQ];
+#pragma unroll
+    for (int e = 0; e < DQ; e += 4) {
+      const f32x4 kq = *reinterpret_cast<const f32x4*>(&s_k[ku * KP + qc * DQ + e]);
+      const f32x4 vq = *reinterpret_cast<const f32x4*>(&s_v[ku * KP + qc * DQ + e]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        kr[e + x] = kq[x];
+        vr[e + x] = vq[x];
+      }
+    }
     for (int r0 = 0; r0 < rec.z; r0 += RB) {
       const int nr = min(RB, rec.z - r0);
       __syncthreads();  // the previous rows' q, g and ds are no longer read
@@ -1113,34 +1126,31 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnParams p) {
       __syncthreads();
       for (int r = 0; r < nr; ++r) {
         float sc = 0.f, dp = 0.f;
+        float qv[DQ], gv[DQ];  // the row's quarter of q and g, read once for both passes
 #pragma unroll
         for (int e = 0; e < DQ; e += 4) {
-          const f32x4 kq = *reinterpret_cast<const f32x4*>(&s_k[ku * KP + qc * DQ + e]);
-          const f32x4 vq = *reinterpret_cast<const f32x4*>(&s_v[ku * KP + qc * DQ + e]);
           const f32x4 qq = *reinterpret_cast<const f32x4*>(&s_q[r][qc * DQ + e]);
           const f32x4 gq = *reinterpret_cast<const f32x4*>(&s_g[r][qc * DQ + e]);
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
-            sc = fmaf(qq[x], kq[x], sc);
-            dp = fmaf(gq[x], vq[x], dp);
+            qv[e + x] = qq[x];
+            gv[e + x] = gq[x];
+            sc = fmaf(qq[x], kr[e + x], sc);
+            dp = fmaf(gq[x], vr[e + x], dp);
           }
         }
-        sc += __shfl_xor(sc, 1, 64);
-        sc += __shfl_xor(sc, 2, 64);
-        dp += __shfl_xor(dp, 1, 64);
-        dp += __shfl_xor(dp, 2, 64);
+        // complete the dot products across the key's four lanes (a DPP quad; every lane runs it)
+        sc += __uint_as_float(dpp32<0xB1>(__float_as_uint(sc), __float_as_uint(sc)));
+        dp += __uint_as_float(dpp32<0xB1>(__float_as_uint(dp), __float_as_uint(dp)));
+        sc += __uint_as_float(dpp32<0x4E>(__float_as_uint(sc), __float_as_uint(sc)));
+        dp += __uint_as_float(dpp32<0x4E>(__float_as_uint(dp), __float_as_uint(dp)));
         const bool ok = ku < nt && key <= s_qpos[r];
         const float pr = ok ? exp2f(sc * p.sl2 - s_lse2[r]) : 0.f;
         const float ds = pr * (dp - s_dl[r]);
 #pragma unroll
-        for (int e = 0; e < DQ; e += 4) {
-          const f32x4 qq = *reinterpret_cast<const f32x4*>(&s_q[r][qc * DQ + e]);
-          const f32x4 gq = *reinterpret_cast<const f32x4*>(&s_g[r][qc * DQ + e]);
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            dk[e + x] = fmaf(ds, qq[x], dk[e + x]);
-            dv[e + x] = fmaf(pr, gq[x], dv[e + x]);
-          }
+        for (int e = 0; e < DQ; ++e) {
+          dk[e] = fmaf(ds, qv[e], dk[e]);
+          dv[e] = fmaf(pr, gv[e], dv[e]);
         }
         if (qc == 0) s_ds[r][ku] = ds;
       }
@@ -1206,7 +1216,7 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(AttnParams p, int64_
 }
 
 // dk / dv of one (b, kv head, block): the items of its buckets summed in
-// query-chunk order; blocks nobody chose get zeros
+// (query chunk, item) order; blocks nobody chose get zeros
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(AttnParams p) {
   const int64_t blk = blockIdx.x;  // (b * Hkv + hk) * Nb + j
@@ -1221,9 +1231,11 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(AttnParams p) {
     for (int c = 0; c < p.NC; ++c) {
       const int64_t bk = (bh * p.NC + c) * p.Nb + j;
       if (p.grid == 0 || p.counts[bk] == 0) continue;  // no selection entries at all: nothing was built
-      const float* src = p.dkv_part + (int64_t)p.tile_off[bk] * 2 * p.block * D;
-      ak += *reinterpret_cast<const f32x4*>(src + (int64_t)u * D + d4);
-      av += *reinterpret_cast<const f32x4*>(src + (int64_t)(p.block + u) * D + d4);
+      for (int it = p.tile_off[bk]; it < p.tile_off[bk + 1]; ++it) {
+        const float* src = p.dkv_part + (int64_t)it * 2 * p.block * D;
+        ak += *reinterpret_cast<const f32x4*>(src + (int64_t)u * D + d4);
+        av += *reinterpret_cast<const f32x4*>(src + (int64_t)(p.block + u) * D + d4);
+      }
     }
     const int64_t orow = (((int64_t)b * p.Lk + key0 + u) * p.Hkv + hk) * D + d4;
     *reinterpret_cast<f32x4*>(p.dk + orow) = ak * p.scale;

@@ -17,7 +17,7 @@ import hashlib
 
 import numpy as np
 
-TID = {"q": 0, "k": 1, "v": 2, "index_q": 3, "index_k": 4, "doc_lengths": 5, "pooled": 6}
+TID = {"q": 0, "k": 1, "v": 2, "index_q": 3, "index_k": 4, "doc_lengths": 5, "pooled": 6, "dout": 7}
 
 CHUNK = 1 << 24  # elements per device chunk
 

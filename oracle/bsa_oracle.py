@@ -526,7 +526,7 @@ def attend_grad(q_row, keys, values, do_row, scale: float):
 
 
 def prefill_backward(q, k, v, dout, sel, *, block: int, causal: bool, gate: str = "head",
-                     scale: float | None = None):
+                     scale: float | None = None, rows=None):
     """Gradients of the prefill output w.r.t. q, k and v with the selection
     held fixed.
 
@@ -537,7 +537,9 @@ def prefill_backward(q, k, v, dout, sel, *, block: int, causal: bool, gate: str 
     block when causal (absolute query position Lk - Lq + t), exactly as in
     prefill(); its gradient contributions are summed into dk, dv over the
     keys it attended.  q and k are the attended (already position-encoded)
-    tensors.  Returns dict dq [B, Lq, Hq, D], dk, dv [B, Lk, Hkv, D].
+    tensors.  rows: optional list of (b, t, h) query rows to evaluate (default
+    all); dq is then filled for those rows only and dk, dv hold only their
+    contributions.  Returns dict dq [B, Lq, Hq, D], dk, dv [B, Lk, Hkv, D].
     """
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
@@ -548,27 +550,27 @@ def prefill_backward(q, k, v, dout, sel, *, block: int, causal: bool, gate: str 
     dq = np.zeros((B, Lq, Hq, D))
     dk = np.zeros((B, Lk, Hkv, D))
     dv = np.zeros((B, Lk, Hkv, D))
-    for b in range(B):
-        for t in range(Lq):
-            qabs = Lk - Lq + t
-            cur = current_block(qabs, block) if causal else None
-            for h in range(Hq):
-                hk = h // G
-                hs = hk if per_group else h
-                idx = []
-                for j in sel[b, hs, t]:
-                    if j < 0:
-                        continue
-                    a, e = _block_tokens(int(j), block, Lk)
-                    if causal and j == cur:
-                        e = min(e, qabs + 1)
-                    idx.extend(range(a, e))
-                idx = np.asarray(idx, dtype=np.int64)
-                if idx.size == 0:
-                    continue
-                gq, gk, gv = attend_grad(q[b, t, h], _rows(k, b, idx, hk), _rows(v, b, idx, hk),
-                                         dout[b, t, h], scale)
-                dq[b, t, h] = gq
-                dk[b, idx, hk] += gk
-                dv[b, idx, hk] += gv
+    if rows is None:
+        rows = [(b, t, h) for b in range(B) for t in range(Lq) for h in range(Hq)]
+    for b, t, h in rows:
+        qabs = Lk - Lq + t
+        cur = current_block(qabs, block) if causal else None
+        hk = h // G
+        hs = hk if per_group else h
+        idx = []
+        for j in sel[b, hs, t]:
+            if j < 0:
+                continue
+            a, e = _block_tokens(int(j), block, Lk)
+            if causal and j == cur:
+                e = min(e, qabs + 1)
+            idx.extend(range(a, e))
+        idx = np.asarray(idx, dtype=np.int64)
+        if idx.size == 0:
+            continue
+        gq, gk, gv = attend_grad(q[b, t, h], _rows(k, b, idx, hk), _rows(v, b, idx, hk),
+                                 dout[b, t, h], scale)
+        dq[b, t, h] = gq
+        dk[b, idx, hk] += gk
+        dv[b, idx, hk] += gv
     return {"dq": dq, "dk": dk, "dv": dv}

@@ -88,6 +88,46 @@ def test_moba_prefill_32k_fullsize(bsa):
     _check_prefill_rows(o, sel, lse, toks, run_oracle, topk, True)
 
 
+def test_moba_backward_32k_fullsize(bsa):
+    """The MoBA-style 32K backward in the benchmark's launch configuration (caller-provided gradient
+    buffers and workspace), through the forward's own selection.  Sampled: dq of 40 tokens with
+    every head (first / last tokens and block edges included), and dk, dv of every key of two
+    whole blocks, (kv head 0, block 63) and (kv head 5, block 40), for which the oracle sums the
+    contributions of every row that chose them.  Bound: 1e-2 of the largest reference gradient
+    of each compared set."""
+    B, L, Hq, Hkv, D, block, topk, sigma = 1, 32768, 32, 8, 128, 512, 3, 128 ** -0.5
+    G = Hq // Hkv
+    _say("case MoBA backward B1 L32768 H32/8 D128 block512 topk3 causal per-head")
+    q = synth.device_tensor((B, L, Hq, D), sigma, SEED, T["q"], "bf16")
+    k = synth.device_tensor((B, L, Hkv, D), sigma, SEED, T["k"], "bf16")
+    v = synth.device_tensor((B, L, Hkv, D), sigma, SEED, T["v"], "bf16")
+    g = synth.device_tensor((B, L, Hq, D), 1.0, SEED, T["dout"], "bf16")
+    o, sel, lse = bsa.sparse_attn_prefill(q, k, v, block, topk, True, return_sel=True, return_lse=True)
+    grads = tuple(torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in (q, k, v))
+    ws = torch.empty(bsa.backward_workspace_bytes(q, k, sel, block=block, causal=True), dtype=torch.uint8,
+                     device="cuda")
+    dq, dk, dv = bsa.sparse_attn_backward(q, k, v, o, lse, sel, g, block, True, out=grads, workspace=ws)
+    torch.cuda.synchronize()
+    _say("  gpu done")
+    qh, kh, vh, gh = q.cpu(), k.cpu(), v.cpu(), g.cpu()
+    sh = sel.cpu().numpy()
+    toks = _sample_tokens(L, block, 30, 101, extra=(block - 1, block, 40 * block + 7))
+    rows = [(0, t, h) for t in toks for h in range(Hq)]
+    ref = oracle.prefill_backward(qh, kh, vh, gh, sh, block=block, causal=True, rows=rows)
+    ti = torch.tensor(toks)
+    assert_close(to_np(dq[0].index_select(0, ti.cuda())), ref["dq"][0, toks],
+                 1e-2 * float(np.abs(ref["dq"][0, toks]).max()), None, what="dq")
+    for hk, j in ((0, 63), (5, 40)):
+        chose = np.nonzero((sh[0, hk * G:(hk + 1) * G] == j).any(axis=-1))  # (head in group, token)
+        rows = [(0, int(t), hk * G + int(hh)) for hh, t in zip(*chose)]
+        _say(f"  block ({hk}, {j}): {len(rows)} rows chose it")
+        ref = oracle.prefill_backward(qh, kh, vh, gh, sh, block=block, causal=True, rows=rows)
+        a, e = j * block, (j + 1) * block
+        for nm, got in (("dk", dk), ("dv", dv)):
+            r = ref[nm][0, a:e, hk]
+            assert_close(to_np(got[0, a:e, hk]), r, 1e-2 * float(np.abs(r).max()), None, what=nm)
+
+
 def test_index_branch_prefill_128k_fullsize(bsa):
     """MiniMax-style 128K: B1, 64/8 heads, D128, block 64, index q/k of dim 64, scores summed per group,
     top-16 + own block, causal, bf16 N(0,1) -- the benchmark's prefill, in its launch configuration

@@ -1029,8 +1029,8 @@ __global__ __launch_bounds__(256) void bwd_sort_kernel(AttnParams p, int nbk) {
   for (int i = threadIdx.x; i < n; i += 256) ent[i] = s_e[i];
 }
 
-// One workgroup per work item (bucket): for each 64-key tile of the block,
-// stage K and V (fp32, LDS), then take the item's rows eight at a time.
+// One workgroup per work item: for each 64-key tile of the block, stage K
+// (fp32, LDS), then take the item's rows sixteen at a time.
 // Wave w owns keys 16w .. 16w+15 of the tile; lane (key, quarter) forms
 // quarter dot products q.k and g.v, completes them across the key's four
 // lanes, and accumulates dk and dv for its key and quarter in registers.
@@ -1038,9 +1038,8 @@ __global__ __launch_bounds__(256) void bwd_sort_kernel(AttnParams p, int nbk) {
 // (row, slot) partial accumulates over the block's tiles.
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnParams p) {
-  constexpr int KT = 64, RB = 8, DQ = D / 4, KP = D + 4;
+  constexpr int KT = 64, RB = 16, DQ = D / 4, KP = D + 4;
   __shared__ __attribute__((aligned(16))) float s_k[KT * KP];
-  __shared__ __attribute__((aligned(16))) float s_v[KT * KP];
   __shared__ __attribute__((aligned(16))) float s_q[RB][D];
   __shared__ __attribute__((aligned(16))) float s_g[RB][D];
   __shared__ float s_ds[RB][KT];
@@ -1068,33 +1067,31 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnParams p) {
     __syncthreads();  // the previous tile's K / V are no longer read
     for (int i = tid; i < KT * (D / 8); i += 256) {
       const int u = i / (D / 8), c8 = i % (D / 8);
-      u16x8 kx = u16x8{0, 0, 0, 0, 0, 0, 0, 0}, vx = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (u < nt) {
-        kx = ld16(kb + (int64_t)(key0 + t0 + u) * p.ks_t + c8 * 8);
-        vx = ld16(vb + (int64_t)(key0 + t0 + u) * p.vs_t + c8 * 8);
-      }
+      u16x8 kx = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (u < nt) kx = ld16(kb + (int64_t)(key0 + t0 + u) * p.ks_t + c8 * 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        s_k[u * KP + c8 * 8 + e] = bf2f(kx[e]);
-        s_v[u * KP + c8 * 8 + e] = bf2f(vx[e]);
-      }
+      for (int e = 0; e < 8; ++e) s_k[u * KP + c8 * 8 + e] = bf2f(kx[e]);
     }
     float dk[DQ], dv[DQ];
 #pragma unroll
     for (int e = 0; e < DQ; ++e) dk[e] = dv[e] = 0.f;
     const int key = key0 + t0 + ku;
     __syncthreads();  // the tile is staged
-    // this lane's quarter of its key and value, held for every row of the item
+    // this lane's quarter of its key (LDS) and value (straight from memory),
+    // held for every row of the item
     float kr[DQ], vr[DQ];
 #pragma unroll
-    for (int e = 0; e < DQ; e += 4) {
-      const f32x4 kq = *reinterpret_cast<const f32x4*>(&s_k[ku * KP + qc * DQ + e]);
-      const f32x4 vq = *reinterpret_cast<const f32x4*>(&s_v[ku * KP + qc * DQ + e]);
+    for (int e = 0; e < DQ; e += 8) {
+      const f32x4 k0 = *reinterpret_cast<const f32x4*>(&s_k[ku * KP + qc * DQ + e]);
+      const f32x4 k1 = *reinterpret_cast<const f32x4*>(&s_k[ku * KP + qc * DQ + e + 4]);
+      const u16x8 vx = ku < nt ? ld16(vb + (int64_t)key * p.vs_t + qc * DQ + e) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        kr[e + x] = kq[x];
-        vr[e + x] = vq[x];
+        kr[e + x] = k0[x];
+        kr[e + 4 + x] = k1[x];
       }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) vr[e + x] = bf2f(vx[x]);
     }
     for (int r0 = 0; r0 < rec.z; r0 += RB) {
       const int nr = min(RB, rec.z - r0);
@@ -1155,10 +1152,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnParams p) {
         if (qc == 0) s_ds[r][ku] = ds;
       }
       __syncthreads();
-      // dq partials: thread (row, D/32 head dims) sums ds_u k_u over the tile
+      // dq partials: thread (row, D/16 head dims) sums ds_u k_u over the tile
       {
-        constexpr int DPT = D / 32;
-        const int r = tid >> 5, d0 = (tid & 31) * DPT;
+        constexpr int DPT = D / 16;
+        const int r = tid >> 4, d0 = (tid & 15) * DPT;
         if (r < nr) {
           float acc[DPT];
 #pragma unroll

@@ -184,6 +184,7 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
   if (!gate_only && (!a->v || !a->o)) return fail(BSA_ERR_INVALID_ARG, "v and o are required");
   if (gate_only && !a->sel_out) return fail(BSA_ERR_INVALID_ARG, "sel_out is required for bsa_select_blocks");
   if ((a->index_q == nullptr) != (a->index_k == nullptr)) return fail(BSA_ERR_INVALID_ARG, "index_q and index_k go together");
+  if (a->pooled && !aligned16(a->pooled)) return fail(BSA_ERR_INVALID_ARG, "pooled must be 16-byte aligned");
   const int elt = a->dtype == BSA_DTYPE_BF16 ? 2 : 4;
   if (!aligned16(a->q) || !aligned16(a->k) || (a->v && !aligned16(a->v)) || (a->o && !aligned16(a->o)))
     return fail(BSA_ERR_INVALID_ARG, "tensor base pointers must be 16-byte aligned");
@@ -290,8 +291,9 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
   P.k32 = (P.rope_k && !P.bf16) ? c.take<float>(B * Lk * a->Hkv * a->D) : nullptr;
   const int64_t npool = (int64_t)a->B * a->Hkv * P.Nb * P.Dg;
   if (P.bf16) {
-    P.p_hi = c.take<uint16_t>(npool);
-    P.p_lo = c.take<uint16_t>(npool);
+    // caller-provided fp32 summaries are read by the gate directly
+    P.p_hi = P.have_pooled ? nullptr : c.take<uint16_t>(npool);
+    P.p_lo = P.have_pooled ? nullptr : c.take<uint16_t>(npool);
     P.pooled32 = nullptr;
   } else {
     P.p_hi = P.p_lo = nullptr;
@@ -398,11 +400,6 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
       k_att = P.bf16 ? (const void*)P.k16 : (const void*)P.k32;
       for (int i = 0; i < 3; ++i) ka_s[i] = kc_s[i];
     }
-    if (!summarize && P.bf16) {
-      const int64_t Nb = P.Nb, Hkv = a->Hkv, Dg = P.Dg;
-      if (!launch_pooled_to_planes(a->pooled, 0, Nb * Hkv * Dg, Hkv * Dg, Dg, a->B, P.Nb, a->Hkv, P.Dg, P.p_hi, P.p_lo, s))
-        return BSA_ERR_HIP;
-    }
   }
   // 3. gate + top-k
   // gate query source: index q, else (rotated) q
@@ -419,8 +416,15 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
     g.q = gq; g.qs_b = gq_s[0]; g.qs_t = gq_s[1]; g.qs_h = gq_s[2];
     g.qkind = gq_f32 ? 1 : (P.per_group ? 2 : 0);
     g.Dg = P.Dg;
-    g.p_hi = P.p_hi; g.p_lo = P.p_lo;
-    g.ps_h = (int64_t)P.Nb * P.Dg; g.ps_b = (int64_t)a->Hkv * g.ps_h; g.ps_j = P.Dg;
+    if (P.have_pooled) {
+      // the caller's fp32 summaries [B, Nb, Hkv, Dg], split into bf16 hi + lo as the gate stages them
+      g.p_hi = g.p_lo = nullptr;
+      g.p_f32 = reinterpret_cast<const float*>(a->pooled);
+      g.ps_h = P.Dg; g.ps_j = (int64_t)a->Hkv * P.Dg; g.ps_b = (int64_t)P.Nb * g.ps_j;
+    } else {
+      g.p_hi = P.p_hi; g.p_lo = P.p_lo; g.p_f32 = nullptr;
+      g.ps_h = (int64_t)P.Nb * P.Dg; g.ps_b = (int64_t)a->Hkv * g.ps_h; g.ps_j = P.Dg;
+    }
     g.Nb = P.Nb; g.causal = a->causal; g.block = a->block; g.lens = nullptr;
     g.topk = P.topk; g.nsplit = P.nsplit; g.span = P.span;
     g.sel = P.sel; g.sel_w = P.sel_w; g.part = P.part_keys; g.tag = "gate";

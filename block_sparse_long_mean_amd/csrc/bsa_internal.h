@@ -67,6 +67,7 @@ struct GateParams {
   int Dg;
   const uint16_t* p_hi;
   const uint16_t* p_lo;  // may be null (summaries exact in bf16)
+  const float* p_f32;    // or fp32 summaries, split into hi / lo while staged (then p_hi, p_lo unused)
   int64_t ps_b, ps_h, ps_j;
   int Nb;
   int causal, block;

@@ -232,7 +232,9 @@ BSA_DEV uint64_t list_kth(const uint64_t (&L)[KR], int lane, int topk) {
   return shfl64(v, (lane & 48) + (e & 15));
 }
 
-template <int W, int DG, int KR, int QK, bool LO>
+// FS: the summaries come as fp32 (p_f32) and are split into the hi / lo
+// planes as each chunk is staged in LDS (LO is then true)
+template <int W, int DG, int KR, int QK, bool LO, bool FS>
 __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParams p) {
   constexpr int ROWS = 16 * W;
   constexpr int PADR = DG + 8;  // padded LDS row (bf16 elements)
@@ -282,8 +284,9 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
   const int c_lo = split * p.span;
   const int c_hi = p.topk > 0 ? min(c_lo + p.span, nc_max) : c_lo;
 
-  const uint16_t* phi = p.p_hi + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h;
-  const uint16_t* plo = LO ? p.p_lo + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h : nullptr;
+  const uint16_t* phi = FS ? nullptr : p.p_hi + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h;
+  const uint16_t* plo = (LO && !FS) ? p.p_lo + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h : nullptr;
+  const float* pf32 = FS ? p.p_f32 + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h : nullptr;
 
   uint64_t L[4][KR];
   uint64_t thr[4], left[4];
@@ -297,19 +300,30 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
     for (int m = 0; m < KR; ++m) L[i][m] = 0ull;
   }
 
-  // register prefetch of one chunk of summaries (hi and lo planes)
-  u16x8 pf_h[NPF], pf_l[LO ? NPF : 1];
+  // register prefetch of one chunk of summaries (hi and lo planes, or fp32)
+  u16x8 pf_h[FS ? 1 : NPF], pf_l[(LO && !FS) ? NPF : 1];
+  f32x4 pf_a[FS ? NPF : 1], pf_b[FS ? NPF : 1];
   auto fetch = [&](int c0) {
 #pragma unroll
     for (int n = 0; n < NPF; ++n) {
       const int idx = tid + n * 64 * W;
       const int jr = idx / CPR, ch = idx % CPR;
       const int j = c0 + jr;
-      pf_h[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if constexpr (LO) pf_l[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (idx < 64 * CPR && j < c_hi) {
-        pf_h[n] = ld16(phi + (int64_t)j * p.ps_j + ch * 8);
-        if constexpr (LO) pf_l[n] = ld16(plo + (int64_t)j * p.ps_j + ch * 8);
+      if constexpr (FS) {
+        pf_a[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pf_b[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (idx < 64 * CPR && j < c_hi) {
+          const float* src = pf32 + (int64_t)j * p.ps_j + ch * 8;
+          pf_a[n] = *reinterpret_cast<const f32x4*>(src);
+          pf_b[n] = *reinterpret_cast<const f32x4*>(src + 4);
+        }
+      } else {
+        pf_h[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if constexpr (LO) pf_l[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (idx < 64 * CPR && j < c_hi) {
+          pf_h[n] = ld16(phi + (int64_t)j * p.ps_j + ch * 8);
+          if constexpr (LO) pf_l[n] = ld16(plo + (int64_t)j * p.ps_j + ch * 8);
+        }
       }
     }
   };
@@ -322,8 +336,21 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
       const int idx = tid + n * 64 * W;
       if (idx < 64 * CPR) {
         const int jr = idx / CPR, ch = idx % CPR;
-        st16(&s_hi[jr * PADR + ch * 8], pf_h[n]);
-        if constexpr (LO) st16(&s_lo[jr * PADR + ch * 8], pf_l[n]);
+        if constexpr (FS) {
+          u16x8 h8, l8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            __bf16 hv, lv;
+            split_bf(e < 4 ? pf_a[n][e] : pf_b[n][e - 4], hv, lv);
+            h8[e] = __builtin_bit_cast(uint16_t, hv);
+            l8[e] = __builtin_bit_cast(uint16_t, lv);
+          }
+          st16(&s_hi[jr * PADR + ch * 8], h8);
+          st16(&s_lo[jr * PADR + ch * 8], l8);
+        } else {
+          st16(&s_hi[jr * PADR + ch * 8], pf_h[n]);
+          if constexpr (LO) st16(&s_lo[jr * PADR + ch * 8], pf_l[n]);
+        }
       }
     }
     __syncthreads();
@@ -493,14 +520,18 @@ __global__ __launch_bounds__(256) void gate_merge_kernel(GateParams p) {
 template <int W, int DG, int KR>
 static void gate_dispatch_q(const GateParams& p, hipStream_t s, int grid) {
   const bool lo = p.p_lo != nullptr;
-#define BSA_GATE_CASE(QK, LO)                                                               \
-  hipLaunchKernelGGL((gate_kernel<W, DG, KR, QK, LO>), dim3(grid), dim3(64 * W), 0, s, p);
-  if (p.qkind == 0) {
-    if (lo) { BSA_GATE_CASE(0, true) } else { BSA_GATE_CASE(0, false) }
+#define BSA_GATE_CASE(QK, LO, FS)                                                               \
+  hipLaunchKernelGGL((gate_kernel<W, DG, KR, QK, LO, FS>), dim3(grid), dim3(64 * W), 0, s, p);
+  if (p.p_f32) {
+    if (p.qkind == 0) { BSA_GATE_CASE(0, true, true) }
+    else if (p.qkind == 1) { BSA_GATE_CASE(1, true, true) }
+    else { BSA_GATE_CASE(2, true, true) }
+  } else if (p.qkind == 0) {
+    if (lo) { BSA_GATE_CASE(0, true, false) } else { BSA_GATE_CASE(0, false, false) }
   } else if (p.qkind == 1) {
-    if (lo) { BSA_GATE_CASE(1, true) } else { BSA_GATE_CASE(1, false) }
+    if (lo) { BSA_GATE_CASE(1, true, false) } else { BSA_GATE_CASE(1, false, false) }
   } else {
-    if (lo) { BSA_GATE_CASE(2, true) } else { BSA_GATE_CASE(2, false) }
+    if (lo) { BSA_GATE_CASE(2, true, false) } else { BSA_GATE_CASE(2, false, false) }
   }
 #undef BSA_GATE_CASE
 }

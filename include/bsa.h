@@ -110,7 +110,8 @@ typedef struct bsa_prefill_args {
     float rope_theta;              /* RoPE base; <= 0 means 10000 (pairs (i, i+D/2)) */
     float scale;                   /* softmax scale; 0 means 1/sqrt(D) */
     const float* pooled;           /* optional precomputed summaries [B, Nb, Hkv, Dg] fp32
-                                      contiguous; when given the summary step is skipped */
+                                      contiguous, 16-byte aligned; when given the summary step
+                                      is skipped and the gate reads them as they are */
     int32_t* sel_out;              /* optional [B, Hs, Lq, topk + causal] int32, Hs = Hq (per head)
                                       or Hkv (per group): chosen blocks ascending, the forced
                                       block last when causal, -1 padded */

@@ -242,6 +242,27 @@ def other_workloads(m, reps):
                               "algorithmic_gb": round(nbytes / 1e9, 4), "distinct_blocks": distinct,
                               "note": "128-token pages in a random order, block table per sequence"}
     _log(f"paged decode (1M caches, shuffled 128-token pages): {ms:.3f} ms, {nbytes / (ms * 1e-3) / 1e9:.1f} GB/s")
+    # the same paged caches with one selection per GQA group (the group's query
+    # heads' scores summed): one block list per (sequence, kv head)
+    wsg = torch.empty(m.decode_workspace_bytes(qd, kp, vp, pooled, block=c["block"], topk=c["topk"], gate="group",
+                                               block_table=table), dtype=torch.uint8, device="cuda")
+
+    def grouped():
+        return m.sparse_attn_decode(qd, kp, vp, pooled, c["topk"], c["block"], gate="group", out=od, workspace=wsg,
+                                    block_table=table, return_sel=True)
+
+    msg = time_call(grouped, max(reps, 10))
+    _, gsel = grouped()
+    torch.cuda.synchronize()
+    gs = gsel.cpu().numpy()  # [B, Hkv, topk + 1]
+    gdist = sum(len(set(int(x) for x in gs[b, hk] if x >= 0)) for b in range(c["B"]) for hk in range(c["Hkv"]))
+    gbytes = (c["B"] * (nb - 1) * c["Hkv"] * c["D"] * 2 + gdist * c["block"] * c["D"] * 2 * 2
+              + 2 * c["B"] * c["Hq"] * c["D"] * 2)
+    out["paged_decode_1m_per_group"] = {"ms": round(msg, 4), "hbm_gbs": round(gbytes / (msg * 1e-3) / 1e9, 1),
+                                        "algorithmic_gb": round(gbytes / 1e9, 4), "distinct_blocks": gdist,
+                                        "note": "per-group gating (group scores summed) on the same paged caches"}
+    _log(f"paged decode, per-group gating: {msg:.3f} ms, {gbytes / (msg * 1e-3) / 1e9:.1f} GB/s")
+    del wsg, gsel
     del kp, vp, od, ws
     torch.cuda.empty_cache()
     # host content tier: the same decode with its 68.7 GB of caches in pinned

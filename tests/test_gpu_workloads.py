@@ -163,8 +163,8 @@ def test_index_branch_prefill_128k_fullsize(bsa):
     _check_prefill_rows(o, sel, lse, toks, run_oracle, topk, True)
 
 
-def _decode_check(bsa, q, kc, vc, pooled, topk, block, lens, table=None):
-    o, sel, lse = bsa.sparse_attn_decode(q, kc, vc, pooled, topk, block, return_sel=True, return_lse=True,
+def _decode_check(bsa, q, kc, vc, pooled, topk, block, lens, table=None, gate="head"):
+    o, sel, lse = bsa.sparse_attn_decode(q, kc, vc, pooled, topk, block, gate=gate, return_sel=True, return_lse=True,
                                          cache_lens=None if lens is None else torch.from_numpy(lens).cuda(),
                                          block_table=None if table is None else torch.from_numpy(table).cuda())
     torch.cuda.synchronize()
@@ -175,7 +175,7 @@ def _decode_check(bsa, q, kc, vc, pooled, topk, block, lens, table=None):
     if table is not None:
         Lc = pooled.shape[1] * block
         kv = (oracle.PagedCache(kv[0], table, block, Lc), oracle.PagedCache(kv[1], table, block, Lc))
-    ref = oracle.decode(qh, *kv, ph, block=block, topk=topk, cache_lens=lens, return_scores=True)
+    ref = oracle.decode(qh, *kv, ph, block=block, topk=topk, gate=gate, cache_lens=lens, return_scores=True)
     B, Hs = ref["sel"].shape[:2]
     nb = pooled.shape[1]
     scores = np.full((B, Hs, 1, nb), np.nan)
@@ -185,7 +185,7 @@ def _decode_check(bsa, q, kc, vc, pooled, topk, block, lens, table=None):
     diff = check_selection(gsel, ref["sel"][:, :, None], scores, topk, True)
     _say(f"  decode rows {B * Hs}, near-tie differences {len(diff)}")
     if diff:
-        ref = oracle.decode(qh, *kv, ph, block=block, topk=topk, cache_lens=lens, force_sel=gsel[:, :, 0])
+        ref = oracle.decode(qh, *kv, ph, block=block, topk=topk, gate=gate, cache_lens=lens, force_sel=gsel[:, :, 0])
     assert_close(to_np(o), ref["o"], 1e-2, 1e-2, bf16_storage=True)
     assert_close(to_np(lse), ref["lse"], 5e-3, None, what="lse")
 
@@ -215,7 +215,8 @@ def test_decode_1m_cache_fullsize(bsa):
 def test_paged_decode_1m_cache_fullsize(bsa):
     """The long-context decode over a paged cache: the 16 sequences' 1,048,576-token caches cut
     into 128-token pages (head-major inside a page), stored in a seeded random order, one table
-    row of 8192 pages per sequence; every (sequence, head) is compared, full and ragged lengths."""
+    row of 8192 pages per sequence; every (sequence, head) is compared, full and ragged lengths,
+    then with per-group gating (the group's scores summed; one block list per kv head)."""
     B, Lc, Hq, Hkv, D, block, topk = 16, 1 << 20, 32, 8, 128, 128, 32
     nb = Lc // block
     P = B * nb
@@ -230,6 +231,8 @@ def test_paged_decode_1m_cache_fullsize(bsa):
                      Lc - 129, Lc - 128, Lc - 1, Lc, 4097], dtype=np.int32)
     _say("case paged decode ragged lengths")
     _decode_check(bsa, q, kp, vp, pooled, topk, block, lens, table)
+    _say("case paged decode, per-group gating")
+    _decode_check(bsa, q, kp, vp, pooled, topk, block, None, table, gate="group")
 
 
 def _check_summary_blocks(got, k, block, blocks, pos=None, bf16_out=False, atol=2e-6):

@@ -38,22 +38,31 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(DecodeGateParams p) 
   const int col = lane & 15, kq = lane >> 4;
   const int nq = p.per_group ? 1 : p.G;
   // B operand: column `col` = query head (or the group sum) for k = 8*kq + 32*ks
+  // (each lane's 8 consecutive head dims come in one 16-byte load per head)
   bf16x8 qh[KS], ql[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    const int d0 = ks * 32 + kq * 8;
+    if (col < nq) {
+      if (p.per_group) {
+        for (int g = 0; g < p.G; ++g) {
+          const u16x8 v = ld16(p.q + (int64_t)b * p.qs_b + (int64_t)(hk * p.G + g) * p.qs_h + d0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] += bf2f(v[e]);
+        }
+      } else {
+        const u16x8 v = ld16(p.q + (int64_t)b * p.qs_b + (int64_t)(hk * p.G + col) * p.qs_h + d0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = bf2f(v[e]);
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int d = ks * 32 + kq * 8 + e;
-      float x = 0.f;
-      if (col < nq) {
-        if (p.per_group) {
-          for (int g = 0; g < p.G; ++g) x += bf2f(p.q[(int64_t)b * p.qs_b + (int64_t)(hk * p.G + g) * p.qs_h + d]);
-        } else {
-          x = bf2f(p.q[(int64_t)b * p.qs_b + (int64_t)(hk * p.G + col) * p.qs_h + d]);
-        }
-      }
       __bf16 h, l;
-      split_bf(x, h, l);
+      split_bf(x[e], h, l);
       qh[ks][e] = h;
       ql[ks][e] = l;
     }

@@ -460,11 +460,15 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
       if (row_ok) {
         int32_t* out = p.sel + srow * p.sel_w;
         const int cur = p.causal ? (int)(qpos_of(p, b, ri.t) / p.block) : -1;
+        // cnt <= topk <= 16 * NR, so the chosen blocks and the forced one sit
+        // in the first NR + 1 groups of 16 slots; every later slot of the row
+        // (a requested topk above the number of blocks) is padding
 #pragma unroll
         for (int r = 0; r <= NR; ++r) {
           const int e = r * 16 + r16;
           if (e < p.sel_w) out[e] = e < cnt ? idx[r < NR ? r : 0] : (e == cnt && p.causal ? cur : -1);
         }
+        for (int e = (NR + 1) * 16 + r16; e < p.sel_w; e += 16) out[e] = -1;
       }
     } else if (row_ok) {
       uint64_t* out = p.part + (srow * p.nsplit + split) * p.topk;

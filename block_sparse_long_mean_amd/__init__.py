@@ -26,6 +26,7 @@ __all__ = [
     "timer_reset",
     "timer_report",
     "version",
+    "build_digest",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -129,12 +130,26 @@ _lib = None
 
 
 def lib():
-    """The loaded libbsa.so (raises if it has not been built)."""
+    """The loaded libbsa.so.  Raises if it has not been built, or if it was built
+    from sources other than the tree's (its embedded digest differs)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_long_mean_amd.build`")
+        from . import build as _build
+
         L = ctypes.CDLL(LIB_PATH)
+        try:
+            fn = L.bsa_build_digest
+        except AttributeError:
+            raise ImportError(f"{LIB_PATH} predates its sources (no build digest): rebuild it with "
+                              f"`python -m block_sparse_long_mean_amd.build`") from None
+        fn.argtypes = []
+        fn.restype = ctypes.c_char_p
+        built, tree = fn().decode(), _build.source_digest()
+        if built != tree:
+            raise ImportError(f"{LIB_PATH} was built from other sources (library {built}, tree {tree}): rebuild it "
+                              f"with `python -m block_sparse_long_mean_amd.build`")
         L.bsa_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
         L.bsa_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.bsa_sparse_attn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), VP, ctypes.c_size_t, VP]
@@ -174,6 +189,11 @@ def _check(st: int):
 
 def version() -> int:
     return lib().bsa_version()
+
+
+def build_digest() -> str:
+    """Digest of the sources the loaded library was built from."""
+    return lib().bsa_build_digest().decode()
 
 
 # --------------------------------------------------------------------------
@@ -293,12 +313,14 @@ def sparse_attn_prefill(q, k, v, block: int, topk: int, causal: bool = True, doc
                         index_q=None, index_k=None, doc_ids_q=None, doc_ids_k=None, rope_theta: float = 10000.0,
                         scale: float | None = None, pooled=None, return_sel: bool = False,
                         return_lse: bool = False, out=None, workspace=None, stream=None, chunk_tokens: int = 0,
-                        chunks_per_pass: int = 0):
+                        chunks_per_pass: int = 0, sel_out=None):
     """Block-sparse attention prefill (see include/bsa.h for the semantics).
 
     q [B, Lq, Hq, D], k/v [B, Lk, Hkv, D] device tensors (bf16 or fp32).
     `doc_ids` sets both doc_ids_q and doc_ids_k.  Returns o, or a tuple
-    (o, sel[, lse]) when return_sel / return_lse are set.
+    (o, sel[, lse]) when return_sel / return_lse are set.  sel_out: optional
+    int32 [B, Hs, Lq, topk + causal] contiguous buffer that receives the
+    selection (implies return_sel).
     """
     torch = _torch()
     if doc_ids is not None:
@@ -308,7 +330,13 @@ def sparse_attn_prefill(q, k, v, block: int, topk: int, causal: bool = True, doc
     Lk, Hkv = k.shape[1], k.shape[2]
     o = out if out is not None else torch.empty(q.shape, dtype=q.dtype, device=_gpu(q))
     hs = Hkv if gate == "group" else Hq
-    sel = torch.empty((B, hs, Lq, topk + (1 if causal else 0)), dtype=torch.int32, device=_gpu(q)) if return_sel else None
+    sel_shape = (B, hs, Lq, topk + (1 if causal else 0))
+    if sel_out is not None:
+        if tuple(sel_out.shape) != sel_shape or sel_out.dtype != torch.int32 or not sel_out.is_contiguous():
+            raise BsaError(BSA_ERR_INVALID_ARG, f"sel_out must be contiguous int32 {list(sel_shape)}")
+        sel, return_sel = sel_out, True
+    else:
+        sel = torch.empty(sel_shape, dtype=torch.int32, device=_gpu(q)) if return_sel else None
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=_gpu(q)) if return_lse else None
     dq = _doc(doc_ids_q, B, Lq, _gpu(q))
     dk = _doc(doc_ids_k, B, Lk, _gpu(k))

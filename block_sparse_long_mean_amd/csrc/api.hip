@@ -828,7 +828,12 @@ BSA_API bsa_status bsa_block_summary(const bsa_summary_args* a, void* ws, size_t
 
 BSA_API const char* bsa_last_error(void) { return g_err.c_str(); }
 
-BSA_API int32_t bsa_version(void) { return 100; }  // 0.1.0
+BSA_API int32_t bsa_version(void) { return 200; }  // 0.2.0
+
+#ifndef BSA_BUILD_DIGEST
+#define BSA_BUILD_DIGEST "unknown"
+#endif
+BSA_API const char* bsa_build_digest(void) { return BSA_BUILD_DIGEST; }
 
 BSA_API void bsa_timer_enable(int32_t level) { g_timer_level = level < 0 ? 0 : level; }
 

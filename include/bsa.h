@@ -248,6 +248,10 @@ bsa_status bsa_sparse_attn_backward(const bsa_backward_args* a, void* workspace,
 const char* bsa_last_error(void);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int32_t bsa_version(void);
+/* Digest of the sources the library was built from (16 hex digits, a static
+ * string): the build hashes every file of the kernel sources and this header,
+ * so a caller can tell a library that no longer matches its sources. */
+const char* bsa_build_digest(void);
 
 /*
  * Optional launch timer (off by default; host-side state, not thread-safe).

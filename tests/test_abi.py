@@ -15,13 +15,30 @@ HEADER = os.path.join(ROOT, "include", "bsa.h")
 @pytest.fixture(scope="module")
 def m():
     import block_sparse_long_mean_amd as m
+    from block_sparse_long_mean_amd import build
 
-    if not os.path.exists(m.LIB_PATH):
-        from block_sparse_long_mean_amd import build
-
-        build.build()
+    if not build.is_current():
+        build.build()  # missing, or built from other sources: this CPU-side check builds it
     m.lib()
     return m
+
+
+def test_library_matches_its_sources(m):
+    """The library carries the digest of the sources it was built from, and the
+    binding refuses one whose digest differs from the tree's."""
+    from block_sparse_long_mean_amd import build
+
+    assert m.build_digest() == build.source_digest()
+    assert re.fullmatch(r"[0-9a-f]{16}", m.build_digest())
+    saved, real = m._lib, build.source_digest
+    try:
+        m._lib = None
+        build.source_digest = lambda: "0" * 16
+        with pytest.raises(ImportError, match="built from other sources"):
+            m.lib()
+    finally:
+        build.source_digest = real
+        m._lib = saved
 
 
 def declared_functions():

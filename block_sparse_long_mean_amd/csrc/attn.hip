@@ -15,9 +15,10 @@
 //    and kept there across consecutive items of the same bucket; each wave
 //    holds 32 gathered query rows.  S^T = K Q^T and O^T += V^T P^T run on
 //    v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the result per
-//    (row, slot) is an unnormalised partial output sum_k p_k v_k (bf16) with
-//    p_k = 2^(s_k * scale * log2(e) - m) and its pair (m, l = sum_k p_k) in
-//    fp32.  Persistent workgroups walk contiguous item ranges and prefetch
+//    (row, slot) is an unnormalised partial output sum_k p_k v_k with
+//    p_k = 2^(s_k * scale * log2(e) - m), stored as 16-bit integers with one
+//    binary exponent per row, and its pair (m, l = sum_k p_k) in fp32 (the
+//    exponent folded in).  Persistent workgroups walk contiguous item ranges and prefetch
 //    the next item's row metadata and queries during the current item's
 //    MFMAs.
 //  * attn_merge: streaming.  D/8 lanes per output row read the row's
@@ -50,7 +51,7 @@ struct AttnSmem {
 template <int D, int W>
 struct QStage {
   static constexpr int QELEMS = (D / 16) * 64 * 8;
-  static constexpr int RS = D + 4;  // padded output row (bf16 elements)
+  static constexpr int RS = D + 4;  // padded output row (16-bit elements)
   static constexpr int OELEMS = 32 * RS;
   static constexpr int ELEMS = QELEMS > OELEMS ? QELEMS : OELEMS;
   uint16_t buf[W][ELEMS];
@@ -123,20 +124,52 @@ BSA_DEV void read_q_lds(const QStage<D, W>& st, bf16x8 (&qf)[D / 16]) {
   for (int s = 0; s < D / 16; ++s) qf[s] = as_bf(*reinterpret_cast<const u16x8*>(&st.buf[w][(s * 64 + l) * 8]));
 }
 
-// O^T tile of the wave's 32 rows -> bf16 rows in LDS -> global:
+// O^T tile of the wave's 32 rows -> 16-bit rows in LDS -> global:
 // D/8 lanes write one row's D elements (16 bytes each), 64*8/D rows per
 // store instruction.  Rows [nvalid, 32) of the wave are not written; row r's
 // destination element offset is held by lane r.
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 
+// Partial outputs are stored as 16-bit integers with one binary exponent per
+// row: q = round(32767 * x * 2^-E), with 2^E above the row's largest |x|, so
+// every element carries an error of at most 2^(E-16) -- about 2^-15 of the
+// row's largest value, where a bf16 element would carry up to 2^-8 of its
+// own.  The exponent is folded into the row's (m, l): m' = m + E and
+// l' = l * 2^-E leave the merge's weights 2^(m' - M) l' and its log-sum-exp
+// unchanged while scaling the stored q back by 2^E (the merge divides by
+// 32767 at the end).  E is kept at or above kPartMinExp so that the
+// exponents of one row's partials stay within the fp32 range of their
+// weights.
+constexpr int kPartMinExp = -20;
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+BSA_DEV int part_exponent(float absmax) { return max(__builtin_amdgcn_frexp_expf(absmax), kPartMinExp); }
+
+BSA_DEV uint32_t pack_norm2(float a, float b, int ex) {
+  const s16x2 r = __builtin_amdgcn_cvt_pknorm_i16(__builtin_amdgcn_ldexpf(a, -ex), __builtin_amdgcn_ldexpf(b, -ex));
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Packs this lane's share of the wave's 32 partial rows (lanes l and l + 32
+// hold the same query column, so the row's exponent takes both); returns E.
 template <int D>
-BSA_DEV void pack_partials(const f32x16 (&o)[D / 32], u16x4_t (&pk)[D / 8]) {
+BSA_DEV int pack_partials(const f32x16 (&o)[D / 32], u16x4_t (&pk)[D / 8]) {
+  float mx = 0.f;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg)
-      pk[dt * 4 + gg] = u16x4_t{f2bf(o[dt][4 * gg]), f2bf(o[dt][4 * gg + 1]), f2bf(o[dt][4 * gg + 2]),
-                                f2bf(o[dt][4 * gg + 3])};
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(o[dt][i]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const int ex = part_exponent(mx);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const uint32_t a = pack_norm2(o[dt][4 * gg], o[dt][4 * gg + 1], ex);
+      const uint32_t b = pack_norm2(o[dt][4 * gg + 2], o[dt][4 * gg + 3], ex);
+      pk[dt * 4 + gg] = u16x4_t{(uint16_t)a, (uint16_t)(a >> 16), (uint16_t)b, (uint16_t)(b >> 16)};
+    }
+  return ex;
 }
 
 // Stores rows N*RPI + lr (N = 0..NMAX-1) of the wave's staged partial rows:
@@ -566,7 +599,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
     // epilogue: pack this item's outputs, take the next item's queries out of
     // the staging area, then reuse the area to write whole partial rows
     u16x4_t pk[D / 8];
-    pack_partials<D>(o, pk);
+    const int pex = pack_partials<D>(o, pk);
     if (has_next) {
       __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_wave_barrier();
@@ -581,7 +614,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
       if (wave_on) store_partials<D, W>(qst, pk, pidx * D, min(32, rec.z - w * 32), p.part_o);
       if (g.valid && hq == 0) {
         typedef float f32x2 __attribute__((ext_vector_type(2)));
-        __builtin_nontemporal_store(f32x2{m, l}, reinterpret_cast<f32x2*>(&p.part_ml[pidx]));
+        __builtin_nontemporal_store(f32x2{m + (float)pex, __builtin_amdgcn_ldexpf(l, -pex)},
+                                    reinterpret_cast<f32x2*>(&p.part_ml[pidx]));
       }
     }
     if (!has_next) break;
@@ -722,21 +756,26 @@ __global__ __launch_bounds__(256) void attn_sparse_kernel(AttnParams p) {
         }
       }
     }
-    // partial rows: lane writes its head dims; lane 0 writes (m, l)
+    // partial rows (16-bit with a row exponent, as the MFMA gather writes
+    // them): lane writes its head dims; lane 0 writes (m', l')
     for (int a = 0; a < nr; ++a) {
       const int hsel = p.per_group ? 0 : g[a].hs - hk * p.G;
       const int64_t prow = (prow_base + hsel) * p.CT + (g[a].t - t_base);
       const int64_t pidx = (prow * p.kslot + g[a].slot) * p.R + g[a].rr;
       uint16_t* dst = p.part_o + pidx * D + lane * DPL;
+      float mx = fabsf(acc[a][0]);
+      if constexpr (DPL == 2) mx = fmaxf(mx, fabsf(acc[a][1]));
+      const int ex = part_exponent(wave_max(mx));
+      const uint32_t packed = pack_norm2(acc[a][0], DPL == 2 ? acc[a][DPL - 1] : 0.f, ex);
       if constexpr (DPL == 2) {
-        const uint32_t packed = (uint32_t)f2bf(acc[a][0]) | ((uint32_t)f2bf(acc[a][1]) << 16);
         __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t*>(dst));
       } else {
-        __builtin_nontemporal_store(f2bf(acc[a][0]), dst);
+        __builtin_nontemporal_store((uint16_t)packed, dst);
       }
       if (lane == 0) {
         typedef float f32x2 __attribute__((ext_vector_type(2)));
-        __builtin_nontemporal_store(f32x2{m[a], l[a]}, reinterpret_cast<f32x2*>(&p.part_ml[pidx]));
+        __builtin_nontemporal_store(f32x2{m[a] + (float)ex, __builtin_amdgcn_ldexpf(l[a], -ex)},
+                                    reinterpret_cast<f32x2*>(&p.part_ml[pidx]));
       }
     }
   }
@@ -781,7 +820,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   }
 #pragma unroll
   for (int m2 = 1; m2 < LPR; m2 <<= 1) n += __shfl_xor(n, m2, 64);
-  // partial s holds sum_k p_k v_k with p = 2^(score*sl2 - m_s) and sum_k p_k = l_s
+  // partial s holds q_s = 32767 * 2^-E_s * sum_k p_k v_k with p = 2^(score*sl2 - m_s), and
+  // (m_s + E_s, 2^-E_s * sum_k p_k)
   float M = -INFINITY, W = 0.f;
   float acc[8];
 #pragma unroll
@@ -815,12 +855,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
       const float wu = __builtin_amdgcn_exp2f(ml[u].x - mb);  // 0 for unused slots
       W = fmaf(wu, ml[u].y, W);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wu, bf2f(ov[u][e]), acc[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wu, (float)(int16_t)ov[u][e], acc[e]);
     }
     M = mb;
   }
   if (!ok) return;
-  const float inv = W > 0.f ? 1.0f / W : 0.f;
+  // the stored partials are 32767 * (partial) * 2^-E; E is folded into (m', l')
+  const float inv = W > 0.f ? 1.0f / (W * 32767.0f) : 0.f;
   u16x8 out;
 #pragma unroll
   for (int e = 0; e < 8; ++e) out[e] = f2bf(acc[e] * inv);

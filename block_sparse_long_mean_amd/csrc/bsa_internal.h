@@ -141,8 +141,8 @@ struct AttnParams {
   int run_items;           // consecutive items a gather workgroup takes at a time
   int64_t sparse_items;    // > 0: sparse-bucket gather, one workgroup per item (grid = this bound)
   // partials of the launch's chunks, row ((c - c0) * Gs + head-sel) * CT + token-in-chunk
-  uint16_t* part_o;        // [rows * kslot * R, D] bf16, sum_k p_k v_k with p = 2^(s*sl2 - m)
-  float2* part_ml;         // (m, l): log2-domain running max and sum of p
+  uint16_t* part_o;        // [rows * kslot * R, D] int16: 32767 * 2^-E * sum_k p_k v_k, p = 2^(s*sl2 - m)
+  float2* part_ml;         // (m + E, 2^-E * l): log2-domain running max and sum of p, row exponent E folded in
   // combine
   const int32_t* sel;
   int sel_w;

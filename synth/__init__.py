@@ -67,6 +67,34 @@ def device_tensor(shape, sigma: float, seed: int, tensor_id: int, dtype: str, de
     return out
 
 
+def dyadic_host(shape, seed: int, tensor_id: int, dtype: str, levels: int = 3, step: float = 0.25):
+    """CPU torch tensor of coarse values: uniform integers in [-levels, levels]
+    times `step` (a power of two), exact in bf16 and fp32.  Sums and products
+    of a few hundred such values stay exact in fp32 and fp64, so two blocks
+    holding the same keys score exactly alike in any arithmetic."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(_seed(seed, tensor_id)))
+    x = rng.integers(-levels, levels + 1, size=tuple(shape)).astype(np.float32) * np.float32(step)
+    t = torch.from_numpy(x)
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def repeat_blocks(x, block: int, period: int, axis: int = 1):
+    """Copy of `x` whose block j (tokens [j*block, (j+1)*block) along `axis`)
+    holds the tokens of block j mod period: blocks repeat with the given
+    period, so equal blocks (and equal block summaries) recur.  A short last
+    block takes the first tokens of its source block."""
+    y = x.clone()
+    L = x.shape[axis]
+    nb = -(-L // block)
+    for j in range(period, nb):
+        a, e = j * block, min(L, (j + 1) * block)
+        src = (j % period) * block
+        y.narrow(axis, a, e - a).copy_(x.narrow(axis, src, e - a))
+    return y
+
+
 def doc_lengths(total: int, n_docs: int, mean: float, sigma_log: float, seed: int) -> np.ndarray:
     """Lognormal document lengths rescaled to sum to exactly `total`.
 

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from bsa_testutil import assert_close, check_selection, ref_with_gpu_sel, to_np
+from bsa_testutil import assert_close, bf16_half_ulp, check_selection, ref_with_gpu_sel, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -363,24 +363,31 @@ def _pinned(t):
 
 def test_host_tier_decode(bsa):
     """Host content tier: the caches stay in pinned host RAM (the kernels read the chosen blocks over
-    the host link), the routing keys in GPU memory.  Routing keys summarised from the host caches,
-    the decode itself, and the decode over host pages are bitwise equal to the device-resident
-    calls, and the decode matches the oracle."""
+    the host link), the routing keys in GPU memory.  The library's routing keys summarised from the
+    host caches equal the device-resident ones bitwise and the oracle's within bf16 rounding; the
+    decode from host caches (contiguous and paged) is bitwise equal to the device-resident call, and
+    its selection and output match the oracle's on the oracle's own routing keys."""
     B, Hq, Hkv, Lc, D, block, topk = 2, 8, 2, 3000, 128, 128, 6
     _say("case host-tier decode B2 H8/2 Lc3000 block128 topk6")
     q = synth.host_tensor((B, Hq, D), 1.0, 34, 0, "bf16")
     k = synth.host_tensor((B, Lc, Hkv, D), 1.0, 34, 1, "bf16")
     v = synth.host_tensor((B, Lc, Hkv, D), 1.0, 34, 2, "bf16")
     kh, vh = _pinned(k), _pinned(v)
-    lens = torch.from_numpy(np.array([3000, 1777], dtype=np.int32)).cuda()
+    lens_np = np.array([3000, 1777], dtype=np.int32)
+    lens = torch.from_numpy(lens_np).cuda()
     p_dev = bsa.block_summary(k.cuda(), block, out_dtype=torch.bfloat16)
     p_host = bsa.block_summary(kh, block, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(p_dev.view(torch.int16), p_host.view(torch.int16))
-    qd = q.cuda()
-    o1, s1, l1 = bsa.sparse_attn_decode(qd, k.cuda(), v.cuda(), p_dev, topk, block, cache_lens=lens,
+    ref_pool = oracle.block_pool(k, block)
+    got_pool = p_host.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got_pool - ref_pool) <= bf16_half_ulp(ref_pool) + 1e-7)
+    # the oracle's own routing keys, rounded to bf16 like a stored input, drive both sides
+    ph = torch.from_numpy(ref_pool).to(torch.bfloat16)
+    qd, pd = q.cuda(), ph.cuda()
+    o1, s1, l1 = bsa.sparse_attn_decode(qd, k.cuda(), v.cuda(), pd, topk, block, cache_lens=lens,
                                         return_sel=True, return_lse=True)
-    o2, s2, l2 = bsa.sparse_attn_decode(qd, kh, vh, p_dev, topk, block, cache_lens=lens,
+    o2, s2, l2 = bsa.sparse_attn_decode(qd, kh, vh, pd, topk, block, cache_lens=lens,
                                         return_sel=True, return_lse=True)
     # the same caches as host pages of 128 tokens, in order
     nb = -(-Lc // block)
@@ -390,15 +397,22 @@ def test_host_tier_decode(bsa):
     kp.view(B, Lp, Hkv, D)[:, :Lc] = k
     vp.view(B, Lp, Hkv, D)[:, :Lc] = v
     table = torch.arange(B * nb, dtype=torch.int32).reshape(B, nb).cuda()
-    o3 = bsa.sparse_attn_decode(qd, kp, vp, p_dev, topk, block, cache_lens=lens, block_table=table)
+    o3 = bsa.sparse_attn_decode(qd, kp, vp, pd, topk, block, cache_lens=lens, block_table=table)
     torch.cuda.synchronize()
     assert torch.equal(s1, s2) and torch.equal(l1, l2)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
-    ph = p_dev.cpu()
-    ref = oracle.decode(q, k, v, ph, block=block, topk=topk, cache_lens=lens.cpu().numpy(),
-                        force_sel=s1.cpu().numpy())
+    ref = oracle.decode(q, k, v, ph, block=block, topk=topk, cache_lens=lens_np, return_scores=True)
+    nbk = ph.shape[1]
+    scores = np.full((B, Hq, 1, nbk), np.nan)
+    for (b, hs), sc in ref["scores"].items():
+        scores[b, hs, 0, : len(sc)] = sc
+    gsel = s2.cpu().numpy()[:, :, None]
+    diff = check_selection(gsel, ref["sel"][:, :, None], scores, topk, True)
+    if diff:
+        ref = oracle.decode(q, k, v, ph, block=block, topk=topk, cache_lens=lens_np, force_sel=gsel[:, :, 0])
     assert_close(to_np(o2), ref["o"], 1e-2, 1e-2, bf16_storage=True)
+    assert_close(to_np(l2), ref["lse"], 5e-3, None, what="lse")
 
 
 @pytest.mark.parametrize("case", ["memory_prerotated", "causal_gather"])
@@ -406,29 +420,58 @@ def test_host_tier_prefill(bsa, case):
     """Host content tier for prefill: keys and values in pinned host RAM.  The memory-bank flow (keys
     stored rotated with their routing keys in GPU memory, a query chunk of its own document,
     non-causal) and a causal prefill whose attention runs on the LDS-staged gather; both bitwise
-    equal to the device-resident call."""
+    equal to the device-resident call, and checked against the oracle (every query of the memory
+    case; sampled queries with every head of the causal case)."""
     if case == "memory_prerotated":
         B, Lq, Lk, Hq, Hkv, D, block, topk, causal = 1, 96, 20000, 8, 2, 128, 64, 16, False
     else:
         B, Lq, Lk, Hq, Hkv, D, block, topk, causal = 1, 3000, 3000, 8, 2, 128, 128, 4, True
     _say(f"case host-tier prefill {case} Lq{Lq} Lk{Lk} H8/2 block{block} topk{topk}")
-    q = synth.host_tensor((B, Lq, Hq, D), 1.0, 35, 0, "bf16").cuda()
+    qh_ = synth.host_tensor((B, Lq, Hq, D), 1.0, 35, 0, "bf16")
+    q = qh_.cuda()
     k = synth.host_tensor((B, Lk, Hkv, D), 1.0, 35, 1, "bf16")
     v = synth.host_tensor((B, Lk, Hkv, D), 1.0, 35, 2, "bf16")
     kw = {}
+    okw = {}
     if case == "memory_prerotated":
-        dk = torch.from_numpy(synth.random_doc_ids(Lk, 700.0, 35)[None]).cuda()
-        pooled, k_rot = bsa.block_summary(k.cuda(), block, doc_ids=dk, return_k_rot=True)
+        ids = synth.random_doc_ids(Lk, 700.0, 35)[None]
+        dk = torch.from_numpy(ids).cuda()
+        # the oracle's routing keys (document-wise RoPE, then block means), fp32 as the gate takes them
+        pos = oracle.doc_positions(ids)
+        pool_ref = oracle.block_pool(k, block, pos=pos)
+        pooled = torch.from_numpy(pool_ref).float().cuda()
+        _, k_rot = bsa.block_summary(k.cuda(), block, doc_ids=dk, return_k_rot=True)
         kd = k_rot
-        kw = dict(doc_ids_q=torch.zeros((B, Lq), dtype=torch.int32, device="cuda"), pooled=pooled)
+        dq_ids = np.zeros((B, Lq), dtype=np.int32)
+        kw = dict(doc_ids_q=torch.from_numpy(dq_ids).cuda(), pooled=pooled)
+        okw = dict(doc_ids_q=dq_ids, doc_ids_k=ids, pooled=pooled.cpu())
+        toks = None
     else:
         kd = k.cuda()
+        toks = sorted({0, 1, 127, 128, 129, 1500, 2998, 2999} |
+                      set(int(x) for x in np.random.default_rng(35).choice(Lq, 24, replace=False)))
     kh, vh = _pinned(kd.cpu()), _pinned(v)
-    o1, s1 = bsa.sparse_attn_prefill(q, kd, v.cuda(), block, topk, causal, return_sel=True, **kw)
-    o2, s2 = bsa.sparse_attn_prefill(q, kh, vh, block, topk, causal, return_sel=True, **kw)
+    o1, s1, l1 = bsa.sparse_attn_prefill(q, kd, v.cuda(), block, topk, causal, return_sel=True, return_lse=True, **kw)
+    o2, s2, l2 = bsa.sparse_attn_prefill(q, kh, vh, block, topk, causal, return_sel=True, return_lse=True, **kw)
     torch.cuda.synchronize()
     assert torch.equal(s1, s2)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+    # the oracle rotates the original keys itself (memory case) and reads the host copies' contents
+    def run_oracle(tokens=None, force_sel=None, scores=False):
+        return oracle.prefill(qh_, k, v, block=block, topk=topk, causal=causal, tokens=tokens, force_sel=force_sel,
+                              return_scores=scores, **okw)
+
+    ref = run_oracle(tokens=toks, scores=True)
+    gsel = s2.cpu().numpy() if toks is None else s2.cpu().numpy()[:, :, toks]
+    diff = check_selection(gsel, ref["sel"], ref["scores"], topk, causal)
+    _say(f"  selection rows {gsel.shape[1] * gsel.shape[2]}, near-tie differences {len(diff)}")
+    ref = ref_with_gpu_sel(ref, diff, gsel, run_oracle, tokens=toks)
+    go = to_np(o2) if toks is None else to_np(o2)[:, toks]
+    gl = to_np(l2) if toks is None else to_np(l2)[:, :, toks]
+    assert_close(go, ref["o"], 1e-2, 1e-2, bf16_storage=True)
+    assert_close(gl, ref["lse"], 5e-3, None, what="lse")
 
 
 def test_pageable_host_memory_rejected(bsa):

@@ -156,6 +156,7 @@ BSA_DEV uint64_t group_sort16_asc(uint64_t v, int li) {
 // it descending.
 template <int KR>
 BSA_DEV void list_merge16(uint64_t (&L)[KR], uint64_t b, int li, int topk) {
+  static_assert(KR == 1 || KR == 2 || KR == 4, "the bitonic merge needs 16 * KR a power of two");
   b = group_sort16_asc(b, li);
   L[KR - 1] = L[KR - 1] > b ? L[KR - 1] : b;
 #pragma unroll
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParam
     if (__ballot(nleft[i] > 0) != 0ull) list_merge16<KR>(L[i], left[i], r16, p.topk);
   // emit: each lane group finishes its four rows from registers -- chosen
   // block ids sorted ascending inside the group, the forced block after them
-  constexpr int NR = KR == 1 ? 1 : (KR == 2 ? 2 : 4);
+  constexpr int NR = KR;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = rbase + 4 * kh + i;
@@ -540,12 +541,13 @@ static void gate_dispatch_q(const GateParams& p, hipStream_t s, int grid) {
 #undef BSA_GATE_CASE
 }
 
+// Registers per row list: the bitonic merge in list_merge16 needs 16 * KR to
+// be a power of two, so a top-k above 32 takes four registers (64 keys).
 template <int W, int DG>
 static void gate_dispatch_k(const GateParams& p, hipStream_t s, int grid) {
-  const int kr = p.topk <= 16 ? 1 : p.topk <= 32 ? 2 : p.topk <= 48 ? 3 : 4;
+  const int kr = p.topk <= 16 ? 1 : p.topk <= 32 ? 2 : 4;
   if (kr == 1) gate_dispatch_q<W, DG, 1>(p, s, grid);
   else if (kr == 2) gate_dispatch_q<W, DG, 2>(p, s, grid);
-  else if (kr == 3) gate_dispatch_q<W, DG, 3>(p, s, grid);
   else gate_dispatch_q<W, DG, 4>(p, s, grid);
 }
 

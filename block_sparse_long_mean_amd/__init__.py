@@ -17,6 +17,7 @@ __all__ = [
     "sparse_attn_prefill",
     "select_blocks",
     "sparse_attn_decode",
+    "sparse_attn_decode_noalloc",
     "block_summary",
     "sparse_attn_backward",
     "backward_workspace_bytes",
@@ -156,6 +157,8 @@ def lib():
         L.bsa_sparse_attn_prefill.restype = ctypes.c_int32
         L.bsa_select_blocks.argtypes = [ctypes.POINTER(PrefillArgs), VP, ctypes.c_size_t, VP]
         L.bsa_select_blocks.restype = ctypes.c_int32
+        L.bsa_sparse_attn_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), VP]
+        L.bsa_sparse_attn_decode_noalloc.restype = ctypes.c_int32
         L.bsa_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
         L.bsa_decode_workspace_bytes.restype = ctypes.c_size_t
         L.bsa_sparse_attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), VP, ctypes.c_size_t, VP]
@@ -452,6 +455,23 @@ def sparse_attn_decode(q, kcache, vcache, pooled, topk: int, block: int, *, gate
     if return_lse:
         res.append(lse)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+NOALLOC_MAX_BYTES = 64 << 20  # BSA_DECODE_NOALLOC_MAX_BYTES
+
+
+def sparse_attn_decode_noalloc(q, kcache, vcache, pooled, topk: int, block: int, *, out, gate: str = "head",
+                               cache_lens=None, scale: float | None = None, sel_out=None, lse_out=None,
+                               stream=None, block_table=None):
+    """sparse_attn_decode through bsa_sparse_attn_decode_noalloc: the library's own per-GPU
+    scratch array is the workspace, so the call allocates nothing.  The caller passes every
+    output (out, and optionally sel_out [B, Hs, topk + 1] int32 and lse_out [B, Hq] fp32) and
+    every input already in the right dtype and on the device (cache_lens int32, block_table
+    int32 [B, table_w] contiguous).  Returns out."""
+    a = _decode_args(q, kcache, vcache, pooled, out, block=block, topk=topk, gate=gate, cache_lens=cache_lens,
+                     scale=scale, sel=sel_out, lse=lse_out, block_table=block_table)
+    _check(lib().bsa_sparse_attn_decode_noalloc(ctypes.byref(a), _stream(stream)))
+    return out
 
 
 def block_summary(k, block: int, doc_ids=None, *, rope_theta: float = 10000.0, out_dtype=None,

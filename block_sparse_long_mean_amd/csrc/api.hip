@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -564,13 +565,16 @@ static bsa_status plan_decode(const bsa_decode_args* a, DecodePlan& P, char* ws)
   return BSA_OK;
 }
 
-static bsa_status run_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes, void* stream) {
+// own_ws: the workspace is the library's own scratch array (device memory by
+// construction), left out of the residency check
+static bsa_status run_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes, void* stream, bool own_ws = false) {
   DecodePlan P;
   bsa_status st = plan_decode(a, P, nullptr);
   if (st != BSA_OK) return st;
   if (!ws || ws_bytes < P.bytes) return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_decode_workspace_bytes");
   if (((uintptr_t)ws & 255) != 0) return fail(BSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  st = resident({a->q, a->kcache, a->vcache, a->pooled, a->cache_lens, a->o, a->sel_out, a->lse_out, a->block_table, ws});
+  st = resident({a->q, a->kcache, a->vcache, a->pooled, a->cache_lens, a->o, a->sel_out, a->lse_out, a->block_table,
+                 own_ws ? nullptr : ws});
   if (st != BSA_OK) return st;
   plan_decode(a, P, reinterpret_cast<char*>(ws));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -805,6 +809,56 @@ BSA_API size_t bsa_decode_workspace_bytes(const bsa_decode_args* a) {
 
 BSA_API bsa_status bsa_sparse_attn_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes, void* stream) {
   return run_decode(a, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// decode without allocation: the workspace is a file-scope device array
+// ---------------------------------------------------------------------------
+// Every GPU the library runs on holds its own copy of `scratch` from module
+// load until the process ends.  In host code the array's name is only a
+// stand-in for the device symbol: its device address, which differs per GPU,
+// comes from hipGetSymbolAddress on the first call on each device and is the
+// only form ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[BSA_DECODE_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static bsa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(BSA_ERR_HIP, "hipGetDevice failed");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(BSA_ERR_UNSUPPORTED, "device index above the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(BSA_ERR_HIP, std::string("hipGetSymbolAddress of the decode scratch failed: ") + hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BSA_OK;
+}
+
+BSA_API bsa_status bsa_sparse_attn_decode_noalloc(const bsa_decode_args* a, void* stream) {
+  DecodePlan P;
+  const bsa_status st = plan_decode(a, P, nullptr);
+  if (st != BSA_OK) return st;
+  if (P.bytes > (size_t)BSA_DECODE_NOALLOC_MAX_BYTES)
+    return fail(BSA_ERR_WORKSPACE, "decode needs " + std::to_string(P.bytes) +
+                                       " bytes of workspace, above the no-allocation limit of " +
+                                       std::to_string((size_t)BSA_DECODE_NOALLOC_MAX_BYTES) +
+                                       " (BSA_DECODE_NOALLOC_MAX_BYTES): call bsa_sparse_attn_decode with a workspace");
+  void* ws = nullptr;
+  const bsa_status sst = scratch_of_current_device(&ws);
+  if (sst != BSA_OK) return sst;
+  return run_decode(a, ws, (size_t)BSA_DECODE_NOALLOC_MAX_BYTES, stream, true);
 }
 
 BSA_API size_t bsa_backward_workspace_bytes(const bsa_backward_args* a) {

@@ -183,6 +183,27 @@ size_t bsa_decode_workspace_bytes(const bsa_decode_args* a);
 bsa_status bsa_sparse_attn_decode(const bsa_decode_args* a, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Decode without allocation, for callers that cannot allocate device memory
+ * around the call: code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation.  Same arguments, kernels and results as
+ * bsa_sparse_attn_decode, but no workspace argument: the workspace is a
+ * library-owned device array of BSA_DECODE_NOALLOC_MAX_BYTES bytes, one per
+ * GPU, held from library load until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks up that device's array (the device current on the
+ * calling thread, which must be the device of `stream` and of the tensors).
+ * Errors: as bsa_sparse_attn_decode, plus BSA_ERR_WORKSPACE when
+ * bsa_decode_workspace_bytes(a) exceeds BSA_DECODE_NOALLOC_MAX_BYTES (the
+ * 16 x 1,048,576-token, 32/8-head, block-128, top-32 decode needs about
+ * 52 MB).  Every call on one GPU shares that GPU's array: calls whose
+ * execution overlaps on one GPU (two streams, two threads) race and give
+ * undefined results; calls serialised on one stream are safe.  No part of
+ * the array needs to start zeroed.
+ */
+#define BSA_DECODE_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+bsa_status bsa_sparse_attn_decode_noalloc(const bsa_decode_args* a, void* stream);
+
+/*
  * Block summaries (the offline encoding of a memory): pooled[b, j, h, :] =
  * mean of the keys of block j (a short last block averages the tokens it
  * has), after document-wise RoPE when doc_ids is given.  Positions restart

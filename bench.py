@@ -343,8 +343,31 @@ def decode_bytes(sel):
     return pooled + kv + qo, distinct
 
 
-def cpu_baseline(q, k, v, iq, ik, budget_s=20.0):
-    """Time the float64 oracle on a seeded sample of prefill tokens."""
+def _host_info():
+    """CPU model, logical CPU count and the BLAS NumPy uses (threadpoolctl)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+
+        libs = [f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas = "; ".join(libs) or blas
+    except Exception:
+        pass
+    return model, os.cpu_count() or 1, blas
+
+
+def _oracle_rate(q, kh, vh, iq, ikh, toks_all, budget_s, threads):
+    """Oracle tokens/s over a seeded sample of prefill tokens; returns (rate, done, seconds, outputs)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -352,11 +375,9 @@ def cpu_baseline(q, k, v, iq, ik, budget_s=20.0):
     import oracle
 
     c = PREFILL
-    rng = np.random.default_rng(1234)
-    toks_all = np.sort(rng.choice(c["L"], size=4096, replace=False))
-    kh, vh, ikh = k.cpu(), v.cpu(), ik.cpu()
-    with threadpool_limits(limits=1):
-        torch.set_num_threads(1)
+    outs = {}
+    with threadpool_limits(limits=threads):
+        torch.set_num_threads(threads)
         t0 = time.perf_counter()
         pooled = oracle.block_pool(ikh, c["block"])
         t_pool = time.perf_counter() - t0
@@ -364,27 +385,57 @@ def cpu_baseline(q, k, v, iq, ik, budget_s=20.0):
         t1 = time.perf_counter()
         step = 16
         while done < len(toks_all) and time.perf_counter() - t1 < budget_s:
-            toks = toks_all[done:done + step].tolist()
+            toks = [int(t) for t in toks_all[done:done + step]]
             qh = q[:, toks].cpu()
             iqh = iq[:, toks].cpu()
-            # the oracle sees the sampled queries as rows Lq-Lk..: give it the
-            # full-length index positions by evaluating tokens in place
-            oracle.prefill(_RowView(qh, toks, c["L"]), kh, vh, block=c["block"], topk=c["topk"], causal=True,
-                           gate="group", index_q=_RowView(iqh, toks, c["L"]), index_k=ikh, pooled=pooled,
-                           tokens=toks)
+            r = oracle.prefill(_RowView(qh, toks, c["L"]), kh, vh, block=c["block"], topk=c["topk"], causal=True,
+                               gate="group", index_q=_RowView(iqh, toks, c["L"]), index_k=ikh, pooled=pooled,
+                               tokens=toks)
+            for i, t in enumerate(toks):
+                outs[t] = (r["o"][:, i], r["sel"][:, :, i])
             done += len(toks)
         t_rows = time.perf_counter() - t1
-    # throughput for the whole sequence: the pooling is paid once per sequence
-    per_token = t_rows / done
-    total = t_pool + per_token * c["L"]
+    total = t_pool + t_rows / done * c["L"]
+    return c["L"] / total, done, t_rows, t_pool, outs
+
+
+def cpu_baseline(q, k, v, iq, ik, o_gpu, sel_gpu, budget_s=12.0):
+    """The float64 oracle timed on a seeded sample of prefill tokens, once on one
+    thread and once with BLAS threads on every host core; the sampled rows'
+    outputs are compared with the GPU's (plain max-abs over rows whose
+    selection matches the oracle's exactly)."""
+    import numpy as np
+
+    c = PREFILL
+    rng = np.random.default_rng(1234)
+    toks_all = np.sort(rng.choice(c["L"], size=4096, replace=False))
+    kh, vh, ikh = k.cpu(), v.cpu(), ik.cpu()
+    model, ncpu, blas = _host_info()
+    r1, d1, s1, p1, _ = _oracle_rate(q, kh, vh, iq, ikh, toks_all, budget_s, 1)
+    rn, dn, sn, pn, outs = _oracle_rate(q, kh, vh, iq, ikh, toks_all, budget_s, ncpu)
+    toks = sorted(outs)
+    og = o_gpu[:, toks].float().cpu().numpy().astype(np.float64)  # [B, T, Hq, D]
+    sg = sel_gpu[:, :, toks].cpu().numpy()  # [B, Hs, T, W]
+    max_abs, same_rows, G = 0.0, 0, c["Hq"] // c["Hkv"]
+    for i, t in enumerate(toks):
+        o_ref, s_ref = outs[t]
+        for hs in range(c["Hkv"]):
+            if np.array_equal(sg[0, hs, i], s_ref[0, hs]):
+                same_rows += 1
+                err = np.abs(og[0, i, hs * G:(hs + 1) * G] - o_ref[0, hs * G:(hs + 1) * G]).max()
+                max_abs = max(max_abs, float(err))
     return {
-        "value": round(c["L"] / total, 3),
+        "value": round(rn, 3),
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": ncpu,
         "kind": "oracle",
-        "sample": f"{done} of {c['L']} prefill tokens (seeded, all 64 heads) in {t_rows:.1f} s plus one full "
-                  f"index-key pooling pass in {t_pool:.1f} s; whole-sequence time extrapolated linearly "
-                  f"({total:.0f} s); float64 NumPy, 1 thread",
+        "sample": f"{dn} of {c['L']} prefill tokens (seeded, all 64 heads) in {sn:.1f} s plus one full index-key "
+                  f"pooling pass in {pn:.1f} s, BLAS threads = {ncpu} (every logical CPU of the host); "
+                  f"whole-sequence time extrapolated linearly; float64 NumPy",
+        "one_thread": {"value": round(r1, 3), "tokens": d1, "seconds": round(s1, 1)},
+        "host": {"cpu_model": model, "logical_cpus": ncpu, "blas": blas},
+        "gpu_parity_on_sample": {"rows": len(toks) * c["Hkv"], "rows_same_selection": same_rows,
+                                 "max_abs": max_abs},
     }
 
 
@@ -403,7 +454,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration": {"bytes_read": n * 2, "bytes_written": n * 2, "launches": 3}}), flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_passes_128k_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_gather_128k_traffic.md")
 GATHER_SOURCES = ["api.hip", "attn.hip", "csr.hip", "bsa_device.h", "bsa_internal.h"]
 
 
@@ -418,9 +469,9 @@ def gather_sources_digest():
 
 
 def measured_traffic():
-    """HBM bytes of the attention passes of one prefill call, from the committed
-    counter summary, or None when their sources have changed since the
-    counters were taken."""
+    """HBM bytes of one attn_gather launch of the 128K prefill, from the
+    committed counter summary, or None when the sources have changed since
+    the counters were taken."""
     import re
 
     try:
@@ -429,14 +480,14 @@ def measured_traffic():
     except OSError:
         return None
     got = {}
-    for key in ("sources_digest", "hbm_bytes_per_call"):
+    for key in ("sources_digest", "hbm_bytes_per_launch"):
         mt = re.search(rf"^{key}:\s*(\S+)\s*$", text, re.M)
         if not mt:
             return None
         got[key] = mt.group(1)
     if got["sources_digest"] != gather_sources_digest():
         return None
-    return float(got["hbm_bytes_per_call"])
+    return float(got["hbm_bytes_per_launch"])
 
 
 class _RowView:
@@ -452,19 +503,96 @@ class _RowView:
         return self.rows[b, self.index[t]]
 
 
+def profile_workload(m, name, reps):
+    """Runs one workload `reps` times after one warm-up call (for rocprofv3:
+    its kernel trace or counters then cover only this workload)."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    t = synth.TID
+    if name == "prefill128k":
+        c = PREFILL
+        q, k, v, iq, ik = make_prefill_inputs()
+        o = torch.empty_like(q)
+        ws = torch.empty(m.prefill_workspace_bytes(q, k, block=c["block"], topk=c["topk"], causal=True,
+                                                   gate="group", index_q=iq, index_k=ik), dtype=torch.uint8,
+                         device="cuda")
+        fn = lambda: m.sparse_attn_prefill(q, k, v, c["block"], c["topk"], True, gate="group", index_q=iq,
+                                           index_k=ik, out=o, workspace=ws)
+    elif name == "decode1m":
+        d = DECODE
+        dq, kc, vc, pooled = make_decode_inputs(m)
+        do = torch.empty_like(dq)
+        ws = torch.empty(m.decode_workspace_bytes(dq, kc, vc, pooled, block=d["block"], topk=d["topk"]),
+                         dtype=torch.uint8, device="cuda")
+        fn = lambda: m.sparse_attn_decode(dq, kc, vc, pooled, d["topk"], d["block"], out=do, workspace=ws)
+    elif name in ("moba32k", "moba32k_backward"):
+        c = MOBA
+        q = synth.device_tensor((c["B"], c["L"], c["Hq"], c["D"]), c["sigma"], SEED, t["q"], "bf16")
+        k = synth.device_tensor((c["B"], c["L"], c["Hkv"], c["D"]), c["sigma"], SEED, t["k"], "bf16")
+        v = synth.device_tensor((c["B"], c["L"], c["Hkv"], c["D"]), c["sigma"], SEED, t["v"], "bf16")
+        if name == "moba32k":
+            o = torch.empty_like(q)
+            ws = torch.empty(m.prefill_workspace_bytes(q, k, block=c["block"], topk=c["topk"], causal=True),
+                             dtype=torch.uint8, device="cuda")
+            fn = lambda: m.sparse_attn_prefill(q, k, v, c["block"], c["topk"], True, out=o, workspace=ws)
+        else:
+            g = synth.device_tensor((c["B"], c["L"], c["Hq"], c["D"]), 1.0, SEED, t["dout"], "bf16")
+            o, sel, lse = m.sparse_attn_prefill(q, k, v, c["block"], c["topk"], True, return_sel=True,
+                                                return_lse=True)
+            grads = tuple(torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in (q, k, v))
+            ws = torch.empty(m.backward_workspace_bytes(q, k, sel, block=c["block"], causal=True), dtype=torch.uint8,
+                             device="cuda")
+            fn = lambda: m.sparse_attn_backward(q, k, v, o, lse, sel, g, c["block"], True, out=grads, workspace=ws)
+    elif name in ("memory_summary", "memory_chunk"):
+        c = MEMORY
+        ids = synth.doc_ids_from_lengths(synth.doc_lengths(c["Lk"], c["docs"], c["doc_mean"], c["doc_sigma"], SEED))
+        dk = torch.from_numpy(ids[None]).cuda()
+        k = synth.device_tensor((1, c["Lk"], c["Hkv"], c["D"]), 1.0, SEED, t["k"], "bf16")
+        if name == "memory_summary":
+            fn = lambda: m.block_summary(k, c["block"], doc_ids=dk)
+        else:
+            q = synth.device_tensor((1, c["Lq"], c["Hq"], c["D"]), 1.0, SEED, t["q"], "bf16")
+            v = synth.device_tensor((1, c["Lk"], c["Hkv"], c["D"]), 1.0, SEED, t["v"], "bf16")
+            pooled, k_rot = m.block_summary(k, c["block"], doc_ids=dk, return_k_rot=True)
+            del k
+            dq = torch.zeros((1, c["Lq"]), dtype=torch.int32, device="cuda")
+            o = torch.empty_like(q)
+            kw = dict(doc_ids_q=dq, pooled=pooled)
+            ws = torch.empty(m.prefill_workspace_bytes(q, k_rot, block=c["block"], topk=c["topk"], causal=False,
+                                                       **kw), dtype=torch.uint8, device="cuda")
+            fn = lambda: m.sparse_attn_prefill(q, k_rot, v, c["block"], c["topk"], False, out=o, workspace=ws, **kw)
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    torch.cuda.synchronize()
+    fn()
+    torch.cuda.synchronize()
+    _log(f"profile {name}: warm-up done")
+    for i in range(reps):
+        fn()
+        torch.cuda.synchronize()
+        _log(f"profile {name}: call {i + 1}/{reps} done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work per CPU-baseline leg (one thread, then every core)")
     ap.add_argument("--also", action="store_true",
                     help="also time the MoBA-style 32K prefill, the 10M-token memory bank and the paged decode "
                          "(extra field)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run an elementwise negation over MIB MiB (read once, written once) -- the "
                          "known-size kernel that scales the HBM byte counters -- and exit")
+    ap.add_argument("--profile", default=None, metavar="WORKLOAD",
+                    help="only run WORKLOAD (prefill128k, decode1m, moba32k, moba32k_backward, memory_summary, "
+                         "memory_chunk) --steps times after one warm-up call, for rocprofv3, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the path shards by KV head or "
@@ -481,6 +609,9 @@ def main():
 
     m.lib()
     torch.cuda.set_device(0)
+    if args.profile:
+        profile_workload(m, args.profile, args.steps)
+        return
     _log("generating prefill inputs")
     q, k, v, iq, ik = make_prefill_inputs()
     _log("generating decode inputs (68.7 GB of KV cache)")
@@ -493,7 +624,6 @@ def main():
                                                 index_q=iq, index_k=ik), dtype=torch.uint8, device="cuda")
     dws = torch.empty(m.decode_workspace_bytes(dq, kc, vc, pooled, block=d["block"], topk=d["topk"]),
                       dtype=torch.uint8, device="cuda")
-    dsel = torch.empty((d["B"], d["Hq"], d["topk"] + 1), dtype=torch.int32, device="cuda")
     _log(f"workspaces: prefill {pws.numel() / 1e9:.2f} GB, decode {dws.numel() / 1e6:.1f} MB")
 
     def prefill():
@@ -535,16 +665,16 @@ def main():
     _log(f"timed {args.steps} steps: prefill {pre_ms:.3f} ms, decode {dec_ms:.3f} ms, step {step_ms:.3f} ms "
          f"(host wall {wall * 1e3 / args.steps:.3f} ms/step)")
     # the breakdown: the same K steps again with the library's launch timer
-    # (HIP events on the launch stream around each launch, and around the
-    # attention passes as one phase)
+    # (HIP events on the launch stream around every launch; "attn" brackets
+    # the attention passes, gathers and merges, as one phase)
     m.timer_reset()
-    m.timer_enable(1)
+    m.timer_enable(2)
     run_steps(args.steps)
     m.timer_enable(0)
 
     kernels = ["doc_chunk_last", "doc_positions", "rope_q", "block_summary", "pooled_to_planes", "gate_topk",
                "gate_merge", "decode_scores", "decode_select", "csr_fill", "csr_count", "csr_scan", "csr_scatter",
-               "attn", "decode_attend", "decode_combine"]
+               "attn_gather", "attn_merge", "attn", "decode_attend", "decode_combine"]
     per_kernel = {}
     for name in kernels:
         ms, n = m.timer_report(name)
@@ -562,23 +692,31 @@ def main():
     tokens = c["B"] * c["L"] + d["B"]
     value = tokens / (step_ms * 1e-3)
 
-    dom = max(per_kernel.items(), key=lambda x: x[1]["ms_total"])[0]
-    if dom == "attn":
-        # the attention passes (gathers + merges) attend every selected block,
-        # the own block included: 4*D flops per attended (query, key) pair
-        achieved = flops_total / (per_kernel[dom]["ms_avg"] * 1e-3) / 1e12
+    # the dominant kernel: the gather, which runs every attended (query, key)
+    # pair of the prefill on MFMA (4*D flops per pair, own blocks included;
+    # one launch per call at this size)
+    single = [n for n, r in per_kernel.items() if n != "attn"]
+    dom = max(single, key=lambda n: per_kernel[n]["ms_total"])
+    if dom == "attn_gather":
+        g_ms = per_kernel[dom]["ms_total"] / args.steps  # per prefill call
+        achieved = flops_total / (g_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                "kernel": "attn_gather + attn_merge (the attention passes of one prefill call)",
-                "kernel_ms": per_kernel[dom]["ms_avg"]}
+                "kernel": "attn_gather_kernel (every attended pair of the 128K prefill)",
+                "kernel_ms": round(g_ms, 4), "launches_per_call": per_kernel[dom]["launches"] // args.steps}
     else:
         roof = {"bound": "unknown", "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None,
                 "kernel": dom, "kernel_ms": per_kernel[dom]["ms_avg"]}
+    attn_ms = per_kernel.get("attn", {}).get("ms_avg")
 
     cpu = None
     if not args.no_cpu_baseline:
-        _log("timing the float64 oracle on a sample of the prefill (CPU)")
-        cpu = cpu_baseline(q, k, v, iq, ik, args.cpu_budget)
+        _log("timing the float64 oracle on a sample of the prefill (CPU), one thread then every core")
+        o_chk, sel_chk = m.sparse_attn_prefill(q, k, v, c["block"], c["topk"], True, gate="group", index_q=iq,
+                                               index_k=ik, return_sel=True)
+        torch.cuda.synchronize()
+        cpu = cpu_baseline(q, k, v, iq, ik, o_chk, sel_chk, args.cpu_budget)
+        del o_chk, sel_chk
 
     others = None
     if args.also:
@@ -612,9 +750,12 @@ def main():
             "prefill_tokens_per_s": round(c["B"] * c["L"] / (pre_ms * 1e-3), 1),
             "prefill_attended_tflops": round(pre_tflops, 2),
             "prefill_attended_tflop": round(flops_total / 1e12, 4),
+            "attention_phase_ms": attn_ms,
+            "attention_phase_tflops": round(flops_total / (attn_ms * 1e-3) / 1e12, 2) if attn_ms else None,
             "decode_ms": round(dec_ms, 4),
             "decode_tokens_per_s": round(d["B"] / (dec_ms * 1e-3), 1),
             "decode_hbm_gbs": round(dec_gbs, 1),
+            "decode_hbm_frac": round(dec_gbs / PEAK_HBM_GBS, 4),
             "decode_algorithmic_gb": round(dbytes / 1e9, 4),
             "decode_distinct_blocks": distinct,
             "kernels_ms_avg": {k2: v2["ms_avg"] for k2, v2 in per_kernel.items()},

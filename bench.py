@@ -503,9 +503,9 @@ class _RowView:
         return self.rows[b, self.index[t]]
 
 
-def profile_workload(m, name, reps):
-    """Runs one workload `reps` times after one warm-up call (for rocprofv3:
-    its kernel trace or counters then cover only this workload)."""
+def make_workload(m, name):
+    """Inputs of one workload on the device and a function that runs one call
+    of it (the tensors stay alive through the function's closure)."""
     import numpy as np
     import torch
 
@@ -567,6 +567,15 @@ def profile_workload(m, name, reps):
     else:
         raise SystemExit(f"unknown workload {name}")
     torch.cuda.synchronize()
+    return fn
+
+
+def profile_workload(m, name, reps):
+    """Runs one workload `reps` times after one warm-up call (for rocprofv3:
+    its kernel trace or counters then cover only this workload)."""
+    import torch
+
+    fn = make_workload(m, name)
     fn()
     torch.cuda.synchronize()
     _log(f"profile {name}: warm-up done")

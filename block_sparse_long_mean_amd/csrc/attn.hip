@@ -34,13 +34,24 @@ namespace bsa {
 constexpr int KT = 64;  // keys per LDS tile
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int VTS = KT + 4;  // V^T row stride: 136 bytes keeps 16 lanes' 8-byte reads on distinct banks
-
+// One staged 64-key tile of a block.  Keys row-major with rows padded by 16
+// bytes (16 lanes reading one 16-byte piece of 16 consecutive rows hit
+// distinct banks); values row-major as stored, with the 16-byte pieces of a
+// row permuted (piece c of row r at c ^ vswz(r)) so that the transposing
+// reads of the P.V operand (four rows x 32 bytes per 16 lanes) hit distinct
+// banks.
 template <int D>
 struct AttnSmem {
   uint16_t k[KT * (D + 8)];
-  uint16_t vt[D * VTS];
+  uint16_t v[KT * D];
 };
+
+// piece permutation of value row r (16-byte pieces; D / 8 per row)
+template <int D>
+BSA_DEV int vswz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3);
+  else return 4 * ((r >> 1) & 1);
+}
 
 // Per-wave LDS staging area, used twice per work item:
 //  * the next item's query rows: for each 16-column chunk s, lane l's 16
@@ -214,8 +225,8 @@ BSA_DEV void store_partials(QStage<D, W>& st, const u16x4_t (&pk)[D / 8], int64_
                                     part_o + c * 8);
 }
 
-// Stage keys [key0, key0 + KT) of one kv head (zero past n_valid) into LDS:
-// K row-major, V transposed.
+// Stage keys [key0, key0 + KT) of one kv head into LDS through registers
+// (rows past n_valid zero).
 template <int D, int NT>
 BSA_DEV void stage_kv(AttnSmem<D>& sm, const uint16_t* kb, int64_t ks_t, const uint16_t* vb, int64_t vs_t,
                       int key0, int n_valid) {
@@ -223,78 +234,47 @@ BSA_DEV void stage_kv(AttnSmem<D>& sm, const uint16_t* kb, int64_t ks_t, const u
   constexpr int CH = D / 8;
   for (int idx = tid; idx < KT * CH; idx += NT) {
     const int kr = idx / CH, ch = idx % CH;
-    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (kr < n_valid) x = ld16(kb + (int64_t)(key0 + kr) * ks_t + ch * 8);
+    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0}, y = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (kr < n_valid) {
+      x = ld16(kb + (int64_t)(key0 + kr) * ks_t + ch * 8);
+      y = ld16(vb + (int64_t)(key0 + kr) * vs_t + ch * 8);
+    }
     st16(&sm.k[kr * (D + 8) + ch * 8], x);
-  }
-  // V: a thread takes 4 consecutive keys x 8 head dims and writes them
-  // transposed; consecutive lanes take consecutive key quads so that their
-  // LDS writes of one V^T row are contiguous
-  for (int idx = tid; idx < (KT / 4) * CH; idx += NT) {
-    const int kq = idx % (KT / 4), ch = idx / (KT / 4);
-    u16x8 r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kr = kq * 4 + i;
-      r[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (kr < n_valid) r[i] = ld16(vb + (int64_t)(key0 + kr) * vs_t + ch * 8);
-    }
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      u16x4 col = {r[0][d], r[1][d], r[2][d], r[3][d]};
-      *reinterpret_cast<u16x4*>(&sm.vt[(ch * 8 + d) * VTS + kq * 4]) = col;
-    }
+    st16(&sm.v[kr * D + ((ch ^ vswz<D>(kr)) * 8)], y);
   }
 }
 
-// Blocks longer than one key tile: the next tile's keys and values are
-// copied global -> LDS by DMA in their natural layout (rows of D elements)
-// while the current tile is computed, then repacked LDS -> LDS into the
-// padded key rows and the transposed values the MFMA reads.  Rows past
-// n_valid copy row 0 of the tile (in bounds); the repack zeroes them.
+// The same tile copied global -> LDS by DMA (global_load_lds: 64 lanes x 16
+// bytes land at consecutive LDS addresses per instruction), straight into
+// the layout above: an LDS position that is row padding loads a piece of its
+// own row; rows past n_valid load row 0 of the tile (finite values, masked
+// out of the scores).  Every thread issues its share; the caller waits.
 template <int D, int NT>
-BSA_DEV void dma_kv(uint16_t* nat, const uint16_t* kb, int64_t ks_t, const uint16_t* vb, int64_t vs_t, int key0,
+BSA_DEV void dma_kv(AttnSmem<D>& sm, const uint16_t* kb, int64_t ks_t, const uint16_t* vb, int64_t vs_t, int key0,
                     int n_valid) {
-  constexpr int CPR = D / 8;       // 16-byte pieces per row
-  constexpr int RPI = 64 / CPR;    // rows per DMA instruction (64 lanes x 16 bytes)
+  constexpr int KP = D / 8 + 1;  // 16-byte pieces per padded key row
+  constexpr int VP = D / 8;      // pieces per value row
   constexpr int NW = NT / 64;
+  constexpr int NK = (KT * KP + 63) / 64;  // DMA instructions for the keys
+  constexpr int NV = KT * VP / 64;         // and for the values
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
-  const int r_in = lane / CPR, c = lane % CPR;
-  for (int i = w; i < KT / RPI; i += NW) {
-    const int r = i * RPI + r_in;
-    const int rr = r < n_valid ? r : 0;
-    __builtin_amdgcn_global_load_lds((const void*)(kb + (int64_t)(key0 + rr) * ks_t + c * 8),
-                                     (lds_ptr_t)(nat + i * RPI * D), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(vb + (int64_t)(key0 + rr) * vs_t + c * 8),
-                                     (lds_ptr_t)(nat + KT * D + i * RPI * D), 16, 0, 0);
-  }
-}
-
-template <int D, int NT>
-BSA_DEV void repack_kv(AttnSmem<D>& sm, const uint16_t* nat, int n_valid) {
-  const int tid = threadIdx.x;
-  constexpr int CH = D / 8;
-  for (int idx = tid; idx < KT * CH; idx += NT) {
-    const int kr = idx / CH, ch = idx % CH;
-    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (kr < n_valid) x = *reinterpret_cast<const u16x8*>(nat + kr * D + ch * 8);
-    st16(&sm.k[kr * (D + 8) + ch * 8], x);
-  }
-  // values transposed as stage_kv writes them
-  for (int idx = tid; idx < (KT / 4) * CH; idx += NT) {
-    const int kq = idx % (KT / 4), ch = idx / (KT / 4);
-    u16x8 r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kr = kq * 4 + i;
-      r[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (kr < n_valid) r[i] = *reinterpret_cast<const u16x8*>(nat + KT * D + kr * D + ch * 8);
-    }
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      u16x4 col = {r[0][d], r[1][d], r[2][d], r[3][d]};
-      *reinterpret_cast<u16x4*>(&sm.vt[(ch * 8 + d) * VTS + kq * 4]) = col;
+  for (int i = w; i < NK + NV; i += NW) {
+    if (i < NK) {
+      const int P = i * 64 + lane;  // piece position in the padded key tile
+      int r = P / KP, c = P % KP;
+      if (c == KP - 1 || r >= KT) c = 0;  // padding (or past the tile): a piece of an in-bounds row
+      if (r >= KT) r = 0;
+      const int rr = r < n_valid ? r : 0;
+      __builtin_amdgcn_global_load_lds((const void*)(kb + (int64_t)(key0 + rr) * ks_t + c * 8),
+                                       (lds_ptr_t)(sm.k + i * 512), 16, 0, 0);
+    } else {
+      const int P = (i - NK) * 64 + lane;
+      const int r = P / VP, pos = P % VP;
+      const int rr = r < n_valid ? r : 0;
+      const int c = pos ^ vswz<D>(r);
+      __builtin_amdgcn_global_load_lds((const void*)(vb + (int64_t)(key0 + rr) * vs_t + c * 8),
+                                       (lds_ptr_t)(sm.v + (i - NK) * 512), 16, 0, 0);
     }
   }
 }
@@ -330,22 +310,29 @@ BSA_DEV void qk_tile(const AttnSmem<D>& sm, const bf16x8 (&qf)[D / 16], f32x16& 
   qk_steps<0, D>(lds_addr(&sm.k[r * (D + 8) + 8 * h]), qf, s0, s1);
 }
 
-// Head-dim tile DT (rows 32 DT + r of V^T) of pv_tile over the tile's 64
-// keys, then the rest.  base = LDS byte address of V^T row r, key 4h.
+// Head-dim tile DT of pv_tile: O^T rows 32 DT .. 32 DT + 31 over the tile's
+// 64 keys.  The A operand (V^T: 8 keys of one head dim per lane) comes from
+// the row-major value tile by transposing reads (ds_read_b64_tr_b16): in
+// each group of 16 lanes, lane i receives element i%4 of the 8 bytes that
+// lane i/4 + 4e addresses (e = 0..3), so a lane s that addresses
+// V[k0 + s/4][d0 + 4(s%4)] hands lane i the keys k0 .. k0+3 of head dim
+// d0 + i.  The keys follow the P operand's order: 16kk + 4h .. +3, then
+// 16kk + 8 + 4h .. +3 (h = lane / 32).  vbase[DT] = LDS byte address this
+// lane addresses for head-dim tile DT in key row 4h + s/4; the key steps are
+// immediate offsets.
 template <int DT, int D>
-BSA_DEV void pv_steps(uint32_t base, const bf16x8 (&pb)[4], f32x16 (&o)[D / 32], bool first) {
+BSA_DEV void pv_steps(const uint32_t (&vbase)[D / 32], const bf16x8 (&pb)[4], f32x16 (&o)[D / 32], bool first) {
   if constexpr (DT < D / 32) {
-    constexpr int OFF = DT * 32 * VTS * 2;
+    constexpr int RB = D * 2;  // bytes per value row
     u16x4 x0, x1, x2, x3, x4, x5, x6, x7;
-    // keys 16kk + 4h .. +3 and 16kk + 8 + 4h .. +3 for kk = 0..3
     asm volatile(
-        "ds_read_b64 %0, %8 offset:%9\n\tds_read_b64 %1, %8 offset:%10\n\t"
-        "ds_read_b64 %2, %8 offset:%11\n\tds_read_b64 %3, %8 offset:%12\n\t"
-        "ds_read_b64 %4, %8 offset:%13\n\tds_read_b64 %5, %8 offset:%14\n\t"
-        "ds_read_b64 %6, %8 offset:%15\n\tds_read_b64 %7, %8 offset:%16\n\ts_waitcnt lgkmcnt(0)"
+        "ds_read_b64_tr_b16 %0, %8 offset:%9\n\tds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:%11\n\tds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%13\n\tds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:%15\n\tds_read_b64_tr_b16 %7, %8 offset:%16\n\ts_waitcnt lgkmcnt(0)"
         : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3), "=v"(x4), "=v"(x5), "=v"(x6), "=v"(x7)
-        : "v"(base), "n"(OFF), "n"(OFF + 16), "n"(OFF + 32), "n"(OFF + 48), "n"(OFF + 64), "n"(OFF + 80),
-          "n"(OFF + 96), "n"(OFF + 112)
+        : "v"(vbase[DT]), "n"(0), "n"(8 * RB), "n"(16 * RB), "n"(24 * RB), "n"(32 * RB), "n"(40 * RB),
+          "n"(48 * RB), "n"(56 * RB)
         : "memory");
     const u16x8 a0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     const u16x8 a1 = {x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
@@ -355,7 +342,21 @@ BSA_DEV void pv_steps(uint32_t base, const bf16x8 (&pb)[4], f32x16 (&o)[D / 32],
     o[DT] = mfma32(as_bf(a1), pb[1], o[DT]);
     o[DT] = mfma32(as_bf(a2), pb[2], o[DT]);
     o[DT] = mfma32(as_bf(a3), pb[3], o[DT]);
-    pv_steps<DT + 1, D>(base, pb, o, first);
+    pv_steps<DT + 1, D>(vbase, pb, o, first);
+  }
+}
+
+// LDS byte addresses of pv_steps for the value tile of `sm`
+template <int D>
+BSA_DEV void pv_bases(const AttnSmem<D>& sm, uint32_t (&vbase)[D / 32]) {
+  const int lane = lane_id();
+  const int s = lane & 15, g = lane >> 4, h = lane >> 5;
+  const int row = 4 * h + (s >> 2);
+  const uint32_t b0 = lds_addr(sm.v) + (uint32_t)(row * D * 2 + 8 * (s & 1));
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int piece = 4 * dt + 2 * (g & 1) + ((s & 3) >> 1);
+    vbase[dt] = b0 + (uint32_t)((piece ^ vswz<D>(row)) * 16);
   }
 }
 
@@ -367,8 +368,6 @@ BSA_DEV void pv_steps(uint32_t base, const bf16x8 (&pb)[4], f32x16 (&o)[D / 32],
 template <int D>
 BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, f32x16 (&o)[D / 32], bool first,
                      float& l) {
-  const int lane = lane_id();
-  const int r = lane & 31, h = lane >> 5;
   bf16x8 pb[4];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -385,7 +384,9 @@ BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, 
     for (int kk = 1; kk < 4; ++kk) rsum = mfma32(ones, pb[kk], rsum);
     l += rsum[0];
   }
-  pv_steps<0, D>(lds_addr(&sm.vt[r * VTS + 4 * h]), pb, o, first);
+  uint32_t vbase[D / 32];
+  pv_bases<D>(sm, vbase);
+  pv_steps<0, D>(vbase, pb, o, first);
 }
 
 // key index (within a 64-key tile) held by result register i of this lane
@@ -393,10 +394,15 @@ BSA_DEV int krow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
 // Online-softmax update of one lane's query column.  s0/s1 hold raw scores
 // (masked entries already -inf); sl2 = softmax scale * log2(e) is applied
-// inside the exponent.  On return s0/s1 hold the probabilities P (0 where
-// masked) and the running sum l and accumulators o are rescaled to the new
-// max; the tile's own sum of P is added by pv_tile.  `first` skips rescaling
-// the still-zero state.
+// inside the exponent.  On return s0/s1 hold the probabilities
+// P = 2^(s * sl2 - m) (0 where masked).  The running max m is set by the
+// first tile and afterwards moves only when a score passes it by more than
+// kRescaleLog2 (then l and the accumulators are rescaled, in a branch the
+// wave takes only when one of its rows needs it): P stays at most 2^8, and
+// the (m, l) the partial is stored with is whatever m ended up as.  The
+// tile's own sum of P is added by pv_tile.
+constexpr float kRescaleLog2 = 8.0f;
+
 template <int D>
 BSA_DEV void softmax_update(f32x16& s0, f32x16& s1, float& m, float& l, f32x16 (&o)[D / 32], float sl2,
                             bool first) {
@@ -404,8 +410,22 @@ BSA_DEV void softmax_update(f32x16& s0, f32x16& s1, float& m, float& l, f32x16 (
 #pragma unroll
   for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, fmaxf(s0[i], s1[i]));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-  const float mnew = fmaxf(m, tmax * sl2);
-  if (mnew == -INFINITY) {
+  const float tm = tmax * sl2;
+  if (first) {
+    m = tm;
+  } else {
+    const bool grow = tm > m + kRescaleLog2;
+    if (__ballot(grow) != 0ull) {
+      const float mnew = grow ? tm : m;
+      const float corr = __builtin_amdgcn_exp2f(m - mnew);
+      l *= corr;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= corr;
+      m = mnew;
+    }
+  }
+  if (m == -INFINITY) {
+    // no visible key yet in this row
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       s0[i] = 0.f;
@@ -415,16 +435,9 @@ BSA_DEV void softmax_update(f32x16& s0, f32x16& s1, float& m, float& l, f32x16 (
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], sl2, -mnew));
-    s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], sl2, -mnew));
+    s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], sl2, -m));
+    s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], sl2, -m));
   }
-  if (!first) {
-    const float corr = __builtin_amdgcn_exp2f(m - mnew);
-    l *= corr;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) o[dt] *= corr;
-  }
-  m = mnew;
 }
 
 template <int D>
@@ -478,10 +491,10 @@ BSA_DEV const uint16_t* q_row(const AttnParams& p, int4 rec, const GRow& g) {
 // SE: entry words through scalar loads (requires R >= 4)
 template <int D, int W, bool SE>
 __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
+  // two tile buffers for blocks longer than a tile (the next tile is copied
+  // by DMA while the current one is computed); one otherwise
+  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm[W == 8 ? 2 : 1];
   __shared__ __attribute__((aligned(16))) QStage<D, W> qst;
-  // natural-layout keys + values of the next tile (blocks longer than a tile)
-  __shared__ __attribute__((aligned(16))) uint16_t s_nat[W == 8 ? 2 * KT * D : 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hq = lane >> 5;
   // work items of this launch's chunks (buckets c0*Nb .. c1*Nb)
@@ -505,7 +518,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
   int run_end = min(it + RUN, end_x);
 
   const int lrow = w * 32 + (lane & 31);
-  int staged = -1;  // bucket whose single key tile sits in LDS
+  int staged = -1;  // bucket whose single key tile sits in LDS (in sm[cur])
+  int tb = 0;       // the buffer the next tile goes to (alternating across items)
+  int cur = 0;      // the buffer holding the tile being computed
 
   const const_int_ptr items = (const_int_ptr)p.items;
   int4 rec = load_item(items, it);
@@ -558,32 +573,40 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
       const bool single = n_keys <= KT;
       if (W == 8 && !single) {
         // tile kt0 arrives by DMA (issued during the previous tile, or now
-        // for the first), is repacked, and the next tile's DMA starts
-        if (kt0 == 0) dma_kv<D, 64 * W>(s_nat, kb, p.ks_t, vb, p.vs_t, key0, n_keys);
+        // for the first: its buffer was last read two tiles ago, before the
+        // previous tile's barrier), then the next tile's DMA goes to the
+        // other buffer, which every wave is done with past this barrier
+        if (kt0 == 0) dma_kv<D, 64 * W>(sm[tb], kb, p.ks_t, vb, p.vs_t, key0, n_keys);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        repack_kv<D, 64 * W>(sm, s_nat, n_keys - kt0);
-        __syncthreads();
-        if (kt0 + KT < n_keys) dma_kv<D, 64 * W>(s_nat, kb, p.ks_t, vb, p.vs_t, key0 + kt0 + KT, n_keys - kt0 - KT);
+        cur = tb;
+        tb ^= 1;
+        if (kt0 + KT < n_keys) dma_kv<D, 64 * W>(sm[tb], kb, p.ks_t, vb, p.vs_t, key0 + kt0 + KT, n_keys - kt0 - KT);
         staged = -1;
       } else if (!(single && staged == bucket)) {
         __syncthreads();
-        stage_kv<D, 64 * W>(sm, kb, p.ks_t, vb, p.vs_t, key0 + kt0, n_keys - kt0);
+        stage_kv<D, 64 * W>(sm[tb], kb, p.ks_t, vb, p.vs_t, key0 + kt0, n_keys - kt0);
         __syncthreads();
+        cur = tb;
+        if (W == 8) tb ^= 1;
         staged = single ? bucket : -1;
       }
+      // keys of the tile this row may see (past n_keys or after the query: none)
+      const int lim = min(n_keys - kt0, p.causal ? qpos - key0 - kt0 + 1 : KT);
+      // a wave whose rows all lie before this tile (the query's own block)
+      // skips it
+      const bool tile_on = wave_on && __ballot(g.valid && lim > 0) != 0ull;
       f32x16 s0, s1;
-      if (wave_on) qk_tile<D>(sm, qf, s0, s1);
+      if (tile_on) qk_tile<D>(sm[cur], qf, s0, s1);
       if (kt0 == 0 && has_next) {
         // queries of the next item into this wave's LDS staging area
         g_n = grow_of(p, rec_n, ent_n, lrow);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the staging area are done
         prefetch_q_lds<D, W>(qst, q_row<D>(p, rec_n, g_n), g_n.valid);
       }
-      if (wave_on) {
+      if (tile_on) {
         // mask only where a key can be past the end or after the query
         // (ragged last tile, or the query's own block); wave-uniform test
-        const int lim = min(n_keys - kt0, p.causal ? qpos - key0 - kt0 + 1 : KT);
         if (__ballot(g.valid && lim < KT) != 0ull) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -593,7 +616,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
           }
         }
         softmax_update<D>(s0, s1, m, l, o, p.sl2, kt0 == 0);
-        pv_tile<D>(sm, s0, s1, o, kt0 == 0, l);
+        pv_tile<D>(sm[cur], s0, s1, o, kt0 == 0, l);
       }
     }
     // epilogue: pack this item's outputs, take the next item's queries out of

@@ -136,16 +136,20 @@ def other_workloads(m, reps):
     for _ in range(2):
         m.sparse_attn_backward(q, k, v, o, lse, sel, g, c["block"], True, out=grads, workspace=bws)
     torch.cuda.synchronize()
-    kms = m.timer_report("attn_bwd")[0] / 2
+    dkv_ms = m.timer_report("attn_bwd_dkv")[0] / 2
+    dq_ms = m.timer_report("attn_bwd_dq")[0] / 2
+    kms = dkv_ms + dq_ms
     m.timer_enable(0)
-    bflops = 2.5 * flops  # per attended pair: q.k, g.v, and the three rank-one updates (dq, dk, dv) = 10 D
-    out["moba_32k_backward"] = {"ms": round(bms, 4), "attn_bwd_ms": round(kms, 4),
+    bflops = 2.5 * flops  # per attended pair: q.k, g.v and the three products for dq, dk, dv = 10 D
+    out["moba_32k_backward"] = {"ms": round(bms, 4), "attn_bwd_dkv_ms": round(dkv_ms, 4),
+                                "attn_bwd_dq_ms": round(dq_ms, 4),
                                 "attended_tflops": round(bflops / (bms * 1e-3) / 1e12, 2),
                                 "kernel_tflops": round(bflops / (kms * 1e-3) / 1e12, 2),
-                                "note": "gradients through the forward's selection; fp32 VALU (chip fp32 vector "
-                                        "peak 157.3 TFLOP/s with packed FP32, 78.6 without, which this build "
-                                        "does not emit)"}
-    _log(f"MoBA-style 32K backward: {bms:.3f} ms (gradient kernel {kms:.3f} ms, "
+                                "kernel_frac_bf16_peak": round(bflops / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                "note": "gradients through the forward's selection; bf16 MFMA, fp32 accumulation; "
+                                        "the dk/dv and dq kernels form 7 products per attended pair (S and dP "
+                                        "in both), the flops counted are the 5 the gradient needs"}
+    _log(f"MoBA-style 32K backward: {bms:.3f} ms (dk/dv {dkv_ms:.3f} ms, dq {dq_ms:.3f} ms, "
          f"{bflops / (kms * 1e-3) / 1e12:.1f} TFLOP/s)")
     del q, k, v, o, ws, g, sel, lse, grads, bws
     c = MEMORY

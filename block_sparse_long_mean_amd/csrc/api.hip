@@ -613,7 +613,7 @@ struct BackwardPlan {
   int32_t *counts, *cursor, *bucket_off, *tile_off, *scan_tmp;
   uint32_t* entries;
   int4* items;
-  float *delta, *dq_part, *dkv_part;
+  float *delta, *dq_part;
   size_t bytes;
 };
 
@@ -657,11 +657,10 @@ static bsa_status plan_backward(const bsa_backward_args* a, BackwardPlan& P, cha
   P.NC = (a->Lq + P.CT - 1) / P.CT;
   P.nbk = (int64_t)a->B * a->Hkv * P.NC * P.Nb;
   if (P.nbk >= (int64_t)1 << 30) return fail(BSA_ERR_UNSUPPORTED, "too many (chunk, block) buckets");
-  // work items: consecutive runs of up to 512 rows of a bucket's sorted
-  // entries (a fixed split, so the sums stay in a fixed order); long buckets
-  // (early blocks that most tokens of a chunk choose) spread over several
-  // workgroups instead of one
-  P.rows_item = std::min(P.CT * P.G, 512);
+  // dq work items: consecutive runs of up to kBwdItemRows rows of a bucket
+  // (each (row, slot) partial is summed inside one item, so any split keeps
+  // the sums in a fixed order)
+  P.rows_item = kBwdItemRows;
   P.max_entries = P.nsel_rows * a->sel_w;
   P.max_items = (P.max_entries * P.R + P.rows_item - 1) / P.rows_item + std::min<int64_t>(P.nbk, P.max_entries);
   if (P.max_items >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "too many work items");
@@ -677,7 +676,6 @@ static bsa_status plan_backward(const bsa_backward_args* a, BackwardPlan& P, cha
   P.delta = c.take<float>((int64_t)a->B * a->Hq * a->Lq);
   // partial rows per (b, kv head, chunk, head of the group): CT each, the last chunk padded
   P.dq_part = c.take<float>((int64_t)a->B * a->Hkv * P.NC * P.Gs * P.CT * P.kslot * P.R * a->D);
-  P.dkv_part = c.take<float>(std::max<int64_t>(P.max_items, 1) * 2 * a->block * a->D);
   P.bytes = c.off + 256;
   return BSA_OK;
 }
@@ -713,7 +711,7 @@ static bsa_status run_backward(const bsa_backward_args* a, void* ws, size_t ws_b
   ap.rows_item = P.rows_item;
   ap.grid = P.max_entries > 0 ? (int)P.max_items : 0;
   ap.sel = a->sel; ap.sel_w = a->sel_w;
-  ap.lse_in = a->lse; ap.delta = P.delta; ap.dq_part = P.dq_part; ap.dkv_part = P.dkv_part;
+  ap.lse_in = a->lse; ap.delta = P.delta; ap.dq_part = P.dq_part;
   ap.dq = a->dq; ap.dk = a->dk; ap.dv = a->dv;
   CsrParams cp;
   cp.B = a->B; cp.Lq = a->Lq; cp.Lk = a->Lk; cp.Hkv = a->Hkv; cp.G = P.G; cp.Hs = P.Hs; cp.per_group = per_group;

@@ -196,7 +196,7 @@ BSA_DEV void store_rows(uint32_t dst_base, uint32_t row_base, int lr, int nvalid
       asm volatile(
           "ds_read_b64 %0, %3 offset:%5\n\tds_read_b64 %1, %4 offset:%6\n\tds_read_b64 %2, %4 offset:%7\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(dst), "=v"(a), "=v"(b)
+          : "=&v"(dst), "=&v"(a), "=&v"(b)
           : "v"(dst_base), "v"(row_base), "n"(N * RPI * 8), "n"(N * RPI * RS * 2), "n"(N * RPI * RS * 2 + 8)
           : "memory");
       const u16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -289,7 +289,7 @@ BSA_DEV void qk_steps(uint32_t base, const bf16x8 (&qf)[D / 16], f32x16& s0, f32
     asm volatile(
         "ds_read_b128 %0, %4 offset:%5\n\tds_read_b128 %1, %4 offset:%6\n\t"
         "ds_read_b128 %2, %4 offset:%7\n\tds_read_b128 %3, %4 offset:%8\n\ts_waitcnt lgkmcnt(0)"
-        : "=v"(a0), "=v"(a1), "=v"(b0), "=v"(b1)
+        : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
         : "v"(base), "n"(S * 32), "n"(R32 + S * 32), "n"(S * 32 + 32), "n"(R32 + S * 32 + 32)
         : "memory");
     s0 = mfma32(as_bf(a0), qf[S], s0);
@@ -300,14 +300,22 @@ BSA_DEV void qk_steps(uint32_t base, const bf16x8 (&qf)[D / 16], f32x16& s0, f32
   }
 }
 
-// S^T (64 keys x 32 queries) for this wave: s0 keys 0..31, s1 keys 32..63.
+// A . B^T for a padded 64-row tile A (rows of D elements, row stride D + 8)
+// and this wave's 32 columns B (qf: lane l holds head dims 16s + 8(l/32) ..
+// +7 of column l%32 in qf[s]): s0 = tile rows 0..31, s1 = rows 32..63.
 template <int D>
-BSA_DEV void qk_tile(const AttnSmem<D>& sm, const bf16x8 (&qf)[D / 16], f32x16& s0, f32x16& s1) {
+BSA_DEV void qk_tile_pad(const uint16_t* tile, const bf16x8 (&qf)[D / 16], f32x16& s0, f32x16& s1) {
   const int lane = lane_id();
   const int r = lane & 31, h = lane >> 5;
   s0 = f32x16{};
   s1 = f32x16{};
-  qk_steps<0, D>(lds_addr(&sm.k[r * (D + 8) + 8 * h]), qf, s0, s1);
+  qk_steps<0, D>(lds_addr(&tile[r * (D + 8) + 8 * h]), qf, s0, s1);
+}
+
+// S^T (64 keys x 32 queries) for this wave: s0 keys 0..31, s1 keys 32..63.
+template <int D>
+BSA_DEV void qk_tile(const AttnSmem<D>& sm, const bf16x8 (&qf)[D / 16], f32x16& s0, f32x16& s1) {
+  qk_tile_pad<D>(sm.k, qf, s0, s1);
 }
 
 // Head-dim tile DT of pv_tile: O^T rows 32 DT .. 32 DT + 31 over the tile's
@@ -330,7 +338,7 @@ BSA_DEV void pv_steps(const uint32_t (&vbase)[D / 32], const bf16x8 (&pb)[4], f3
         "ds_read_b64_tr_b16 %2, %8 offset:%11\n\tds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
         "ds_read_b64_tr_b16 %4, %8 offset:%13\n\tds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
         "ds_read_b64_tr_b16 %6, %8 offset:%15\n\tds_read_b64_tr_b16 %7, %8 offset:%16\n\ts_waitcnt lgkmcnt(0)"
-        : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3), "=v"(x4), "=v"(x5), "=v"(x6), "=v"(x7)
+        : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4), "=&v"(x5), "=&v"(x6), "=&v"(x7)
         : "v"(vbase[DT]), "n"(0), "n"(8 * RB), "n"(16 * RB), "n"(24 * RB), "n"(32 * RB), "n"(40 * RB),
           "n"(48 * RB), "n"(56 * RB)
         : "memory");
@@ -346,13 +354,14 @@ BSA_DEV void pv_steps(const uint32_t (&vbase)[D / 32], const bf16x8 (&pb)[4], f3
   }
 }
 
-// LDS byte addresses of pv_steps for the value tile of `sm`
+// LDS byte addresses of pv_steps for a 64-row tile in the permuted layout
+// (the value tile of AttnSmem)
 template <int D>
-BSA_DEV void pv_bases(const AttnSmem<D>& sm, uint32_t (&vbase)[D / 32]) {
+BSA_DEV void pv_bases(const uint16_t* tile, uint32_t (&vbase)[D / 32]) {
   const int lane = lane_id();
   const int s = lane & 15, g = lane >> 4, h = lane >> 5;
   const int row = 4 * h + (s >> 2);
-  const uint32_t b0 = lds_addr(sm.v) + (uint32_t)(row * D * 2 + 8 * (s & 1));
+  const uint32_t b0 = lds_addr(tile) + (uint32_t)(row * D * 2 + 8 * (s & 1));
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     const int piece = 4 * dt + 2 * (g & 1) + ((s & 3) >> 1);
@@ -385,7 +394,7 @@ BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, 
     l += rsum[0];
   }
   uint32_t vbase[D / 32];
-  pv_bases<D>(sm, vbase);
+  pv_bases<D>(sm.v, vbase);
   pv_steps<0, D>(vbase, pb, o, first);
 }
 
@@ -1034,10 +1043,31 @@ bool launch_attn_rowwise_f32(const AttnF32Params& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Backward through the fixed selection.  A bucket's entries (one query
-// chunk's rows that chose one (b, kv head, block)) are sorted first and cut
-// into work items of consecutive rows, so every sum over the rows that chose
-// a block runs in a fixed order.
+// Backward through the fixed selection, on bf16 MFMA with fp32 accumulation.
+// With the forward's log-sum-exp lse_r of row r and delta_r = dout_r . o_r:
+//   p_rk = exp(scale q_r . k_k - lse_r),  dp_rk = dout_r . v_k,
+//   ds_rk = p_rk (dp_rk - delta_r),
+//   dq_r = scale sum_k ds_rk k_k,  dk_k = scale sum_r ds_rk q_r,
+//   dv_k = sum_r p_rk dout_r,
+// the sums running over the (row, key) pairs the forward attended.  A
+// bucket's entries (one query chunk's rows that chose one (b, kv head,
+// block)) are sorted first, so every sum runs in a fixed order and two calls
+// give the same bits.
+//  * attn_bwd_dkv: one workgroup per (b, kv head, block, 32W keys).  Wave w
+//    holds keys 32w .. 32w+31 of the unit (their k and v rows as MFMA
+//    operands in registers) and their dk^T, dv^T accumulators; the workgroup
+//    walks every row that chose the block -- the block's buckets in query
+//    chunk order, each bucket's sorted entries -- 64 rows at a time.  A batch
+//    of gathered q and dout rows is copied by DMA into LDS twice: padded
+//    rows for S = Q K^T and dP = dO V^T, and rows with permuted pieces for the
+//    transposing reads of dV^T += dO^T P and dK^T += Q^T dS.  The next
+//    batch's copy runs during the current batch's MFMAs.  dk and dv are
+//    written once per key.
+//  * attn_bwd_dq: the forward's work items (a bucket's rows, 32 per wave);
+//    a wave holds its rows' q and dout as MFMA operands, the block streams
+//    through LDS in 64-key tiles (keys padded and permuted, values padded),
+//    and S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.  One fp32 partial per
+//    (row, slot); bwd_dq_reduce sums a row's slots in slot order.
 // ---------------------------------------------------------------------------
 
 // delta[b, h, t] = dout . o of each output row, fp32 (D/8 lanes per row)
@@ -1093,24 +1123,311 @@ __global__ __launch_bounds__(256) void bwd_sort_kernel(AttnParams p, int nbk) {
   for (int i = threadIdx.x; i < n; i += 256) ent[i] = s_e[i];
 }
 
-// One workgroup per work item: for each 64-key tile of the block, stage K
-// (fp32, LDS), then take the item's rows sixteen at a time.
-// Wave w owns keys 16w .. 16w+15 of the tile; lane (key, quarter) forms
-// quarter dot products q.k and g.v, completes them across the key's four
-// lanes, and accumulates dk and dv for its key and quarter in registers.
-// The rows' ds values go through LDS for dq = sum_u ds_u k_u, which each
-// (row, slot) partial accumulates over the block's tiles.
+// One batch of 64 gathered rows of the dk / dv kernel.
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnParams p) {
-  constexpr int KT = 64, RB = 16, DQ = D / 4, KP = D + 4;
-  __shared__ __attribute__((aligned(16))) float s_k[KT * KP];
-  __shared__ __attribute__((aligned(16))) float s_q[RB][D];
-  __shared__ __attribute__((aligned(16))) float s_g[RB][D];
-  __shared__ float s_ds[RB][KT];
-  __shared__ float s_lse2[RB], s_dl[RB];
-  __shared__ int s_qpos[RB];
-  __shared__ int64_t s_pidx[RB];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+struct BwdRows {
+  uint16_t qp[64 * (D + 8)];  // q rows, padded (row-wise operand reads)
+  uint16_t gp[64 * (D + 8)];  // dout rows, padded
+  uint16_t qs[64 * D];        // q rows, pieces permuted (transposing reads)
+  uint16_t gs[64 * D];        // dout rows, pieces permuted
+  float lse[64];              // the rows' log-sum-exp (natural log)
+  float dl[64];               // the rows' delta
+  uint32_t ent[64];           // the rows' entry words (0 past the batch's rows)
+};
+static_assert(offsetof(BwdRows<128>, dl) == offsetof(BwdRows<128>, lse) + 256 &&
+                  offsetof(BwdRows<128>, ent) == offsetof(BwdRows<128>, lse) + 512 &&
+                  offsetof(BwdRows<64>, dl) == offsetof(BwdRows<64>, lse) + 256 &&
+                  offsetof(BwdRows<64>, ent) == offsetof(BwdRows<64>, lse) + 512,
+              "bwd_row_stats reads lse, dl and ent at fixed distances");
+
+// DMA instruction i of a 64-row tile of gathered rows: row r's first
+// 16-byte piece sits at piece offset `off` of `base`, held by lane r of the
+// wave.  PAD: rows of D + 8 elements (a padding piece loads piece 0 of its
+// row); otherwise rows of D elements with piece c of row r at c ^ vswz(r).
+template <int D, bool PAD>
+BSA_DEV void dma_gathered(uint16_t* tile, const uint16_t* base, uint32_t off, int i) {
+  constexpr int RP = PAD ? D / 8 + 1 : D / 8;
+  const int P = i * 64 + lane_id();
+  const int r = P / RP;
+  int c = P % RP;
+  if constexpr (PAD) c = c == RP - 1 ? 0 : c;
+  else c ^= vswz<D>(r);
+  const uint32_t ro = (uint32_t)__shfl((int)off, r, 64);
+  __builtin_amdgcn_global_load_lds((const void*)(base + ((int64_t)ro << 3) + c * 8), (lds_ptr_t)(tile + i * 512), 16,
+                                   0, 0);
+}
+
+// DMA instruction i of a 64-row tile of consecutive rows row0 .. row0+63 of
+// `base` (row stride rs elements); rows past n_valid load row row0.
+template <int D, bool PAD>
+BSA_DEV void dma_rows(uint16_t* tile, const uint16_t* base, int64_t rs, int row0, int n_valid, int i) {
+  constexpr int RP = PAD ? D / 8 + 1 : D / 8;
+  const int P = i * 64 + lane_id();
+  const int r = P / RP;
+  int c = P % RP;
+  if constexpr (PAD) c = c == RP - 1 ? 0 : c;
+  else c ^= vswz<D>(r);
+  const int rr = r < n_valid ? r : 0;
+  __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)(row0 + rr) * rs + c * 8),
+                                   (lds_ptr_t)(tile + i * 512), 16, 0, 0);
+}
+
+// pv_steps over a permuted 64-row tile with the B operand taken from two
+// 32x32 result tiles (rows 0..31 in x0, 32..63 in x1), rounded to bf16
+template <int D>
+BSA_DEV void pv_acc(const uint16_t* tile, const f32x16& x0, const f32x16& x1, f32x16 (&o)[D / 32]) {
+  bf16x8 pb[4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pb[0][e] = (__bf16)x0[e];
+    pb[1][e] = (__bf16)x0[8 + e];
+    pb[2][e] = (__bf16)x1[e];
+    pb[3][e] = (__bf16)x1[8 + e];
+  }
+  uint32_t vbase[D / 32];
+  pv_bases<D>(tile, vbase);
+  pv_steps<0, D>(vbase, pb, o, false);
+}
+
+BSA_DEV float lse_log2(float lse) {
+  // rows with no visible key carry lse = -inf: no probability anywhere
+  return lse == -INFINITY ? INFINITY : lse * 1.4426950408889634f;
+}
+
+// Stores a 32x32 result tile set (rows 32dt + krow(i, h) of column lane%32)
+// as fp32 rows: dst points at the column's row of D elements.
+template <int D>
+BSA_DEV void store_cols(float* dst, const f32x16 (&o)[D / 32], float mul) {
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * q + 4 * h) =
+          f32x4{o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]} * mul;
+}
+
+// lse and delta of the lane's 32 result rows of a batch, rows
+// 8(q&3) + 4h + 32(q>>2) .. +3 in ls[q] / dl[q] (base = address of lse[4h]);
+// LDS reads through asm, as for the key / value tiles, so that they do not
+// wait for the next batch's copy
+BSA_DEV void bwd_row_stats(uint32_t base, f32x4 (&ls)[8], f32x4 (&dl)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:0\n\tds_read_b128 %1, %16 offset:32\n\t"
+      "ds_read_b128 %2, %16 offset:64\n\tds_read_b128 %3, %16 offset:96\n\t"
+      "ds_read_b128 %4, %16 offset:128\n\tds_read_b128 %5, %16 offset:160\n\t"
+      "ds_read_b128 %6, %16 offset:192\n\tds_read_b128 %7, %16 offset:224\n\t"
+      "ds_read_b128 %8, %16 offset:256\n\tds_read_b128 %9, %16 offset:288\n\t"
+      "ds_read_b128 %10, %16 offset:320\n\tds_read_b128 %11, %16 offset:352\n\t"
+      "ds_read_b128 %12, %16 offset:384\n\tds_read_b128 %13, %16 offset:416\n\t"
+      "ds_read_b128 %14, %16 offset:448\n\tds_read_b128 %15, %16 offset:480\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(ls[0]), "=&v"(ls[1]), "=&v"(ls[2]), "=&v"(ls[3]), "=&v"(ls[4]), "=&v"(ls[5]), "=&v"(ls[6]), "=&v"(ls[7]),
+        "=&v"(dl[0]), "=&v"(dl[1]), "=&v"(dl[2]), "=&v"(dl[3]), "=&v"(dl[4]), "=&v"(dl[5]), "=&v"(dl[6]), "=&v"(dl[7])
+      : "v"(base)
+      : "memory");
+}
+
+// the rows' entry words, in the same arrangement (ent follows dl)
+BSA_DEV void bwd_row_ents(uint32_t base, u32x4 (&en)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:512\n\tds_read_b128 %1, %8 offset:544\n\t"
+      "ds_read_b128 %2, %8 offset:576\n\tds_read_b128 %3, %8 offset:608\n\t"
+      "ds_read_b128 %4, %8 offset:640\n\tds_read_b128 %5, %8 offset:672\n\t"
+      "ds_read_b128 %6, %8 offset:704\n\tds_read_b128 %7, %8 offset:736\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(en[0]), "=&v"(en[1]), "=&v"(en[2]), "=&v"(en[3]), "=&v"(en[4]), "=&v"(en[5]), "=&v"(en[6]), "=&v"(en[7])
+      : "v"(base)
+      : "memory");
+}
+
+// Batch cursor of the dk / dv kernel (wave-uniform): query chunk c (NC =
+// done), first row of the batch within the bucket, the bucket's rows and its
+// first entry.
+struct BwdCursor {
+  int c, start, rows, eoff;
+};
+
+BSA_DEV void bwd_seek(const AttnParams& p, int64_t bh, int j, int c, BwdCursor& s) {
+  const const_int_ptr off = (const const_int_ptr)p.bucket_off;
+  for (; p.grid > 0 && c < p.NC; ++c) {  // grid 0: no selection entries, nothing built
+    const int64_t bk = (bh * p.NC + c) * p.Nb + j;
+    const int a = off[bk];
+    const int n = (off[bk + 1] - a) << p.lgR;
+    if (n > 0) {
+      s = BwdCursor{c, 0, n, a};
+      return;
+    }
+  }
+  s = BwdCursor{p.NC, 0, 0, 0};
+}
+
+BSA_DEV void bwd_advance(const AttnParams& p, int64_t bh, int j, BwdCursor& s) {
+  if (s.start + 64 < s.rows) s.start += 64;
+  else bwd_seek(p, bh, j, s.c + 1, s);
+}
+
+// entry word of this lane's row (row = lane) of the cursor's batch; rows
+// past the bucket's end read the batch's first row
+BSA_DEV uint32_t bwd_entry(const AttnParams& p, const BwdCursor& s) {
+  if (s.c >= p.NC) return 0u;
+  const int lr = s.start + lane_id();
+  const int lrc = lr < s.rows ? lr : s.start;
+  return p.entries[s.eoff + (lrc >> p.lgR)];
+}
+
+template <int D, int W>
+BSA_DEV void bwd_issue_batch(const AttnParams& p, BwdRows<D>& buf, const BwdCursor& s, uint32_t ent, int b, int hk) {
+  const int lane = lane_id();
+  const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = s.start + lane;
+  const bool valid = lr < s.rows;
+  const int lrc = valid ? lr : s.start;
+  const int rr = lrc & ((1 << p.lgR) - 1);
+  const int t = (int)(ent >> p.sh_t);
+  const int hh = (int)((ent >> p.sh_h) & ((1u << (p.sh_t - p.sh_h)) - 1u));
+  const int qh = p.per_group ? hk * p.G + rr : hk * p.G + hh;
+  const uint32_t qo = (uint32_t)(((int64_t)b * p.qs_b + (int64_t)t * p.qs_t + (int64_t)qh * p.qs_h) >> 3);
+  const uint32_t go = (uint32_t)(((int64_t)b * p.dos_b + (int64_t)t * p.dos_t + (int64_t)qh * p.dos_h) >> 3);
+  const int64_t orow = ((int64_t)b * p.Hq + qh) * p.Lq + t;
+  constexpr int NP = D / 8 + 1, NS = D / 8, N = 2 * NP + 2 * NS + 2;
+  for (int i = wu; i < N; i += W) {
+    if (i < NP) dma_gathered<D, true>(buf.qp, p.q, qo, i);
+    else if (i < 2 * NP) dma_gathered<D, true>(buf.gp, p.dout, go, i - NP);
+    else if (i < 2 * NP + NS) dma_gathered<D, false>(buf.qs, p.q, qo, i - 2 * NP);
+    else if (i < 2 * NP + 2 * NS) dma_gathered<D, false>(buf.gs, p.dout, go, i - 2 * NP - NS);
+    else if (i == 2 * NP + 2 * NS)
+      __builtin_amdgcn_global_load_lds((const void*)(p.lse_in + orow), (lds_ptr_t)buf.lse, 4, 0, 0);
+    else __builtin_amdgcn_global_load_lds((const void*)(p.delta + orow), (lds_ptr_t)buf.dl, 4, 0, 0);
+  }
+  if (wu == 0) buf.ent[lane] = valid ? ent : 0u;
+}
+
+template <int D, int W>
+__global__ __launch_bounds__(64 * W, 1) void attn_bwd_dkv_kernel(AttnParams p, int nkt) {
+  __shared__ __attribute__((aligned(16))) BwdRows<D> rb[2];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5;
+  // unit groups (j, bh), group g = j * BH + bh, each of nkt key slices:
+  // group g runs on XCD g % 8 (workgroup i runs on XCD i % 8), so that the
+  // slices of one block share its rows through that XCD's L2, and every XCD
+  // takes the groups in order of j -- low blocks first (under causal
+  // selection they collect the most rows) and the heavy ones spread over
+  // all XCDs
+  const int BH = p.B * p.Hkv;
+  const int slot = blockIdx.x >> 3;
+  const int64_t grp = (int64_t)(slot / nkt) * 8 + (blockIdx.x & 7);
+  if (grp >= (int64_t)p.Nb * BH) return;  // padding of the grid; uniform
+  const int kt = slot % nkt;
+  const int bh = (int)(grp % BH);
+  const int j = (int)(grp / BH);
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int key0 = j * p.block + kt * 32 * W;
+  const int n_keys = min(min(32 * W, p.block - kt * 32 * W), p.Lk - key0);
+  if (n_keys <= 0) return;  // a slice past the end of a ragged last block; uniform
+  const bool wave_on = 32 * w < n_keys;
+  // this lane's key (column lane%32 of the wave's tiles) as B operands
+  const int kcol = 32 * w + (lane & 31);
+  const int key = key0 + kcol;
+  bf16x8 kf[D / 16], vf[D / 16];
+  load_qf<D>(p.k + (int64_t)b * p.ks_b + (int64_t)key * p.ks_t + (int64_t)hk * p.ks_h, kcol < n_keys, kf);
+  load_qf<D>(p.v + (int64_t)b * p.vs_b + (int64_t)key * p.vs_t + (int64_t)hk * p.vs_h, kcol < n_keys, vf);
+  // a row sees this key when its token t >= key - (Lk - Lq), i.e. when its
+  // entry word is at least tk << sh_t
+  const int tk = key - (p.Lk - p.Lq);
+  const uint32_t ent_min = (p.causal && tk > 0) ? (uint32_t)tk << p.sh_t : 0u;
+  // the wave's last key: a batch whose first (lowest) token sees it needs no mask
+  const int tk_last = min(key0 + 32 * w + 31, key0 + n_keys - 1) - (p.Lk - p.Lq);
+  f32x16 dkt[D / 32], dvt[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dkt[dt] = dvt[dt] = f32x16{};
+
+  BwdCursor nx;
+  bwd_seek(p, bh, j, 0, nx);
+  bool have = nx.c < p.NC;
+  int nv = have ? min(64, nx.rows - nx.start) : 0;
+  if (have) {
+    const uint32_t e0 = bwd_entry(p, nx);
+    bwd_issue_batch<D, W>(p, rb[0], nx, e0, b, hk);
+    bwd_advance(p, bh, j, nx);
+  }
+  uint32_t ent_n = bwd_entry(p, nx);
+  for (int n = 0; have; ++n) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // batch n is in rb[n & 1]; every wave is done with rb[(n + 1) & 1]
+    const bool have_n = nx.c < p.NC;
+    int nv_n = 0;
+    if (have_n) {
+      bwd_issue_batch<D, W>(p, rb[(n + 1) & 1], nx, ent_n, b, hk);
+      nv_n = min(64, nx.rows - nx.start);
+      bwd_advance(p, bh, j, nx);
+      ent_n = bwd_entry(p, nx);
+    }
+    if (wave_on) {
+      const BwdRows<D>& bf = rb[n & 1];
+      f32x16 s0, s1, d0, d1;
+      qk_tile_pad<D>(bf.qp, kf, s0, s1);
+      qk_tile_pad<D>(bf.gp, vf, d0, d1);
+      // the batch's rows are sorted by token: the first has the lowest
+      const uint32_t sbase = lds_addr(&bf.lse[4 * h]);
+      uint32_t ent0;
+      asm volatile("ds_read_b32 %0, %1 offset:%2\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(ent0)
+                   : "v"(lds_addr(bf.ent)), "n"(0)
+                   : "memory");
+      const bool msk = nv < 64 || (p.causal && (int)(ent0 >> p.sh_t) < tk_last);
+      f32x4 ls[8], dl[8];
+      bwd_row_stats(sbase, ls, dl);
+      u32x4 en[8];
+      if (msk) bwd_row_ents(sbase, en);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int r0 = 8 * (q & 3) + 4 * h + 32 * (q >> 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f32x16& s = q < 4 ? s0 : s1;
+          f32x16& d = q < 4 ? d0 : d1;
+          const int i = 4 * (q & 3) + e;
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[i], p.sl2, -lse_log2(ls[q][e])));
+          if (msk && !(r0 + e < nv && en[q][e] >= ent_min)) pr = 0.f;
+          s[i] = pr;
+          d[i] = pr * (d[i] - dl[q][e]);
+        }
+      }
+      pv_acc<D>(bf.gs, s0, s1, dvt);
+      pv_acc<D>(bf.qs, d0, d1, dkt);
+    }
+    have = have_n;
+    nv = nv_n;
+  }
+  if (kcol < n_keys) {
+    const int64_t orow = (((int64_t)b * p.Lk + key) * p.Hkv + hk) * D;
+    store_cols<D>(p.dk + orow, dkt, p.scale);
+    store_cols<D>(p.dv + orow, dvt, 1.f);
+  }
+}
+
+// One 64-key tile of the dq kernel
+template <int D>
+struct BwdKv {
+  uint16_t kp[KT * (D + 8)];  // keys, padded
+  uint16_t vp[KT * (D + 8)];  // values, padded
+  uint16_t ks[KT * D];        // keys, pieces permuted
+};
+
+template <int D, int W>
+BSA_DEV void dma_bwd_kv(BwdKv<D>& sm, const uint16_t* kb, int64_t ks_t, const uint16_t* vb, int64_t vs_t, int row0,
+                        int n_valid) {
+  constexpr int NP = D / 8 + 1, NS = D / 8;
+  const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int i = wu; i < 2 * NP + NS; i += W) {
+    if (i < NP) dma_rows<D, true>(sm.kp, kb, ks_t, row0, n_valid, i);
+    else if (i < 2 * NP) dma_rows<D, true>(sm.vp, vb, vs_t, row0, n_valid, i - NP);
+    else dma_rows<D, false>(sm.ks, kb, ks_t, row0, n_valid, i - 2 * NP);
+  }
+}
+
+template <int D, int W>
+__global__ __launch_bounds__(64 * W, 1) void attn_bwd_dq_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) BwdKv<D> sm[2];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5;
   const int item = blockIdx.x;
   if (item >= p.tile_off[(int64_t)p.B * p.Hkv * p.NC * p.Nb]) return;  // past the built items; uniform
   const int4 rec = load_item((const_int_ptr)p.items, item);
@@ -1123,131 +1440,53 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnParams p) {
   const int n_keys = min(p.block, p.Lk - key0);
   const uint16_t* kb = p.k + (int64_t)b * p.ks_b + (int64_t)hk * p.ks_h;
   const uint16_t* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
-  const int ku = 16 * w + (lane >> 2), qc = lane & 3;  // this lane's key in the tile and quarter
-  float* dst = p.dkv_part + (int64_t)item * 2 * p.block * D;
-  const float L2E = 1.4426950408889634f;
-  for (int t0 = 0; t0 < n_keys; t0 += KT) {
-    const int nt = min(KT, n_keys - t0);
-    __syncthreads();  // the previous tile's K / V are no longer read
-    for (int i = tid; i < KT * (D / 8); i += 256) {
-      const int u = i / (D / 8), c8 = i % (D / 8);
-      u16x8 kx = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (u < nt) kx = ld16(kb + (int64_t)(key0 + t0 + u) * p.ks_t + c8 * 8);
+  const int lrow = w * 32 + (lane & 31);
+  const GRow g = grow_of(p, rec, entry_of(p, rec, lrow), lrow);
+  bf16x8 qf[D / 16], gf[D / 16];
+  load_qf<D>(q_row<D>(p, rec, g), g.valid, qf);
+  load_qf<D>(p.dout + (int64_t)b * p.dos_b + (int64_t)g.t * p.dos_t + (int64_t)g.qh * p.dos_h, g.valid, gf);
+  const int64_t orow = ((int64_t)b * p.Hq + g.qh) * p.Lq + g.t;
+  const float lse2 = g.valid ? lse_log2(p.lse_in[orow]) : INFINITY;
+  const float dl = g.valid ? p.delta[orow] : 0.f;
+  const int qpos = p.Lk - p.Lq + g.t;
+  const bool wave_on = w * 32 < rec.z;
+  f32x16 dqt[D / 32];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_k[u * KP + c8 * 8 + e] = bf2f(kx[e]);
-    }
-    float dk[DQ], dv[DQ];
+  for (int dt = 0; dt < D / 32; ++dt) dqt[dt] = f32x16{};
+  int tb = 0;
+  for (int kt0 = 0; kt0 < n_keys; kt0 += KT) {
+    // tile kt0 arrives by DMA (issued during the previous tile, or now for
+    // the first), then the next tile's DMA goes to the other buffer, which
+    // every wave is done with past this barrier
+    if (kt0 == 0) dma_bwd_kv<D, W>(sm[0], kb, p.ks_t, vb, p.vs_t, key0, n_keys);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int cur = tb;
+    tb ^= 1;
+    if (kt0 + KT < n_keys) dma_bwd_kv<D, W>(sm[tb], kb, p.ks_t, vb, p.vs_t, key0 + kt0 + KT, n_keys - kt0 - KT);
+    const int lim = min(n_keys - kt0, p.causal ? qpos - key0 - kt0 + 1 : KT);
+    if (wave_on && __ballot(g.valid && lim > 0) != 0ull) {
+      f32x16 s0, s1, d0, d1;
+      qk_tile_pad<D>(sm[cur].kp, qf, s0, s1);
+      qk_tile_pad<D>(sm[cur].vp, gf, d0, d1);
 #pragma unroll
-    for (int e = 0; e < DQ; ++e) dk[e] = dv[e] = 0.f;
-    const int key = key0 + t0 + ku;
-    __syncthreads();  // the tile is staged
-    // this lane's quarter of its key (LDS) and value (straight from memory),
-    // held for every row of the item
-    float kr[DQ], vr[DQ];
-#pragma unroll
-    for (int e = 0; e < DQ; e += 8) {
-      const f32x4 k0 = *reinterpret_cast<const f32x4*>(&s_k[ku * KP + qc * DQ + e]);
-      const f32x4 k1 = *reinterpret_cast<const f32x4*>(&s_k[ku * KP + qc * DQ + e + 4]);
-      const u16x8 vx = ku < nt ? ld16(vb + (int64_t)key * p.vs_t + qc * DQ + e) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        kr[e + x] = k0[x];
-        kr[e + 4 + x] = k1[x];
+      for (int i = 0; i < 16; ++i) {
+        const int kr = krow(i, h);
+        const float p0 = kr < lim ? __builtin_amdgcn_exp2f(fmaf(s0[i], p.sl2, -lse2)) : 0.f;
+        const float p1 = kr + 32 < lim ? __builtin_amdgcn_exp2f(fmaf(s1[i], p.sl2, -lse2)) : 0.f;
+        d0[i] = p0 * (d0[i] - dl);
+        d1[i] = p1 * (d1[i] - dl);
       }
-#pragma unroll
-      for (int x = 0; x < 8; ++x) vr[e + x] = bf2f(vx[x]);
-    }
-    for (int r0 = 0; r0 < rec.z; r0 += RB) {
-      const int nr = min(RB, rec.z - r0);
-      __syncthreads();  // the previous rows' q, g and ds are no longer read
-      // stage the batch's rows: q, g (fp32), lse (log2), delta, position, partial index
-      for (int i = tid; i < RB * (D / 8); i += 256) {
-        const int r = i / (D / 8), c8 = i % (D / 8);
-        u16x8 qx = u16x8{0, 0, 0, 0, 0, 0, 0, 0}, gx = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        if (r < nr) {
-          const GRow g = grow_of(p, rec, entry_of(p, rec, r0 + r), r0 + r);
-          qx = ld16(q_row<D>(p, rec, g) + c8 * 8);
-          gx = ld16(p.dout + (int64_t)b * p.dos_b + (int64_t)g.t * p.dos_t + (int64_t)g.qh * p.dos_h + c8 * 8);
-          if (c8 == 0) {
-            const int64_t orow = ((int64_t)b * p.Hq + g.qh) * p.Lq + g.t;
-            s_lse2[r] = p.lse_in[orow] * L2E;
-            s_dl[r] = p.delta[orow];
-            s_qpos[r] = p.causal ? p.Lk - p.Lq + g.t : 0x7FFFFFFF;
-            const int hsel = p.per_group ? 0 : g.hs - hk * p.G;
-            const int64_t prow = (prow_base + hsel) * p.CT + (g.t - t_base);
-            s_pidx[r] = (prow * p.kslot + g.slot) * p.R + g.rr;
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          s_q[r][c8 * 8 + e] = bf2f(qx[e]);
-          s_g[r][c8 * 8 + e] = bf2f(gx[e]);
-        }
-      }
-      __syncthreads();
-      for (int r = 0; r < nr; ++r) {
-        float sc = 0.f, dp = 0.f;
-        float qv[DQ], gv[DQ];  // the row's quarter of q and g, read once for both passes
-#pragma unroll
-        for (int e = 0; e < DQ; e += 4) {
-          const f32x4 qq = *reinterpret_cast<const f32x4*>(&s_q[r][qc * DQ + e]);
-          const f32x4 gq = *reinterpret_cast<const f32x4*>(&s_g[r][qc * DQ + e]);
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            qv[e + x] = qq[x];
-            gv[e + x] = gq[x];
-            sc = fmaf(qq[x], kr[e + x], sc);
-            dp = fmaf(gq[x], vr[e + x], dp);
-          }
-        }
-        // complete the dot products across the key's four lanes (a DPP quad; every lane runs it)
-        sc += __uint_as_float(dpp32<0xB1>(__float_as_uint(sc), __float_as_uint(sc)));
-        dp += __uint_as_float(dpp32<0xB1>(__float_as_uint(dp), __float_as_uint(dp)));
-        sc += __uint_as_float(dpp32<0x4E>(__float_as_uint(sc), __float_as_uint(sc)));
-        dp += __uint_as_float(dpp32<0x4E>(__float_as_uint(dp), __float_as_uint(dp)));
-        const bool ok = ku < nt && key <= s_qpos[r];
-        const float pr = ok ? exp2f(sc * p.sl2 - s_lse2[r]) : 0.f;
-        const float ds = pr * (dp - s_dl[r]);
-#pragma unroll
-        for (int e = 0; e < DQ; ++e) {
-          dk[e] = fmaf(ds, qv[e], dk[e]);
-          dv[e] = fmaf(pr, gv[e], dv[e]);
-        }
-        if (qc == 0) s_ds[r][ku] = ds;
-      }
-      __syncthreads();
-      // dq partials: thread (row, D/16 head dims) sums ds_u k_u over the tile
-      {
-        constexpr int DPT = D / 16;
-        const int r = tid >> 4, d0 = (tid & 15) * DPT;
-        if (r < nr) {
-          float acc[DPT];
-#pragma unroll
-          for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
-          for (int u = 0; u < nt; ++u) {
-            const float dsu = s_ds[r][u];
-#pragma unroll
-            for (int e = 0; e < DPT; ++e) acc[e] = fmaf(dsu, s_k[u * KP + d0 + e], acc[e]);
-          }
-          float* dqp = p.dq_part + s_pidx[r] * D + d0;
-#pragma unroll
-          for (int e = 0; e < DPT; ++e) dqp[e] = t0 == 0 ? acc[e] : dqp[e] + acc[e];
-        }
-      }
-    }
-    // this item's dk / dv sums for the tile's keys
-    if (ku < nt) {
-      float* dkp = dst + (int64_t)(t0 + ku) * D + qc * DQ;
-      float* dvp = dst + (int64_t)(p.block + t0 + ku) * D + qc * DQ;
-#pragma unroll
-      for (int e = 0; e < DQ; e += 4) {
-        *reinterpret_cast<f32x4*>(dkp + e) = f32x4{dk[e], dk[e + 1], dk[e + 2], dk[e + 3]};
-        *reinterpret_cast<f32x4*>(dvp + e) = f32x4{dv[e], dv[e + 1], dv[e + 2], dv[e + 3]};
-      }
+      pv_acc<D>(sm[cur].ks, d0, d1, dqt);
     }
   }
+  if (g.valid) {
+    const int hsel = p.per_group ? 0 : g.hs - hk * p.G;
+    const int64_t prow = (prow_base + hsel) * p.CT + (g.t - t_base);
+    const int64_t pidx = (prow * p.kslot + g.slot) * p.R + g.rr;
+    store_cols<D>(p.dq_part + pidx * D, dqt, 1.f);
+  }
 }
-
 // dq row (b, t, h) = scale * sum of its selection row's slot partials, in slot
 // order (D/4 lanes per row, four head dims each)
 template <int D>
@@ -1276,34 +1515,6 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(AttnParams p, int64_
   *reinterpret_cast<f32x4*>(p.dq + row * D + li * 4) = acc * p.scale;
 }
 
-// dk / dv of one (b, kv head, block): the items of its buckets summed in
-// (query chunk, item) order; blocks nobody chose get zeros
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(AttnParams p) {
-  const int64_t blk = blockIdx.x;  // (b * Hkv + hk) * Nb + j
-  const int j = (int)(blk % p.Nb);
-  const int64_t bh = blk / p.Nb;
-  const int hk = (int)(bh % p.Hkv), b = (int)(bh / p.Hkv);
-  const int key0 = j * p.block;
-  const int n_keys = min(p.block, p.Lk - key0);
-  for (int i = threadIdx.x; i < n_keys * (D / 4); i += 256) {
-    const int u = i / (D / 4), d4 = (i % (D / 4)) * 4;
-    f32x4 ak = f32x4{0.f, 0.f, 0.f, 0.f}, av = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < p.NC; ++c) {
-      const int64_t bk = (bh * p.NC + c) * p.Nb + j;
-      if (p.grid == 0 || p.counts[bk] == 0) continue;  // no selection entries at all: nothing was built
-      for (int it = p.tile_off[bk]; it < p.tile_off[bk + 1]; ++it) {
-        const float* src = p.dkv_part + (int64_t)it * 2 * p.block * D;
-        ak += *reinterpret_cast<const f32x4*>(src + (int64_t)u * D + d4);
-        av += *reinterpret_cast<const f32x4*>(src + (int64_t)(p.block + u) * D + d4);
-      }
-    }
-    const int64_t orow = (((int64_t)b * p.Lk + key0 + u) * p.Hkv + hk) * D + d4;
-    *reinterpret_cast<f32x4*>(p.dk + orow) = ak * p.scale;
-    *reinterpret_cast<f32x4*>(p.dv + orow) = av;
-  }
-}
-
 bool launch_attn_backward(const AttnParams& p, int64_t nrows_out, hipStream_t s) {
   const int nbk = p.B * p.Hkv * p.NC * p.Nb;
   {
@@ -1319,15 +1530,26 @@ bool launch_attn_backward(const AttnParams& p, int64_t nrows_out, hipStream_t s)
     hipLaunchKernelGGL(bwd_sort_kernel, dim3((unsigned)nbk), dim3(256), 0, s, p, nbk);
   }
   if (!launch_ok("bwd_sort")) return false;
+  {
+    // every (b, kv head, block) unit runs, so that keys nobody attended get zeros
+    LaunchScope ls("attn_bwd_dkv", s);
+    constexpr int W = kBwdKeyWaves;
+    const int nkt = (p.block + 32 * W - 1) / (32 * W);
+    const int64_t groups = (int64_t)p.B * p.Hkv * p.Nb;  // (block, b, kv head); 8 per round, one per XCD
+    const unsigned grid = (unsigned)((groups + 7) / 8 * 8 * nkt);
+    if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkv_kernel<128, W>), dim3(grid), dim3(64 * W), 0, s, p, nkt);
+    else hipLaunchKernelGGL((attn_bwd_dkv_kernel<64, W>), dim3(grid), dim3(64 * W), 0, s, p, nkt);
+  }
+  if (!launch_ok("attn_bwd_dkv")) return false;
   if (p.grid > 0) {
-    LaunchScope ls("attn_bwd", s);
+    LaunchScope ls("attn_bwd_dq", s);
     // grid = the bound on the item count (items are built on the device);
     // workgroups past the built items exit at once
-    const unsigned grid = (unsigned)p.grid;
-    if (p.D == 128) hipLaunchKernelGGL(attn_bwd_kernel<128>, dim3(grid), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(attn_bwd_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+    constexpr int W = kBwdItemRows / 32;
+    if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dq_kernel<128, W>), dim3((unsigned)p.grid), dim3(64 * W), 0, s, p);
+    else hipLaunchKernelGGL((attn_bwd_dq_kernel<64, W>), dim3((unsigned)p.grid), dim3(64 * W), 0, s, p);
   }
-  if (!launch_ok("attn_bwd")) return false;
+  if (!launch_ok("attn_bwd_dq")) return false;
   {
     LaunchScope ls("bwd_dq_reduce", s);
     const int64_t thr = nrows_out * (p.D / 4);
@@ -1335,14 +1557,7 @@ bool launch_attn_backward(const AttnParams& p, int64_t nrows_out, hipStream_t s)
     if (p.D == 128) hipLaunchKernelGGL(bwd_dq_reduce_kernel<128>, dim3(grid), dim3(256), 0, s, p, nrows_out);
     else hipLaunchKernelGGL(bwd_dq_reduce_kernel<64>, dim3(grid), dim3(256), 0, s, p, nrows_out);
   }
-  if (!launch_ok("bwd_dq_reduce")) return false;
-  {
-    LaunchScope ls("bwd_dkv_reduce", s);
-    const unsigned grid = (unsigned)((int64_t)p.B * p.Hkv * p.Nb);
-    if (p.D == 128) hipLaunchKernelGGL(bwd_dkv_reduce_kernel<128>, dim3(grid), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(bwd_dkv_reduce_kernel<64>, dim3(grid), dim3(256), 0, s, p);
-  }
-  return launch_ok("bwd_dkv_reduce");
+  return launch_ok("bwd_dq_reduce");
 }
 
 }  // namespace bsa

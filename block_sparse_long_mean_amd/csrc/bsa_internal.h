@@ -149,13 +149,12 @@ struct AttnParams {
   uint16_t* o;
   int64_t os_b, os_t, os_h;
   float* lse_out;  // natural log, [B, Hq, Lq] or null
-  // backward through the fixed selection (one work item per bucket, entries sorted)
+  // backward through the fixed selection (buckets' entries sorted)
   const uint16_t* dout;
   int64_t dos_b, dos_t, dos_h;
   const float* lse_in;      // [B, Hq, Lq] natural log
   float* delta;             // [B, Hq, Lq]: dout . o per row
   float* dq_part;           // [rows * kslot * R, D]: sum over the slot's keys of ds * k
-  float* dkv_part;          // [items, 2, block, D]: per item, sum over its rows of ds * q and p * dout
   const int32_t* counts;    // entries per bucket
   float* dq;                // [B, Lq, Hq, D]
   float* dk;                // [B, Lk, Hkv, D]
@@ -165,8 +164,11 @@ struct AttnParams {
 int gather_waves(int block);  // waves per gather workgroup for this block size
 bool launch_attn_gather(const AttnParams& p, hipStream_t s);
 bool launch_attn_merge(const AttnParams& p, hipStream_t s);
-// backward: delta, per-bucket entry sort, gradient partials, ordered reductions
+// backward: delta, per-bucket entry sort, dk / dv per key, dq partials per
+// (row, slot), the ordered dq reduction
 constexpr int kBwdSortCap = 8192;  // entries per bucket the LDS sort holds
+constexpr int kBwdKeyWaves = 4;    // dk / dv workgroups: 32 keys per wave
+constexpr int kBwdItemRows = 256;  // dq work items: 32 rows per wave of 8
 bool launch_attn_backward(const AttnParams& p, int64_t nrows_out, hipStream_t s);
 
 struct AttnF32Params {

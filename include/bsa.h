@@ -240,9 +240,11 @@ bsa_status bsa_block_summary(const bsa_summary_args* a, void* workspace, size_t 
  * q and k are the attended tensors (after RoPE when the forward applied it;
  * the rotation's own backward is the caller's).  o, lse and sel are the
  * forward call's outputs (sel entries -1 or in [0, Nb); entries outside that
- * range are skipped).  bf16 inputs, fp32 outputs, fp32 arithmetic; outputs
- * are bitwise deterministic (the rows that chose a block are summed in a
- * fixed order).
+ * range are skipped).  bf16 inputs, fp32 outputs; the five products run on
+ * bf16 MFMA with fp32 accumulation (p and ds rounded to bf16 as operands),
+ * the softmax terms in fp32.  Outputs are bitwise deterministic: the rows
+ * that chose a block are summed in a fixed order (query chunk, then the
+ * sorted selection entries), a row's slots in slot order.
  */
 typedef struct bsa_backward_args {
     int32_t dtype;                 /* BSA_DTYPE_BF16 */

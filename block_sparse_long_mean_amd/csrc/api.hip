@@ -512,8 +512,9 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
 // decode plan
 // ---------------------------------------------------------------------------
 struct DecodePlan {
-  int Nb, Hs, G, topk, umax, sel_w;
-  float* scores;
+  int Nb, Hs, G, topk, umax, sel_w, nshare;
+  uint64_t* skeys;
+  int32_t* scnt;
   int32_t* sel;
   int32_t *ulist, *ucount;
   float *part_o, *part_lse;
@@ -555,7 +556,9 @@ static bsa_status plan_decode(const bsa_decode_args* a, DecodePlan& P, char* ws)
   Carver c;
   c.base = ws;
   const int64_t nrows = (int64_t)a->B * P.Hs;
-  P.scores = c.take<float>(nrows * P.Nb);
+  P.nshare = (P.Nb + kDecShare - 1) / kDecShare;
+  P.skeys = c.take<uint64_t>(nrows * P.nshare * std::max(P.topk, 1));
+  P.scnt = c.take<int32_t>(nrows * P.nshare);
   P.sel = a->sel_out ? a->sel_out : c.take<int32_t>(nrows * P.sel_w);
   P.ulist = c.take<int32_t>((int64_t)a->B * a->Hkv * P.umax);
   P.ucount = c.take<int32_t>((int64_t)a->B * a->Hkv);
@@ -585,7 +588,7 @@ static bsa_status run_decode(const bsa_decode_args* a, void* ws, size_t ws_bytes
   g.q = reinterpret_cast<const uint16_t*>(a->q); g.qs_b = a->q_stride[0]; g.qs_h = a->q_stride[1];
   g.pooled = a->pooled; g.pooled_bf16 = a->pooled_dtype == BSA_DTYPE_BF16;
   g.ps_b = a->p_stride[0]; g.ps_j = a->p_stride[1]; g.ps_h = a->p_stride[2];
-  g.scores = P.scores; g.sel = P.sel; g.ulist = P.ulist; g.ucount = P.ucount; g.umax = P.umax;
+  g.nshare = P.nshare; g.skeys = P.skeys; g.scnt = P.scnt; g.sel = P.sel; g.ulist = P.ulist; g.ucount = P.ucount; g.umax = P.umax;
   if (!launch_decode_gate(g, s)) return BSA_ERR_HIP;
   DecodeAttnParams d;
   d.B = a->B; d.Lc = a->Lc; d.Hq = a->Hq; d.Hkv = a->Hkv; d.G = P.G; d.D = a->D; d.block = a->block; d.Hs = P.Hs;

@@ -218,12 +218,15 @@ struct DecodeGateParams {
   const void* pooled;  // [B, Nb, Hkv, D] summaries, bf16 or fp32
   int pooled_bf16;
   int64_t ps_b, ps_j, ps_h;
-  float* scores;  // [B, Hs, Nb] workspace
+  int nshare;          // candidate shares of kDecShare blocks (over the longest sequence)
+  uint64_t* skeys;     // [B, Hs, nshare, topk] each share's best keys, descending (workspace)
+  int32_t* scnt;       // [B, Hs, nshare] their counts
   int32_t* sel;   // [B, Hs, sel_w]
   int32_t* ulist;  // [B * Hkv, umax] union of a (b, kv head)'s rows (j << 8 | head mask)
   int32_t* ucount; // [B * Hkv]
   int umax;
 };
+constexpr int kDecShare = 2048;  // decode gate: candidate blocks per pass-1 workgroup
 bool launch_decode_gate(const DecodeGateParams& p, hipStream_t s);
 bool launch_decode_attend(const DecodeAttnParams& p, hipStream_t s);
 bool launch_decode_combine(const DecodeAttnParams& p, hipStream_t s);

@@ -22,21 +22,78 @@ BSA_DEV int dec_len(const DecodeAttnParams& p, int b) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode gate, pass 1: stream the routing keys once.  A wave scores 16
-// summary rows per step on a 16x16x32 bf16 MFMA: A = 16 rows x 32 head dims
-// (lanes read 16-byte pieces, four lanes per row per step), B = the group's
-// query heads as columns (G of 16 used; per group their fp32 sum, split into
-// bf16 hi + lo).  bf16 summaries times bf16 queries are exact products; fp32
-// summaries are split into hi + lo as well.  Writes fp32 scores [B, Hs, Nb].
-template <typename PT, int D>
+// Decode gate, pass 1: stream the routing keys once and keep, per selection
+// row, the top-k of each share of kDecShare candidates.  One workgroup per
+// (share, b, kv head): its waves score 64 summary rows per step on 16x16x32
+// bf16 MFMAs -- A = 16 rows x 32 head dims (lanes read 16-byte pieces, four
+// lanes per row per step), B = the group's query heads as columns (G of 16
+// used; per group their fp32 sum, split into bf16 hi + lo).  bf16 summaries
+// times bf16 queries are exact products; fp32 summaries are split into hi +
+// lo as well.  The scores stay in LDS; a wave per row then keeps the share's
+// best keys by (score desc, index asc) -- a threshold filter (the k-th best
+// of the lanes' maxima bounds the share's k-th best from below) plus an LDS
+// buffer compacted by a wave-wide bitonic sort -- and writes them, sorted,
+// to the workspace.
+constexpr int kDecCap = 128;     // key buffer per wave: topk (<= 64) kept + 64 new
+
+template <int V>
+BSA_DEV void lds_row_topk(const float* sc, int j0, int nc, uint64_t* buf, int* cnt, uint64_t* thr, int topk) {
+  constexpr int U = kDecShare / 64;
+  const int lane = lane_id();
+  float sv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = u * 64 + lane;
+    sv[u] = i < nc ? sc[i] : 0.f;
+  }
+  // starting threshold: the k-th best of the 64 lanes' maxima
+  uint64_t lm[1] = {0ull};
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = u * 64 + lane;
+    const uint64_t key = i < nc ? make_key(sv[u], (uint32_t)(j0 + i)) : 0ull;
+    lm[0] = key > lm[0] ? key : lm[0];
+  }
+  wave_sort_desc<1>(lm);
+  const uint64_t tk = shfl64(lm[0], topk - 1);
+  if (lane == 0 && tk > 0ull) *thr = tk - 1ull;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = u * 64 + lane;
+    const uint64_t key = i < nc ? make_key(sv[u], (uint32_t)(j0 + i)) : 0ull;
+    const bool hit = key > *thr;
+    const uint64_t m = __ballot(hit);
+    if (m) {
+      const int c = *cnt;
+      if (hit) buf[c + __popcll(m & ((1ull << lane) - 1ull))] = key;
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 0) *cnt = c + __popcll(m);
+      __builtin_amdgcn_wave_barrier();
+      if (*cnt > kDecCap - 64) row_compact<V>(buf, cnt, thr, topk);
+    }
+  }
+  row_compact<V>(buf, cnt, thr, topk);
+}
+
+template <typename PT, int D, int NR>
 __global__ __launch_bounds__(256) void decode_scores_kernel(DecodeGateParams p) {
   constexpr int KS = D / 32;
-  constexpr int ROWS_PER_WAVE = 64;  // 4 MFMA row tiles
-  const int bh = blockIdx.y;
+  __shared__ float s_sc[NR][kDecShare];
+  __shared__ uint64_t s_buf[4][kDecCap];
+  __shared__ int s_cnt[4];
+  __shared__ uint64_t s_thr[4];
+  const int bh = blockIdx.y, share = blockIdx.x;
   const int b = bh / p.Hkv, hk = bh % p.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, kq = lane >> 4;
   const int nq = p.per_group ? 1 : p.G;
+  int n = p.lens ? p.lens[b] : p.Lc;
+  n = n < 1 ? 1 : (n > p.Lc ? p.Lc : n);
+  const int cur = (n - 1) / p.block;  // candidates: blocks before the token's own
+  const int j0 = share * kDecShare;
+  const int nc = min(kDecShare, cur - j0);
+  if (nc <= 0 || p.topk <= 0) return;  // uniform
   // B operand: column `col` = query head (or the group sum) for k = 8*kq + 32*ks
   // (each lane's 8 consecutive head dims come in one 16-byte load per head)
   bf16x8 qh[KS], ql[KS];
@@ -67,202 +124,172 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(DecodeGateParams p) 
       ql[ks][e] = l;
     }
   }
-  const int j0 = (blockIdx.x * 4 + w) * ROWS_PER_WAVE;
   const PT* base = reinterpret_cast<const PT*>(p.pooled) + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h;
-  // A operands for 4 row tiles, all loads issued before the MFMAs
-  u32x4 raw[4][KS][sizeof(PT) / 2];
+  // wave w scores 64-row steps w, w + 4, ... of the share; the A operands
+  // of the next step (4 row tiles) are loaded while the current one is
+  // computed
+  u32x4 raw[4][KS][sizeof(PT) / 2], nxt[4][KS][sizeof(PT) / 2];
+  auto fetch = [&](int c0, u32x4 (&dst)[4][KS][sizeof(PT) / 2]) {
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int j = j0 + rt * 16 + col;
+    for (int rt = 0; rt < 4; ++rt) {
+      const int i = c0 + rt * 16 + col;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int hpart = 0; hpart < (int)(sizeof(PT) / 2); ++hpart) {
-        raw[rt][ks][hpart] = u32x4{0u, 0u, 0u, 0u};
-        if (j < p.Nb)
-          raw[rt][ks][hpart] = *reinterpret_cast<const u32x4*>(base + (int64_t)j * p.ps_j + ks * 32 + kq * 8 + hpart * 4);
-      }
-  }
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (sizeof(PT) == 2) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, raw[rt][ks][0]);
-        acc = mfma16(a, qh[ks], acc);
-        if (p.per_group) acc = mfma16(a, ql[ks], acc);
-      } else {
-        bf16x8 ah, al;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = __uint_as_float(raw[rt][ks][e >> 2][e & 3]);
-          __bf16 h, l;
-          split_bf(x, h, l);
-          ah[e] = h;
-          al[e] = l;
+        for (int hpart = 0; hpart < (int)(sizeof(PT) / 2); ++hpart) {
+          dst[rt][ks][hpart] = u32x4{0u, 0u, 0u, 0u};
+          if (i < nc)
+            dst[rt][ks][hpart] =
+                *reinterpret_cast<const u32x4*>(base + (int64_t)(j0 + i) * p.ps_j + ks * 32 + kq * 8 + hpart * 4);
         }
-        acc = mfma16(ah, qh[ks], acc);
-        acc = mfma16(al, qh[ks], acc);
-        if (p.per_group) acc = mfma16(ah, ql[ks], acc);
-      }
     }
-    // result: lane holds column `col` (query head) of rows 4*kq + i
-    if (col < nq) {
-      const int hs = p.per_group ? hk : hk * p.G + col;
-      float* out = p.scores + ((int64_t)b * p.Hs + hs) * p.Nb;
+  };
+  if (w * 64 < nc) fetch(w * 64, nxt);
+  for (int c0 = w * 64; c0 < nc; c0 += 256) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = j0 + rt * 16 + 4 * kq + i;
-        if (j < p.Nb) out[j] = acc[i];
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int hpart = 0; hpart < (int)(sizeof(PT) / 2); ++hpart) raw[rt][ks][hpart] = nxt[rt][ks][hpart];
+    if (c0 + 256 < nc) fetch(c0 + 256, nxt);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (sizeof(PT) == 2) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, raw[rt][ks][0]);
+          acc = mfma16(a, qh[ks], acc);
+          if (p.per_group) acc = mfma16(a, ql[ks], acc);
+        } else {
+          bf16x8 ah, al;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = __uint_as_float(raw[rt][ks][e >> 2][e & 3]);
+            __bf16 h, l;
+            split_bf(x, h, l);
+            ah[e] = h;
+            al[e] = l;
+          }
+          acc = mfma16(ah, qh[ks], acc);
+          acc = mfma16(al, qh[ks], acc);
+          if (p.per_group) acc = mfma16(ah, ql[ks], acc);
+        }
+      }
+      // result: lane holds column `col` (query head) of rows 4*kq + i
+      if (col < nq) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_sc[col][c0 + rt * 16 + 4 * kq + i] = acc[i];
       }
     }
+  }
+  __syncthreads();
+  // the share's top-k of each row: wave w takes rows w, w + 4
+  for (int r = w; r < nq; r += 4) {
+    if (lane == 0) {
+      s_cnt[w] = 0;
+      s_thr[w] = 0ull;
+    }
+    __builtin_amdgcn_wave_barrier();
+    lds_row_topk<2>(s_sc[r], j0, nc, s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+    const int cnt = s_cnt[w];
+    const int64_t row = (int64_t)b * p.Hs + (p.per_group ? hk : hk * p.G + r);
+    const int64_t li = row * p.nshare + share;
+    for (int e = lane; e < cnt; e += 64) p.skeys[li * p.topk + e] = s_buf[w][e];
+    if (lane == 0) p.scnt[li] = cnt;
   }
 }
 
-// Union of the selections of one (b, kv head) by one wave: sel[r][s] for
-// rows r < nrow, slots s < w (-1 = none) -> distinct block ids ascending,
-// each with a bit mask of the heads that chose it, packed (j << 8 | mask).
-BSA_DEV int unite_rows(const int32_t (*sel)[65], int nrow, int w, int G, bool per_group, uint64_t* s_v,
-                       int32_t* out) {
-  constexpr int V = 8;  // up to 512 (head, block) pairs
-  const int lane = lane_id();
-  uint64_t v[V];
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int e = i * 64 + lane;
-    uint64_t key = 0ull;
-    if (e < nrow * w) {
-      const int hh = e / w, sl = e % w;
-      const int j = sel[hh][sl];
-      if (j >= 0) key = ~(((uint64_t)(uint32_t)j << 8) | (uint64_t)hh);  // descending ~val = ascending val
-    }
-    v[i] = key;
+// whether the ascending ids row[0 .. w) (then -1 padding) hold j
+BSA_DEV bool row_has(const int32_t* row, int w, int j) {
+  int lo = 0, hi = w;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int x = row[mid];
+    if (x >= 0 && x < j) lo = mid + 1;
+    else hi = mid;
   }
-  wave_sort_desc<V>(v);
-#pragma unroll
-  for (int i = 0; i < V; ++i) s_v[i * 64 + lane] = v[i];
-  __builtin_amdgcn_wave_barrier();
-  // element e starts a run of equal block ids when its id differs from
-  // element e-1's; a run holds at most G entries (one per head)
-  int total = 0;
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int e = i * 64 + lane;
-    const uint64_t key = s_v[e];
-    bool head = false;
-    int val = 0;
-    if (key != 0ull) {
-      const int j = (int)((~key) >> 8);
-      head = e == 0 || (int)((~s_v[e - 1]) >> 8) != j;
-      if (head) {
-        int mask = 0;
-        for (int f = e; f < 64 * V && f < e + 8; ++f) {
-          const uint64_t kf = s_v[f];
-          if (kf == 0ull || (int)((~kf) >> 8) != j) break;
-          mask |= per_group ? ((1 << G) - 1) : (1 << (int)((~kf) & 255));
-        }
-        val = (j << 8) | mask;
-      }
-    }
-    const uint64_t hm = __ballot(head);
-    if (head) out[total + __popcll(hm & ((1ull << lane) - 1ull))] = val;
-    total += __popcll(hm);
-  }
-  return total;
+  return lo < w && row[lo] == j;
 }
 
-// Decode gate, pass 2, and the union, for one (b, kv head) per workgroup.
-// Its 16 waves split the candidates j < cur of the selection rows (G rows
-// per head, one per group): each wave keeps the top-k of its share by (score
-// desc, index asc) -- a threshold filter plus an LDS buffer compacted by a
-// wave-wide bitonic sort -- the shares of a row are merged pairwise, each row
-// is written ascending with the forced own block last, -1 padded, and wave 0
-// unites the rows' blocks for the attention.
-template <int V>
-__global__ __launch_bounds__(1024) void decode_select_kernel(DecodeGateParams p) {
-  constexpr int CAP = 64 * V;
-  constexpr int NW = 16;
-  __shared__ uint64_t s_buf[NW][CAP];
-  __shared__ int s_cnt[NW];
-  __shared__ uint64_t s_thr[NW];
+// Union of the selection rows of one (b, kv head), by the whole workgroup:
+// rows r < nrow of sel hold ascending block ids, then -1.  Each distinct id
+// once, ascending, with the bit mask of the rows (query heads) that chose it,
+// packed (j << 8 | mask).  An id counts at the row that holds it first; its
+// place is the number of such first ids below it.  Returns the count.
+template <int NT>
+BSA_DEV int unite_rows(const int32_t (*sel)[65], int nrow, int w, int G, bool per_group, int32_t* s_first,
+                       int* s_total, int32_t* out) {
+  const int tid = threadIdx.x;
+  const int n = nrow * w;
+  if (tid == 0) *s_total = 0;
+  for (int e = tid; e < n; e += NT) {
+    const int r = e / w;
+    const int j = sel[r][e % w];
+    bool first = j >= 0;
+    for (int r2 = 0; first && r2 < r; ++r2) first = !row_has(sel[r2], w, j);
+    s_first[e] = first ? j : -1;
+  }
+  __syncthreads();
+  for (int e = tid; e < n; e += NT) {
+    const int j = s_first[e];
+    if (j < 0) continue;
+    const int r = e / w;
+    int mask = per_group ? (1 << G) - 1 : 1 << r;
+    if (!per_group)
+      for (int r2 = r + 1; r2 < nrow; ++r2)
+        if (row_has(sel[r2], w, j)) mask |= 1 << r2;
+    int rank = 0;
+    for (int e2 = 0; e2 < n; ++e2) {
+      const int x = s_first[e2];
+      rank += (x >= 0 && x < j) ? 1 : 0;
+    }
+    out[rank] = (j << 8) | mask;
+    atomicAdd(s_total, 1);
+  }
+  __syncthreads();
+  return *s_total;
+}
+
+// Decode gate, pass 2, and the union, for one (b, kv head) per workgroup:
+// wave w merges the share lists of rows w, w + 4 (appended into its LDS
+// buffer, compacted to the best k whenever the next list might not fit),
+// writes each row ascending with the forced own block last, -1 padded; then
+// every thread helps unite the rows' blocks for the attention.
+__global__ __launch_bounds__(256) void decode_select_kernel(DecodeGateParams p) {
+  __shared__ uint64_t s_buf[4][kDecCap];
+  __shared__ int s_cnt[4];
+  __shared__ uint64_t s_thr[4];
   __shared__ int32_t s_sel[8][65];
-  __shared__ uint64_t s_v[512];
+  __shared__ int32_t s_first[512];
+  __shared__ int s_total;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bh = blockIdx.x;
   const int b = bh / p.Hkv, hk = bh % p.Hkv;
   const int nrow = p.per_group ? 1 : p.G;
-  const int wpr = NW / nrow;  // waves per row
-  const int r = w / wpr, q = w % wpr;
-  const bool active = r < nrow;
   int n = p.lens ? p.lens[b] : p.Lc;
   n = n < 1 ? 1 : (n > p.Lc ? p.Lc : n);
   const int cur = (n - 1) / p.block;
-  const int hs = p.per_group ? hk : hk * p.G + (active ? r : 0);
-  const int64_t row = (int64_t)b * p.Hs + hs;
-  if (lane == 0) {
-    s_cnt[w] = 0;
-    s_thr[w] = 0ull;
-  }
-  __builtin_amdgcn_wave_barrier();
-  if (active) {
-    const float* sc = p.scores + row * p.Nb;
-    constexpr int U = 32;  // chunks of 64 candidates loaded together
-    for (int c0 = q * 64 * U; c0 < cur; c0 += wpr * 64 * U) {
-      float sv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = c0 + u * 64 + lane;
-        sv[u] = j < cur ? sc[j] : 0.f;
-      }
-      if (c0 == q * 64 * U && p.topk > 0) {
-        // starting threshold: the k-th best of the 64 lanes' maxima is a
-        // lower bound of the share's k-th best key (k distinct keys reach
-        // it), so only keys at or above it need to enter the buffer
-        uint64_t lm[1] = {0ull};
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int j = c0 + u * 64 + lane;
-          const uint64_t key = j < cur ? make_key(sv[u], (uint32_t)j) : 0ull;
-          lm[0] = key > lm[0] ? key : lm[0];
-        }
-        wave_sort_desc<1>(lm);
-        const uint64_t tk = shfl64(lm[0], p.topk - 1);
-        if (lane == 0 && tk > 0ull) s_thr[w] = tk - 1ull;
-        __builtin_amdgcn_wave_barrier();
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = c0 + u * 64 + lane;
-        const uint64_t key = j < cur ? make_key(sv[u], (uint32_t)j) : 0ull;
-        const bool hit = key > s_thr[w];
-        const uint64_t m = __ballot(hit);
-        if (m) {
-          const int c = s_cnt[w];
-          if (hit) s_buf[w][c + __popcll(m & ((1ull << lane) - 1ull))] = key;
-          __builtin_amdgcn_wave_barrier();
-          if (lane == 0) s_cnt[w] = c + __popcll(m);
-          __builtin_amdgcn_wave_barrier();
-          if (s_cnt[w] > CAP - 64) row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
-        }
-      }
+  const int nsh = p.topk > 0 ? (cur + kDecShare - 1) / kDecShare : 0;
+  for (int r = w; r < nrow; r += 4) {
+    const int64_t row = (int64_t)b * p.Hs + (p.per_group ? hk : hk * p.G + r);
+    if (lane == 0) {
+      s_cnt[w] = 0;
+      s_thr[w] = 0ull;
     }
-    row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
-  }
-  // pairwise merges of a row's shares: wave q absorbs wave q + st (at most
-  // 2k keys, within the buffer), keeps the best k
-  for (int st = 1; st < wpr; st <<= 1) {
-    __syncthreads();
-    if (active && (q % (2 * st)) == 0 && q + st < wpr) {
-      const int c = s_cnt[w], co = s_cnt[w + st];
-      for (int e = lane; e < co; e += 64) s_buf[w][c + e] = s_buf[w + st][e];
+    __builtin_amdgcn_wave_barrier();
+    for (int sh = 0; sh < nsh; ++sh) {
+      const int64_t li = row * p.nshare + sh;
+      const int c = p.scnt[li];
+      if (s_cnt[w] + c > kDecCap) row_compact<2>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+      const int base = s_cnt[w];
+      for (int e = lane; e < c; e += 64) s_buf[w][base + e] = p.skeys[li * p.topk + e];
       __builtin_amdgcn_wave_barrier();
-      if (lane == 0) s_cnt[w] = c + co;
+      if (lane == 0) s_cnt[w] = base + c;
       __builtin_amdgcn_wave_barrier();
-      row_compact<V>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
     }
-  }
-  if (active && q == 0) {
+    row_compact<2>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
     const int cnt = s_cnt[w];
     int idx = lane < cnt ? (int)key_index(s_buf[w][lane]) : 0x7FFFFFFF;
     idx = wave_sort_asc_i32(idx);
@@ -274,32 +301,35 @@ __global__ __launch_bounds__(1024) void decode_select_kernel(DecodeGateParams p)
     }
   }
   __syncthreads();
-  if (w == 0) {
-    const int total = unite_rows(s_sel, nrow, p.sel_w, p.G, p.per_group != 0, s_v, p.ulist + (int64_t)bh * p.umax);
-    if (lane == 0) p.ucount[bh] = total;
-  }
+  const int total = unite_rows<256>(s_sel, nrow, p.sel_w, p.G, p.per_group != 0, s_first, &s_total,
+                                    p.ulist + (int64_t)bh * p.umax);
+  if (threadIdx.x == 0) p.ucount[bh] = total;
 }
 
 bool launch_decode_gate(const DecodeGateParams& p, hipStream_t s) {
   {
     LaunchScope ls("decode_scores", s);
-    const dim3 grid((unsigned)((p.Nb + 255) / 256), (unsigned)(p.B * p.Hkv));  // 4 waves x 64 rows
+    const dim3 grid((unsigned)p.nshare, (unsigned)(p.B * p.Hkv));
+    const int nr = p.per_group ? 1 : (p.G <= 4 ? 4 : 8);
+#define BSA_DEC_SCORES(PT, DD)                                                                               \
+  do {                                                                                                       \
+    if (nr == 1) hipLaunchKernelGGL((decode_scores_kernel<PT, DD, 1>), grid, dim3(256), 0, s, p);            \
+    else if (nr == 4) hipLaunchKernelGGL((decode_scores_kernel<PT, DD, 4>), grid, dim3(256), 0, s, p);       \
+    else hipLaunchKernelGGL((decode_scores_kernel<PT, DD, 8>), grid, dim3(256), 0, s, p);                    \
+  } while (0)
     if (p.pooled_bf16) {
-      if (p.D == 128) hipLaunchKernelGGL((decode_scores_kernel<uint16_t, 128>), grid, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((decode_scores_kernel<uint16_t, 64>), grid, dim3(256), 0, s, p);
+      if (p.D == 128) BSA_DEC_SCORES(uint16_t, 128);
+      else BSA_DEC_SCORES(uint16_t, 64);
     } else {
-      if (p.D == 128) hipLaunchKernelGGL((decode_scores_kernel<float, 128>), grid, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((decode_scores_kernel<float, 64>), grid, dim3(256), 0, s, p);
+      if (p.D == 128) BSA_DEC_SCORES(float, 128);
+      else BSA_DEC_SCORES(float, 64);
     }
+#undef BSA_DEC_SCORES
   }
   if (!launch_ok("decode_scores")) return false;
   {
     LaunchScope ls("decode_select", s);
-    const unsigned grid = (unsigned)(p.B * p.Hkv);
-    if (2 * p.topk + 64 <= 128)
-      hipLaunchKernelGGL(decode_select_kernel<2>, dim3(grid), dim3(1024), 0, s, p);
-    else
-      hipLaunchKernelGGL(decode_select_kernel<4>, dim3(grid), dim3(1024), 0, s, p);
+    hipLaunchKernelGGL(decode_select_kernel, dim3((unsigned)(p.B * p.Hkv)), dim3(256), 0, s, p);
   }
   return launch_ok("decode_select");
 }

@@ -260,3 +260,11 @@ BSA_DEV void rope_sincos(int pos, double omega, float& c, float& s) {
   const float af = (float)a;
   sincosf(af, &s, &c);
 }
+
+// The same in double precision throughout.
+BSA_DEV void rope_sincos_d(int pos, double omega, double& c, double& s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double a = (double)pos * omega;
+  a -= two_pi * rint(a * (1.0 / two_pi));
+  sincos(a, &s, &c);
+}

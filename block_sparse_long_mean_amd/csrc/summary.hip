@@ -194,12 +194,42 @@ __global__ __launch_bounds__(256) void block_summary_kernel(SummaryParams p, int
     load_rows(s0, s0 + ns, lo, hi);
     if constexpr (ROPE) {
       __syncthreads();  // the previous sub-block's table is no longer read
-      for (int idx = tid; idx < ns * HALF; idx += 256) {
-        const int tt = idx / HALF, i = idx % HALF;
-        float cc, ss;
-        rope_sincos(p.pos[(int64_t)b * p.L + t0 + s0 + tt], p.omega[i], cc, ss);
-        s_cos[tt][i] = cc;
-        s_sin[tt][i] = ss;
+      // the rotation table, by one wave: lane i walks the sub-block's tokens
+      // for frequency i in double precision -- the first token's angle
+      // reduced and evaluated directly, every next one by a rotation through
+      // omega_i when its position is the previous one + 1 (exactly 1, 0 at a
+      // document start, directly again after any other jump) -- and rounds
+      // each (cos, sin) to fp32 once
+      if (tid < 64) {
+        // lane tt of wave 0 holds token tt's position (ns <= SUB = 64)
+        const int pl = tid < ns ? p.pos[(int64_t)b * p.L + t0 + s0 + tid] : 0;
+        if (tid < HALF) {
+          const int i = tid;
+          const double om = p.omega[i];
+          double sd, cd;
+          sincos(om, &sd, &cd);
+          double cv, sv;
+          int prev = __builtin_amdgcn_readfirstlane(pl);
+          rope_sincos_d(prev, om, cv, sv);
+          s_cos[0][i] = (float)cv;
+          s_sin[0][i] = (float)sv;
+          for (int tt = 1; tt < ns; ++tt) {
+            const int ps = __builtin_amdgcn_readlane(pl, tt);
+            if (ps == prev + 1) {
+              const double c2 = cv * cd - sv * sd;
+              sv = fma(sv, cd, cv * sd);
+              cv = c2;
+            } else if (ps == 0) {
+              cv = 1.0;
+              sv = 0.0;
+            } else {
+              rope_sincos_d(ps, om, cv, sv);
+            }
+            prev = ps;
+            s_cos[tt][i] = (float)cv;
+            s_sin[tt][i] = (float)sv;
+          }
+        }
       }
       __syncthreads();
     }

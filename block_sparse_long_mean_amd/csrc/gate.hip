@@ -235,8 +235,16 @@ BSA_DEV uint64_t list_kth(const uint64_t (&L)[KR], int lane, int topk) {
 
 // FS: the summaries come as fp32 (p_f32) and are split into the hi / lo
 // planes as each chunk is staged in LDS (LO is then true)
+// Occupancy requested per instantiation (workgroups of W waves per CU), set
+// to what its register use reaches: four waves per SIMD for one 16-key list
+// over 64-wide summaries, three over 128-wide ones, no request otherwise.
+template <int W, int DG, int KR>
+constexpr int gate_min_blocks() {
+  return W == 4 && KR == 1 ? (DG == 64 ? 4 : 3) : 1;
+}
+
 template <int W, int DG, int KR, int QK, bool LO, bool FS>
-__global__ __launch_bounds__(64 * W, KR == 1 ? 4 : 1) void gate_kernel(GateParams p) {
+__global__ __launch_bounds__(64 * W, (gate_min_blocks<W, DG, KR>())) void gate_kernel(GateParams p) {
   constexpr int ROWS = 16 * W;
   constexpr int PADR = DG + 8;  // padded LDS row (bf16 elements)
   constexpr int KS = DG / 32;

@@ -670,7 +670,10 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
 // probability by v_readlane.  Rows go two at a time; the partials have the
 // gather's format.
 template <int D>
-__global__ __launch_bounds__(256) void attn_sparse_kernel(AttnParams p) {
+// four workgroups per CU (four waves per SIMD): each wave's item is a
+// chain of dependent loads (queries, the key rows, the values), so the
+// number of items in flight sets the bandwidth
+__global__ __launch_bounds__(256, 4) void attn_sparse_kernel(AttnParams p) {
   constexpr int NR = 2;        // rows per pass (most sparse buckets hold one or two)
   constexpr int DPL = D / 64;  // head dims per lane (values)
   __shared__ __attribute__((aligned(16))) float s_q[4][NR][D];
@@ -720,38 +723,47 @@ __global__ __launch_bounds__(256) void attn_sparse_kernel(AttnParams p) {
       const int key = k0 + lane;
       const bool kv = key < n_keys;
       const uint16_t* krow = kb + (int64_t)(key0 + (kv ? key : 0)) * p.ks_t;
-      // scores of this lane's key against the rows, 8 head dims at a time
+      // scores of this lane's key against the rows: the whole key row is
+      // loaded at once (D/8 16-byte pieces in flight together)
       float sc[NR];
 #pragma unroll
       for (int a = 0; a < NR; ++a) sc[a] = 0.f;
-      // four 16-byte pieces of the key row at a time, the next four in flight
-      u16x8 kx[4], kn[4];
+      u16x8 kx[D / 8];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kx[c] = kv ? ld16(krow + c * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 1
-      for (int c0 = 0; c0 < D / 8; c0 += 4) {
+      for (int c = 0; c < D / 8; ++c) kx[c] = kv ? ld16(krow + c * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          kn[c] = (kv && c0 + 4 < D / 8) ? ld16(krow + (c0 + 4 + c) * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int c = 0; c < D / 8; ++c) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int a = 0; a < NR; ++a) {
+          const f32x4 q0 = *reinterpret_cast<const f32x4*>(&s_q[w][a][c * 8]);
+          const f32x4 q1 = *reinterpret_cast<const f32x4*>(&s_q[w][a][c * 8 + 4]);
+          float part = sc[a];
 #pragma unroll
-          for (int a = 0; a < NR; ++a) {
-            const f32x4 q0 = *reinterpret_cast<const f32x4*>(&s_q[w][a][(c0 + c) * 8]);
-            const f32x4 q1 = *reinterpret_cast<const f32x4*>(&s_q[w][a][(c0 + c) * 8 + 4]);
-            float part = sc[a];
+          for (int e = 0; e < 4; ++e) part = fmaf(q0[e], bf2f(kx[c][e]), part);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) part = fmaf(q0[e], bf2f(kx[c][e]), part);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) part = fmaf(q1[e], bf2f(kx[c][4 + e]), part);
-            sc[a] = part;
-          }
+          for (int e = 0; e < 4; ++e) part = fmaf(q1[e], bf2f(kx[c][4 + e]), part);
+          sc[a] = part;
         }
+        // the step's sums are complete before the next step's query reads
+        // (so that not all NR x D query values are read ahead and held)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kx[c] = kn[c];
+        for (int a = 0; a < NR; ++a) asm volatile("" : "+v"(sc[a])::"memory");
       }
-      // this pass's values: lane owns head dims lane*DPL .. +DPL-1 of every key
+      // this pass's values: lane owns head dims lane*DPL .. +DPL-1 of every
+      // key; 16 keys' values per batch, the next batch in flight while the
+      // current one is used
       const int nk = min(64, n_keys - k0);
+      const uint16_t* vr0 = vb + (int64_t)(key0 + k0) * p.vs_t + lane * DPL;
+      auto load_v = [&](int kk0, uint32_t (&vx)[16]) {
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const int kq = kk0 + kk;
+          const uint16_t* vr = vr0 + (int64_t)(kq < nk ? kq : 0) * p.vs_t;
+          vx[kk] = kq < nk ? (DPL == 2 ? *reinterpret_cast<const uint32_t*>(vr) : (uint32_t)*vr) : 0u;
+        }
+      };
+      uint32_t vcur[16], vnext[16];
+      load_v(0, vnext);
       float pr[NR];
 #pragma unroll
       for (int a = 0; a < NR; ++a) {
@@ -766,18 +778,14 @@ __global__ __launch_bounds__(256) void attn_sparse_kernel(AttnParams p) {
         pr[a] = e0;
       }
       for (int kk0 = 0; kk0 < nk; kk0 += 16) {
-        uint32_t vx[16];
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-          const int kq = kk0 + kk;
-          const uint16_t* vr = vb + (int64_t)(key0 + k0 + (kq < nk ? kq : 0)) * p.vs_t + lane * DPL;
-          vx[kk] = kq < nk ? (DPL == 2 ? *reinterpret_cast<const uint32_t*>(vr) : (uint32_t)*vr) : 0u;
-        }
+        for (int kk = 0; kk < 16; ++kk) vcur[kk] = vnext[kk];
+        if (kk0 + 16 < nk) load_v(kk0 + 16, vnext);
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
           const int kq = kk0 + kk;
           if (kq < nk) {  // wave-uniform
-            const float v0 = bf2f((uint16_t)(vx[kk] & 0xFFFFu)), v1 = bf2f((uint16_t)(vx[kk] >> 16));
+            const float v0 = bf2f((uint16_t)(vcur[kk] & 0xFFFFu)), v1 = bf2f((uint16_t)(vcur[kk] >> 16));
 #pragma unroll
             for (int a = 0; a < NR; ++a) {
               const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr[a]), kq));

@@ -375,7 +375,7 @@ BSA_DEV void pv_bases(const uint16_t* tile, uint32_t (&vbase)[D / 32]) {
 // product uses -- comes from four more MFMAs with an all-ones A operand and is
 // added to l.
 template <int D>
-BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, f32x16 (&o)[D / 32], bool first,
+BSA_DEV void pv_tile(const uint16_t* vt, const f32x16& p0, const f32x16& p1, f32x16 (&o)[D / 32], bool first,
                      float& l) {
   bf16x8 pb[4];
 #pragma unroll
@@ -394,7 +394,7 @@ BSA_DEV void pv_tile(const AttnSmem<D>& sm, const f32x16& p0, const f32x16& p1, 
     l += rsum[0];
   }
   uint32_t vbase[D / 32];
-  pv_bases<D>(sm.v, vbase);
+  pv_bases<D>(vt, vbase);
   pv_steps<0, D>(vbase, pb, o, first);
 }
 
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
           }
         }
         softmax_update<D>(s0, s1, m, l, o, p.sl2, kt0 == 0);
-        pv_tile<D>(sm[cur], s0, s1, o, kt0 == 0, l);
+        pv_tile<D>(sm[cur].v, s0, s1, o, kt0 == 0, l);
       }
     }
     // epilogue: pack this item's outputs, take the next item's queries out of
@@ -1566,6 +1566,107 @@ bool launch_attn_backward(const AttnParams& p, int64_t nrows_out, hipStream_t s)
     else hipLaunchKernelGGL(bwd_dq_reduce_kernel<64>, dim3(grid), dim3(256), 0, s, p, nrows_out);
   }
   return launch_ok("bwd_dq_reduce");
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention on MFMA: one wave per distinct (b, kv head, block) of the
+// decode's union, for every query head of the group at once.  S^T = K Q^T on
+// v_mfma_f32_32x32x16_bf16 with the keys as rows -- each lane loads its key
+// row's 16-byte pieces straight into the A operand (a block of one kv head is
+// contiguous in a head-major cache, so one load instruction reads 1 KB) --
+// and the group's query heads as columns (G of 32 used).  Online softmax per
+// column as in the gather; O^T += V^T P^T with each 64-key tile of values
+// copied by DMA into LDS (pieces permuted) and read transposed, the next
+// tile's copy in flight while the current one is used.  Writes each chosen
+// head's normalised partial and its log2-domain log-sum-exp, as the combine
+// reads them.
+template <int D>
+__global__ __launch_bounds__(64) void decode_attend_mfma_kernel(DecodeAttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[KT * D];
+  const int bh = blockIdx.x / p.umax, u = blockIdx.x % p.umax;
+  if (u >= p.ucount[bh]) return;  // uniform
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int ent = p.ulist[(int64_t)bh * p.umax + u];
+  const int j = ent >> 8, mask = ent & 255;
+  int n = p.lens ? p.lens[b] : p.Lc;
+  n = n < 1 ? 1 : (n > p.Lc ? p.Lc : n);
+  const int ka = j * p.block;
+  int nk = min(p.block, n - ka);
+  int64_t ko, vo;
+  if (p.table) {
+    const int pg = p.table[(int64_t)b * p.table_w + j];
+    if (pg < 0 || pg >= p.num_pages) nk = 0;  // no keys: nothing is read
+    ko = (int64_t)pg * p.ks_b;
+    vo = (int64_t)pg * p.vs_b;
+  } else {
+    ko = (int64_t)b * p.ks_b + (int64_t)ka * p.ks_t;
+    vo = (int64_t)b * p.vs_b + (int64_t)ka * p.vs_t;
+  }
+  // the block's first key and value row
+  const uint16_t* kb = p.k + ko + (int64_t)hk * p.ks_h;
+  const uint16_t* vb = p.v + vo + (int64_t)hk * p.vs_h;
+  const int lane = lane_id(), col = lane & 31, h = lane >> 5;
+  // B operand: column col = query head hk * G + col (zero past G)
+  bf16x8 qf[D / 16];
+  load_qf<D>(p.q + (int64_t)b * p.qs_b + (int64_t)(hk * p.G + (col < p.G ? col : 0)) * p.qs_h, col < p.G, qf);
+  float m = -INFINITY, l = 0.f;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+  constexpr int NV = KT * D / 8 / 64;  // DMA instructions per value tile
+  for (int t0 = 0; t0 < nk; t0 += KT) {
+    const int nt = min(KT, nk - t0);
+    // the tile's values by DMA into LDS (the previous tile's P.V, which read
+    // the buffer, waited for its own reads) and its keys straight into the A
+    // operand (lane: key 32 mt + col, head dims 16 s + 8 h), all in flight
+    // together
+#pragma unroll
+    for (int i = 0; i < NV; ++i) dma_rows<D, false>(s_v, vb, p.vs_t, t0, nt, i);
+    bf16x8 kf[2][D / 16];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int key = 32 * mt + col;
+      const uint16_t* kr = kb + (int64_t)(t0 + (key < nt ? key : 0)) * p.ks_t + 8 * h;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
+        kf[mt][st] = as_bf(key < nt ? ld16(kr + 16 * st) : u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+    }
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      s0 = mfma32(kf[0][st], qf[st], s0);
+      s1 = mfma32(kf[1][st], qf[st], s1);
+    }
+    if (nt < KT) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kr = krow(i, h);
+        s0[i] = kr < nt ? s0[i] : -INFINITY;
+        s1[i] = kr + 32 < nt ? s1[i] : -INFINITY;
+      }
+    }
+    softmax_update<D>(s0, s1, m, l, o, p.sl2, t0 == 0);
+    // the values' copy must have landed: the compiler may order the copy
+    // after the key loads, so their wait does not cover it
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    pv_tile<D>(s_v, s0, s1, o, t0 == 0, l);
+  }
+  if (col < p.G && ((mask >> col) & 1)) {
+    const int64_t pidx = ((int64_t)bh * p.umax + u) * p.G + col;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    store_cols<D>(p.part_o + pidx * D, o, inv);
+    if (h == 0) p.part_lse[pidx] = l > 0.f ? m + __log2f(l) : -INFINITY;
+  }
+}
+
+bool launch_decode_attend_mfma(const DecodeAttnParams& p, hipStream_t s) {
+  const unsigned grid = (unsigned)(p.B * p.Hkv * p.umax);
+  {
+    LaunchScope ls("decode_attend", s);
+    if (p.D == 128) hipLaunchKernelGGL(decode_attend_mfma_kernel<128>, dim3(grid), dim3(64), 0, s, p);
+    else hipLaunchKernelGGL(decode_attend_mfma_kernel<64>, dim3(grid), dim3(64), 0, s, p);
+  }
+  return launch_ok("decode_attend");
 }
 
 }  // namespace bsa

@@ -229,6 +229,7 @@ struct DecodeGateParams {
 constexpr int kDecShare = 2048;  // decode gate: candidate blocks per pass-1 workgroup
 bool launch_decode_gate(const DecodeGateParams& p, hipStream_t s);
 bool launch_decode_attend(const DecodeAttnParams& p, hipStream_t s);
+bool launch_decode_attend_mfma(const DecodeAttnParams& p, hipStream_t s);  // attn.hip
 bool launch_decode_combine(const DecodeAttnParams& p, hipStream_t s);
 
 void set_error(const std::string& msg);

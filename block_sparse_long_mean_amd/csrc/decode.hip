@@ -334,181 +334,6 @@ bool launch_decode_gate(const DecodeGateParams& p, hipStream_t s) {
   return launch_ok("decode_select");
 }
 
-// One workgroup per (b, kv head, distinct block): scores for the heads that
-// chose the block, softmax over its keys, weighted sum of its values.
-template <int D, int NH>
-__global__ __launch_bounds__(256) void decode_attend_kernel(DecodeAttnParams p) {
-  constexpr int KC = 64;  // keys per pass (a small pass keeps registers low: 4 waves per SIMD)
-  constexpr int CH = D / 8;
-  constexpr int KG = 256 / CH;  // key groups in the value pass
-  __shared__ float s_q[8][D];
-  __shared__ float s_s[8][KC];
-  __shared__ float s_m[8], s_l[8], s_c[8];
-  __shared__ float s_red[KG][D];
-  __shared__ int s_heads[8];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int bh = blockIdx.x / p.umax, u = blockIdx.x % p.umax;
-  if (u >= p.ucount[bh]) return;  // uniform for the workgroup, before any barrier
-  const int b = bh / p.Hkv, hk = bh % p.Hkv;
-  const int ent = p.ulist[(int64_t)bh * p.umax + u];
-  const int j = ent >> 8, mask = ent & 255;
-  int nh = 0;
-  for (int hh = 0; hh < p.G; ++hh)
-    if (mask & (1 << hh)) nh++;
-  if (tid == 0) {
-    int c = 0;
-    for (int hh = 0; hh < p.G; ++hh)
-      if (mask & (1 << hh)) s_heads[c++] = hh;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < nh * D; idx += 256) {
-    const int a = idx / D, d = idx % D;
-    const int hq = hk * p.G + s_heads[a];
-    s_q[a][d] = bf2f(p.q[(int64_t)b * p.qs_b + (int64_t)hq * p.qs_h + d]);
-  }
-  if (tid < 8) {
-    s_m[tid] = -INFINITY;
-    s_l[tid] = 0.f;
-  }
-  const int n = dec_len(p, b);
-  const int ka = j * p.block;
-  int ke = min(ka + p.block, n);
-  // kb / vb: the block's first key and value row (token ka of sequence b)
-  int64_t ko, vo;
-  if (p.table) {
-    const int pg = p.table[(int64_t)b * p.table_w + j];
-    if (pg < 0 || pg >= p.num_pages) ke = ka;  // no keys: the sequence's output is undefined, nothing is read
-    ko = (int64_t)pg * p.ks_b;
-    vo = (int64_t)pg * p.vs_b;
-  } else {
-    ko = (int64_t)b * p.ks_b + (int64_t)ka * p.ks_t;
-    vo = (int64_t)b * p.vs_b + (int64_t)ka * p.vs_t;
-  }
-  const uint16_t* kb = p.k + ko + (int64_t)hk * p.ks_h;
-  const uint16_t* vb = p.v + vo + (int64_t)hk * p.vs_h;
-  const int dc = tid % CH, kg = tid / CH;
-  float acc[NH][8];
-#pragma unroll
-  for (int a = 0; a < NH; ++a)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
-  __syncthreads();
-
-  constexpr int KPG = KC / KG;
-  for (int k0 = ka; k0 < ke; k0 += KC) {
-    const int nk = min(KC, ke - k0);
-    // this chunk's values, loaded now so they are in flight with the keys
-    u16x8 vx[KPG];
-#pragma unroll
-    for (int kk = 0; kk < KPG; ++kk) {
-      const int key = kg * KPG + kk;
-      vx[kk] = key < nk ? ld16(vb + (int64_t)(k0 - ka + key) * p.vs_t + dc * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-    // scores: 16 lanes per key row (8 head dims each), 16 rows per pass;
-    // the partial dot products are summed across the row's 16 lanes
-    {
-      constexpr int CPR = D / 8;   // lanes per key row
-      constexpr int RPP = 256 / CPR;  // rows per pass
-      const int c = tid % CPR, rsub = tid / CPR;
-      float qv[NH][8];
-#pragma unroll
-      for (int a = 0; a < NH; ++a)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[a][e] = a < nh ? s_q[a][c * 8 + e] : 0.f;
-      u16x8 kx[KC / RPP];
-#pragma unroll
-      for (int ps = 0; ps < KC / RPP; ++ps) {
-        const int key = ps * RPP + rsub;
-        kx[ps] = key < nk ? ld16(kb + (int64_t)(k0 - ka + key) * p.ks_t + c * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int ps = 0; ps < KC / RPP; ++ps) {
-        const int key = ps * RPP + rsub;
-        float part[NH];
-#pragma unroll
-        for (int a = 0; a < NH; ++a) {
-          part[a] = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) part[a] = fmaf(qv[a][e], bf2f(kx[ps][e]), part[a]);
-        }
-#pragma unroll
-        for (int a = 0; a < NH; ++a) {
-          if (a < nh) {
-            float tot = part[a];
-#pragma unroll
-            for (int m2 = 1; m2 < CPR; m2 <<= 1) tot += __shfl_xor(tot, m2, 64);
-            if (c == 0) s_s[a][key] = key < nk ? tot * p.sl2 : -INFINITY;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    // softmax statistics per head (wave a handles heads a, a+4)
-    for (int a = w; a < nh; a += 4) {
-      const float x0 = lane < KC ? s_s[a][lane] : -INFINITY;
-      const float x1 = KC > 64 ? s_s[a][(lane + 64) % KC] : -INFINITY;
-      const float mx = wave_max(fmaxf(x0, x1));
-      const float mold = s_m[a];
-      const float mnew = fmaxf(mold, mx);
-      const float e0 = exp2f(x0 - mnew), e1 = exp2f(x1 - mnew);
-      if (lane < KC) s_s[a][lane] = e0;
-      if (KC > 64) s_s[a][(lane + 64) % KC] = e1;
-      const float sum = wave_sum(e0 + e1);
-      if (lane == 0) {
-        const float c = exp2f(mold - mnew);
-        s_c[a] = c;
-        s_l[a] = s_l[a] * c + sum;
-        s_m[a] = mnew;
-      }
-    }
-    __syncthreads();
-    // weighted values: thread = (key group kg, 8-wide d chunk dc)
-    {
-#pragma unroll
-      for (int a = 0; a < NH; ++a) {
-        if (a < nh) {
-          const float c = s_c[a];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[a][e] *= c;
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < KPG; ++kk) {
-        const int key = kg * KPG + kk;
-        if (key < nk) {
-          const u16x8 x = vx[kk];
-#pragma unroll
-          for (int a = 0; a < NH; ++a) {
-            if (a < nh) {
-              const float pw = s_s[a][key];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(pw, bf2f(x[e]), acc[a][e]);
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-  // reduce the key groups and write the per-head partials
-#pragma unroll
-  for (int a = 0; a < NH; ++a) {
-    if (a >= nh) break;  // nh is uniform across the workgroup
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s_red[kg][dc * 8 + e] = acc[a][e];
-    __syncthreads();
-    if (tid < D) {
-      float sum = 0.f;
-      for (int g = 0; g < KG; ++g) sum += s_red[g][tid];
-      const int hh = s_heads[a];
-      const int64_t pidx = ((int64_t)bh * p.umax + u) * p.G + hh;
-      p.part_o[pidx * D + tid] = sum / s_l[a];
-      if (tid == 0) p.part_lse[pidx] = s_m[a] + log2f(s_l[a]);
-    }
-    __syncthreads();
-  }
-}
-
 // One wave per (b, query head): LSE-merge the partials of its blocks.
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnParams p) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -576,20 +401,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnParams p)
     p.lse_out[(int64_t)b * p.Hq + h] = l > 0.f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY;
 }
 
-bool launch_decode_attend(const DecodeAttnParams& p, hipStream_t s) {
-  const int grid = p.B * p.Hkv * p.umax;
-  {
-    LaunchScope ls("decode_attend", s);
-    if (p.D == 128) {
-      if (p.G <= 4) hipLaunchKernelGGL((decode_attend_kernel<128, 4>), dim3(grid), dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((decode_attend_kernel<128, 8>), dim3(grid), dim3(256), 0, s, p);
-    } else {
-      if (p.G <= 4) hipLaunchKernelGGL((decode_attend_kernel<64, 4>), dim3(grid), dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((decode_attend_kernel<64, 8>), dim3(grid), dim3(256), 0, s, p);
-    }
-  }
-  return launch_ok("decode_attend");
-}
+// the attention itself runs on MFMA (decode_attend_mfma_kernel, attn.hip)
+bool launch_decode_attend(const DecodeAttnParams& p, hipStream_t s) { return launch_decode_attend_mfma(p, s); }
 
 bool launch_decode_combine(const DecodeAttnParams& p, hipStream_t s) {
   {

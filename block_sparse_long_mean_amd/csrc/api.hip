@@ -151,7 +151,11 @@ struct PrefillPlan {
 };
 
 // consecutive work items a gather workgroup takes at a time (runs are dealt
-// round-robin to the workgroups of an XCD)
+// round-robin to the workgroups of an XCD).  Blocks of one 64-key tile stay
+// staged across consecutive items of a bucket, so their workgroups take long
+// runs; longer blocks are re-staged by every item, and single items dealt
+// round-robin keep the XCD's workgroups on the same few blocks at once (their
+// keys and values then come from the XCD's L2).
 constexpr int kGatherRun = 64;
 // below this many rows per selected (b, kv head, block) on average, the
 // gather takes the sparse-bucket kernel
@@ -472,7 +476,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
   ap.NC = P.NC; ap.CT = P.CT;
   ap.grid = P.attn_grid;
   ap.rows_item = 32 * gather_waves(a->block);
-  ap.run_items = kGatherRun;
+  ap.run_items = gather_waves(a->block) > 4 ? 1 : kGatherRun;
   // a few rows per selected block on average (a short query chunk over a very
   // long memory): the sparse-bucket gather streams each block from HBM
   // instead of staging it for an MFMA tile of mostly empty rows.  The test

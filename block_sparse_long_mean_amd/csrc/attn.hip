@@ -170,7 +170,7 @@ BSA_DEV int pack_partials(const f32x16 (&o)[D / 32], u16x4_t (&pk)[D / 8]) {
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(o[dt][i]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = max_halves(mx);
   const int ex = part_exponent(mx);
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -400,6 +400,19 @@ BSA_DEV void pv_tile(const uint16_t* vt, const f32x16& p0, const f32x16& p1, f32
 
 // key index (within a 64-key tile) held by result register i of this lane
 BSA_DEV int krow(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+// the same less the lane's 4h: a constant for an unrolled i, so that masks
+// compare against limit - 4h instead of holding 16 row indices per lane
+BSA_DEV constexpr int krow0(int i) { return 8 * (i >> 2) + (i & 3); }
+
+// Scores of the tile's keys at or past `lim` (tile-relative) -> -inf.
+BSA_DEV void mask_tile(f32x16& s0, f32x16& s1, int lim, int h) {
+  const int l2 = lim - 4 * h;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s0[i] = krow0(i) < l2 ? s0[i] : -INFINITY;
+    s1[i] = krow0(i) + 32 < l2 ? s1[i] : -INFINITY;
+  }
+}
 
 // Online-softmax update of one lane's query column.  s0/s1 hold raw scores
 // (masked entries already -inf); sl2 = softmax scale * log2(e) is applied
@@ -415,10 +428,10 @@ constexpr float kRescaleLog2 = 8.0f;
 template <int D>
 BSA_DEV void softmax_update(f32x16& s0, f32x16& s1, float& m, float& l, f32x16 (&o)[D / 32], float sl2,
                             bool first) {
-  float tmax = -INFINITY;
+  float tmax = max_raw(s0[0], s1[0]);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, fmaxf(s0[i], s1[i]));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  for (int i = 1; i < 16; ++i) tmax = max3_raw(tmax, s0[i], s1[i]);
+  tmax = max_halves(tmax);
   const float tm = tmax * sl2;
   if (first) {
     m = tm;
@@ -606,7 +619,15 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
       // skips it
       const bool tile_on = wave_on && __ballot(g.valid && lim > 0) != 0ull;
       f32x16 s0, s1;
-      if (tile_on) qk_tile<D>(sm[cur], qf, s0, s1);
+      // the MFMA phases (scores, P.V) issue at a raised wave priority: a wave
+      // of the SIMD that is in its softmax (VALU) then fills the issue slots
+      // the other wave's MFMAs leave, instead of both waves contending for
+      // the same unit in lockstep after each tile barrier
+      if (tile_on) {
+        __builtin_amdgcn_s_setprio(1);
+        qk_tile<D>(sm[cur], qf, s0, s1);
+        __builtin_amdgcn_s_setprio(0);
+      }
       if (kt0 == 0 && has_next) {
         // queries of the next item into this wave's LDS staging area
         g_n = grow_of(p, rec_n, ent_n, lrow);
@@ -616,16 +637,11 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
       if (tile_on) {
         // mask only where a key can be past the end or after the query
         // (ragged last tile, or the query's own block); wave-uniform test
-        if (__ballot(g.valid && lim < KT) != 0ull) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kr = krow(i, hq);
-            s0[i] = kr < lim ? s0[i] : -INFINITY;
-            s1[i] = kr + 32 < lim ? s1[i] : -INFINITY;
-          }
-        }
+        if (__ballot(g.valid && lim < KT) != 0ull) mask_tile(s0, s1, lim, hq);
         softmax_update<D>(s0, s1, m, l, o, p.sl2, kt0 == 0);
+        __builtin_amdgcn_s_setprio(1);
         pv_tile<D>(sm[cur].v, s0, s1, o, kt0 == 0, l);
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     // epilogue: pack this item's outputs, take the next item's queries out of
@@ -1477,11 +1493,11 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bwd_dq_kernel(AttnParams p) {
       f32x16 s0, s1, d0, d1;
       qk_tile_pad<D>(sm[cur].kp, qf, s0, s1);
       qk_tile_pad<D>(sm[cur].vp, gf, d0, d1);
+      const int l2 = lim - 4 * h;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kr = krow(i, h);
-        const float p0 = kr < lim ? __builtin_amdgcn_exp2f(fmaf(s0[i], p.sl2, -lse2)) : 0.f;
-        const float p1 = kr + 32 < lim ? __builtin_amdgcn_exp2f(fmaf(s1[i], p.sl2, -lse2)) : 0.f;
+        const float p0 = krow0(i) < l2 ? __builtin_amdgcn_exp2f(fmaf(s0[i], p.sl2, -lse2)) : 0.f;
+        const float p1 = krow0(i) + 32 < l2 ? __builtin_amdgcn_exp2f(fmaf(s1[i], p.sl2, -lse2)) : 0.f;
         d0[i] = p0 * (d0[i] - dl);
         d1[i] = p1 * (d1[i] - dl);
       }
@@ -1637,14 +1653,7 @@ __global__ __launch_bounds__(64) void decode_attend_mfma_kernel(DecodeAttnParams
       s0 = mfma32(kf[0][st], qf[st], s0);
       s1 = mfma32(kf[1][st], qf[st], s1);
     }
-    if (nt < KT) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kr = krow(i, h);
-        s0[i] = kr < nt ? s0[i] : -INFINITY;
-        s1[i] = kr + 32 < nt ? s1[i] : -INFINITY;
-      }
-    }
+    if (nt < KT) mask_tile(s0, s1, nt, h);
     softmax_update<D>(s0, s1, m, l, o, p.sl2, t0 == 0);
     // the values' copy must have landed: the compiler may order the copy
     // after the key loads, so their wait does not cover it

@@ -131,6 +131,26 @@ BSA_DEV float wave_max(float v) {
   for (int m = 32; m > 0; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
   return v;
 }
+
+// Maxima without the NaN quieting that fmaxf adds around every operand
+// (v_max_f32 / v_max3_f32 as they are; the operands here are scores, finite
+// or -inf).
+BSA_DEV float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+BSA_DEV float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// max of v over lanes l and l ^ 32: v_permlane32_swap exchanges the two
+// halves of the wave in registers (no LDS round trip)
+BSA_DEV float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 BSA_DEV float wave_sum(float v) {
   for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
   return v;

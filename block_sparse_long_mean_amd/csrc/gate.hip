@@ -233,6 +233,22 @@ BSA_DEV uint64_t list_kth(const uint64_t (&L)[KR], int lane, int topk) {
   return shfl64(v, (lane & 48) + (e & 15));
 }
 
+// Largest key held by the 16 lanes of this lane's group (butterfly over the
+// row through DPP; every lane of the group ends with it).
+BSA_DEV uint64_t group_max64(uint64_t v, int li) {
+#pragma unroll
+  for (int st = 1; st < 16; st <<= 1) {
+    const uint64_t o = row_xor64_any(v, st, li);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// At most kSmallK best keys of a row whose candidates all sit in one staged
+// chunk are taken by repeated group maxima (each round's winner removed from
+// its lane) instead of the list merge: a few DPP butterflies per chosen key.
+constexpr int kSmallK = 4;
+
 // FS: the summaries come as fp32 (p_f32) and are split into the hi / lo
 // planes as each chunk is staged in LDS (LO is then true)
 // Occupancy requested per instantiation (workgroups of W waves per CU), set
@@ -378,6 +394,31 @@ __global__ __launch_bounds__(64 * W, (gate_min_blocks<W, DG, KR>())) void gate_k
         }
         if constexpr (QK != 0) acc[ct] = mfma16(ql[ks], bh16, acc[ct]);
       }
+    }
+    if (KR == 1 && p.topk <= kSmallK && c_lo + 64 >= c_hi) {
+      // the row's only chunk and a small k: the k best keys directly, in
+      // descending order, into list elements 0 .. k-1
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint64_t key[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int j = c0 + ct * 16 + r16;
+          key[ct] = (j < c_hi && j < ncand[i]) ? make_key(acc[ct][i], (uint32_t)j) : 0ull;
+        }
+        uint64_t res = 0ull;
+        for (int r = 0; r < p.topk; ++r) {
+          uint64_t bst = key[0];
+#pragma unroll
+          for (int ct = 1; ct < 4; ++ct) bst = key[ct] > bst ? key[ct] : bst;
+          bst = group_max64(bst, r16);
+          if (r16 == r) res = bst;
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) key[ct] = key[ct] == bst ? 0ull : key[ct];
+        }
+        L[i][0] = res;
+      }
+      continue;
     }
     // merge this chunk into the running lists: each lane group appends its
     // row's candidates that beat the row's k-th key to an LDS list (after the

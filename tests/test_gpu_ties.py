@@ -11,7 +11,8 @@ straddle the k-th place in most rows.  Selections are compared with the
 oracle's strictly (array equality, no tie window), and outputs as usual.
 
 Covered: the per-head and per-group prefill gate with one, three and four
-16-key register lists; a long candidate list split over workgroups and
+16-key register lists, and with a small k over a single chunk of candidates
+(taken by repeated group maxima); a long candidate list split over workgroups and
 merged (non-causal, a few queries over a long key sequence); the fp32 gate;
 the decode selection per head and per group, including its 4-buffer
 variant.  Also the regression case of a requested top-k above the number of
@@ -65,6 +66,9 @@ PREFILL_CASES = {
     "head_noncausal_split_k20": ("bf16", 1, 64, 16384, 8, 2, 128, 16, 20, False, "head", None, 7),
     "group_noncausal_split_k64": ("bf16", 1, 32, 32768, 8, 2, 64, 16, 64, False, "group", None, 9),
     "f32_head_causal_k3": ("f32", 1, 1024, 1024, 2, 1, 64, 64, 3, True, "head", None, 2),
+    # at most 64 candidate blocks and k <= 4: the repeated-maximum path
+    "head_causal_k3_one_chunk": ("bf16", 1, 4096, 4096, 4, 2, 128, 64, 3, True, "head", None, 2),
+    "group_causal_k4_one_chunk": ("bf16", 1, 2048, 2048, 8, 2, 64, 64, 4, True, "group", None, 3),
 }
 
 

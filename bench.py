@@ -160,12 +160,12 @@ def other_workloads(m, reps):
     k = synth.device_tensor((1, c["Lk"], c["Hkv"], c["D"]), 1.0, SEED, t["k"], "bf16")
     v = synth.device_tensor((1, c["Lk"], c["Hkv"], c["D"]), 1.0, SEED, t["v"], "bf16")
     ms_sum = time_call(lambda: m.block_summary(k, c["block"], doc_ids=dk), reps)
-    # the memory's offline encoding: routing keys and document-wise rotated
-    # content keys, stored once
-    pooled, k_rot = m.block_summary(k, c["block"], doc_ids=dk, return_k_rot=True)
+    # the memory's offline encoding: routing keys (stored as the gate's bf16
+    # hi / lo planes) and document-wise rotated content keys, stored once
+    pooled, k_rot, planes = m.block_summary(k, c["block"], doc_ids=dk, return_k_rot=True, return_planes=True)
     del k
     o = torch.empty_like(q)
-    kw = dict(doc_ids_q=dq, pooled=pooled)  # keys arrive rotated; the query chunk is rotated per call
+    kw = dict(doc_ids_q=dq, pooled=planes)  # keys arrive rotated; the query chunk is rotated per call
     ws = torch.empty(m.prefill_workspace_bytes(q, k_rot, block=c["block"], topk=c["topk"], causal=False, **kw),
                      dtype=torch.uint8, device="cuda")
     ms = time_call(lambda: m.sparse_attn_prefill(q, k_rot, v, c["block"], c["topk"], False, out=o, workspace=ws,
@@ -173,7 +173,7 @@ def other_workloads(m, reps):
     out["memory_10m_summary"] = {"ms": round(ms_sum, 4),
                                  "read_gbs": round(2 * c["Lk"] * c["Hkv"] * c["D"] / (ms_sum * 1e-3) / 1e9, 1)}
     out["memory_10m_query_chunk"] = {"ms": round(ms, 4), "query_tokens_per_s": round(c["Lq"] / (ms * 1e-3), 1),
-                                     "note": "keys stored rotated with their routing keys (offline encoding)"}
+                                     "note": "keys stored rotated, routing keys stored as the gate's bf16 hi / lo planes (offline encoding)"}
     _log(f"memory bank: summaries {ms_sum:.3f} ms, 512-token query chunk {ms:.3f} ms")
     # host content tier: the memory's rotated keys and its values (41 GB) in
     # pinned host RAM, its routing keys in GPU memory; only the chosen blocks
@@ -214,7 +214,7 @@ def other_workloads(m, reps):
                 "(each distinct (kv head, block) once) / attention-phase time"}
     _log(f"host-tier memory bank query chunk: {ms_h:.3f} ms, attention {att_ms:.3f} ms, "
          f"{kv_bytes / (att_ms * 1e-3) / 1e9:.1f} GB/s over the host link")
-    del q, kh, vh, o, ws, pooled, dk, dq, sel, keys
+    del q, kh, vh, o, ws, pooled, planes, dk, dq, sel, keys
     torch.cuda.empty_cache()
     # the decode workload over a paged cache: the same 1,048,576-token caches
     # cut into 128-token pages (head-major inside a page) stored in a seeded
@@ -560,11 +560,12 @@ def make_workload(m, name):
         else:
             q = synth.device_tensor((1, c["Lq"], c["Hq"], c["D"]), 1.0, SEED, t["q"], "bf16")
             v = synth.device_tensor((1, c["Lk"], c["Hkv"], c["D"]), 1.0, SEED, t["v"], "bf16")
-            pooled, k_rot = m.block_summary(k, c["block"], doc_ids=dk, return_k_rot=True)
+            # the memory's offline encoding: rotated keys and the routing keys as the gate's planes
+            _, k_rot, planes = m.block_summary(k, c["block"], doc_ids=dk, return_k_rot=True, return_planes=True)
             del k
             dq = torch.zeros((1, c["Lq"]), dtype=torch.int32, device="cuda")
             o = torch.empty_like(q)
-            kw = dict(doc_ids_q=dq, pooled=pooled)
+            kw = dict(doc_ids_q=dq, pooled=planes)
             ws = torch.empty(m.prefill_workspace_bytes(q, k_rot, block=c["block"], topk=c["topk"], causal=False,
                                                        **kw), dtype=torch.uint8, device="cuda")
             fn = lambda: m.sparse_attn_prefill(q, k_rot, v, c["block"], c["topk"], False, out=o, workspace=ws, **kw)

@@ -65,6 +65,7 @@ class PrefillArgs(ctypes.Structure):
         ("lse_out", VP),
         ("chunk_tokens", ctypes.c_int32),
         ("chunks_per_pass", ctypes.c_int32),
+        ("pooled_hi", VP), ("pooled_lo", VP),
     ]
 
 
@@ -99,6 +100,7 @@ class SummaryArgs(ctypes.Structure):
         ("pooled_dtype", ctypes.c_int32),
         ("k_rot", VP),
         ("pos_out", VP),
+        ("plane_hi", VP), ("plane_lo", VP),
     ]
 
 
@@ -285,7 +287,11 @@ def _prefill_args(q, k, v, o, *, block, topk, causal, gate, index_q, index_k, do
     a.doc_ids_k = _ptr(doc_ids_k)
     a.rope_theta = float(rope_theta)
     a.scale = 0.0 if scale is None else float(scale)
-    a.pooled = _ptr(pooled)
+    if isinstance(pooled, (tuple, list)):
+        # the gate's bf16 planes (hi, lo), each [B, Hkv, Nb, Dg]
+        a.pooled_hi, a.pooled_lo = _ptr(pooled[0]), _ptr(pooled[1])
+    else:
+        a.pooled = _ptr(pooled)
     a.sel_out = _ptr(sel)
     a.lse_out = _ptr(lse)
     a.chunk_tokens = int(chunk_tokens)
@@ -475,8 +481,11 @@ def sparse_attn_decode_noalloc(q, kcache, vcache, pooled, topk: int, block: int,
 
 
 def block_summary(k, block: int, doc_ids=None, *, rope_theta: float = 10000.0, out_dtype=None,
-                  return_k_rot: bool = False, return_pos: bool = False, stream=None):
-    """Mean-pooled block summaries [B, Nb, H, D] (after document-wise RoPE when doc_ids is given)."""
+                  return_k_rot: bool = False, return_pos: bool = False, return_planes: bool = False, stream=None):
+    """Mean-pooled block summaries [B, Nb, H, D] (after document-wise RoPE when doc_ids is given).
+
+    return_planes adds the summaries split into the prefill gate's bf16 planes, a tuple
+    (hi, lo) of [B, H, Nb, D] tensors: pass it as sparse_attn_prefill's `pooled`."""
     torch = _torch()
     B, L, H, D = k.shape
     nb = -(-L // block)
@@ -485,6 +494,9 @@ def block_summary(k, block: int, doc_ids=None, *, rope_theta: float = 10000.0, o
     d = _doc(doc_ids, B, L, _gpu(k))
     k_rot = torch.empty((B, L, H, D), dtype=k.dtype, device=_gpu(k)) if return_k_rot else None
     pos = torch.empty((B, L), dtype=torch.int32, device=_gpu(k)) if return_pos else None
+    planes = None
+    if return_planes:
+        planes = tuple(torch.empty((B, H, nb, D), dtype=torch.bfloat16, device=_gpu(k)) for _ in range(2))
     a = SummaryArgs()
     a.dtype = _dtype_code(k)
     a.B, a.L, a.H, a.D, a.block = B, L, H, D, int(block)
@@ -495,6 +507,8 @@ def block_summary(k, block: int, doc_ids=None, *, rope_theta: float = 10000.0, o
     a.pooled_dtype = _dtype_code(pooled)
     a.k_rot = _ptr(k_rot)
     a.pos_out = _ptr(pos)
+    if planes is not None:
+        a.plane_hi, a.plane_lo = _ptr(planes[0]), _ptr(planes[1])
     n = lib().bsa_summary_workspace_bytes(ctypes.byref(a))
     if n == 0:
         raise BsaError(BSA_ERR_INVALID_ARG, lib().bsa_last_error().decode())
@@ -505,6 +519,8 @@ def block_summary(k, block: int, doc_ids=None, *, rope_theta: float = 10000.0, o
         res.append(k_rot)
     if return_pos:
         res.append(pos)
+    if return_planes:
+        res.append(planes)
     return res[0] if len(res) == 1 else tuple(res)
 
 

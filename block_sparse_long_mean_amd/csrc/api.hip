@@ -190,6 +190,14 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
   if (gate_only && !a->sel_out) return fail(BSA_ERR_INVALID_ARG, "sel_out is required for bsa_select_blocks");
   if ((a->index_q == nullptr) != (a->index_k == nullptr)) return fail(BSA_ERR_INVALID_ARG, "index_q and index_k go together");
   if (a->pooled && !aligned16(a->pooled)) return fail(BSA_ERR_INVALID_ARG, "pooled must be 16-byte aligned");
+  if ((a->pooled_hi == nullptr) != (a->pooled_lo == nullptr))
+    return fail(BSA_ERR_INVALID_ARG, "pooled_hi and pooled_lo go together");
+  if (a->pooled_hi) {
+    if (a->pooled) return fail(BSA_ERR_INVALID_ARG, "give pooled or pooled_hi / pooled_lo, not both");
+    if (a->dtype != BSA_DTYPE_BF16) return fail(BSA_ERR_UNSUPPORTED, "pooled_hi / pooled_lo are for bf16 inputs");
+    if (!aligned16(a->pooled_hi) || !aligned16(a->pooled_lo))
+      return fail(BSA_ERR_INVALID_ARG, "pooled_hi / pooled_lo must be 16-byte aligned");
+  }
   const int elt = a->dtype == BSA_DTYPE_BF16 ? 2 : 4;
   if (!aligned16(a->q) || !aligned16(a->k) || (a->v && !aligned16(a->v)) || (a->o && !aligned16(a->o)))
     return fail(BSA_ERR_INVALID_ARG, "tensor base pointers must be 16-byte aligned");
@@ -217,7 +225,7 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
   P.Gs = P.per_group ? 1 : P.G;
   P.rope_q = a->doc_ids_q != nullptr;
   P.rope_k = a->doc_ids_k != nullptr;
-  P.have_pooled = a->pooled != nullptr;
+  P.have_pooled = a->pooled != nullptr || a->pooled_hi != nullptr;
   if (P.per_group && P.G > 8 && !P.bf16) {
     // fp32 path sums in the gate kernel, no restriction; keep for symmetry
   }
@@ -334,7 +342,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
   if (st != BSA_OK) return st;
   if (!ws || ws_bytes < P.bytes) return fail(BSA_ERR_WORKSPACE, "workspace smaller than bsa_prefill_workspace_bytes");
   if (((uintptr_t)ws & 255) != 0) return fail(BSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  st = resident({a->q, a->k, a->v, a->o, a->index_q, a->index_k, a->doc_ids_q, a->doc_ids_k, a->pooled, a->sel_out,
+  st = resident({a->q, a->k, a->v, a->o, a->index_q, a->index_k, a->doc_ids_q, a->doc_ids_k, a->pooled, a->pooled_hi, a->pooled_lo, a->sel_out,
                  a->lse_out, ws});
   if (st != BSA_OK) return st;
   plan_prefill(a, P, reinterpret_cast<char*>(ws), gate_only);
@@ -421,7 +429,11 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
     g.q = gq; g.qs_b = gq_s[0]; g.qs_t = gq_s[1]; g.qs_h = gq_s[2];
     g.qkind = gq_f32 ? 1 : (P.per_group ? 2 : 0);
     g.Dg = P.Dg;
-    if (P.have_pooled) {
+    if (a->pooled_hi) {
+      // the caller's planes [B, Hkv, Nb, Dg], laid out as the library's own
+      g.p_hi = a->pooled_hi; g.p_lo = a->pooled_lo; g.p_f32 = nullptr;
+      g.ps_h = (int64_t)P.Nb * P.Dg; g.ps_b = (int64_t)a->Hkv * g.ps_h; g.ps_j = P.Dg;
+    } else if (P.have_pooled) {
       // the caller's fp32 summaries [B, Nb, Hkv, Dg], split into bf16 hi + lo as the gate stages them
       g.p_hi = g.p_lo = nullptr;
       g.p_f32 = reinterpret_cast<const float*>(a->pooled);
@@ -744,6 +756,7 @@ static bsa_status plan_summary(const bsa_summary_args* a, int32_t** chunk, int32
   if (!a->k || !a->pooled) return fail(BSA_ERR_INVALID_ARG, "k and pooled are required");
   if (a->pooled_dtype != BSA_DTYPE_F32 && a->pooled_dtype != BSA_DTYPE_BF16) return fail(BSA_ERR_INVALID_ARG, "pooled_dtype");
   if ((a->k_rot || a->pos_out) && !a->doc_ids) return fail(BSA_ERR_INVALID_ARG, "k_rot/pos_out need doc_ids");
+  if ((a->plane_hi == nullptr) != (a->plane_lo == nullptr)) return fail(BSA_ERR_INVALID_ARG, "plane_hi and plane_lo go together");
   const int elt = a->dtype == BSA_DTYPE_BF16 ? 2 : 4;
   if (!aligned16(a->k) || !strides_ok(a->k_stride, 3, a->D, elt)) return fail(BSA_ERR_INVALID_ARG, "k alignment/strides");
   if ((int64_t)a->B * ((a->L + a->block - 1) / a->block) >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "too many blocks");
@@ -769,7 +782,7 @@ static bsa_status run_summary(const bsa_summary_args* a, void* ws, size_t ws_byt
     if (((uintptr_t)ws & 255) != 0) return fail(BSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     plan_summary(a, &chunk, &pos, reinterpret_cast<char*>(ws), &need);
   }
-  st = resident({a->k, a->doc_ids, a->pooled, a->k_rot, a->pos_out, a->doc_ids ? ws : nullptr});
+  st = resident({a->k, a->doc_ids, a->pooled, a->k_rot, a->pos_out, a->plane_hi, a->plane_lo, a->doc_ids ? ws : nullptr});
   if (st != BSA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (a->doc_ids && !launch_doc_positions(a->doc_ids, a->B, a->L, chunk, pos, s)) return BSA_ERR_HIP;
@@ -782,7 +795,8 @@ static bsa_status run_summary(const bsa_summary_args* a, void* ws, size_t ws_byt
   omega_table(a->rope_theta > 0.f ? (double)a->rope_theta : 10000.0, a->D, sp.omega);
   sp.pooled_f32 = a->pooled_dtype == BSA_DTYPE_F32 ? reinterpret_cast<float*>(a->pooled) : nullptr;
   sp.pooled_bf16 = a->pooled_dtype == BSA_DTYPE_BF16 ? reinterpret_cast<uint16_t*>(a->pooled) : nullptr;
-  sp.plane_hi = sp.plane_lo = nullptr;
+  sp.plane_hi = a->plane_hi;
+  sp.plane_lo = a->plane_lo;
   sp.k_rot = a->k_rot;
   return launch_block_summary(sp, s) ? BSA_OK : BSA_ERR_HIP;
 }

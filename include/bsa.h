@@ -124,6 +124,15 @@ typedef struct bsa_prefill_args {
                                       one merge launch); 0 = as many as a 40 GiB partial-output
                                       budget holds, > 0 forces that many (the last pass may hold
                                       fewer) */
+    /* optional, bf16 prefill only, instead of `pooled`: the summaries as the
+       gate's two bf16 planes, each [B, Hkv, Nb, Dg] contiguous and 16-byte
+       aligned, with hi = bf16(s) and lo = bf16(s - hi) (round to nearest even)
+       for the fp32 summary s -- the planes bsa_block_summary writes.  Both or
+       neither; the gate stages them as they are, so a memory queried many
+       times is split once, when it is encoded.  Results equal those with
+       `pooled` = s. */
+    const uint16_t* pooled_hi;
+    const uint16_t* pooled_lo;
 } bsa_prefill_args;
 
 /* Workspace bytes bsa_sparse_attn_prefill needs for `a` (0 if `a` is invalid;
@@ -222,6 +231,11 @@ typedef struct bsa_summary_args {
     void* k_rot;                   /* optional [B, L, H, D] contiguous rotated keys (k's dtype);
                                       needs doc_ids */
     int32_t* pos_out;              /* optional [B, L] per-document positions; needs doc_ids */
+    /* optional [B, H, Nb, D] contiguous outputs (both or neither): the fp32
+       summaries split into the prefill gate's bf16 planes, hi = bf16(s),
+       lo = bf16(s - hi) (bsa_prefill_args pooled_hi / pooled_lo) */
+    uint16_t* plane_hi;
+    uint16_t* plane_lo;
 } bsa_summary_args;
 
 size_t bsa_summary_workspace_bytes(const bsa_summary_args* a);

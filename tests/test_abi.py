@@ -115,6 +115,35 @@ def test_prefill_misaligned_and_null(m):
     assert m.lib().bsa_select_blocks(ctypes.byref(_args(m)[0]), None, 0, None) == m.BSA_ERR_INVALID_ARG  # no sel_out
 
 
+def test_prefill_gate_planes_validation(m):
+    """The summaries as the gate's bf16 planes: both planes or neither, not
+    together with fp32 `pooled`, bf16 inputs only, 16-byte aligned."""
+    a, buf = _args(m)
+    base = a.q
+    a.pooled_hi = base
+    assert m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a)) == 0  # lo missing
+    assert m.lib().bsa_sparse_attn_prefill(ctypes.byref(a), None, 0, None) == m.BSA_ERR_INVALID_ARG
+    a.pooled_lo = base
+    assert m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a)) > 0
+    a.pooled = base
+    assert m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a)) == 0  # both forms
+    a.pooled = None
+    a.pooled_lo = base + 2
+    assert m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a)) == 0  # misaligned
+    a, buf2 = _args(m, dtype=m.BSA_DTYPE_F32)
+    a.pooled_hi = a.pooled_lo = a.q
+    assert m.lib().bsa_sparse_attn_prefill(ctypes.byref(a), None, 0, None) == m.BSA_ERR_UNSUPPORTED
+    s = m.SummaryArgs()
+    s.dtype, s.B, s.L, s.H, s.D, s.block = m.BSA_DTYPE_BF16, 1, 100, 2, 128, 64
+    s.k = s.pooled = base
+    s.k_stride = m.I64x3(100 * 2 * 128, 2 * 128, 128)
+    s.pooled_dtype = m.BSA_DTYPE_F32
+    s.plane_hi = base
+    assert m.lib().bsa_summary_workspace_bytes(ctypes.byref(s)) == 0  # plane_lo missing
+    s.plane_lo = base
+    assert m.lib().bsa_summary_workspace_bytes(ctypes.byref(s)) > 0
+
+
 def test_decode_and_summary_validation(m):
     d = m.DecodeArgs()
     d.dtype = m.BSA_DTYPE_F32

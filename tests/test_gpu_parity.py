@@ -272,6 +272,40 @@ def test_prerotated_keys_equal_internal_rotation(bsa):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+@pytest.mark.parametrize("case", ["memory_split_candidates", "causal_group", "causal_head"])
+def test_gate_planes_equal_fp32_summaries(bsa, case):
+    """Summaries handed to the prefill as the gate's bf16 planes (written by the block summary) give
+    the same selection and the same output, bit for bit, as the fp32 summaries they split; and the
+    planes are that split: hi = bf16(s), lo = bf16(s - hi), round to nearest even."""
+    causal = case != "memory_split_candidates"
+    gate = "group" if case == "causal_group" else "head"
+    if causal:
+        B, Lq, Lk, Hq, Hkv, D, block, topk = 1, 3000, 3000, 8, 2, 128, 64, 6
+    else:  # a few queries over a long memory: the candidates split over workgroups, then merged
+        B, Lq, Lk, Hq, Hkv, D, block, topk = 1, 128, 200000, 8, 2, 128, 64, 16
+    _say(f"case gate planes {case}: Lq{Lq} Lk{Lk} H{Hq}/{Hkv} block{block} topk{topk} {gate}")
+    q = synth.host_tensor((B, Lq, Hq, D), 1.0, 23, 0, "bf16").cuda()
+    k = synth.host_tensor((B, Lk, Hkv, D), 1.0, 23, 1, "bf16").cuda()
+    v = synth.host_tensor((B, Lk, Hkv, D), 1.0, 23, 2, "bf16").cuda()
+    kw = {}
+    if causal:
+        pooled, planes = bsa.block_summary(k, block, return_planes=True)
+        k_att = k
+    else:
+        dk = torch.from_numpy(synth.random_doc_ids(Lk, 700.0, 23)[None]).cuda()
+        kw["doc_ids_q"] = torch.zeros((B, Lq), dtype=torch.int32, device="cuda")
+        pooled, k_att, planes = bsa.block_summary(k, block, doc_ids=dk, return_k_rot=True, return_planes=True)
+    hi = pooled.to(torch.bfloat16)
+    lo = (pooled - hi.float()).to(torch.bfloat16)
+    assert torch.equal(planes[0].view(torch.int16), hi.permute(0, 2, 1, 3).contiguous().view(torch.int16))
+    assert torch.equal(planes[1].view(torch.int16), lo.permute(0, 2, 1, 3).contiguous().view(torch.int16))
+    o1, s1 = bsa.sparse_attn_prefill(q, k_att, v, block, topk, causal, gate=gate, pooled=pooled, return_sel=True, **kw)
+    o2, s2 = bsa.sparse_attn_prefill(q, k_att, v, block, topk, causal, gate=gate, pooled=planes, return_sel=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 def test_decode_head_major_cache(bsa):
     """Caches stored head-major ([B, Hkv, Lc, D]) and passed as strided [B, Lc, Hkv, D] views."""
     B, Hq, Hkv, Lc, D, block, topk = 2, 8, 2, 3000, 128, 128, 6

@@ -478,7 +478,7 @@ static bsa_status run_prefill(const bsa_prefill_args* a, void* ws, size_t ws_byt
   AttnParams ap;
   ap.B = a->B; ap.Lq = a->Lq; ap.Lk = a->Lk; ap.Hq = a->Hq; ap.Hkv = a->Hkv; ap.G = P.G; ap.D = a->D;
   ap.block = a->block; ap.Nb = P.Nb; ap.Hs = P.Hs; ap.per_group = P.per_group; ap.Gs = P.Gs; ap.R = P.R;
-  ap.kslot = P.kslot; ap.causal = a->causal;
+  ap.kslot = P.kslot; ap.causal = a->causal; ap.topk = P.topk;
   ap.sh_h = P.sh_h; ap.sh_t = P.sh_t; ap.lgR = P.lgR;
   ap.q = reinterpret_cast<const uint16_t*>(q_att); ap.qs_b = qa_s[0]; ap.qs_t = qa_s[1]; ap.qs_h = qa_s[2];
   ap.k = reinterpret_cast<const uint16_t*>(k_att); ap.ks_b = ka_s[0]; ap.ks_t = ka_s[1]; ap.ks_h = ka_s[2];

@@ -863,19 +863,16 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const bool ok = row < nrows && t < p.Lq;
   const int b = bh / p.Hkv, hk = bh % p.Hkv;
   const int h = hk * p.G + hh;
-  const int hs = p.per_group ? hk : h;
   const int rr = p.per_group ? hh : 0;
   const int64_t prow = ((int64_t)c_rel * p.Gs + (p.per_group ? 0 : hh)) * p.CT + t_loc;
-  const int64_t srow = ((int64_t)b * p.Hs + hs) * p.Lq + (ok ? t : 0);
-  const int32_t* sr = p.sel + srow * p.sel_w;
-  // number of valid slots (valid entries come first, -1 after): the row's
-  // lanes count a strided share each, then sum across the row's lanes
+  // number of valid slots: the gate keeps min(topk, candidates) blocks, then
+  // the forced own block when causal (the valid entries of a selection row
+  // come first), so the count follows from the token's position alone
   int n = 0;
   if (ok) {
-    for (int s = li; s < p.sel_w; s += LPR) n += sr[s] >= 0 ? 1 : 0;
+    const int ncand = p.causal ? min((p.Lk - p.Lq + t) / p.block, p.Nb) : p.Nb;
+    n = min(p.topk, ncand) + (p.causal ? 1 : 0);
   }
-#pragma unroll
-  for (int m2 = 1; m2 < LPR; m2 <<= 1) n += __shfl_xor(n, m2, 64);
   // partial s holds q_s = 32767 * 2^-E_s * sum_k p_k v_k with p = 2^(score*sl2 - m_s), and
   // (m_s + E_s, 2^-E_s * sum_k p_k)
   float M = -INFINITY, W = 0.f;

@@ -123,6 +123,7 @@ bool launch_csr(const CsrParams& p, hipStream_t s);
 struct AttnParams {
   int B, Lq, Lk, Hq, Hkv, G, D, block, Nb, Hs, per_group, Gs, R, kslot, causal;
   int sh_h, sh_t, lgR;  // entry bit fields; R = 1 << lgR
+  int topk;             // gate-chosen blocks per row before the candidate count caps it: min(topk, Nb)
   const uint16_t* q;
   int64_t qs_b, qs_t, qs_h;
   const uint16_t* k;

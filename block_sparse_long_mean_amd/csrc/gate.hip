@@ -571,6 +571,279 @@ __global__ __launch_bounds__(256) void gate_merge_kernel(GateParams p) {
   emit_row<V>(q, s_buf[w], s_cnt[w], b, hs, t, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Small candidate sets (MoBA-style gating over a few dozen blocks): every
+// row's candidates fit one chunk of 64 summaries and k <= kSmallK, per-head
+// gate queries.  The chunk is staged in LDS once per workgroup; each of its
+// W waves then walks `tpw` tiles of 16 rows, the next tile's gate queries in
+// flight while it scores the current one and takes its k best by repeated
+// group maxima (the rule of gate_kernel's single-chunk path), then writes the
+// rows.  Workgroup g of a (b, kv head) owns rows [RT tpw g, RT tpw (g + 1))
+// with RT = 16 W; wave w takes its tiles w, w + W, w + 2W, ...  Row indices
+// are tracked as (token, head) pairs advanced without divisions.
+// ---------------------------------------------------------------------------
+template <int KS, int QK>
+struct GateQRaw {
+  u16x8 h[QK == 0 ? KS : 1];
+  f32x4 a[QK == 1 ? KS : 1], c[QK == 1 ? KS : 1];
+};
+
+// Gate-query fragment of token t, head hh of the group (ok false: zeros).
+template <int KS, int QK>
+BSA_DEV void gate_q_fetch(const GateParams& p, int b, int hk, int t, int hh, bool ok, GateQRaw<KS, QK>& r) {
+  const int d_lane = (lane_id() >> 4) * 8;
+  if constexpr (QK == 0) {
+    const uint16_t* base = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.qs_b + (int64_t)t * p.qs_t +
+                           (int64_t)(hk * p.G + hh) * p.qs_h + d_lane;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) r.h[ks] = ok ? ld16(base + ks * 32) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  } else {
+    const float* base = reinterpret_cast<const float*>(p.q) + (int64_t)b * p.qs_b + (int64_t)t * p.qs_t +
+                        (int64_t)(hk * p.G + hh) * p.qs_h + d_lane;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      r.a[ks] = ok ? *reinterpret_cast<const f32x4*>(base + ks * 32) : f32x4{0.f, 0.f, 0.f, 0.f};
+      r.c[ks] = ok ? *reinterpret_cast<const f32x4*>(base + ks * 32 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+// (token, head) of a per-head row advanced by n rows: dt = n / G, dh = n % G.
+BSA_DEV void rows_advance(int& t, int& hh, int G, int dt, int dh) {
+  t += dt;
+  hh += dh;
+  if (hh >= G) {
+    hh -= G;
+    ++t;
+  }
+}
+
+// MFMA operands of the fetched fragment: exact bf16 queries are the operand
+// as loaded (no low part); fp32 ones are split into hi + lo.
+template <int KS, int QK>
+BSA_DEV void gate_q_split(const GateQRaw<KS, QK>& r, bf16x8 (&hi)[KS], bf16x8 (&lo)[KS]) {
+  if constexpr (QK == 0) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      hi[ks] = __builtin_bit_cast(bf16x8, r.h[ks]);
+      lo[ks] = __builtin_bit_cast(bf16x8, u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+    }
+    return;
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x;
+      if constexpr (QK == 0) x = bf2f(r.h[ks][e]);
+      else x = e < 4 ? r.a[ks][e] : r.c[ks][e - 4];
+      __bf16 h, l;
+      split_bf(x, h, l);
+      hi[ks][e] = h;
+      lo[ks][e] = l;
+    }
+  }
+}
+
+template <int W, int DG, int QK, bool LO, bool FS>
+__global__ __launch_bounds__(64 * W) void gate_small_kernel(GateParams p, int tpw, int nwg) {
+  constexpr int PADR = DG + 8;
+  constexpr int KS = DG / 32;
+  constexpr int CPR = DG / 8;
+  static_assert(QK == 0 || QK == 1, "per-head gate queries only");
+  __shared__ __attribute__((aligned(16))) uint16_t s_hi[64 * PADR];
+  __shared__ __attribute__((aligned(16))) uint16_t s_lo[LO ? 64 * PADR : 8];
+
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int wg = lid % nwg, bh = lid / nwg;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, kh = lane >> 4;
+  constexpr int RT = 16 * W;  // rows of one round of tiles (one per wave)
+  const int row0 = wg * RT * tpw;
+  const int row_end = min(row0 + RT * tpw, p.rows_per_bh);
+  // candidates of the workgroup's last row (the most of any of its rows; <= 64)
+  const int nc = ncand_of(p, b, row_to_th(row_end - 1, p).t);
+
+  // Row bookkeeping in 32-bit integers, advanced without divisions: the
+  // fetched row (this lane's A-operand row) and the lane group's first result
+  // row, each as (token, head of the group); rows advance by RT per tile.
+  const int G = p.G, dt = RT / G, dh = RT % G;
+  const int qbase = p.Lk - p.Lq;  // key position of query token 0
+  int frow = row0 + 16 * w + r16;
+  int ft = frow / G, fh = frow - (frow / G) * G;
+  int rrow = row0 + 16 * w + 4 * kh;
+  int rt = rrow / G, rh = rrow - (rrow / G) * G;
+  int32_t* sel_b = p.sel + (int64_t)b * p.Hs * p.Lq * p.sel_w;
+
+  // the first tile's gate queries, then the chunk of summaries j < nc
+  GateQRaw<KS, QK> nxt;
+  gate_q_fetch<KS, QK>(p, b, hk, ft, fh, frow < p.rows_per_bh, nxt);
+  for (int idx = tid; idx < 64 * CPR; idx += 64 * W) {
+    const int jr = idx / CPR, ch = idx % CPR;
+    u16x8 h8 = u16x8{0, 0, 0, 0, 0, 0, 0, 0}, l8 = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (jr < nc) {
+      if constexpr (FS) {
+        const float* src = p.p_f32 + (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h + (int64_t)jr * p.ps_j + ch * 8;
+        const f32x4 fa = *reinterpret_cast<const f32x4*>(src), fb = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __bf16 hv, lv;
+          split_bf(e < 4 ? fa[e] : fb[e - 4], hv, lv);
+          h8[e] = __builtin_bit_cast(uint16_t, hv);
+          l8[e] = __builtin_bit_cast(uint16_t, lv);
+        }
+      } else {
+        const int64_t off = (int64_t)b * p.ps_b + (int64_t)hk * p.ps_h + (int64_t)jr * p.ps_j + ch * 8;
+        h8 = ld16(p.p_hi + off);
+        if constexpr (LO) l8 = ld16(p.p_lo + off);
+      }
+    }
+    st16(&s_hi[jr * PADR + ch * 8], h8);
+    if constexpr (LO) st16(&s_lo[jr * PADR + ch * 8], l8);
+  }
+  __syncthreads();
+
+  for (int u = 0; u < tpw; ++u) {
+    const int rbase = row0 + 16 * w + RT * u;
+    if (rbase >= row_end) break;  // wave-uniform; no workgroup barrier follows
+    bf16x8 qh[KS], ql[KS];
+    gate_q_split<KS, QK>(nxt, qh, ql);
+    frow += RT;
+    rows_advance(ft, fh, G, dt, dh);
+    if (u + 1 < tpw && rbase + RT < row_end) gate_q_fetch<KS, QK>(p, b, hk, ft, fh, frow < p.rows_per_bh, nxt);
+    f32x4 acc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 bh16 = as_bf(ld16(&s_hi[(ct * 16 + r16) * PADR + ks * 32 + kh * 8]));
+        acc[ct] = mfma16(qh[ks], bh16, acc[ct]);
+        if constexpr (LO) {
+          const bf16x8 bl16 = as_bf(ld16(&s_lo[(ct * 16 + r16) * PADR + ks * 32 + kh * 8]));
+          acc[ct] = mfma16(qh[ks], bl16, acc[ct]);
+        }
+        if constexpr (QK != 0) acc[ct] = mfma16(ql[ks], bh16, acc[ct]);
+      }
+    }
+    // lane group kh holds rows rrow + i (i < 4): token t[i], head hh[i], own
+    // block cur[i] = (qbase + t) / block
+    int t[4], hh[4], cur[4], ncand[4];
+    {
+      int tt = rt, h = rh;
+      int c = p.causal ? (qbase + tt) / p.block : 0;
+      int crem = p.causal ? (qbase + tt) - c * p.block : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i > 0 && ++h == G) {
+          h = 0;
+          ++tt;
+          if (++crem == p.block) {
+            crem = 0;
+            ++c;
+          }
+        }
+        t[i] = tt;
+        hh[i] = h;
+        cur[i] = c;
+        ncand[i] = rrow + i < row_end ? (p.causal ? min(c, p.Nb) : p.Nb) : 0;
+      }
+    }
+    // each row's k best keys by repeated group maxima; the four rows' chains
+    // are independent and interleave
+    uint64_t key[4][4], res[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      res[i] = 0ull;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int j = ct * 16 + r16;
+        const uint64_t kk = make_key(acc[ct][i], (uint32_t)j);
+        key[i][ct] = j < ncand[i] ? kk : 0ull;
+      }
+    }
+    for (int r = 0; r < p.topk; ++r) {
+      uint64_t bst[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bst[i] = key[i][0];
+#pragma unroll
+        for (int ct = 1; ct < 4; ++ct) bst[i] = key[i][ct] > bst[i] ? key[i][ct] : bst[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bst[i] = group_max64(bst[i], r16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        res[i] = r16 == r ? bst[i] : res[i];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) key[i][ct] = key[i][ct] == bst[i] ? 0ull : key[i][ct];
+      }
+    }
+    // lanes 0 .. cnt-1 of the group hold a row's chosen blocks; each takes
+    // its rank among them (the first quad of the group reads its four
+    // lanes), which is its slot in the ascending list; the forced block
+    // follows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = r16 < p.topk && res[i] != 0ull;
+      const int cnt = __popc((uint32_t)(__ballot(valid) >> (16 * kh)) & 0xFFFFu);
+      const uint32_t my = key_index(res[i]);
+      const uint32_t v0 = dpp32<0x00>(my, my), v1 = dpp32<0x55>(my, my);
+      const uint32_t v2 = dpp32<0xAA>(my, my), v3 = dpp32<0xFF>(my, my);
+      const int rank = (cnt > 0 && v0 < my) + (cnt > 1 && v1 < my) + (cnt > 2 && v2 < my) + (cnt > 3 && v3 < my);
+      if (rrow + i < row_end) {
+        int32_t* out = sel_b + ((hk * G + hh[i]) * p.Lq + t[i]) * p.sel_w;
+        const int e = r16 < cnt ? rank : r16;
+        const int val = r16 < cnt ? (int)my : (r16 == cnt && p.causal ? cur[i] : -1);
+        if (e < p.sel_w) out[e] = val;
+        // cnt <= topk <= kSmallK: every slot from 16 on (a requested topk
+        // above the number of blocks) is padding
+        for (int e2 = 16 + r16; e2 < p.sel_w; e2 += 16) out[e2] = -1;
+      }
+    }
+    rrow += RT;
+    rows_advance(rt, rh, G, dt, dh);
+  }
+}
+
+// Host check and launch of the small-candidate path; false when it does not
+// apply.  About 2048 workgroups (eight per CU), at most kSmallTiles tiles per
+// wave.
+constexpr int kSmallTiles = 16;
+constexpr int kSmallWaves = 8;  // waves per workgroup (4: 0.152 ms, 8: 0.143 ms on the MoBA-style 32K gate)
+
+static bool gate_small_applies(const GateParams& p) {
+  if (p.nsplit != 1 || p.topk < 1 || p.topk > kSmallK || p.lens || p.per_group) return false;
+  if (p.qkind != 0 && p.qkind != 1) return false;
+  if (p.rows_per_bh <= 16) return false;
+  // row offsets inside one sequence's selection in 32-bit integers
+  if ((int64_t)p.Hs * p.Lq * p.sel_w >= ((int64_t)1 << 31)) return false;
+  const int64_t maxc = p.causal ? std::min<int64_t>(p.Nb, ((int64_t)p.Lk - 1) / p.block) : p.Nb;
+  return maxc <= 64;
+}
+
+template <int DG>
+static void gate_small_launch(const GateParams& p, hipStream_t s) {
+  const int64_t nbh = (int64_t)p.B * p.Hkv;
+  const int64_t rows = nbh * p.rows_per_bh;
+  constexpr int RT = 16 * kSmallWaves;
+  const int tpw = (int)std::max<int64_t>(1, std::min<int64_t>(kSmallTiles, rows / (2048 * RT)));
+  const int nwg = (p.rows_per_bh + RT * tpw - 1) / (RT * tpw);
+  const dim3 grid((unsigned)(nbh * nwg));
+  const bool lo = p.p_lo != nullptr;
+#define BSA_GATE_SMALL(QK, LO, FS) \
+  hipLaunchKernelGGL((gate_small_kernel<kSmallWaves, DG, QK, LO, FS>), grid, dim3(64 * kSmallWaves), 0, s, p, tpw, nwg);
+  if (p.p_f32) {
+    if (p.qkind == 0) { BSA_GATE_SMALL(0, true, true) } else { BSA_GATE_SMALL(1, true, true) }
+  } else if (p.qkind == 0) {
+    if (lo) { BSA_GATE_SMALL(0, true, false) } else { BSA_GATE_SMALL(0, false, false) }
+  } else {
+    if (lo) { BSA_GATE_SMALL(1, true, false) } else { BSA_GATE_SMALL(1, false, false) }
+  }
+#undef BSA_GATE_SMALL
+}
+
 template <int W, int DG, int KR>
 static void gate_dispatch_q(const GateParams& p, hipStream_t s, int grid) {
   const bool lo = p.p_lo != nullptr;
@@ -608,7 +881,10 @@ bool launch_gate(const GateParams& p, hipStream_t s) {
   const int grid = p.B * p.Hkv * p.nsplit * p.ntiles;
   {
     LaunchScope ls(p.tag && p.tag[0] == 'd' ? "decode_gate" : "gate_topk", s);
-    if (p.Dg == 128) {
+    if (W == 4 && gate_small_applies(p)) {
+      if (p.Dg == 128) gate_small_launch<128>(p, s);
+      else gate_small_launch<64>(p, s);
+    } else if (p.Dg == 128) {
       if (W == 4) gate_dispatch_k<4, 128>(p, s, grid);
       else gate_dispatch_k<1, 128>(p, s, grid);
     } else {

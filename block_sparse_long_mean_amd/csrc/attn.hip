@@ -1583,18 +1583,34 @@ bool launch_attn_backward(const AttnParams& p, int64_t nrows_out, hipStream_t s)
 
 // ---------------------------------------------------------------------------
 // Decode attention on MFMA: one wave per distinct (b, kv head, block) of the
-// decode's union, for every query head of the group at once.  S^T = K Q^T on
-// v_mfma_f32_32x32x16_bf16 with the keys as rows -- each lane loads its key
-// row's 16-byte pieces straight into the A operand (a block of one kv head is
-// contiguous in a head-major cache, so one load instruction reads 1 KB) --
-// and the group's query heads as columns (G of 32 used).  Online softmax per
-// column as in the gather; O^T += V^T P^T with each 64-key tile of values
-// copied by DMA into LDS (pieces permuted) and read transposed, the next
-// tile's copy in flight while the current one is used.  Writes each chosen
-// head's normalised partial and its log2-domain log-sum-exp, as the combine
-// reads them.
+// decode's union, for every query head of the group at once, on
+// v_mfma_f32_16x16x32_bf16 (at most 8 of its 16 columns are query heads, so
+// the accumulators, scores and operands stay small enough for two or more
+// waves per SIMD: one wave's loads are in flight while another computes).
+//  * S^T = K Q^T per 16-key tile kt: the A operand is the keys themselves --
+//    lane l loads 16 bytes of key row 16 kt + l % 16 (head dims 32 ks +
+//    8 (l / 16) ..), straight from the cache into registers -- and B the
+//    group's query heads as columns.  Lane l then holds column l % 16 and
+//    keys 16 kt + 4 (l / 16) + i, i < 4.
+//  * O^T += V^T P^T per 32-key step s: the B operand (P^T) of lane l takes
+//    its own probabilities of keys 32 s + 4 g + i and 32 s + 16 + 4 g + i
+//    (g = l / 16), rounded to bf16; the A operand (V^T) must list the same
+//    keys for head dim 16 dt + l % 16.  Each 64-key tile of values is copied
+//    by DMA into LDS (row-major, 16-byte pieces permuted as in the gather)
+//    and read with ds_read_b64_tr_b16: in a group of 16 lanes, lane i gets
+//    element i % 4 of the 8 bytes that lane i / 4 + 4 e addresses (e < 4),
+//    so lane c addressing V[k0 + c / 4][d0 + 4 (c % 4)] hands lane i keys
+//    k0 .. k0 + 3 of head dim d0 + i.
+//  * Online softmax per column with the gather's lazy rescale; the row sum l
+//    comes from the same bf16 probabilities through an all-ones A operand.
+// Writes each chosen head's normalised partial and its log2-domain
+// log-sum-exp, as the combine reads them.  Three waves per SIMD (168
+// registers at D = 128; left to itself the compiler takes 206, two waves).
 template <int D>
-__global__ __launch_bounds__(64) void decode_attend_mfma_kernel(DecodeAttnParams p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void decode_attend_mfma_kernel(DecodeAttnParams p) {
+  constexpr int KS = D / 32;  // 32-dim steps of a key row
+  constexpr int DT = D / 16;  // 16-dim tiles of the output
+  constexpr int RB = 2 * D;   // bytes per value row in LDS
   __shared__ __attribute__((aligned(16))) uint16_t s_v[KT * D];
   const int bh = blockIdx.x / p.umax, u = blockIdx.x % p.umax;
   if (u >= p.ucount[bh]) return;  // uniform
@@ -1618,50 +1634,122 @@ __global__ __launch_bounds__(64) void decode_attend_mfma_kernel(DecodeAttnParams
   // the block's first key and value row
   const uint16_t* kb = p.k + ko + (int64_t)hk * p.ks_h;
   const uint16_t* vb = p.v + vo + (int64_t)hk * p.vs_h;
-  const int lane = lane_id(), col = lane & 31, h = lane >> 5;
-  // B operand: column col = query head hk * G + col (zero past G)
-  bf16x8 qf[D / 16];
-  load_qf<D>(p.q + (int64_t)b * p.qs_b + (int64_t)(hk * p.G + (col < p.G ? col : 0)) * p.qs_h, col < p.G, qf);
-  float m = -INFINITY, l = 0.f;
-  f32x16 o[D / 32];
+  const int lane = lane_id(), col = lane & 15, g = lane >> 4;
+  // B operand of the scores: column col = query head hk * G + col (zero past G)
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qr = p.q + (int64_t)b * p.qs_b + (int64_t)(hk * p.G + (col < p.G ? col : 0)) * p.qs_h + 8 * g;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf(col < p.G ? ld16(qr + 32 * ks) : u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+  }
+  // LDS byte address this lane reads for head-dim tile dt of a value tile:
+  // row 4 g + col / 4 (+ 16 and + 32 keys as immediate offsets), head dims
+  // 16 dt + 4 (col % 4) ..; the piece permutation of a row depends only on
+  // the row's low bits, equal for every key offset used
+  const int vrow = 4 * g + (col >> 2);
+  const uint32_t vbase = lds_addr(s_v) + (uint32_t)(vrow * RB + 8 * (col & 1));
+  const int vpc = (col & 3) >> 1;  // piece within the dim tile's two
+  const int vsw = vswz<D>(vrow);
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int NV = KT * D / 8 / 64;  // DMA instructions per value tile
   for (int t0 = 0; t0 < nk; t0 += KT) {
     const int nt = min(KT, nk - t0);
     // the tile's values by DMA into LDS (the previous tile's P.V, which read
     // the buffer, waited for its own reads) and its keys straight into the A
-    // operand (lane: key 32 mt + col, head dims 16 s + 8 h), all in flight
-    // together
+    // operands, all in flight together
 #pragma unroll
     for (int i = 0; i < NV; ++i) dma_rows<D, false>(s_v, vb, p.vs_t, t0, nt, i);
-    bf16x8 kf[2][D / 16];
+    bf16x8 kf[4][KS];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int key = 32 * mt + col;
-      const uint16_t* kr = kb + (int64_t)(t0 + (key < nt ? key : 0)) * p.ks_t + 8 * h;
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = 16 * kt + col;
+      const uint16_t* kr = kb + (int64_t)(t0 + (key < nt ? key : 0)) * p.ks_t + 8 * g;
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st)
-        kf[mt][st] = as_bf(key < nt ? ld16(kr + 16 * st) : u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+      for (int ks = 0; ks < KS; ++ks)
+        kf[kt][ks] = as_bf(key < nt ? ld16(kr + 32 * ks) : u16x8{0, 0, 0, 0, 0, 0, 0, 0});
     }
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    f32x4 sc[4];
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      s0 = mfma32(kf[0][st], qf[st], s0);
-      s1 = mfma32(kf[1][st], qf[st], s1);
+    for (int kt = 0; kt < 4; ++kt) {
+      sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sc[kt] = mfma16(kf[kt][ks], qf[ks], sc[kt]);
     }
-    if (nt < KT) mask_tile(s0, s1, nt, h);
-    softmax_update<D>(s0, s1, m, l, o, p.sl2, t0 == 0);
+    // keys at or past nt -> -inf (key 16 kt + 4 g + i)
+    if (nt < KT) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[kt][i] = 16 * kt + 4 * g + i < nt ? sc[kt][i] : -INFINITY;
+    }
+    // column maximum over the tile: the lane's 16 scores, then the four
+    // lane groups holding the column
+    float tmax = max_raw(sc[0][0], sc[0][1]);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = (kt == 0 ? 2 : 0); i < 4; i += 2) tmax = max3_raw(tmax, sc[kt][i], sc[kt][i + 1]);
+    tmax = max_raw(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = max_raw(tmax, __shfl_xor(tmax, 32, 64));
+    const float tm = tmax * p.sl2;
+    if (t0 == 0) {
+      m = tm;
+    } else {
+      const bool grow = tm > m + kRescaleLog2;
+      if (__ballot(grow) != 0ull) {
+        const float mnew = grow ? tm : m;
+        const float corr = __builtin_amdgcn_exp2f(m - mnew);
+        l *= corr;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
+        m = mnew;
+      }
+    }
+    // probabilities 2^(s sl2 - m) as the B operands of the two 32-key steps
+    bf16x8 pb[2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pr = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fmaf(sc[kt][i], p.sl2, -m));
+        pb[kt >> 1][4 * (kt & 1) + i] = (__bf16)pr;
+      }
+    {
+      const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                           (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+      f32x4 rsum = mfma16(ones, pb[0], f32x4{0.f, 0.f, 0.f, 0.f});
+      rsum = mfma16(ones, pb[1], rsum);
+      l += rsum[0];
+    }
     // the values' copy must have landed: the compiler may order the copy
     // after the key loads, so their wait does not cover it
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    pv_tile<D>(s_v, s0, s1, o, t0 == 0, l);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t va = vbase + (uint32_t)(((2 * dt + vpc) ^ vsw) * 16);
+      u16x4 x0, x1, x2, x3;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %4 offset:0\n\tds_read_b64_tr_b16 %1, %4 offset:%5\n\t"
+          "ds_read_b64_tr_b16 %2, %4 offset:%6\n\tds_read_b64_tr_b16 %3, %4 offset:%7\n\ts_waitcnt lgkmcnt(0)"
+          : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+          : "v"(va), "n"(16 * RB), "n"(32 * RB), "n"(48 * RB)
+          : "memory");
+      const u16x8 a0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      const u16x8 a1 = {x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
+      o[dt] = mfma16(as_bf(a0), pb[0], o[dt]);
+      o[dt] = mfma16(as_bf(a1), pb[1], o[dt]);
+    }
   }
   if (col < p.G && ((mask >> col) & 1)) {
     const int64_t pidx = ((int64_t)bh * p.umax + u) * p.G + col;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    store_cols<D>(p.part_o + pidx * D, o, inv);
-    if (h == 0) p.part_lse[pidx] = l > 0.f ? m + __log2f(l) : -INFINITY;
+    float* dst = p.part_o + pidx * D + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt] * inv;
+    if (g == 0) p.part_lse[pidx] = l > 0.f ? m + __log2f(l) : -INFINITY;
   }
 }
 

@@ -677,27 +677,35 @@ __global__ __launch_bounds__(64 * W, 8 / W) void attn_gather_kernel(AttnParams p
 // ---------------------------------------------------------------------------
 // Gather for sparse buckets (a few rows per selected block, as when a short
 // query chunk selects from a very long memory): the MFMA gather would stage
-// each block for one or two rows.  Here one wave takes one work item and
-// streams its block's keys and values straight from HBM, flash-decoding
-// style, with no workgroup barrier (so many items per CU are in flight):
-// lane k scores key k of a 64-key pass against the rows' queries (read from
-// LDS by broadcast), an fp32 online softmax per row runs across the wave, and
-// for the weighted values each lane owns D/64 head dims and takes every key's
-// probability by v_readlane.  Rows go two at a time; the partials have the
-// gather's format.
+// each block in LDS for one or two rows of a 32-row tile.  Here one wave takes
+// one work item and streams its block from HBM as the decode attention does:
+// v_mfma_f32_16x16x32_bf16 with the block's keys as the A operand of
+// S^T = K Q^T, loaded straight into registers (lane l: key 16 kt + l % 16,
+// head dims 32 ks + 8 (l / 16) ..), the item's rows as the 16 columns (its
+// query rows, 16 at a time; most items hold one or two), and each 64-key
+// tile of values copied by DMA into LDS and read transposed for
+// O^T += V^T P^T (keys 32 s + 4 g + i and 32 s + 16 + 4 g + i of the B
+// operand P^T, g = lane / 16, as in the decode attention).  Online softmax
+// per column with the lazy rescale of the MFMA gather; per-key causal masks.
+// The partials have the gather's format (16-bit with a row exponent, and
+// (m', l') in the log2 domain).  No workgroup barrier, so many items per CU
+// are in flight: two waves per SIMD (226 registers at D = 128; three spill),
+// 16 KB of LDS per wave.
+// DMA of a 64-row tile of consecutive rows (defined with the backward)
+template <int D, bool PAD>
+BSA_DEV void dma_rows(uint16_t* tile, const uint16_t* base, int64_t rs, int row0, int n_valid, int i);
+
 template <int D>
-// four workgroups per CU (four waves per SIMD): each wave's item is a
-// chain of dependent loads (queries, the key rows, the values), so the
-// number of items in flight sets the bandwidth
-__global__ __launch_bounds__(256, 4) void attn_sparse_kernel(AttnParams p) {
-  constexpr int NR = 2;        // rows per pass (most sparse buckets hold one or two)
-  constexpr int DPL = D / 64;  // head dims per lane (values)
-  __shared__ __attribute__((aligned(16))) float s_q[4][NR][D];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_sparse_kernel(AttnParams p) {
+  constexpr int KS = D / 32;  // 32-dim steps of a key row
+  constexpr int DT = D / 16;  // 16-dim tiles of the output
+  constexpr int RB = 2 * D;   // bytes per value row in LDS
+  constexpr int NV = KT * D / 8 / 64;  // DMA instructions per value tile
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[KT * D];
   const int it_lo = p.tile_off[(int64_t)p.c0 * p.Nb];
   const int nitems = p.tile_off[(int64_t)p.c1 * p.Nb] - it_lo;
-  const int item = (int)blockIdx.x * 4 + w;
-  if (item >= nitems) return;  // wave-uniform; no workgroup barrier follows
+  const int item = (int)blockIdx.x;
+  if (item >= nitems) return;  // uniform
   const int4 rec = load_item((const_int_ptr)p.items, it_lo + item);
   const int bucket = rec.x, hk = rec.w & 0xFFFF, b = rec.w >> 16;
   const int cid = bucket / p.Nb;
@@ -708,129 +716,139 @@ __global__ __launch_bounds__(256, 4) void attn_sparse_kernel(AttnParams p) {
   const int n_keys = min(p.block, p.Lk - key0);
   const uint16_t* kb = p.k + (int64_t)b * p.ks_b + (int64_t)hk * p.ks_h;
   const uint16_t* vb = p.v + (int64_t)b * p.vs_b + (int64_t)hk * p.vs_h;
-  for (int r0 = 0; r0 < rec.z; r0 += NR) {
-    const int nr = min(NR, rec.z - r0);
-    GRow g[NR];
-    int qpos[NR];
+  const int lane = lane_id(), col = lane & 15, g = lane >> 4;
+  // LDS byte address of this lane's transposing reads (see the decode
+  // attention): row 4 g + col / 4, head dims 16 dt + 4 (col % 4) ..
+  const int vrow = 4 * g + (col >> 2);
+  const uint32_t vbase = lds_addr(s_v) + (uint32_t)(vrow * RB + 8 * (col & 1));
+  const int vpc = (col & 3) >> 1;
+  const int vsw = vswz<D>(vrow);
+  for (int r0 = 0; r0 < rec.z; r0 += 16) {
+    // column col = row r0 + col of the item
+    const int lr = r0 + col;
+    const bool cv = lr < rec.z;
+    const GRow gr = grow_of(p, rec, entry_of(p, rec, lr), lr);
+    const int qpos = (p.causal && cv) ? p.Lk - p.Lq + gr.t : 0x7FFFFFFF;
+    bf16x8 qf[KS];
+    {
+      const uint16_t* qr = q_row<D>(p, rec, gr) + 8 * g;
 #pragma unroll
-    for (int a = 0; a < NR; ++a) {
-      const int lr = r0 + (a < nr ? a : 0);
-      g[a] = grow_of(p, rec, entry_of(p, rec, lr), lr);
-      qpos[a] = p.causal ? p.Lk - p.Lq + g[a].t : 0x7FFFFFFF;
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf(cv ? ld16(qr + 32 * ks) : u16x8{0, 0, 0, 0, 0, 0, 0, 0});
     }
-    __builtin_amdgcn_wave_barrier();  // the previous rows' queries are no longer read
+    float m = -INFINITY, l = 0.f;
+    f32x4 o[DT];
 #pragma unroll
-    for (int a = 0; a < NR; ++a) {
-      const uint16_t* qr = q_row<D>(p, rec, g[a]);
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t0 = 0; t0 < n_keys; t0 += KT) {
+      const int nt = min(KT, n_keys - t0);
+      // values by DMA into LDS (the previous tile's P.V waited for its own
+      // reads), keys straight into the A operands, all in flight together
 #pragma unroll
-      for (int d = lane; d < D; d += 64) s_q[w][a][d] = a < nr ? bf2f(qr[d]) : 0.f;
-    }
-    __builtin_amdgcn_wave_barrier();
-    float m[NR], l[NR], acc[NR][DPL];
+      for (int i = 0; i < NV; ++i) dma_rows<D, false>(s_v, vb, p.vs_t, key0 + t0, nt, i);
+      bf16x8 kf[4][KS];
 #pragma unroll
-    for (int a = 0; a < NR; ++a) {
-      m[a] = -INFINITY;
-      l[a] = 0.f;
+      for (int kt = 0; kt < 4; ++kt) {
+        const int key = 16 * kt + col;
+        const uint16_t* kr = kb + (int64_t)(key0 + t0 + (key < nt ? key : 0)) * p.ks_t + 8 * g;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[a][e] = 0.f;
-    }
-    for (int k0 = 0; k0 < n_keys; k0 += 64) {
-      asm volatile("" ::: "memory");  // the query reads below stay in the pass (not hoisted: NR rows x D floats)
-      const int key = k0 + lane;
-      const bool kv = key < n_keys;
-      const uint16_t* krow = kb + (int64_t)(key0 + (kv ? key : 0)) * p.ks_t;
-      // scores of this lane's key against the rows: the whole key row is
-      // loaded at once (D/8 16-byte pieces in flight together)
-      float sc[NR];
-#pragma unroll
-      for (int a = 0; a < NR; ++a) sc[a] = 0.f;
-      u16x8 kx[D / 8];
-#pragma unroll
-      for (int c = 0; c < D / 8; ++c) kx[c] = kv ? ld16(krow + c * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-#pragma unroll
-        for (int a = 0; a < NR; ++a) {
-          const f32x4 q0 = *reinterpret_cast<const f32x4*>(&s_q[w][a][c * 8]);
-          const f32x4 q1 = *reinterpret_cast<const f32x4*>(&s_q[w][a][c * 8 + 4]);
-          float part = sc[a];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) part = fmaf(q0[e], bf2f(kx[c][e]), part);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) part = fmaf(q1[e], bf2f(kx[c][4 + e]), part);
-          sc[a] = part;
-        }
-        // the step's sums are complete before the next step's query reads
-        // (so that not all NR x D query values are read ahead and held)
-#pragma unroll
-        for (int a = 0; a < NR; ++a) asm volatile("" : "+v"(sc[a])::"memory");
+        for (int ks = 0; ks < KS; ++ks)
+          kf[kt][ks] = as_bf(key < nt ? ld16(kr + 32 * ks) : u16x8{0, 0, 0, 0, 0, 0, 0, 0});
       }
-      // this pass's values: lane owns head dims lane*DPL .. +DPL-1 of every
-      // key; 16 keys' values per batch, the next batch in flight while the
-      // current one is used
-      const int nk = min(64, n_keys - k0);
-      const uint16_t* vr0 = vb + (int64_t)(key0 + k0) * p.vs_t + lane * DPL;
-      auto load_v = [&](int kk0, uint32_t (&vx)[16]) {
+      f32x4 sc[4];
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-          const int kq = kk0 + kk;
-          const uint16_t* vr = vr0 + (int64_t)(kq < nk ? kq : 0) * p.vs_t;
-          vx[kk] = kq < nk ? (DPL == 2 ? *reinterpret_cast<const uint32_t*>(vr) : (uint32_t)*vr) : 0u;
-        }
-      };
-      uint32_t vcur[16], vnext[16];
-      load_v(0, vnext);
-      float pr[NR];
+      for (int kt = 0; kt < 4; ++kt) {
+        sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int a = 0; a < NR; ++a) {
-        const float x = (kv && key0 + key <= qpos[a]) ? sc[a] * p.sl2 : -INFINITY;
-        const float mnew = fmaxf(m[a], wave_max(x));
-        const float e0 = mnew == -INFINITY ? 0.f : exp2f(x - mnew);
-        const float c = mnew == -INFINITY ? 1.f : exp2f(m[a] - mnew);
-        l[a] = l[a] * c + wave_sum(e0);
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[a][e] *= c;
-        m[a] = mnew;
-        pr[a] = e0;
+        for (int ks = 0; ks < KS; ++ks) sc[kt] = mfma16(kf[kt][ks], qf[ks], sc[kt]);
       }
-      for (int kk0 = 0; kk0 < nk; kk0 += 16) {
+      // keys past the block or after the column's query -> -inf (key
+      // t0 + 16 kt + 4 g + i of the block)
+      const int rel = qpos - (key0 + t0);  // the column's query, relative to the tile
+      const int lim = rel >= nt - 1 ? nt : rel + 1;
+      if (lim < KT) {
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) vcur[kk] = vnext[kk];
-        if (kk0 + 16 < nk) load_v(kk0 + 16, vnext);
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-          const int kq = kk0 + kk;
-          if (kq < nk) {  // wave-uniform
-            const float v0 = bf2f((uint16_t)(vcur[kk] & 0xFFFFu)), v1 = bf2f((uint16_t)(vcur[kk] >> 16));
-#pragma unroll
-            for (int a = 0; a < NR; ++a) {
-              const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr[a]), kq));
-              acc[a][0] = fmaf(pw, v0, acc[a][0]);
-              if constexpr (DPL == 2) acc[a][1] = fmaf(pw, v1, acc[a][1]);
-            }
-          }
-        }
+          for (int i = 0; i < 4; ++i) sc[kt][i] = 16 * kt + 4 * g + i < lim ? sc[kt][i] : -INFINITY;
       }
-    }
-    // partial rows (16-bit with a row exponent, as the MFMA gather writes
-    // them): lane writes its head dims; lane 0 writes (m', l')
-    for (int a = 0; a < nr; ++a) {
-      const int hsel = p.per_group ? 0 : g[a].hs - hk * p.G;
-      const int64_t prow = (prow_base + hsel) * p.CT + (g[a].t - t_base);
-      const int64_t pidx = (prow * p.kslot + g[a].slot) * p.R + g[a].rr;
-      uint16_t* dst = p.part_o + pidx * D + lane * DPL;
-      float mx = fabsf(acc[a][0]);
-      if constexpr (DPL == 2) mx = fmaxf(mx, fabsf(acc[a][1]));
-      const int ex = part_exponent(wave_max(mx));
-      const uint32_t packed = pack_norm2(acc[a][0], DPL == 2 ? acc[a][DPL - 1] : 0.f, ex);
-      if constexpr (DPL == 2) {
-        __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t*>(dst));
+      float tmax = max_raw(sc[0][0], sc[0][1]);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = (kt == 0 ? 2 : 0); i < 4; i += 2) tmax = max3_raw(tmax, sc[kt][i], sc[kt][i + 1]);
+      tmax = max_raw(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = max_raw(tmax, __shfl_xor(tmax, 32, 64));
+      const float tm = tmax * p.sl2;
+      if (t0 == 0) {
+        m = tm;
       } else {
-        __builtin_nontemporal_store((uint16_t)packed, dst);
+        const bool grow = tm > m + kRescaleLog2;
+        if (__ballot(grow) != 0ull) {
+          const float mnew = grow ? tm : m;
+          const float corr = __builtin_amdgcn_exp2f(m - mnew);
+          l *= corr;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
+          m = mnew;
+        }
       }
-      if (lane == 0) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pr = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fmaf(sc[kt][i], p.sl2, -m));
+          pb[kt >> 1][4 * (kt & 1) + i] = (__bf16)pr;
+        }
+      {
+        const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                             (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+        f32x4 rsum = mfma16(ones, pb[0], f32x4{0.f, 0.f, 0.f, 0.f});
+        rsum = mfma16(ones, pb[1], rsum);
+        l += rsum[0];
+      }
+      // the values' copy must have landed (see the decode attention)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t va = vbase + (uint32_t)(((2 * dt + vpc) ^ vsw) * 16);
+        u16x4 x0, x1, x2, x3;
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %4 offset:0\n\tds_read_b64_tr_b16 %1, %4 offset:%5\n\t"
+            "ds_read_b64_tr_b16 %2, %4 offset:%6\n\tds_read_b64_tr_b16 %3, %4 offset:%7\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+            : "v"(va), "n"(16 * RB), "n"(32 * RB), "n"(48 * RB)
+            : "memory");
+        const u16x8 a0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        const u16x8 a1 = {x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
+        o[dt] = mfma16(as_bf(a0), pb[0], o[dt]);
+        o[dt] = mfma16(as_bf(a1), pb[1], o[dt]);
+      }
+    }
+    // partial row of column col: 16-bit with the row's exponent (its D dims
+    // sit in the four lanes col, col + 16, col + 32, col + 48), then (m', l')
+    float mx = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(o[dt][i]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const int ex = part_exponent(mx);
+    if (cv) {
+      const int hsel = p.per_group ? 0 : gr.hs - hk * p.G;
+      const int64_t prow = (prow_base + hsel) * p.CT + (gr.t - t_base);
+      const int64_t pidx = (prow * p.kslot + gr.slot) * p.R + gr.rr;
+      uint16_t* dst = p.part_o + pidx * D + 4 * g;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x2 pk = {pack_norm2(o[dt][0], o[dt][1], ex), pack_norm2(o[dt][2], o[dt][3], ex)};
+        __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(dst + 16 * dt));
+      }
+      if (g == 0) {
         typedef float f32x2 __attribute__((ext_vector_type(2)));
-        __builtin_nontemporal_store(f32x2{m[a] + (float)ex, __builtin_amdgcn_ldexpf(l[a], -ex)},
+        __builtin_nontemporal_store(f32x2{m + (float)ex, __builtin_amdgcn_ldexpf(l, -ex)},
                                     reinterpret_cast<f32x2*>(&p.part_ml[pidx]));
       }
     }
@@ -956,11 +974,11 @@ static void launch_gather_dw(const AttnParams& p, hipStream_t s) {
 bool launch_attn_gather(const AttnParams& p, hipStream_t s) {
   if (p.sparse_items > 0) {
     LaunchScope ls("attn_gather", s, 2);
-    const unsigned grid = (unsigned)((p.sparse_items + 3) / 4);  // one wave per item
+    const unsigned grid = (unsigned)p.sparse_items;  // one wave per item
     if (p.D == 128)
-      hipLaunchKernelGGL(attn_sparse_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(attn_sparse_kernel<128>, dim3(grid), dim3(64), 0, s, p);
     else
-      hipLaunchKernelGGL(attn_sparse_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(attn_sparse_kernel<64>, dim3(grid), dim3(64), 0, s, p);
     return launch_ok("attn_gather");
   }
   {

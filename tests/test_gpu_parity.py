@@ -272,14 +272,17 @@ def test_prerotated_keys_equal_internal_rotation(bsa):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
-@pytest.mark.parametrize("case", ["memory_split_candidates", "causal_group", "causal_head"])
+@pytest.mark.parametrize("case", ["memory_split_candidates", "causal_group", "causal_head", "causal_head_small"])
 def test_gate_planes_equal_fp32_summaries(bsa, case):
     """Summaries handed to the prefill as the gate's bf16 planes (written by the block summary) give
     the same selection and the same output, bit for bit, as the fp32 summaries they split; and the
     planes are that split: hi = bf16(s), lo = bf16(s - hi), round to nearest even."""
     causal = case != "memory_split_candidates"
     gate = "group" if case == "causal_group" else "head"
-    if causal:
+    if case == "causal_head_small":
+        # at most 46 candidates and k = 3: the gate's small-candidate path stages either form
+        B, Lq, Lk, Hq, Hkv, D, block, topk = 1, 3000, 3000, 8, 2, 128, 64, 3
+    elif causal:
         B, Lq, Lk, Hq, Hkv, D, block, topk = 1, 3000, 3000, 8, 2, 128, 64, 6
     else:  # a few queries over a long memory: the candidates split over workgroups, then merged
         B, Lq, Lk, Hq, Hkv, D, block, topk = 1, 128, 200000, 8, 2, 128, 64, 16

@@ -71,15 +71,16 @@ BSA_DEV uint64_t shfl64(uint64_t v, int src) {
 // operand modifier, no LDS round trip).  Controls: quad_perm [1,0,3,2] = 0xB1,
 // quad_perm [2,3,0,1] = 0x4E, row_shl:n = 0x100+n (lane i reads i+n),
 // row_shr:n = 0x110+n (lane i reads i-n), row_ror:n = 0x120+n (lane i reads
-// (i-n) mod 16).  Lanes whose source falls outside the row keep `old`.
+// (i-n) mod 16).  Lanes whose source falls outside the row read 0 (so no
+// prior value has to be copied into the destination first).
 template <int CTRL>
-BSA_DEV uint32_t dpp32(uint32_t old, uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, 0xF, 0xF, false);
+BSA_DEV uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 BSA_DEV uint64_t dpp64(uint64_t v) {
   const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  return ((uint64_t)dpp32<CTRL>(hi, hi) << 32) | dpp32<CTRL>(lo, lo);
+  return ((uint64_t)dpp32<CTRL>(hi) << 32) | dpp32<CTRL>(lo);
 }
 // value held by lane (li ^ M) of the same row, M in {1, 2, 4, 8}; li = lane % 16
 template <int M>
@@ -108,15 +109,15 @@ BSA_DEV uint64_t row_xor64_any(uint64_t v, int m, int li) {
 BSA_DEV int row_xor32_any(int v, int m, int li) {
   const uint32_t u = (uint32_t)v;
   switch (m) {
-    case 1: return (int)dpp32<0xB1>(u, u);
-    case 2: return (int)dpp32<0x4E>(u, u);
+    case 1: return (int)dpp32<0xB1>(u);
+    case 2: return (int)dpp32<0x4E>(u);
     case 4: {
       // both exchanges run on every lane (a lane must not read a lane that a
       // branch has switched off), then each lane keeps its partner's value
-      const uint32_t up = dpp32<0x104>(u, u), dn = dpp32<0x114>(u, u);
+      const uint32_t up = dpp32<0x104>(u), dn = dpp32<0x114>(u);
       return (int)((li & 4) ? dn : up);
     }
-    default: return (int)dpp32<0x128>(u, u);
+    default: return (int)dpp32<0x128>(u);
   }
 }
 
@@ -166,6 +167,14 @@ BSA_DEV uint32_t order_f32(float s) {
   uint32_t u = __float_as_uint(s);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// One side of a compare-exchange with partner o: the larger of the two when
+// keep_max, else the smaller.  Selecting the partner on (v > o) != keep_max
+// takes one compare and one select per 32-bit half, instead of forming both
+// the maximum and the minimum and then choosing.  Equal operands are the same
+// value either way.
+BSA_DEV uint64_t cx_keep(uint64_t v, uint64_t o, bool keep_max) { return ((v > o) != keep_max) ? o : v; }
+BSA_DEV int cx_keep_i32(int v, int o, bool keep_max) { return ((v > o) != keep_max) ? o : v; }
+
 BSA_DEV uint64_t make_key(float s, uint32_t j) {
   return ((uint64_t)order_f32(s) << 32) | (uint64_t)(0xFFFFFFFFu - j);
 }
@@ -203,9 +212,7 @@ BSA_DEV void wave_sort_desc(uint64_t (&v)[V]) {
           const bool lower = (lane & stride) == 0;
           const bool desc = (e & size) == 0;
           const bool keep_max = (lower == desc);
-          const uint64_t mx = v[i] > o ? v[i] : o;
-          const uint64_t mn = v[i] > o ? o : v[i];
-          v[i] = keep_max ? mx : mn;
+          v[i] = cx_keep(v[i], o, keep_max);
         }
       }
     }
@@ -223,7 +230,7 @@ BSA_DEV int wave_sort_asc_i32(int v) {
       const bool lower = (lane & stride) == 0;
       const bool asc = (lane & size) == 0;
       const bool keep_min = (lower == asc);
-      v = keep_min ? min(v, o) : max(v, o);
+      v = cx_keep_i32(v, o, !keep_min);
     }
   }
   return v;

@@ -141,8 +141,7 @@ BSA_DEV uint64_t group_sort16_asc(uint64_t v, int li) {
       const uint64_t o = row_xor64_any(v, stride, li);
       const bool lower = (li & stride) == 0;
       const bool asc = (li & size) == 0 || size == 16;
-      const uint64_t mx = v > o ? v : o, mn = v > o ? o : v;
-      v = (lower == asc) ? mn : mx;
+      v = cx_keep(v, o, lower != asc);
     }
   }
   return v;
@@ -177,8 +176,7 @@ BSA_DEV void list_merge16(uint64_t (&L)[KR], uint64_t b, int li, int topk) {
       for (int r = 0; r < KR; ++r) {
         const uint64_t o = row_xor64_any(L[r], stride, li);
         const bool lower = (li & stride) == 0;
-        const uint64_t mx = L[r] > o ? L[r] : o, mn = L[r] > o ? o : L[r];
-        L[r] = lower ? mx : mn;
+        L[r] = cx_keep(L[r], o, lower);
       }
     }
   }
@@ -214,8 +212,7 @@ BSA_DEV void group_sort_asc(int (&v)[NR], int li) {
           const int o = row_xor32_any(v[r], stride, li);
           const bool lower = (li & stride) == 0;
           const bool asc = ((r * 16 + li) & size) == 0;
-          const int mn = v[r] < o ? v[r] : o, mx = v[r] < o ? o : v[r];
-          v[r] = (lower == asc) ? mn : mx;
+          v[r] = cx_keep_i32(v[r], o, lower != asc);
         }
       }
     }
@@ -456,10 +453,10 @@ __global__ __launch_bounds__(64 * W, (gate_min_blocks<W, DG, KR>())) void gate_k
       // slots: exclusive scan of the per-lane counts over the 16-lane group
       const int n_me = __popc(pend);
       int inc = n_me;
-      inc += (int)dpp32<0x111>(0u, (uint32_t)inc);  // row_shr:1
-      inc += (int)dpp32<0x112>(0u, (uint32_t)inc);  // row_shr:2
-      inc += (int)dpp32<0x114>(0u, (uint32_t)inc);  // row_shr:4
-      inc += (int)dpp32<0x118>(0u, (uint32_t)inc);  // row_shr:8
+      inc += (int)dpp32<0x111>((uint32_t)inc);  // row_shr:1
+      inc += (int)dpp32<0x112>((uint32_t)inc);  // row_shr:2
+      inc += (int)dpp32<0x114>((uint32_t)inc);  // row_shr:4
+      inc += (int)dpp32<0x118>((uint32_t)inc);  // row_shr:8
       // group totals (lane 15 of each group)
       const int n0 = __builtin_amdgcn_readlane(inc, 15), n1 = __builtin_amdgcn_readlane(inc, 31);
       const int n2 = __builtin_amdgcn_readlane(inc, 47), n3 = __builtin_amdgcn_readlane(inc, 63);
@@ -789,8 +786,8 @@ __global__ __launch_bounds__(64 * W) void gate_small_kernel(GateParams p, int tp
       const bool valid = r16 < p.topk && res[i] != 0ull;
       const int cnt = __popc((uint32_t)(__ballot(valid) >> (16 * kh)) & 0xFFFFu);
       const uint32_t my = key_index(res[i]);
-      const uint32_t v0 = dpp32<0x00>(my, my), v1 = dpp32<0x55>(my, my);
-      const uint32_t v2 = dpp32<0xAA>(my, my), v3 = dpp32<0xFF>(my, my);
+      const uint32_t v0 = dpp32<0x00>(my), v1 = dpp32<0x55>(my);
+      const uint32_t v2 = dpp32<0xAA>(my), v3 = dpp32<0xFF>(my);
       const int rank = (cnt > 0 && v0 < my) + (cnt > 1 && v1 < my) + (cnt > 2 && v2 < my) + (cnt > 3 && v3 < my);
       if (rrow + i < row_end) {
         int32_t* out = sel_b + ((hk * G + hh[i]) * p.Lq + t[i]) * p.sel_w;

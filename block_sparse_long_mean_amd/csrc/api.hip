@@ -277,12 +277,16 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
   const int ncand_max = P.Nb;
   P.nsplit = 1;
   if (P.bf16 && P.topk > 0 && base_wg < 2048) {
-    // Too few row tiles to fill the chip: split the candidates, aiming at
-    // about 512 workgroups (two per CU).  Each split pays for its own top-k
-    // warm-up and merge entries, so more splits cost more than they gain: the
-    // 10M-token memory's 512-query chunk (256 row tiles) measured gate + merge
-    // 4.07 ms with 2 splits, 4.6 with 4, 5.2 with 8, 6.0 with 16, 5.7 with 1.
-    const int want = (int)std::min<int64_t>((512 + base_wg - 1) / base_wg, (ncand_max + 255) / 256);
+    // Too few row tiles to fill the chip: split the candidates, aiming at the
+    // workgroups the device holds at once -- three per CU for lists of more
+    // than 16 keys (their summaries staged by DMA, three waves per SIMD), two
+    // otherwise.  Each split pays for its own top-k warm-up and merge
+    // entries, so more splits than that cost more than they gain: the 10M-token
+    // memory's 512-query chunk (256 row tiles, top-64) measured its gate at
+    // 3.37 ms with 3 splits and 3.77 with 2 (gate + merge with registers
+    // staging the summaries: 4.07 ms with 2, 4.6 with 4, 5.2 with 8, 5.7 with 1).
+    const int fill = P.topk > 16 ? 768 : 512;
+    const int want = (int)std::min<int64_t>((fill + base_wg - 1) / base_wg, (ncand_max + 255) / 256);
     P.nsplit = std::max(1, want);
   }
   P.span = (ncand_max + P.nsplit - 1) / P.nsplit;

@@ -246,6 +246,25 @@ BSA_DEV uint64_t group_max64(uint64_t v, int li) {
 // its lane) instead of the list merge: a few DPP butterflies per chosen key.
 constexpr int kSmallK = 4;
 
+// DMA instruction i of a chunk of 64 summary rows into the padded LDS layout
+// (rows of DG + 8 elements): global_load_lds puts lane l's 16 bytes at the
+// wave-uniform LDS base + 16 l, so the lanes walk the padded positions in
+// order; a lane whose position is a row's padding loads piece 0 of that row
+// again, and rows past n_valid load the chunk's first row (finite values whose
+// keys are masked out).  DG / 8 + 1 instructions cover a chunk.
+typedef __attribute__((address_space(3))) void* gate_lds_ptr_t;
+template <int DG>
+BSA_DEV void gate_dma_rows(uint16_t* tile, const uint16_t* base, int64_t rs, int row0, int n_valid, int i) {
+  constexpr int RP = DG / 8 + 1;
+  const int P = i * 64 + lane_id();
+  const int r = P / RP;
+  int c = P % RP;
+  c = c == RP - 1 ? 0 : c;
+  const int rr = r < n_valid ? r : 0;
+  __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)(row0 + rr) * rs + c * 8),
+                                   (gate_lds_ptr_t)(tile + i * 512), 16, 0, 0);
+}
+
 // FS: the summaries come as fp32 (p_f32) and are split into the hi / lo
 // planes as each chunk is staged in LDS (LO is then true)
 // Occupancy requested per instantiation (workgroups of W waves per CU), set
@@ -264,6 +283,13 @@ __global__ __launch_bounds__(64 * W, (gate_min_blocks<W, DG, KR>())) void gate_k
   constexpr int CPR = DG / 8;                       // 16-byte chunks per summary row
   constexpr int NPF = (64 * CPR + 64 * W - 1) / (64 * W);  // chunks per thread per plane
   constexpr int STAGE_BYTES = (LO ? 2 : 1) * 64 * PADR * 2;
+  // bf16 planes are copied by DMA straight into the stage buffer, the next
+  // chunk's copy issued once every wave has scored the current one, so that
+  // it is in flight during the top-k work, with no registers held for it
+  // (lists of 32 or 64 keys: the registers then allow three waves per SIMD);
+  // fp32 summaries, and the instantiations with an occupancy request, go
+  // through registers
+  constexpr bool DMA = !FS && gate_min_blocks<W, DG, KR>() == 1;
   constexpr int SMEM = STAGE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   // per (wave, lane group): the chunk's candidates that beat the row's k-th key
@@ -349,9 +375,24 @@ __global__ __launch_bounds__(64 * W, (gate_min_blocks<W, DG, KR>())) void gate_k
       }
     }
   };
-  if (c_lo < c_hi) fetch(c_lo);
+  // the DMA form: a wave's share of the copy instructions of one chunk
+  auto dma_chunk = [&](int c0) {
+    for (int i = w; i < DG / 8 + 1; i += W) {
+      gate_dma_rows<DG>(s_hi, phi, p.ps_j, c0, c_hi - c0, i);
+      if constexpr (LO) gate_dma_rows<DG>(s_lo, plo, p.ps_j, c0, c_hi - c0, i);
+    }
+  };
+  if (c_lo < c_hi) {
+    if constexpr (DMA) dma_chunk(c_lo);
+    else fetch(c_lo);
+  }
 
   for (int c0 = c_lo; c0 < c_hi; c0 += 64) {
+    if constexpr (DMA) {
+      // this chunk's copy has landed (every wave waits for its own share)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    } else {
     __syncthreads();
 #pragma unroll
     for (int n = 0; n < NPF; ++n) {
@@ -377,6 +418,7 @@ __global__ __launch_bounds__(64 * W, (gate_min_blocks<W, DG, KR>())) void gate_k
     }
     __syncthreads();
     if (c0 + 64 < c_hi) fetch(c0 + 64);
+    }
     f32x4 acc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -391,6 +433,12 @@ __global__ __launch_bounds__(64 * W, (gate_min_blocks<W, DG, KR>())) void gate_k
         }
         if constexpr (QK != 0) acc[ct] = mfma16(ql[ks], bh16, acc[ct]);
       }
+    }
+    if constexpr (DMA) {
+      // every wave has read the chunk (its MFMAs consumed the reads): the
+      // next chunk's copy overwrites it during the top-k work below
+      __syncthreads();
+      if (c0 + 64 < c_hi) dma_chunk(c0 + 64);
     }
     if (KR == 1 && p.topk <= kSmallK && c_lo + 64 >= c_hi) {
       // the row's only chunk and a small k: the k best keys directly, in

@@ -263,6 +263,7 @@ static bsa_status plan_prefill(const bsa_prefill_args* a, PrefillPlan& P, char* 
     const int64_t fit = std::max<int64_t>(1, budget / std::max<int64_t>(1, per_tok * P.CT));
     P.CPL = (int)std::min<int64_t>(nbh * P.NC, a->chunks_per_pass > 0 ? a->chunks_per_pass : fit);
     if (nbh * P.NC * P.Nb >= (int64_t)1 << 30) return fail(BSA_ERR_UNSUPPORTED, "too many (chunk, block) buckets");
+    if (nbh * P.NC * P.CT * P.G >= (int64_t)1 << 31) return fail(BSA_ERR_UNSUPPORTED, "too many query rows");
   }
   P.nbk = a->B * a->Hkv * P.NC * P.Nb;
   P.max_entries = P.nsel_rows * (P.topk + (a->causal ? 1 : 0));

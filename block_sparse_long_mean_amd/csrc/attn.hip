@@ -868,18 +868,21 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int li = lane % LPR;
   // rows of this launch: (chunk - c0, token in chunk, head in group), so a
-  // token's G output heads are adjacent
-  const int64_t nrows = (int64_t)(p.c1 - p.c0) * p.CT * p.G;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + w) * RPW + lane / LPR;
-  const int64_t rr_ = row < nrows ? row : 0;
-  const int hh = (int)(rr_ % p.G);
-  const int t_loc = (int)((rr_ / p.G) % p.CT);
-  const int c_rel = (int)(rr_ / ((int64_t)p.G * p.CT));
+  // token's G output heads are adjacent; every index fits 32 bits (the plan
+  // bounds the query rows below 2^31), so the divisions are 32-bit ones
+  const unsigned nrows = (unsigned)(p.c1 - p.c0) * (unsigned)p.CT * (unsigned)p.G;
+  const unsigned row = (blockIdx.x * 4u + (unsigned)w) * RPW + (unsigned)(lane / LPR);
+  const unsigned rr_ = row < nrows ? row : 0u;
+  const unsigned q_g = rr_ / (unsigned)p.G;
+  const int hh = (int)(rr_ - q_g * (unsigned)p.G);
+  const unsigned c_rel_u = q_g / (unsigned)p.CT;
+  const int t_loc = (int)(q_g - c_rel_u * (unsigned)p.CT);
+  const int c_rel = (int)c_rel_u;
   const int cid = p.c0 + c_rel;
-  const int bh = cid / p.NC;
-  const int t = (cid % p.NC) * p.CT + t_loc;
+  const int bh = (int)((unsigned)cid / (unsigned)p.NC);
+  const int t = (cid - bh * p.NC) * p.CT + t_loc;
   const bool ok = row < nrows && t < p.Lq;
-  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int b = (int)((unsigned)bh / (unsigned)p.Hkv), hk = bh - b * p.Hkv;
   const int h = hk * p.G + hh;
   const int rr = p.per_group ? hh : 0;
   const int64_t prow = ((int64_t)c_rel * p.Gs + (p.per_group ? 0 : hh)) * p.CT + t_loc;
@@ -891,6 +894,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     const int ncand = p.causal ? min((p.Lk - p.Lq + t) / p.block, p.Nb) : p.Nb;
     n = min(p.topk, ncand) + (p.causal ? 1 : 0);
   }
+  // the row's slot 0; slot s is s * R records further
+  const int64_t pidx0 = prow * p.kslot * p.R + rr;
+  const float2* ml0 = p.part_ml + pidx0;
+  const uint16_t* o0 = p.part_o + pidx0 * D + li * 8;
   // partial s holds q_s = 32767 * 2^-E_s * sum_k p_k v_k with p = 2^(score*sl2 - m_s), and
   // (m_s + E_s, 2^-E_s * sum_k p_k)
   float M = -INFINITY, W = 0.f;
@@ -906,12 +913,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
       ml[u] = make_float2(-INFINITY, 0.f);
       ov[u] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (s < n) {
-        const int64_t pidx = (prow * p.kslot + s) * p.R + rr;
         // streaming loads: every partial is read exactly once
         typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const f32x2 v2 = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(&p.part_ml[pidx]));
+        const f32x2 v2 = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(ml0 + s * p.R));
         ml[u] = make_float2(v2[0], v2[1]);
-        ov[u] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p.part_o + pidx * D + li * 8));
+        ov[u] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(o0 + (int64_t)(s * p.R) * D));
       }
     }
     float mb = M;

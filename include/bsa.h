@@ -142,7 +142,9 @@ size_t bsa_prefill_workspace_bytes(const bsa_prefill_args* a);
 /* Runs the whole prefill: [positions + RoPE] -> block summaries -> gate and
  * top-k -> selection inversion -> gathered attention -> combine.
  * Errors: BSA_ERR_INVALID_ARG / BSA_ERR_UNSUPPORTED for bad or unsupported
- * arguments, BSA_ERR_WORKSPACE if ws_bytes is below the query's answer,
+ * arguments (among the latter, 2^31 or more query rows -- B * Hq times Lq
+ * rounded up to whole query chunks -- or 2^30 or more (query chunk, block)
+ * buckets), BSA_ERR_WORKSPACE if ws_bytes is below the query's answer,
  * BSA_ERR_HIP if a launch fails. */
 bsa_status bsa_sparse_attn_prefill(const bsa_prefill_args* a, void* workspace, size_t ws_bytes, void* stream);
 

@@ -93,6 +93,23 @@ def test_prefill_rejects_bad_arguments(m, field, value, status):
     assert m.lib().bsa_last_error()
 
 
+def test_prefill_rejects_2_31_query_rows(m):
+    """B * Hq * Lq (in whole query chunks) must stay below 2^31: 64 query heads over 2^25 tokens
+    reach it.  Per-group gating keeps the selection entries (one row per kv head) under their own
+    bound, and a large block keeps the bucket count small, so this is the bound that applies."""
+    L = 1 << 25
+    a, _buf = _args(m, Lq=L, Lk=L, Hq=64, Hkv=8, block=1 << 20, topk=2, gate_mode=1)
+    a.q_stride = m.I64x3(L * 64 * 128, 64 * 128, 128)
+    a.k_stride = a.v_stride = m.I64x3(L * 8 * 128, 8 * 128, 128)
+    a.o_stride = a.q_stride
+    assert m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a)) == 0
+    assert m.lib().bsa_sparse_attn_prefill(ctypes.byref(a), None, 0, None) == m.BSA_ERR_UNSUPPORTED
+    assert b"query rows" in m.lib().bsa_last_error()
+    a.Hq = 32  # half the rows: planned
+    a.q_stride = a.o_stride = m.I64x3(L * 32 * 128, 32 * 128, 128)
+    assert m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a)) > 0
+
+
 def test_prefill_short_workspace(m):
     a, _buf = _args(m)
     need = m.lib().bsa_prefill_workspace_bytes(ctypes.byref(a))

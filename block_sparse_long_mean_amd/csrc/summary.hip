@@ -153,9 +153,18 @@ __global__ __launch_bounds__(256) void block_summary_kernel(SummaryParams p, int
   constexpr int HALF = D / 2;
   constexpr int SUB = 64;  // tokens per rotation table
   constexpr int UNR = 4;   // passes whose rows are loaded together
-  __shared__ float s_cos[ROPE ? SUB : 1][ROPE ? HALF : 1];
-  __shared__ float s_sin[ROPE ? SUB : 1][ROPE ? HALF : 1];
-  __shared__ float s_red[2 * E][256];
+  // the rotation table and the closing reduction share the LDS (a barrier
+  // separates the table's last read from the reduction's first write)
+  __shared__ union {
+    struct {
+      float cs[ROPE ? SUB : 1][ROPE ? HALF : 1];
+      float sn[ROPE ? SUB : 1][ROPE ? HALF : 1];
+    } tab;
+    float red[2 * E][256];
+  } s_mem;
+  auto& s_cos = s_mem.tab.cs;
+  auto& s_sin = s_mem.tab.sn;
+  auto& s_red = s_mem.red;
   const int U = hpw * UPH;
   const int TP = 256 / U;
   const int tid = threadIdx.x;
@@ -194,27 +203,31 @@ __global__ __launch_bounds__(256) void block_summary_kernel(SummaryParams p, int
     load_rows(s0, s0 + ns, lo, hi);
     if constexpr (ROPE) {
       __syncthreads();  // the previous sub-block's table is no longer read
-      // the rotation table, by one wave: lane i walks the sub-block's tokens
-      // for frequency i in double precision -- the first token's angle
-      // reduced and evaluated directly, every next one by a rotation through
-      // omega_i when its position is the previous one + 1 (exactly 1, 0 at a
-      // document start, directly again after any other jump) -- and rounds
-      // each (cos, sin) to fp32 once
-      if (tid < 64) {
-        // lane tt of wave 0 holds token tt's position (ns <= SUB = 64)
-        const int pl = tid < ns ? p.pos[(int64_t)b * p.L + t0 + s0 + tid] : 0;
-        if (tid < HALF) {
-          const int i = tid;
+      // the rotation table, 16 tokens per wave: lane i of wave w walks tokens
+      // 16w .. 16w + 15 of the sub-block for frequency i in double precision
+      // -- the first token's angle reduced and evaluated directly, every next
+      // one by a rotation through omega_i when its position is the previous
+      // one + 1 (exactly 1, 0 at a document start, directly again after any
+      // other jump) -- and rounds each (cos, sin) to fp32 once
+      {
+        constexpr int TPW = SUB / 4;
+        const int wv = tid >> 6, ln = tid & 63;
+        const int tb = wv * TPW;
+        // lane l of the wave holds token tb + l's position (l < TPW)
+        const int pl = (ln < TPW && tb + ln < ns) ? p.pos[(int64_t)b * p.L + t0 + s0 + tb + ln] : 0;
+        if (ln < HALF && tb < ns) {
+          const int te = min(tb + TPW, ns);
+          const int i = ln;
           const double om = p.omega[i];
           double sd, cd;
           sincos(om, &sd, &cd);
           double cv, sv;
           int prev = __builtin_amdgcn_readfirstlane(pl);
           rope_sincos_d(prev, om, cv, sv);
-          s_cos[0][i] = (float)cv;
-          s_sin[0][i] = (float)sv;
-          for (int tt = 1; tt < ns; ++tt) {
-            const int ps = __builtin_amdgcn_readlane(pl, tt);
+          s_cos[tb][i] = (float)cv;
+          s_sin[tb][i] = (float)sv;
+          for (int tt = tb + 1; tt < te; ++tt) {
+            const int ps = __builtin_amdgcn_readlane(pl, tt - tb);
             if (ps == prev + 1) {
               const double c2 = cv * cd - sv * sd;
               sv = fma(sv, cd, cv * sd);
@@ -271,6 +284,7 @@ __global__ __launch_bounds__(256) void block_summary_kernel(SummaryParams p, int
       }
     }
   }
+  if constexpr (ROPE) __syncthreads();  // every thread is done with the table
 #pragma unroll
   for (int e = 0; e < 2 * E; ++e) s_red[e][tid] = acc[e];
   __syncthreads();

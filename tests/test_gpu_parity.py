@@ -202,6 +202,28 @@ def test_block_summary_with_doc_rope(bsa):
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-7)
 
 
+@pytest.mark.parametrize("block,D,L", [(1, 128, 300), (40, 64, 1000), (100, 128, 1950), (64, 64, 2000)])
+def test_block_summary_doc_rope_block_sizes(bsa, block, D, L):
+    """Rotation tables of sub-blocks that leave some of the four table-building waves without
+    tokens (blocks of 1 and 40), two sub-blocks per block (100 = 64 + 36), a ragged last block,
+    and half-width frequency lanes (D 64); short documents so that many blocks restart a
+    document inside them."""
+    B, H = 2, 2
+    _say(f"case block_summary doc-rope block{block} D{D} L{L}")
+    k = synth.host_tensor((B, L, H, D), 1.0, 31, 1, "bf16")
+    ids = np.stack([synth.random_doc_ids(L, 90.0, 31 + b) for b in range(B)])
+    pooled, k_rot, pos = bsa.block_summary(k.cuda(), block, doc_ids=torch.from_numpy(ids).cuda(),
+                                           return_k_rot=True, return_pos=True)
+    torch.cuda.synchronize()
+    pos_ref = oracle.doc_positions(ids)
+    assert np.array_equal(pos.cpu().numpy(), pos_ref)
+    rot_ref = oracle.rope_rotate_half(k, pos_ref)
+    got = k_rot.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - rot_ref) <= np.abs(rot_ref) * 2.0 ** -8 + 1e-6)
+    pool_ref = oracle.block_pool(k, block, pos=pos_ref)
+    assert_close(pooled.cpu().numpy(), pool_ref, 2e-6, None, what="pooled")
+
+
 @pytest.mark.parametrize("gate", ["head", "group"])
 def test_decode_ragged_lengths(bsa, gate):
     B, Hq, Hkv, Lc, D, block, topk = 3, 8, 2, 5000, 128, 128, 8

@@ -91,6 +91,13 @@ def test_fp32_group_ragged(bsa):
                      gate="group", seed=1, atol=1e-5, rel=None, lse_atol=1e-5)
 
 
+def test_fp32_doc_rope_memory(bsa):
+    """fp32 inputs with document-wise RoPE: a 64-token query chunk over 4000 keys of short
+    documents, non-causal, top-4 per head (the fp32 rotation tables and summaries)."""
+    run_prefill_case(bsa, dtype="f32", B=1, Lq=64, Lk=4000, Hq=4, Hkv=2, D=64, block=64, topk=4, causal=False,
+                     seed=6, doc_mean=300.0, atol=1e-5, rel=None, lse_atol=1e-5)
+
+
 def test_bf16_per_head_moba_like(bsa):
     """GQA 8/2, D128, block 256, top-3 + own block, N(0,1)/sqrt(128), ragged length."""
     run_prefill_case(bsa, dtype="bf16", B=1, Lq=3000, Lk=3000, Hq=8, Hkv=2, D=128, block=256, topk=3, causal=True,
@@ -202,15 +209,16 @@ def test_block_summary_with_doc_rope(bsa):
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-7)
 
 
-@pytest.mark.parametrize("block,D,L", [(1, 128, 300), (40, 64, 1000), (100, 128, 1950), (64, 64, 2000)])
-def test_block_summary_doc_rope_block_sizes(bsa, block, D, L):
+@pytest.mark.parametrize("block,D,L,dtype", [(1, 128, 300, "bf16"), (40, 64, 1000, "bf16"), (100, 128, 1950, "bf16"),
+                                             (64, 64, 2000, "bf16"), (40, 64, 1000, "f32"), (100, 128, 1950, "f32")])
+def test_block_summary_doc_rope_block_sizes(bsa, block, D, L, dtype):
     """Rotation tables of sub-blocks that leave some of the four table-building waves without
     tokens (blocks of 1 and 40), two sub-blocks per block (100 = 64 + 36), a ragged last block,
-    and half-width frequency lanes (D 64); short documents so that many blocks restart a
-    document inside them."""
+    and half-width frequency lanes (D 64), for bf16 and fp32 keys; short documents so that many
+    blocks restart a document inside them."""
     B, H = 2, 2
-    _say(f"case block_summary doc-rope block{block} D{D} L{L}")
-    k = synth.host_tensor((B, L, H, D), 1.0, 31, 1, "bf16")
+    _say(f"case block_summary doc-rope block{block} D{D} L{L} {dtype}")
+    k = synth.host_tensor((B, L, H, D), 1.0, 31, 1, dtype)
     ids = np.stack([synth.random_doc_ids(L, 90.0, 31 + b) for b in range(B)])
     pooled, k_rot, pos = bsa.block_summary(k.cuda(), block, doc_ids=torch.from_numpy(ids).cuda(),
                                            return_k_rot=True, return_pos=True)
@@ -219,7 +227,10 @@ def test_block_summary_doc_rope_block_sizes(bsa, block, D, L):
     assert np.array_equal(pos.cpu().numpy(), pos_ref)
     rot_ref = oracle.rope_rotate_half(k, pos_ref)
     got = k_rot.float().cpu().numpy().astype(np.float64)
-    assert np.all(np.abs(got - rot_ref) <= np.abs(rot_ref) * 2.0 ** -8 + 1e-6)
+    if dtype == "bf16":  # bf16 storage: within half an ulp of the float64 value (plus fp32 rotation error)
+        assert np.all(np.abs(got - rot_ref) <= np.abs(rot_ref) * 2.0 ** -8 + 1e-6)
+    else:  # fp32 (cos, sin) and fp32 products: a few fp32 ulps of the pair's magnitude
+        assert np.all(np.abs(got - rot_ref) <= 1e-5)
     pool_ref = oracle.block_pool(k, block, pos=pos_ref)
     assert_close(pooled.cpu().numpy(), pool_ref, 2e-6, None, what="pooled")
 

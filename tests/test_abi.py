@@ -81,7 +81,7 @@ def _args(m, **kw):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("B", 0, 1), ("Hq", 3, 1), ("D", 96, 2), ("block", 0, 1), ("topk", -1, 1), ("topk", 65, 2),
+    ("B", 0, 1), ("Lq", 0, 1), ("Lk", 0, 1), ("Hkv", 0, 1), ("Hq", 3, 1), ("D", 96, 2), ("block", 0, 1), ("topk", -1, 1), ("topk", 65, 2),
     ("causal", 2, 1), ("gate_mode", 7, 1), ("dtype", 5, 1), ("chunk_tokens", -1, 1),
     ("chunks_per_pass", -2, 1),
 ])

@@ -56,6 +56,45 @@ BSA_DEV void lds_row_topk(const float* sc, int j0, int nc, uint64_t* buf, int* c
   }
   wave_sort_desc<1>(lm);
   const uint64_t tk = shfl64(lm[0], topk - 1);
+  const uint64_t thr0 = tk > 0ull ? tk - 1ull : 0ull;
+  // the keys above the threshold, placed in one pass: each lane's count, its
+  // place from a wave prefix sum formed bit by bit from ballots, then one
+  // compaction -- unless more than the buffer holds pass (only when the best
+  // keys crowd into few lanes), which takes the incremental path below
+  uint32_t hitm = 0u;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = u * 64 + lane;
+    const uint64_t key = i < nc ? make_key(sv[u], (uint32_t)(j0 + i)) : 0ull;
+    hitm |= (key > thr0 ? 1u : 0u) << u;
+  }
+  const int nh = __popc(hitm);
+  const uint64_t below = (1ull << lane) - 1ull;
+  int before = 0, total = 0;
+#pragma unroll
+  for (int bit = 0; (1 << bit) <= U; ++bit) {
+    const uint64_t mb = __ballot((nh >> bit) & 1);
+    before += __popcll(mb & below) << bit;
+    total += __popcll(mb) << bit;
+  }
+  if (total <= kDecCap) {
+    int e = before;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if ((hitm >> u) & 1u) {
+        buf[e] = make_key(sv[u], (uint32_t)(j0 + u * 64 + lane));
+        ++e;
+      }
+    }
+    if (lane == 0) {
+      *cnt = total;
+      *thr = thr0;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (total <= 64) row_compact<1>(buf, cnt, thr, topk);  // one key per lane: a shorter sort
+    else row_compact<V>(buf, cnt, thr, topk);
+    return;
+  }
   if (lane == 0 && tk > 0ull) *thr = tk - 1ull;
   __builtin_amdgcn_wave_barrier();
 #pragma unroll

@@ -318,17 +318,46 @@ __global__ __launch_bounds__(256) void decode_select_kernel(DecodeGateParams p) 
       s_thr[w] = 0ull;
     }
     __builtin_amdgcn_wave_barrier();
-    for (int sh = 0; sh < nsh; ++sh) {
-      const int64_t li = row * p.nshare + sh;
-      const int c = p.scnt[li];
-      if (s_cnt[w] + c > kDecCap) row_compact<2>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
-      const int base = s_cnt[w];
-      for (int e = lane; e < c; e += 64) s_buf[w][base + e] = p.skeys[li * p.topk + e];
+    if (nsh * p.topk <= kDecCap) {
+      // every share's list at once -- entry e of their concatenation is rank
+      // e % k of share e / k, loaded beside that share's count and kept when
+      // the rank is below it (a real key is never 0) -- then one sort
+      uint64_t v[2] = {0ull, 0ull};
+      if (nsh > 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int e = i * 64 + lane;
+          const int sh = e / p.topk, rk = e - sh * p.topk;
+          if (sh < nsh) {
+            const int64_t li = row * p.nshare + sh;
+            const uint64_t kk = p.skeys[li * p.topk + rk];
+            v[i] = rk < p.scnt[li] ? kk : 0ull;
+          }
+        }
+      }
+      const int nk = __popcll(__ballot(v[0] != 0ull)) + __popcll(__ballot(v[1] != 0ull));
+      wave_sort_desc<2>(v);
+      const int keep = nk < p.topk ? nk : p.topk;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int e = i * 64 + lane;
+        if (e < keep) s_buf[w][e] = v[i];
+      }
+      if (lane == 0) s_cnt[w] = keep;
       __builtin_amdgcn_wave_barrier();
-      if (lane == 0) s_cnt[w] = base + c;
-      __builtin_amdgcn_wave_barrier();
+    } else {
+      for (int sh = 0; sh < nsh; ++sh) {
+        const int64_t li = row * p.nshare + sh;
+        const int c = p.scnt[li];
+        if (s_cnt[w] + c > kDecCap) row_compact<2>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
+        const int base = s_cnt[w];
+        for (int e = lane; e < c; e += 64) s_buf[w][base + e] = p.skeys[li * p.topk + e];
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0) s_cnt[w] = base + c;
+        __builtin_amdgcn_wave_barrier();
+      }
+      row_compact<2>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
     }
-    row_compact<2>(s_buf[w], &s_cnt[w], &s_thr[w], p.topk);
     const int cnt = s_cnt[w];
     int idx = lane < cnt ? (int)key_index(s_buf[w][lane]) : 0x7FFFFFFF;
     idx = wave_sort_asc_i32(idx);

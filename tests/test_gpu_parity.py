@@ -261,6 +261,33 @@ def test_decode_ragged_lengths(bsa, gate):
     assert_close(to_np(lse), ref["lse"], 5e-3, None, what="lse")
 
 
+@pytest.mark.parametrize("topk", [32, 48])
+def test_decode_three_share_lists(bsa, topk):
+    """4375 candidate blocks, so that each head's candidates fall in three shares: their lists
+    hold 96 keys at top-32 (merged in one sort) and 144 at top-48 (merged list by list)."""
+    B, Hq, Hkv, Lc, D, block = 2, 4, 1, 70000, 64, 16
+    _say(f"case decode three shares B2 H4/1 Lc70000 D64 block16 topk{topk}")
+    q = synth.host_tensor((B, Hq, D), 1.0, 21, 0, "bf16")
+    k = synth.host_tensor((B, Lc, Hkv, D), 1.0, 21, 1, "bf16")
+    v = synth.host_tensor((B, Lc, Hkv, D), 1.0, 21, 2, "bf16")
+    lens = np.array([70000, 50001], dtype=np.int32)
+    pooled = torch.from_numpy(oracle.block_pool(k, block)).to(torch.bfloat16)
+    o, sel, lse = bsa.sparse_attn_decode(q.cuda(), k.cuda(), v.cuda(), pooled.cuda(), topk, block,
+                                         cache_lens=torch.from_numpy(lens).cuda(), return_sel=True, return_lse=True)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q, k, v, pooled, block=block, topk=topk, cache_lens=lens, return_scores=True)
+    nb = pooled.shape[1]
+    scores = np.full((B, Hq, 1, nb), np.nan)
+    for (b, hs), s in ref["scores"].items():
+        scores[b, hs, 0, : len(s)] = s
+    gsel = sel.cpu().numpy()[:, :, None]
+    diff = check_selection(gsel, ref["sel"][:, :, None], scores, topk, True)
+    if diff:
+        ref = oracle.decode(q, k, v, pooled, block=block, topk=topk, cache_lens=lens, force_sel=gsel[:, :, 0])
+    assert_close(to_np(o), ref["o"], 1e-2, 1e-2, bf16_storage=True)
+    assert_close(to_np(lse), ref["lse"], 5e-3, None, what="lse")
+
+
 def test_decode_topk60_group_of_8(bsa):
     """Eight query heads per KV head with top-60 each: 488 (head, block) pairs per group to unite."""
     B, Hq, Hkv, Lc, D, block, topk = 2, 16, 2, 20000, 128, 64, 60
